@@ -1,0 +1,382 @@
+// Time-domain backprojection kernels for gfx950 (CDNA4, wave64).
+//
+// Computes, for every pixel p of the grid and every pulse n,
+//   I(p) += interp(s_n, u) * exp(+j 4 pi R / lambda),  R = |p - a_n|,  u = (R - r0) / dr,
+// the coherent sum of the page "基于GPU的SAR后向投影成像优化与CUDA加速实践"
+// (GPU-based SAR backprojection): section 1.1 (per-pixel sum over pulses),
+// section 2.2 (pixel coordinates -> range -> interpolated sample -> phase
+// compensation and accumulation; nearest / linear / sinc interpolation;
+// hardware square root and trigonometry), section 2.3 (stage the echo block a
+// pixel tile touches in on-chip memory because every thread re-reads it).
+//
+// Design on gfx950 (not the page's one-thread-per-pixel CUDA kernel):
+//
+// * A workgroup of 4 wave64s owns a 64 (x) by 32 (y) pixel tile; each lane keeps
+//   8 pixels of one column (register blocking) and accumulates them in fp32
+//   registers across all pulses, so the image is written once.
+// * Pulses are processed in chunks.  For each pulse of a chunk one lane
+//   computes, in fp64, the tile-centre range R_t and derived fp32 constants;
+//   the pixels then need only the fp32 range *difference* to the tile centre,
+//      num = |d|^2 + 2 d.(c - a),   d = p - c,
+//      R - R_t = R_t (sqrt(1 + num / R_t^2) - 1)
+//   evaluated by its Taylor series in q = num / R_t^2 (2 or 3 terms, picked
+//   per chunk from a bound on the truncation error) or, when q is not small,
+//   by the exact form num / (R_t (1 + sqrt(1 + q))).  This keeps the bin
+//   position to ~1e-6 bins, which fp32 absolute ranges (~1e-3 m at 11 km)
+//   could not (section 2.2 warns about fp32 range precision).
+// * The echo window a tile can touch (the tile's range extent plus interpolator
+//   taps; bounded by the tile diagonal) is staged per pulse in LDS, already
+//   multiplied by the bin-centre carrier phase exp(+j 4 pi r_k / lambda).  For a
+//   pixel at u = k + f the remaining phase is exp(j 2 pi kappa f) with
+//   kappa = 2 dr / lambda, so one v_sin_f32 / v_cos_f32 pair (inputs in
+//   revolutions) on a bounded argument replaces a large-argument reduction.
+// * Linear interpolation stages (A, D) = (s[k] E[k], (s[k+1] - s[k]) E[k]) per
+//   bin so a sample is one ds_read_b128 and two FMAs.  Floor and fraction come
+//   from the 2^23 magic-number rounding, whose float bits also give the LDS
+//   address.
+// * Nearest interpolation rechecks lanes within tie_eps of a rounding tie in
+//   fp64, in the definition's operation order, so the chosen bin matches the
+//   double-precision definition exactly.
+// * Workgroups are remapped so each XCD (8 per GPU, round-robin dispatch) owns
+//   a contiguous band of tiles whose echo windows overlap in its L2.
+#include <math.h>
+
+#include "sarbp_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace {
+
+constexpr float kMagicFloor = 8388607.5f; // 2^23 - 1/2: ub + this rounds to 2^23 + floor(ub) for ub >= 1
+constexpr float kMagicRound = 8388608.0f; // 2^23: ub + this rounds ub to the nearest integer
+constexpr float kTwo23 = 8388608.0f;
+constexpr uint32_t kTwo23Bits = 0x4B000000u;
+
+// cos(pi m / 4) and sin(pi m / 4) for the sinc8 tap offsets m = -3 .. 4
+constexpr float kH = 0.70710678118654752f;
+__device__ constexpr float kCosQuarter[8] = {-kH, 0.f, kH, 1.f, kH, 0.f, -kH, -1.f};
+__device__ constexpr float kSinQuarter[8] = {-kH, -1.f, -kH, 0.f, kH, 1.f, kH, 0.f};
+
+template <int INTERP>
+__device__ constexpr int entry_bytes() {
+    return INTERP == SARBP_NEAREST ? 8 : 16;
+}
+
+// Per-pulse constants of the current tile, two float4 per pulse:
+//   c0 = (2 ux, 2 uy, ft, a)   c1 = (b, c, 1/R_t^2, 1/(R_t dr))
+// with u = c - a_n, ft = u_c - k_lo (fractional bin of the tile centre within
+// the window), a = 1/(2 R_t dr), b = -1/(8 R_t^3 dr), c = 1/(16 R_t^5 dr).
+// Returns the accuracy mode this pulse needs (0: 2 terms, 1: 3 terms, 2: exact).
+__device__ int pulse_setup(const BpArgs& A, int n, double cx, double cy, double cz, float4* cst, int* klo_out) {
+    const double ax = A.pos[3 * (size_t)n], ay = A.pos[3 * (size_t)n + 1], az = A.pos[3 * (size_t)n + 2];
+    const double ux = cx - ax, uy = cy - ay, uz = cz - az;
+    const double R2 = ux * ux + uy * uy + uz * uz;
+    const double Rt = sqrt(R2);
+    const double uc = (Rt - A.r0) * A.inv_dr;
+    const double klo_d = floor(uc - A.half_span_bins) - (double)A.margin_lo;
+    const bool ok = isfinite(Rt) && Rt > 0.0 && isfinite(uc) && fabs(klo_d) < 1.0e9;
+    if (!ok) {
+        // Non-finite geometry: park every pixel on window entry margin_lo and
+        // let the staging fill the window with NaN, so NaN propagates.
+        cst[0] = make_float4(0.f, 0.f, (float)A.margin_lo + 0.25f, 0.f);
+        cst[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        *klo_out = INT32_MIN;
+        return 0;
+    }
+    const double inv_r = 1.0 / Rt;
+    const double idr = A.inv_dr;
+    cst[0] = make_float4((float)(2.0 * ux), (float)(2.0 * uy), (float)(uc - klo_d), (float)(0.5 * inv_r * idr));
+    cst[1] = make_float4((float)(-0.125 * inv_r * inv_r * inv_r * idr),
+                         (float)(0.0625 * inv_r * inv_r * inv_r * inv_r * inv_r * idr), (float)(inv_r * inv_r),
+                         (float)(inv_r * idr));
+    *klo_out = (int)klo_d;
+    // Truncation error of the series for the worst pixel of the tile, in bins.
+    const double hs = A.half_span;
+    const double q = (hs * hs + 2.0 * hs * Rt) * inv_r * inv_r;
+    const double e2 = Rt * q * q * q * (1.0 / 16.0) * idr;
+    const double e3 = Rt * q * q * q * q * (5.0 / 128.0) * idr;
+    return (q > 0.25 || e3 > 1e-6) ? 2 : (e2 > 1e-6 ? 1 : 0);
+}
+
+// Bin position of a pixel within its pulse window: ub = ft + (R - R_t) / dr.
+template <int MODE>
+__device__ __forceinline__ float bin_position(float num, const float4& c0, const float4& c1) {
+    if constexpr (MODE == 0) {
+        return fmaf(num, fmaf(num, c1.x, c0.w), c0.z);
+    } else if constexpr (MODE == 1) {
+        return fmaf(num, fmaf(num, fmaf(num, c1.y, c1.x), c0.w), c0.z);
+    } else {
+        const float s = __builtin_amdgcn_sqrtf(fmaxf(fmaf(num, c1.z, 1.0f), 0.0f));
+        return fmaf(num * c1.w, __builtin_amdgcn_rcpf(1.0f + s), c0.z);
+    }
+}
+
+// Rotation of a complex sample by exp(j 2 pi x), x in revolutions (|x| < 256).
+__device__ __forceinline__ void sincos_rev(float x, float* s, float* c) {
+    *s = __builtin_amdgcn_sinf(x);
+    *c = __builtin_amdgcn_cosf(x);
+}
+
+// Exact nearest-bin decision for one pixel and pulse, in the definition's
+// double-precision operation order (no contraction): floor(u + 1/2).
+// Arguments by value so the rare call needs no stack.
+__device__ __attribute__((noinline)) int nearest_bin_fp64(double ax, double ay, double az, double x0, double y0,
+                                                          double z0, double dx, double dy, double r0, double dr,
+                                                          int i, int j) {
+    const double x = __dadd_rn(x0, __dmul_rn((double)i, dx));
+    const double y = __dadd_rn(y0, __dmul_rn((double)j, dy));
+    const double ddx = __dsub_rn(x, ax);
+    const double ddy = __dsub_rn(y, ay);
+    const double ddz = __dsub_rn(z0, az);
+    const double s2 = __dadd_rn(__dadd_rn(__dmul_rn(ddx, ddx), __dmul_rn(ddy, ddy)), __dmul_rn(ddz, ddz));
+    const double R = __dsqrt_rn(s2);
+    const double u = __ddiv_rn(__dsub_rn(R, r0), dr);
+    return (int)floor(__dadd_rn(u, 0.5));
+}
+
+template <int INTERP, int MODE>
+__device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* smem, const float4* cst,
+                                                 const int* klo_s, int np, int n0, int i_pix, int j_pix0,
+                                                 float dxl, const float* dyv, const float* ddv, float* accr,
+                                                 float* acci) {
+    const int eb = entry_bytes<INTERP>();
+    const uint32_t wstride = (uint32_t)(A.win * eb);
+    const float kappa = A.kappa;
+    for (int p = 0; p < np; ++p) {
+        const float4 c0 = cst[2 * p];
+        const float4 c1 = cst[2 * p + 1];
+        const float X = dxl * c0.x;
+        const uint32_t wbase = (uint32_t)p * wstride + A.addr_bias;
+#pragma unroll
+        for (int m = 0; m < BP_PPT; ++m) {
+            const float num = fmaf(dyv[m], c0.y, ddv[m] + X);
+            const float ub = bin_position<MODE>(num, c0, c1);
+            if constexpr (INTERP == SARBP_LINEAR) {
+                const float t = ub + kMagicFloor;
+                const float f = ub - (t - kTwo23);
+                const uint32_t addr = (__float_as_uint(t) << 4) + wbase;
+                const float4 ad = *reinterpret_cast<const float4*>(smem + addr);
+                const float vr = fmaf(f, ad.z, ad.x);
+                const float vi = fmaf(f, ad.w, ad.y);
+                float sn, cs;
+                sincos_rev(kappa * f, &sn, &cs);
+                accr[m] = fmaf(vr, cs, accr[m]);
+                accr[m] = fmaf(-vi, sn, accr[m]);
+                acci[m] = fmaf(vr, sn, acci[m]);
+                acci[m] = fmaf(vi, cs, acci[m]);
+            } else if constexpr (INTERP == SARBP_NEAREST) {
+                const float t = ub + kMagicRound;
+                float f = ub - (t - kTwo23);
+                uint32_t tb = __float_as_uint(t); // 2^23 bits + window entry
+                if (fabsf(f) > 0.5f - A.tie_eps) {
+                    // within tie_eps of a rounding tie: take the fp64 decision
+                    const size_t pn = 3 * (size_t)(n0 + p);
+                    const int kabs = nearest_bin_fp64(A.pos[pn], A.pos[pn + 1], A.pos[pn + 2], A.x0, A.y0, A.z0,
+                                                      A.dx, A.dy, A.r0, A.dr, i_pix, j_pix0 + BP_WAVES * m);
+                    int kr = kabs - klo_s[p];
+                    kr = kr < 0 ? 0 : (kr > A.win - 1 ? A.win - 1 : kr);
+                    tb = kTwo23Bits + (uint32_t)kr;
+                    f = ub - (float)kr;
+                }
+                const float2 sv = *reinterpret_cast<const float2*>(smem + ((tb << 3) + wbase));
+                float sn, cs;
+                sincos_rev(kappa * f, &sn, &cs);
+                accr[m] = fmaf(sv.x, cs, accr[m]);
+                accr[m] = fmaf(-sv.y, sn, accr[m]);
+                acci[m] = fmaf(sv.x, sn, acci[m]);
+                acci[m] = fmaf(sv.y, cs, acci[m]);
+            } else {
+                // 8-tap Hamming-windowed sinc around k = floor(ub), taps k-3 .. k+4
+                const float t = ub + kMagicFloor;
+                const float f = ub - (t - kTwo23);
+                const uint32_t addr = (__float_as_uint(t) << 4) + wbase - 3u * 16u;
+                const float4* e = reinterpret_cast<const float4*>(smem + addr);
+                const float sp = __builtin_amdgcn_sinf(0.5f * f);   // sin(pi f)
+                const float sq = __builtin_amdgcn_sinf(0.125f * f); // sin(pi f / 4)
+                const float cq = __builtin_amdgcn_cosf(0.125f * f); // cos(pi f / 4)
+                float vr = 0.f, vi = 0.f;
+#pragma unroll
+                for (int tp = 0; tp < 8; ++tp) {
+                    const int mo = tp - 3; // tap offset -3 .. 4
+                    const float tt = f - (float)mo;
+                    // sin(pi (f - mo)) = (-1)^mo sin(pi f)
+                    const float sgn_sp = (mo & 1) ? -sp : sp;
+                    const float pt = 3.14159265358979f * tt;
+                    const float sinc = fabsf(tt) < 1e-4f ? fmaf(-pt * pt, 1.0f / 6.0f, 1.0f)
+                                                         : sgn_sp * __builtin_amdgcn_rcpf(pt);
+                    // cos(pi (f - mo) / 4) = cos(pi f/4) cos(pi mo/4) + sin(pi f/4) sin(pi mo/4)
+                    const float cm = kCosQuarter[tp], sm = kSinQuarter[tp];
+                    const float w = sinc * fmaf(0.46f, fmaf(cq, cm, sq * sm), 0.54f);
+                    const float4 s = e[tp];
+                    vr = fmaf(w, s.x, vr);
+                    vi = fmaf(w, s.y, vi);
+                }
+                const float4 ec = e[3]; // carrier phase of bin k
+                float sn, cs;
+                sincos_rev(kappa * f, &sn, &cs);
+                const float pr = ec.z * cs - ec.w * sn;
+                const float pi_ = ec.z * sn + ec.w * cs;
+                accr[m] = fmaf(vr, pr, accr[m]);
+                accr[m] = fmaf(-vi, pi_, accr[m]);
+                acci[m] = fmaf(vr, pi_, acci[m]);
+                acci[m] = fmaf(vi, pr, acci[m]);
+            }
+        }
+    }
+}
+
+// Stage the echo windows of one chunk into LDS: wave w takes pulses w, w+4, ...;
+// lanes take consecutive bins (coalesced loads of the echo row).
+template <int INTERP>
+__device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int np, int n0, int wave, int lane) {
+    const int W = A.win, nr = A.n_range;
+    for (int p = wave; p < np; p += BP_WAVES) {
+        const int klo = klo_s[p];
+        const float2* row = A.echo + (size_t)(n0 + p) * (size_t)nr;
+        const bool bad = (klo == INT32_MIN);
+        for (int kk = lane; kk < W; kk += 64) {
+            const int k = klo + kk;
+            float2 s0 = make_float2(0.f, 0.f), s1 = make_float2(0.f, 0.f), e = make_float2(0.f, 0.f);
+            if (!bad) {
+                if (k >= 0 && k < nr) s0 = row[k];
+                if (k + 1 >= 0 && k + 1 < nr) s1 = row[k + 1];
+                if (k >= -1 && k <= nr) e = A.phase[k + 1];
+            }
+            if constexpr (INTERP == SARBP_LINEAR) {
+                float4 v;
+                v.x = s0.x * e.x - s0.y * e.y;
+                v.y = s0.x * e.y + s0.y * e.x;
+                const float drx = s1.x - s0.x, dry = s1.y - s0.y;
+                v.z = drx * e.x - dry * e.y;
+                v.w = drx * e.y + dry * e.x;
+                if (bad) v = make_float4(NAN, NAN, NAN, NAN);
+                reinterpret_cast<float4*>(smem)[p * W + kk] = v;
+            } else if constexpr (INTERP == SARBP_NEAREST) {
+                float2 v = make_float2(s0.x * e.x - s0.y * e.y, s0.x * e.y + s0.y * e.x);
+                if (bad) v = make_float2(NAN, NAN);
+                reinterpret_cast<float2*>(smem)[p * W + kk] = v;
+            } else {
+                float4 v = make_float4(s0.x, s0.y, e.x, e.y);
+                if (bad) v = make_float4(NAN, NAN, NAN, NAN);
+                reinterpret_cast<float4*>(smem)[p * W + kk] = v;
+            }
+        }
+    }
+}
+
+template <int INTERP>
+__global__ __launch_bounds__(BP_THREADS) void bp_kernel(BpArgs A) {
+    extern __shared__ __align__(16) char smem[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    // XCD-aware tile order: workgroup b runs on XCD (b mod 8); give each XCD a
+    // contiguous range of tiles (rows of tiles share echo bins in its L2).
+    int tile = blockIdx.x;
+    const int nt8 = (A.ntiles / 8) * 8;
+    if (tile < nt8) tile = (tile & 7) * (nt8 / 8) + (tile >> 3);
+    const int tx = tile % A.tiles_x, ty = tile / A.tiles_x;
+    const int i0 = tx * BP_TX, j0 = ty * BP_TY;
+
+    // tile centre (fp64) and this lane's pixel offsets from it
+    const double cxp = (double)i0 + 0.5 * (BP_TX - 1), cyp = (double)j0 + 0.5 * (BP_TY - 1);
+    const double cx = A.x0 + cxp * A.dx, cy = A.y0 + cyp * A.dy, cz = A.z0;
+    const double ddx = ((double)lane - 0.5 * (BP_TX - 1)) * A.dx;
+    const float dxl = (float)ddx;
+    float dyv[BP_PPT], ddv[BP_PPT], accr[BP_PPT], acci[BP_PPT];
+#pragma unroll
+    for (int m = 0; m < BP_PPT; ++m) {
+        const double ddy = ((double)(wave + BP_WAVES * m) - 0.5 * (BP_TY - 1)) * A.dy;
+        dyv[m] = (float)ddy;
+        ddv[m] = (float)(ddx * ddx + ddy * ddy);
+        accr[m] = 0.f;
+        acci[m] = 0.f;
+    }
+
+    const int P = A.chunk, W = A.win;
+    float4* cst = reinterpret_cast<float4*>(smem + (size_t)P * W * entry_bytes<INTERP>());
+    int* klo_s = reinterpret_cast<int*>(cst + 2 * P);
+
+    for (int n0 = 0; n0 < A.n; n0 += P) {
+        const int np = min(P, A.n - n0);
+        int need = 0;
+        if (tid < np) need = pulse_setup(A, n0 + tid, cx, cy, cz, cst + 2 * tid, klo_s + tid);
+        const int m1 = __syncthreads_or(need & 1);
+        const int m2 = __syncthreads_or(need & 2);
+        stage_chunk<INTERP>(A, smem, klo_s, np, n0, wave, lane);
+        __syncthreads();
+        if (m2)
+            accumulate_chunk<INTERP, 2>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv, accr, acci);
+        else if (m1)
+            accumulate_chunk<INTERP, 1>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv, accr, acci);
+        else
+            accumulate_chunk<INTERP, 0>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv, accr, acci);
+        __syncthreads();
+    }
+
+    const int i = i0 + lane;
+    if (i < A.nx) {
+#pragma unroll
+        for (int m = 0; m < BP_PPT; ++m) {
+            const int j = j0 + wave + BP_WAVES * m;
+            if (j < A.ny) {
+                float2* o = A.image + (size_t)j * A.nx + i;
+                if (A.accumulate) {
+                    const float2 old = *o;
+                    *o = make_float2(old.x + accr[m], old.y + acci[m]);
+                } else {
+                    *o = make_float2(accr[m], acci[m]);
+                }
+            }
+        }
+    }
+}
+
+} // namespace
+
+int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* echo, float2* image, int n,
+                    int accumulate, hipStream_t stream) {
+    const sarbp_params& p = plan->p;
+    BpArgs A;
+    A.pos = pos;
+    A.echo = echo;
+    A.image = image;
+    A.phase = plan->phase_tab;
+    A.n = n;
+    A.n_range = p.n_range;
+    A.nx = p.nx;
+    A.ny = p.ny;
+    A.tiles_x = plan->tiles_x;
+    A.ntiles = plan->tiles_x * plan->tiles_y;
+    A.win = plan->win;
+    A.margin_lo = plan->margin_lo;
+    A.chunk = plan->chunk;
+    A.accumulate = accumulate;
+    A.r0 = p.r0;
+    A.dr = p.dr;
+    A.inv_dr = 1.0 / p.dr;
+    A.x0 = p.x0;
+    A.y0 = p.y0;
+    A.z0 = p.z0;
+    A.dx = p.dx;
+    A.dy = p.dy;
+    A.half_span = plan->half_span;
+    A.half_span_bins = plan->half_span / p.dr;
+    A.kappa = (float)(2.0 * p.dr / p.wavelength);
+    A.tie_eps = 4e-5f;
+    // (float bits of 2^23 + k) << log2(entry bytes) wraps to k * entry bytes
+    // once this bias is added (mod 2^32)
+    A.addr_bias = p.interp == SARBP_NEAREST ? (uint32_t)0u - (0x4B000000u << 3) : (uint32_t)0u - (0x4B000000u << 4);
+    const dim3 grid(A.ntiles), block(BP_THREADS);
+    switch (p.interp) {
+        case SARBP_NEAREST:
+            hipLaunchKernelGGL(bp_kernel<SARBP_NEAREST>, grid, block, plan->lds_bytes, stream, A);
+            break;
+        case SARBP_LINEAR:
+            hipLaunchKernelGGL(bp_kernel<SARBP_LINEAR>, grid, block, plan->lds_bytes, stream, A);
+            break;
+        default:
+            hipLaunchKernelGGL(bp_kernel<SARBP_SINC8>, grid, block, plan->lds_bytes, stream, A);
+            break;
+    }
+    return hipGetLastError() == hipSuccess ? SARBP_OK : SARBP_EDEVICE;
+}

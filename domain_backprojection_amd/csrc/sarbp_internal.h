@@ -1,0 +1,58 @@
+// Internal declarations shared by the host side of the sarbp library.
+// Not installed; the public interface is include/sarbp.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sarbp.h"
+
+// Backprojection tiling (see sarbp_bp.hip): a workgroup of BP_WAVES wave64s
+// owns a tile of BP_TX (along x) by BP_WAVES * BP_PPT (along y) pixels; each
+// lane keeps BP_PPT pixels of one column in registers.
+#define BP_TX 64
+#define BP_WAVES 4
+#define BP_PPT 8
+#define BP_TY (BP_WAVES * BP_PPT)
+#define BP_THREADS (64 * BP_WAVES)
+#define BP_MAX_CHUNK 64           // pulses staged in LDS per step
+#define BP_LDS_BUDGET (52 * 1024) // bytes per workgroup: three workgroups per CU
+
+struct sarbp_plan {
+    sarbp_params p;
+    int device;
+    // exp(+j 4 pi (r0 + k dr) / lambda) for k = -1 .. n_range, stored at [k + 1]
+    float2* phase_tab;
+    // backprojection launch geometry
+    int tiles_x, tiles_y;
+    int win;          // LDS window entries per pulse
+    int margin_lo;    // bins below the tile's lowest range kept in the window
+    int chunk;        // pulses per LDS step
+    size_t lds_bytes; // dynamic LDS per workgroup
+    double half_span; // half tile diagonal [m]
+    // range compression
+    int rc_log2;       // log2(n_fast), 0 when disabled
+    float2* rc_filter; // conj(FFT(ref)) * W / n_fast
+    float2* rc_twiddle;// exp(-2 pi i t / n_fast), t in [0, n_fast)
+};
+
+// Argument block of the backprojection kernels (passed by value).
+struct BpArgs {
+    const double* pos;     // [n][3]
+    const float2* echo;    // [n][n_range]
+    float2* image;         // [ny][nx]
+    const float2* phase;   // phase_tab
+    int n, n_range, nx, ny;
+    int tiles_x, ntiles;
+    int win, margin_lo, chunk, accumulate;
+    double r0, dr, inv_dr, x0, y0, z0, dx, dy;
+    double half_span;      // half tile diagonal [m]
+    double half_span_bins; // half_span / dr
+    float kappa;           // 2 dr / lambda: phase cycles per bin
+    float tie_eps;         // nearest: fp64 recheck band around a rounding tie [bins]
+    uint32_t addr_bias;    // LDS address bias that cancels the 2^23 exponent bits
+};
+
+int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* echo, float2* image,
+                    int n, int accumulate, hipStream_t stream);
+int sarbp_launch_rc(const sarbp_plan* plan, const float2* raw, float2* out, int n, hipStream_t stream);

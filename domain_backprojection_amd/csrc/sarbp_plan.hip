@@ -1,0 +1,231 @@
+// Host side of the sarbp C ABI: argument validation, plan creation (read-only
+// device tables), dispatch and status strings.  See include/sarbp.h.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <complex>
+#include <new>
+#include <vector>
+
+#include "sarbp_internal.h"
+
+int sarbp_rc_prepare_device();
+
+namespace {
+
+constexpr double kPi = 3.14159265358979323846;
+
+bool finite_pos(double v) { return isfinite(v) && v > 0.0; }
+
+bool aligned8(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+
+// In-place iterative radix-2 FFT (forward, exp(-2 pi i n k / N)) in double
+// precision, used once at plan creation for the matched filter's spectrum.
+void fft_host(std::vector<std::complex<double>>& a) {
+    const size_t n = a.size();
+    for (size_t i = 1, j = 0; i < n; ++i) {
+        size_t bit = n >> 1;
+        for (; j & bit; bit >>= 1) j ^= bit;
+        j ^= bit;
+        if (i < j) std::swap(a[i], a[j]);
+    }
+    for (size_t len = 2; len <= n; len <<= 1) {
+        for (size_t i = 0; i < n; i += len) {
+            for (size_t k = 0; k < len / 2; ++k) {
+                const double ang = -2.0 * kPi * (double)k / (double)len;
+                const std::complex<double> w(cos(ang), sin(ang));
+                const std::complex<double> u = a[i + k], v = a[i + k + len / 2] * w;
+                a[i + k] = u + v;
+                a[i + k + len / 2] = u - v;
+            }
+        }
+    }
+}
+
+int validate(const sarbp_params* p) {
+    if (p == nullptr) return SARBP_EINVAL;
+    if (p->n_pulses < 1 || p->nx < 1 || p->ny < 1) return SARBP_EINVAL;
+    if (p->interp < SARBP_NEAREST || p->interp > SARBP_SINC8) return SARBP_EINVAL;
+    if (p->n_range < (p->interp == SARBP_SINC8 ? 8 : 2)) return SARBP_EINVAL;
+    if (!isfinite(p->r0) || !finite_pos(p->dr) || !finite_pos(p->dx) || !finite_pos(p->dy)) return SARBP_EINVAL;
+    if (!isfinite(p->x0) || !isfinite(p->y0) || !isfinite(p->z0) || !finite_pos(p->wavelength)) return SARBP_EINVAL;
+    if ((int64_t)p->nx * p->ny > (int64_t)1 << 40) return SARBP_EINVAL;
+    if (p->n_fast != 0) {
+        if (p->n_fast < 64 || p->n_fast > 16384 || (p->n_fast & (p->n_fast - 1)) != 0) return SARBP_EINVAL;
+        if (!finite_pos(p->fs) || !finite_pos(p->chirp_T) || !finite_pos(p->chirp_B)) return SARBP_EINVAL;
+        const double L = floor(p->chirp_T * p->fs + 0.5);
+        if (L < 1.0 || L > (double)p->n_fast) return SARBP_EINVAL;
+        if (p->window != 0 && p->window != 1) return SARBP_EINVAL;
+    }
+    return SARBP_OK;
+}
+
+template <typename T>
+int upload(const std::vector<T>& host, T** dev) {
+    *dev = nullptr;
+    if (hipMalloc(reinterpret_cast<void**>(dev), host.size() * sizeof(T)) != hipSuccess) {
+        *dev = nullptr;
+        return SARBP_ENOMEM;
+    }
+    if (hipMemcpy(*dev, host.data(), host.size() * sizeof(T), hipMemcpyHostToDevice) != hipSuccess) return SARBP_EDEVICE;
+    return SARBP_OK;
+}
+
+void release(sarbp_plan* plan) {
+    if (plan == nullptr) return;
+    int cur = -1;
+    const bool switch_dev = hipGetDevice(&cur) == hipSuccess && cur != plan->device;
+    if (switch_dev) (void)hipSetDevice(plan->device);
+    if (plan->phase_tab) (void)hipFree(plan->phase_tab);
+    if (plan->rc_filter) (void)hipFree(plan->rc_filter);
+    if (plan->rc_twiddle) (void)hipFree(plan->rc_twiddle);
+    if (switch_dev) (void)hipSetDevice(cur);
+    delete plan;
+}
+
+// Carrier phase of each range bin: exp(+j 4 pi (r0 + k dr) / lambda) at [k + 1],
+// k = -1 .. n_range, reduced modulo one cycle in double precision.
+std::vector<float2> phase_table(const sarbp_params& p) {
+    std::vector<float2> t((size_t)p.n_range + 2);
+    for (int64_t k = -1; k <= p.n_range; ++k) {
+        const double cyc = 2.0 * (p.r0 + (double)k * p.dr) / p.wavelength;
+        const double fr = cyc - floor(cyc);
+        t[(size_t)(k + 1)] = make_float2((float)cos(2.0 * kPi * fr), (float)sin(2.0 * kPi * fr));
+    }
+    return t;
+}
+
+} // namespace
+
+extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
+    if (out == nullptr) return SARBP_EINVAL;
+    *out = nullptr;
+    int st = validate(params);
+    if (st != SARBP_OK) return st;
+    sarbp_plan* plan = new (std::nothrow) sarbp_plan();
+    if (plan == nullptr) return SARBP_ENOMEM;
+    memset(plan, 0, sizeof(*plan));
+    plan->p = *params;
+    const sarbp_params& p = plan->p;
+    if (hipGetDevice(&plan->device) != hipSuccess) {
+        delete plan;
+        return SARBP_EDEVICE;
+    }
+
+    // Backprojection tiling and LDS window size.  Every pixel of a tile lies
+    // within half_span of the tile centre, so (triangle inequality) its range
+    // lies within R_t +- half_span and its bin within the window below.
+    plan->tiles_x = (p.nx + BP_TX - 1) / BP_TX;
+    plan->tiles_y = (p.ny + BP_TY - 1) / BP_TY;
+    if ((int64_t)plan->tiles_x * plan->tiles_y > INT32_MAX) {
+        release(plan);
+        return SARBP_EINVAL;
+    }
+    plan->half_span = 0.5 * sqrt((BP_TX * p.dx) * (BP_TX * p.dx) + (BP_TY * p.dy) * (BP_TY * p.dy));
+    const double span_bins = ceil(2.0 * plan->half_span / p.dr);
+    const int taps_hi = p.interp == SARBP_SINC8 ? 4 : 1;
+    plan->margin_lo = p.interp == SARBP_SINC8 ? 5 : 2;
+    if (span_bins > 1.0e6) {
+        release(plan);
+        return SARBP_EUNSUPPORTED;
+    }
+    plan->win = (int)span_bins + plan->margin_lo + 2 + taps_hi;
+    const int eb = p.interp == SARBP_NEAREST ? 8 : 16;
+    const int per_pulse = plan->win * eb + 2 * 16 + 4;
+    int chunk = (BP_LDS_BUDGET - 64) / per_pulse;
+    if (chunk > BP_MAX_CHUNK) chunk = BP_MAX_CHUNK;
+    if (chunk < 1) {
+        release(plan);
+        return SARBP_EUNSUPPORTED;
+    }
+    plan->chunk = chunk;
+    plan->lds_bytes = (size_t)chunk * per_pulse;
+
+    st = upload(phase_table(p), &plan->phase_tab);
+    if (st != SARBP_OK) {
+        release(plan);
+        return st;
+    }
+
+    if (p.n_fast != 0) {
+        const int N = p.n_fast;
+        int lg = 0;
+        while ((1 << lg) < N) ++lg;
+        plan->rc_log2 = lg;
+        // reference chirp: ref[m mod N] = exp(j pi K t^2), t = m / fs, m = -L/2 .. L - L/2 - 1
+        const int L = (int)floor(p.chirp_T * p.fs + 0.5);
+        const double K = p.chirp_B / p.chirp_T;
+        std::vector<std::complex<double>> ref((size_t)N, 0.0);
+        for (int m = -(L / 2); m < L - L / 2; ++m) {
+            const double t = (double)m / p.fs;
+            const double ph = kPi * K * t * t;
+            ref[(size_t)((m % N + N) % N)] = std::complex<double>(cos(ph), sin(ph));
+        }
+        fft_host(ref);
+        std::vector<float2> filt((size_t)N), tw((size_t)N);
+        for (int m = 0; m < N; ++m) {
+            const double f = (m < N / 2 ? (double)m : (double)(m - N)) * p.fs / (double)N; // fftfreq
+            double w = 1.0;
+            if (p.window == 1) w = fabs(f) <= 0.5 * p.chirp_B ? 0.54 + 0.46 * cos(2.0 * kPi * f / p.chirp_B) : 0.0;
+            const std::complex<double> h = std::conj(ref[(size_t)m]) * (w / (double)N);
+            filt[(size_t)m] = make_float2((float)h.real(), (float)h.imag());
+            const double a = -2.0 * kPi * (double)m / (double)N;
+            tw[(size_t)m] = make_float2((float)cos(a), (float)sin(a));
+        }
+        st = upload(filt, &plan->rc_filter);
+        if (st == SARBP_OK) st = upload(tw, &plan->rc_twiddle);
+        if (st == SARBP_OK) st = sarbp_rc_prepare_device();
+        if (st != SARBP_OK) {
+            release(plan);
+            return st;
+        }
+    }
+    *out = plan;
+    return SARBP_OK;
+}
+
+namespace {
+int check_device(const sarbp_plan* plan) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return SARBP_EDEVICE;
+    return cur == plan->device ? SARBP_OK : SARBP_EINVAL;
+}
+} // namespace
+
+extern "C" int sarbp_backproject(const sarbp_plan* plan, const double* positions_d, const void* echo_d, void* image_d,
+                                 int32_t n, int32_t accumulate, void* stream) {
+    if (plan == nullptr || !aligned8(positions_d) || !aligned8(echo_d) || !aligned8(image_d)) return SARBP_EINVAL;
+    if (n < 1 || n > plan->p.n_pulses || (accumulate != 0 && accumulate != 1)) return SARBP_EINVAL;
+    const int st = check_device(plan);
+    if (st != SARBP_OK) return st;
+    return sarbp_launch_bp(plan, positions_d, static_cast<const float2*>(echo_d), static_cast<float2*>(image_d), n,
+                           accumulate, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int sarbp_range_compress(const sarbp_plan* plan, const void* raw_d, void* out_d, int32_t n, void* stream) {
+    if (plan == nullptr || plan->p.n_fast == 0 || !aligned8(raw_d) || !aligned8(out_d) || n < 1) return SARBP_EINVAL;
+    const uintptr_t bytes = (uintptr_t)n * (uintptr_t)plan->p.n_fast * sizeof(float2);
+    const uintptr_t a = reinterpret_cast<uintptr_t>(raw_d), b = reinterpret_cast<uintptr_t>(out_d);
+    if (a < b + bytes && b < a + bytes) return SARBP_EINVAL; // overlapping buffers
+    const int st = check_device(plan);
+    if (st != SARBP_OK) return st;
+    return sarbp_launch_rc(plan, static_cast<const float2*>(raw_d), static_cast<float2*>(out_d), n,
+                           static_cast<hipStream_t>(stream));
+}
+
+extern "C" void sarbp_destroy(sarbp_plan* plan) { release(plan); }
+
+extern "C" const char* sarbp_status_string(int status) {
+    switch (status) {
+        case SARBP_OK: return "success";
+        case SARBP_EINVAL: return "invalid argument";
+        case SARBP_ENOMEM: return "out of memory";
+        case SARBP_EDEVICE: return "HIP runtime or kernel launch failure";
+        case SARBP_EUNSUPPORTED: return "unsupported configuration";
+        default: return "unknown status";
+    }
+}
+
+extern "C" int sarbp_version(void) { return 100; }

@@ -1,0 +1,215 @@
+"""ctypes binding of the sarbp C ABI (include/sarbp.h).
+
+Argument marshalling only: tensors become device pointers and the current
+torch stream becomes the hipStream_t.  Every step of the computation runs in
+the HIP library ``libsarbp.so`` built in this directory; importing this module
+raises if that library is missing -- there is no fallback.
+
+The functions keep the C names: :func:`sarbp_plan_create`,
+:func:`sarbp_backproject`, :func:`sarbp_range_compress`, :func:`sarbp_destroy`,
+:func:`sarbp_status_string`, :func:`sarbp_version`.  :class:`Plan` wraps a plan
+handle's lifetime.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsarbp.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m domain_backprojection_amd.build` "
+        "(hipcc, gfx950). There is no CPU fallback.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+SARBP_OK = 0
+SARBP_EINVAL = -1
+SARBP_ENOMEM = -2
+SARBP_EDEVICE = -3
+SARBP_EUNSUPPORTED = -4
+
+SARBP_NEAREST = 0
+SARBP_LINEAR = 1
+SARBP_SINC8 = 2
+INTERP = {"nearest": SARBP_NEAREST, "linear": SARBP_LINEAR, "sinc8": SARBP_SINC8}
+
+
+class sarbp_params(ctypes.Structure):
+    """Mirror of ``sarbp_params`` (same field order and C alignment)."""
+
+    _fields_ = [
+        ("n_pulses", ctypes.c_int32),
+        ("n_range", ctypes.c_int32),
+        ("r0", ctypes.c_double),
+        ("dr", ctypes.c_double),
+        ("nx", ctypes.c_int32),
+        ("ny", ctypes.c_int32),
+        ("x0", ctypes.c_double),
+        ("y0", ctypes.c_double),
+        ("z0", ctypes.c_double),
+        ("dx", ctypes.c_double),
+        ("dy", ctypes.c_double),
+        ("wavelength", ctypes.c_double),
+        ("interp", ctypes.c_int32),
+        ("n_fast", ctypes.c_int32),
+        ("fs", ctypes.c_double),
+        ("chirp_T", ctypes.c_double),
+        ("chirp_B", ctypes.c_double),
+        ("window", ctypes.c_int32),
+    ]
+
+
+_vp = ctypes.c_void_p
+_lib.sarbp_plan_create.argtypes = [ctypes.POINTER(sarbp_params), ctypes.POINTER(_vp)]
+_lib.sarbp_plan_create.restype = ctypes.c_int
+_lib.sarbp_backproject.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp]
+_lib.sarbp_backproject.restype = ctypes.c_int
+_lib.sarbp_range_compress.argtypes = [_vp, _vp, _vp, ctypes.c_int32, _vp]
+_lib.sarbp_range_compress.restype = ctypes.c_int
+_lib.sarbp_destroy.argtypes = [_vp]
+_lib.sarbp_destroy.restype = None
+_lib.sarbp_status_string.argtypes = [ctypes.c_int]
+_lib.sarbp_status_string.restype = ctypes.c_char_p
+_lib.sarbp_version.argtypes = []
+_lib.sarbp_version.restype = ctypes.c_int
+
+EXPORTS = ("sarbp_plan_create", "sarbp_backproject", "sarbp_range_compress", "sarbp_destroy",
+           "sarbp_status_string", "sarbp_version")
+
+
+class SarbpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {sarbp_status_string(status)} ({status})")
+        self.status = status
+
+
+def sarbp_status_string(status: int) -> str:
+    return _lib.sarbp_status_string(int(status)).decode()
+
+
+def sarbp_version() -> int:
+    return int(_lib.sarbp_version())
+
+
+def make_params(n_pulses, n_range, r0, dr, nx, ny, x0, y0, z0, dx, dy, wavelength, interp="linear",
+                n_fast=0, fs=0.0, chirp_T=0.0, chirp_B=0.0, window=0) -> sarbp_params:
+    return sarbp_params(int(n_pulses), int(n_range), float(r0), float(dr), int(nx), int(ny), float(x0),
+                        float(y0), float(z0), float(dx), float(dy), float(wavelength),
+                        INTERP[interp] if isinstance(interp, str) else int(interp), int(n_fast), float(fs),
+                        float(chirp_T), float(chirp_B), int(window))
+
+
+def sarbp_plan_create(params: sarbp_params) -> int:
+    """Create a plan on the current device; returns the opaque handle (an int)."""
+    h = _vp()
+    st = _lib.sarbp_plan_create(ctypes.byref(params), ctypes.byref(h))
+    if st != SARBP_OK:
+        raise SarbpError(st, "sarbp_plan_create")
+    return h.value
+
+
+def sarbp_destroy(handle) -> None:
+    _lib.sarbp_destroy(handle)
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev_ptr(t: torch.Tensor, dtype, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def sarbp_backproject(handle, positions: torch.Tensor, echo: torch.Tensor, image: torch.Tensor,
+                      n: int | None = None, accumulate: int = 0, stream=None) -> None:
+    """positions float64 (n, 3), echo complex64 (n, n_range), image complex64 (ny, nx), all on the device."""
+    if n is None:
+        n = positions.shape[0]
+    if positions.dim() != 2 or positions.shape[1] != 3 or positions.shape[0] < n or echo.shape[0] < n:
+        raise ValueError("positions must be (>= n, 3) and echo (>= n, n_range)")
+    st = _lib.sarbp_backproject(handle, _dev_ptr(positions, torch.float64, "positions"),
+                                _dev_ptr(echo, torch.complex64, "echo"), _dev_ptr(image, torch.complex64, "image"),
+                                int(n), int(accumulate), _stream(stream))
+    if st != SARBP_OK:
+        raise SarbpError(st, "sarbp_backproject")
+
+
+def sarbp_range_compress(handle, raw: torch.Tensor, out: torch.Tensor, n: int | None = None, stream=None) -> None:
+    """raw and out complex64 (n, n_fast) on the device."""
+    if n is None:
+        n = raw.shape[0]
+    if raw.shape[0] < n or out.shape[0] < n:
+        raise ValueError("raw and out must hold n pulses")
+    st = _lib.sarbp_range_compress(handle, _dev_ptr(raw, torch.complex64, "raw"),
+                                   _dev_ptr(out, torch.complex64, "out"), int(n), _stream(stream))
+    if st != SARBP_OK:
+        raise SarbpError(st, "sarbp_range_compress")
+
+
+class Plan:
+    """Owns one plan handle; checks tensor shapes against the plan's sizes."""
+
+    def __init__(self, **kw):
+        self.params = make_params(**kw)
+        self.handle = sarbp_plan_create(self.params)
+
+    @classmethod
+    def for_scene(cls, scene, n_fast=None, **over):
+        kw = dict(scene.params())
+        kw.update(over)
+        if n_fast:
+            kw.update(n_fast=n_fast, fs=scene.fs, chirp_T=scene.chirp_T, chirp_B=scene.chirp_B, window=scene.window)
+        return cls(**kw)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            sarbp_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def new_image(self, device="cuda") -> torch.Tensor:
+        return torch.zeros((self.params.ny, self.params.nx), dtype=torch.complex64, device=device)
+
+    def backproject(self, positions, echo, image=None, n=None, accumulate=0, stream=None) -> torch.Tensor:
+        if image is None:
+            image = torch.empty((self.params.ny, self.params.nx), dtype=torch.complex64, device=echo.device)
+        if tuple(image.shape) != (self.params.ny, self.params.nx):
+            raise ValueError("image shape does not match the plan")
+        if echo.dim() != 2 or echo.shape[1] != self.params.n_range:
+            raise ValueError("echo must be (n, n_range)")
+        sarbp_backproject(self.handle, positions, echo, image, n=n, accumulate=accumulate, stream=stream)
+        return image
+
+    def range_compress(self, raw, out=None, n=None, stream=None) -> torch.Tensor:
+        if out is None:
+            out = torch.empty_like(raw)
+        if raw.dim() != 2 or raw.shape[1] != self.params.n_fast:
+            raise ValueError("raw must be (n, n_fast)")
+        sarbp_range_compress(self.handle, raw, out, n=n, stream=stream)
+        return out

@@ -1,0 +1,121 @@
+/*
+ * sarbp.h -- time-domain SAR backprojection on AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one of the page "基于GPU的SAR后向投影成像优化与CUDA加速实践"
+ * (GPU-based SAR backprojection imaging and CUDA acceleration):
+ *
+ *   I(x, y) = sum over pulses n of  interp(s_n, R_n(x, y)) * exp(+j 4 pi R_n / lambda)
+ *
+ * (section 1.1 for the coherent sum over pulses at each pixel's range history;
+ * section 2.2 for the four per-pulse steps and the interpolation choices;
+ * section 3.3 for the argument list: antenna X/Y/Z per pulse, the
+ * range-compressed complex matrix indexed [pulse * n_range + bin], the range
+ * axis r0 and dr, the pixel grid x = x0 + i dx, y = y0 + j dy, and the image
+ * indexed [j * nx + i]; section 4.2 for the carrier wavelength in the phase).
+ * Range compression (section 3.1) is an FFT matched filter with an optional
+ * Hamming window, batched over pulses.
+ *
+ * Conventions shared by every entry point:
+ *   - Complex data are complex64: interleaved (re, im) float pairs.
+ *   - Device pointers are caller-owned device memory on the plan's device;
+ *     the library never frees or retains them.  Every pointer must be 8-byte
+ *     aligned.  Array contents are not inspected: NaN in gives NaN out.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  Argument checks are synchronous and return SARBP_EINVAL
+ *     before anything is enqueued; a failed launch returns SARBP_EDEVICE.
+ *   - A plan is immutable after creation and owns only read-only device
+ *     tables, so calls with one plan on different streams may run
+ *     concurrently.  Calls that write the same image must be ordered by the
+ *     caller.  No entry point allocates device memory except
+ *     sarbp_plan_create.
+ */
+#ifndef SARBP_H
+#define SARBP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SARBP_OK 0
+#define SARBP_EINVAL (-1)       /* an argument is out of range, null or misaligned */
+#define SARBP_ENOMEM (-2)       /* a device or host allocation failed (plan creation only) */
+#define SARBP_EDEVICE (-3)      /* a HIP runtime call or kernel launch failed */
+#define SARBP_EUNSUPPORTED (-4) /* valid request this build cannot serve (e.g. LDS too small) */
+
+/* Interpolation of the range-compressed echo at a fractional bin u (section 2.2):
+ *   NEAREST: s[floor(u + 1/2)]
+ *   LINEAR : (1 - f) s[k] + f s[k + 1],  k = floor(u), f = u - k
+ *   SINC8  : sum_{m=-3..4} s[k + m] h(f - m),
+ *            h(t) = sinc(t) (0.54 + 0.46 cos(pi t / 4)) for |t| < 4
+ * Samples outside [0, n_range - 1] are zero. */
+typedef enum { SARBP_NEAREST = 0, SARBP_LINEAR = 1, SARBP_SINC8 = 2 } sarbp_interp;
+
+/* Plan parameters.  Lengths in metres, frequencies in Hz, times in seconds. */
+typedef struct {
+    int32_t n_pulses;   /* Na: the most pulses one sarbp_backproject call may take (>= 1)      */
+    int32_t n_range;    /* Nr: bins per range-compressed pulse (>= 2; >= 8 for SINC8)           */
+    double r0;          /* range of bin 0                                                       */
+    double dr;          /* bin spacing (> 0): bin k lies at r0 + k * dr                         */
+    int32_t nx, ny;     /* image size (>= 1 each); image[j * nx + i]                           */
+    double x0, y0, z0;  /* centre of pixel (0, 0); every pixel lies in the plane z = z0          */
+    double dx, dy;      /* pixel spacing (> 0): pixel (i, j) centre = (x0 + i dx, y0 + j dy, z0) */
+    double wavelength;  /* carrier wavelength lambda (> 0) of the phase term exp(+j 4 pi R / lambda) */
+    int32_t interp;     /* sarbp_interp                                                         */
+    /* Range compression (sarbp_range_compress); n_fast = 0 disables it. */
+    int32_t n_fast;     /* samples per raw pulse = FFT length: a power of two in [64, 16384]    */
+    double fs;          /* fast-time sampling rate (> 0)                                        */
+    double chirp_T;     /* LFM pulse length (> 0); round(chirp_T * fs) samples, <= n_fast      */
+    double chirp_B;     /* LFM bandwidth (> 0), up-chirp exp(j pi (B/T) t^2), -T/2 <= t < T/2   */
+    int32_t window;     /* 0: none; 1: Hamming 0.54 + 0.46 cos(2 pi f / B) over |f| <= B/2     */
+} sarbp_params;
+
+typedef struct sarbp_plan sarbp_plan; /* opaque */
+
+/* Validate `params`, build the plan's read-only device tables on the current
+ * HIP device and return the plan in *out (set to NULL on failure).
+ * Returns SARBP_EINVAL for invalid parameters, SARBP_ENOMEM if an allocation
+ * fails, SARBP_EDEVICE if the HIP runtime fails. */
+int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out);
+
+/* Backproject n pulses into the image (sections 1.1, 2.2 and 3.3 of the page).
+ *   positions_d : device, float64 [n][3] antenna phase centres (x, y, z)
+ *   echo_d      : device, complex64 [n][n_range] range-compressed echo, bin fastest
+ *   image_d     : device, complex64 [ny][nx], x fastest; written (accumulate = 0)
+ *                 or added to (accumulate = 1)
+ *   n           : pulses in this call, 1 <= n <= plan n_pulses
+ * Because the sum is linear in the echo, a long aperture can be streamed in
+ * pulse chunks with accumulate = 1.  Returns SARBP_EINVAL (null plan or
+ * pointer, misalignment, n out of range, accumulate not 0/1, or the current
+ * device is not the plan's), SARBP_EDEVICE on a launch failure. */
+int sarbp_backproject(const sarbp_plan* plan, const double* positions_d, const void* echo_d,
+                      void* image_d, int32_t n, int32_t accumulate, void* stream);
+
+/* Range-compress n raw pulses (section 3.1 of the page):
+ *   out_n = IFFT( FFT(raw_n) * conj(FFT(ref)) * W ) with 1/n_fast on the inverse,
+ *   ref[m mod n_fast] = p(m / fs), m = -L/2 .. L/2 - 1, L = round(chirp_T * fs).
+ *   raw_d : device, complex64 [n][n_fast]
+ *   out_d : device, complex64 [n][n_fast]; must not overlap raw_d
+ * Output bin k corresponds to the range of raw sample k.  Returns
+ * SARBP_EINVAL (as above, or the plan has n_fast = 0, or the buffers
+ * overlap), SARBP_EDEVICE on a launch failure. */
+int sarbp_range_compress(const sarbp_plan* plan, const void* raw_d, void* out_d, int32_t n,
+                         void* stream);
+
+/* Release the plan and its device tables.  NULL is a no-op.  The caller must
+ * ensure no call using the plan is still running. */
+void sarbp_destroy(sarbp_plan* plan);
+
+/* Static description of a status code (never NULL). */
+const char* sarbp_status_string(int status);
+
+/* Library version as 10000 * major + 100 * minor + patch. */
+int sarbp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SARBP_H */

@@ -1,0 +1,54 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI and
+compare with the CPU oracle under the acceptance bar.
+
+Acceptance bar (floating point, from the workload statement):
+  * rel-L2 = ||I_gpu - I_oracle|| / ||I_oracle|| <= 2e-3 over the compared pixels
+  * every target's strongest pixel in a +-ceil(rho_az/dx) x +-ceil(rho_rg/dy) window
+    around its true pixel is the same pixel in both images
+  * | 20 log10(|I_gpu| / |I_oracle|) | <= 0.05 dB at that pixel
+Integer decisions (nearest bin) must match exactly.
+"""
+import math
+
+import numpy as np
+
+REL_L2 = 2e-3
+PEAK_DB = 0.05
+
+
+def rel_l2(got, want):
+    return float(np.linalg.norm(got - want) / np.linalg.norm(want))
+
+
+def target_windows(scene):
+    """(K, list of (i, j) arrays) pixel windows around each target, clipped to the grid."""
+    import synth
+
+    rho_az, rho_rg = synth.resolution(scene)
+    hx = max(1, math.ceil(rho_az / scene.dx))
+    hy = max(1, math.ceil(rho_rg / scene.dy))
+    wins = []
+    for (i, j) in scene.targets:
+        ii, jj = np.meshgrid(np.arange(i - hx, i + hx + 1), np.arange(j - hy, j + hy + 1), indexing="xy")
+        ok = (ii >= 0) & (ii < scene.nx) & (jj >= 0) & (jj < scene.ny)
+        wins.append(np.stack([ii[ok], jj[ok]], 1))
+    return wins
+
+
+def check_peaks(got_at, want_at, wins):
+    """got_at / want_at: callables mapping an (P, 2) pixel array to complex values."""
+    for w in wins:
+        g = got_at(w)
+        o = want_at(w)
+        kg, ko = int(np.argmax(np.abs(g))), int(np.argmax(np.abs(o)))
+        assert kg == ko, f"peak moved: gpu {w[kg]} oracle {w[ko]}"
+        db = 20 * math.log10(abs(g[kg]) / abs(o[ko]))
+        assert abs(db) <= PEAK_DB, f"peak magnitude differs by {db:.4f} dB at {w[ko]}"
+
+
+def sample_pixels(scene, count, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    i = rng.integers(0, scene.nx, count)
+    j = rng.integers(0, scene.ny, count)
+    edge = np.array([[0, 0], [scene.nx - 1, 0], [0, scene.ny - 1], [scene.nx - 1, scene.ny - 1]])
+    return np.concatenate([np.stack([i, j], 1), edge])

@@ -1,0 +1,246 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on seeded inputs."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from _parity import PEAK_DB, REL_L2, check_peaks, rel_l2, sample_pixels, target_windows
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sb(gpu_device):
+    from domain_backprojection_amd import sarbp
+
+    return sarbp
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _run_bp(sb, scene, echo=None, positions=None, interp=None, **over):
+    import torch
+
+    e = scene.echo if echo is None else echo
+    p = scene.positions if positions is None else positions
+    kw = dict(over)
+    if interp is not None:
+        kw["interp"] = interp
+    with sb.Plan.for_scene(scene, **kw) as plan:
+        pos = torch.from_numpy(np.ascontiguousarray(p)).cuda()
+        ech = torch.from_numpy(np.ascontiguousarray(e, dtype=np.complex64)).cuda()
+        img = plan.backproject(pos, ech)
+        torch.cuda.synchronize()
+        return img.cpu().numpy().astype(np.complex128)
+
+
+# ----------------------------------------------------------------------------- small, full image
+
+@pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
+def test_tiny_config_full_image(sb, interp):
+    s = synth.make_scene(1, interp=interp)
+    _say(f"[tiny {interp}] {s.nx}x{s.ny} na={s.na}")
+    got = _run_bp(sb, s)
+    want = oracle.scene_backproject(s)
+    assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
+    check_peaks(lambda w: got[w[:, 1], w[:, 0]], lambda w: want[w[:, 1], w[:, 0]], target_windows(s))
+
+
+@pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
+@pytest.mark.parametrize("shape", [(150, 70, 100), (64, 32, 64), (1, 1, 1), (65, 33, 129)])
+def test_ragged_tiles_and_chunks(sb, interp, shape):
+    """Grids that are not multiples of the 64x32 tile, pulse counts that are not
+    multiples of the LDS chunk, perturbed track, clutter."""
+    nx, ny, na = shape
+    s = synth.make_scene(4, na=na, nr=1024, nx=nx, ny=ny, interp=interp, n_targets=1)
+    _say(f"[ragged {interp}] {nx}x{ny} na={na}")
+    got = _run_bp(sb, s)
+    want = oracle.scene_backproject(s)
+    assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
+
+
+def test_accumulate_over_pulse_chunks(sb):
+    """image = BP(first half) then += BP(second half) equals one call over all pulses."""
+    import torch
+
+    s = synth.make_scene(2, na=300, nr=1024, nx=96, ny=80)
+    with sb.Plan.for_scene(s) as plan:
+        pos = torch.from_numpy(s.positions).cuda()
+        ech = torch.from_numpy(s.echo).cuda()
+        full = plan.backproject(pos, ech)
+        part = plan.backproject(pos[:170], ech[:170])
+        plan.backproject(pos[170:].contiguous(), ech[170:].contiguous(), image=part, accumulate=1)
+        torch.cuda.synchronize()
+        a, b = full.cpu().numpy(), part.cpu().numpy()
+    assert np.linalg.norm(a - b) / np.linalg.norm(a) < 1e-5
+
+
+@pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
+def test_linearity_and_pulse_order(sb, interp):
+    s = synth.make_scene(4, na=200, nr=1024, nx=80, ny=64, interp=interp)
+    rng = np.random.Generator(np.random.PCG64(12))
+    s2 = (rng.standard_normal(s.echo.shape) + 1j * rng.standard_normal(s.echo.shape)).astype(np.complex64)
+    a, b = np.complex64(0.75 - 0.5j), np.complex64(-1.25 + 0.25j)
+    lhs = _run_bp(sb, s, echo=(a * s.echo + b * s2).astype(np.complex64))
+    rhs = a * _run_bp(sb, s) + b * _run_bp(sb, s, echo=s2)
+    assert np.linalg.norm(lhs - rhs) / np.linalg.norm(rhs) < 1e-5
+    perm = rng.permutation(s.na)
+    c = _run_bp(sb, s, echo=s.echo[perm], positions=s.positions[perm])
+    d = _run_bp(sb, s)
+    assert np.linalg.norm(c - d) / np.linalg.norm(d) < 1e-5
+
+
+def test_zero_extension_and_far_pixels(sb):
+    """A short record that only part of the grid's ranges fall into: samples beyond
+    the record contribute zero, as in the oracle."""
+    s = synth.make_scene(1, na=40, nx=96, ny=96, interp="linear")
+    nr = 48
+    r0 = s.r0 + (s.nr // 2 - 10) * s.dr  # the record covers only the near half of the scene
+    sh = synth.Scene(**{**s.__dict__, "nr": nr, "r0": r0, "echo": np.ascontiguousarray(s.echo[:, 246:246 + nr])})
+    got = _run_bp(sb, sh)
+    want = oracle.scene_backproject(sh)
+    assert np.count_nonzero(np.abs(want) == 0) > 0
+    assert rel_l2(got, want) <= REL_L2
+    assert np.max(np.abs(got[np.abs(want) == 0])) == 0.0
+
+
+def test_nonfinite_positions_propagate_nan(sb):
+    s = synth.make_scene(1, na=16, nx=64, ny=32)
+    pos = s.positions.copy()
+    pos[5, 0] = np.nan
+    got = _run_bp(sb, s, positions=pos)
+    assert np.isnan(got).all()
+
+
+# ----------------------------------------------------------------------------- nearest: bit-exact index
+
+def _index_probe(sb, scene, pulses):
+    """One pulse per call with echo s[k] = k + 1: |I| - 1 is the bin the GPU chose."""
+    import torch
+
+    ramp = torch.arange(1, scene.nr + 1, dtype=torch.float32).to(torch.complex64).cuda()[None, :].contiguous()
+    ii, jj = np.meshgrid(np.arange(scene.nx), np.arange(scene.ny), indexing="xy")
+    ij = np.stack([ii.ravel(), jj.ravel()], 1)
+    mismatches = 0
+    with sb.Plan.for_scene(scene, interp="nearest", n_pulses=1) as plan:
+        img = plan.new_image()
+        for n in pulses:
+            pos = torch.from_numpy(scene.positions[n:n + 1].copy()).cuda()
+            plan.backproject(pos, ramp, image=img)
+            mag = img.abs().cpu().numpy().ravel().astype(np.float64)
+            k_gpu = np.rint(mag) - 1
+            assert np.max(np.abs(mag - np.rint(mag))) < 0.02
+            k_orc = oracle.nearest_index(scene.positions[n], scene.r0, scene.dr, scene.x0, scene.y0, scene.z0,
+                                         scene.dx, scene.dy, ij)
+            mismatches += int(np.count_nonzero(k_gpu != k_orc))
+    return mismatches
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_nearest_index_bit_exact(sb, cfg):
+    """>= 64 evenly spaced pulses plus the first and last of each geometry, every pixel."""
+    spec = synth.CONFIGS[cfg]
+    # geometry only: the echo is replaced by the index probe
+    s = synth.make_scene(cfg, nr=spec["nr"], na=spec["na"], clutter=False, n_targets=1) if cfg == 1 else None
+    if s is None:
+        rng = np.random.Generator(np.random.PCG64(1000 + cfg))
+        na = spec["na"]
+        pos = synth.track(na, rng, perturbed=spec["track"] == "perturbed")
+        nx, ny, nr = spec["nx"], spec["ny"], spec["nr"]
+        s = synth.Scene(cfg=cfg, name=spec["name"], seed=1000 + cfg, na=na, nr=nr, nx=nx, ny=ny,
+                        x0=-(nx // 2) * synth.PIXEL, y0=-(ny // 2) * synth.PIXEL, z0=0.0, dx=synth.PIXEL,
+                        dy=synth.PIXEL, r0=synth.RC_CENTRE - (nr // 2) * synth.DR, dr=synth.DR,
+                        wavelength=synth.WAVELENGTH, interp="nearest", positions=pos, echo=None, raw=None,
+                        targets=np.zeros((0, 2), np.int64))
+    pulses = sorted(set(np.linspace(0, s.na - 1, 64).astype(int).tolist()) | {0, s.na - 1})
+    _say(f"[index probe cfg {cfg}] {len(pulses)} pulses x {s.nx * s.ny} pixels")
+    assert _index_probe(sb, s, pulses) == 0
+
+
+# ----------------------------------------------------------------------------- range compression
+
+def test_range_compression_matches_oracle(sb):
+    import torch
+
+    s = synth.make_scene(5, na=64)
+    with sb.Plan.for_scene(s, n_fast=s.nr) as plan:
+        out = plan.range_compress(torch.from_numpy(s.raw).cuda())
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.complex128)
+    want = oracle.rc.range_compress(s.raw, s.fs, s.chirp_T, s.chirp_B, s.window)
+    assert rel_l2(got, want) < 1e-5, rel_l2(got, want)
+
+
+@pytest.mark.parametrize("n_fast", [64, 128, 512, 1024, 2048, 4096, 16384])
+@pytest.mark.parametrize("window", [0, 1])
+def test_range_compression_sizes(sb, n_fast, window):
+    import torch
+
+    rng = np.random.Generator(np.random.PCG64(n_fast + window))
+    x = (rng.standard_normal((5, n_fast)) + 1j * rng.standard_normal((5, n_fast))).astype(np.complex64)
+    T = min(synth.CHIRP_T, 0.5 * n_fast / synth.FS)
+    with sb.Plan(n_pulses=1, n_range=n_fast, r0=0.0, dr=1.0, nx=1, ny=1, x0=0, y0=0, z0=0, dx=1, dy=1,
+                 wavelength=0.03, interp="linear", n_fast=n_fast, fs=synth.FS, chirp_T=T,
+                 chirp_B=synth.BANDWIDTH, window=window) as plan:
+        out = plan.range_compress(torch.from_numpy(x).cuda())
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.complex128)
+    want = oracle.rc.range_compress(x, synth.FS, T, synth.BANDWIDTH, window)
+    assert rel_l2(got, want) < 1e-5
+
+
+# ----------------------------------------------------------------------------- full-size configs, sampled
+
+@pytest.mark.parametrize("cfg", [2, 4, 3])
+def test_full_size_sampled(sb, cfg):
+    import time
+
+    t = time.time()
+    s = synth.make_scene(cfg)
+    _say(f"[full cfg {cfg}] generated {s.na}x{s.nr} echo, {s.nx}x{s.ny} grid in {time.time() - t:.1f}s")
+    import torch
+
+    with sb.Plan.for_scene(s) as plan:
+        img = plan.backproject(torch.from_numpy(s.positions).cuda(), torch.from_numpy(s.echo).cuda())
+        torch.cuda.synchronize()
+        got = img.cpu().numpy()
+    wins = target_windows(s)
+    ij = np.concatenate([sample_pixels(s, 1500, 77 + cfg)] + wins)
+    want = oracle.scene_pixels(s, ij)
+    g = got[ij[:, 1], ij[:, 0]].astype(np.complex128)
+    assert rel_l2(g, want) <= REL_L2, rel_l2(g, want)
+    lut = {tuple(p): v for p, v in zip(ij.tolist(), want)}
+    check_peaks(lambda w: got[w[:, 1], w[:, 0]], lambda w: np.array([lut[tuple(p)] for p in w.tolist()]), wins)
+    _say(f"[full cfg {cfg}] rel-L2 {rel_l2(g, want):.2e} on {len(ij)} pixels")
+
+
+def test_end_to_end_sampled(sb):
+    """Raw LFM echoes -> GPU range compression -> GPU backprojection, against the fp64
+    oracle chain (numpy matched filter, then the C oracle on sampled pixels)."""
+    import torch
+
+    s = synth.make_scene(5)
+    _say(f"[e2e] raw {s.na}x{s.nr}")
+    with sb.Plan.for_scene(s, n_fast=s.nr) as plan:
+        raw = torch.from_numpy(s.raw).cuda()
+        rc = plan.range_compress(raw)
+        img = plan.backproject(torch.from_numpy(s.positions).cuda(), rc)
+        torch.cuda.synchronize()
+        rc_gpu = rc.cpu().numpy()
+        got = img.cpu().numpy()
+    rc_orc = oracle.rc.range_compress(s.raw, s.fs, s.chirp_T, s.chirp_B, s.window)
+    assert rel_l2(rc_gpu.astype(np.complex128), rc_orc) < 1e-5
+    wins = target_windows(s)
+    ij = np.concatenate([sample_pixels(s, 1000, 55)] + wins)
+    want = oracle.backproject_pixels(s.positions, rc_orc, s.r0, s.dr, s.x0, s.y0, s.z0, s.dx, s.dy,
+                                     s.wavelength, s.interp, ij)
+    g = got[ij[:, 1], ij[:, 0]].astype(np.complex128)
+    assert rel_l2(g, want) <= REL_L2, rel_l2(g, want)
+    lut = {tuple(p): v for p, v in zip(ij.tolist(), want)}
+    check_peaks(lambda w: got[w[:, 1], w[:, 0]], lambda w: np.array([lut[tuple(p)] for p in w.tolist()]), wins)

@@ -118,6 +118,27 @@ def aux_end_to_end(sb, steps, warmup):
             "e2e_G_updates_per_s": s.updates / e2e_ms / 1e6}
 
 
+def aux_interpolators(sb, steps, warmup):
+    """Nearest on the standard geometry and sinc8 on the hi-fi (perturbed-track) scene."""
+    import torch
+
+    import synth
+
+    out = {}
+    for cfg, interp in ((2, "nearest"), (4, "sinc8")):
+        s = synth.make_scene(cfg, interp=interp)
+        with sb.Plan.for_scene(s) as plan:
+            pos = torch.from_numpy(s.positions).cuda()
+            echo = torch.from_numpy(s.echo).cuda()
+            img = plan.new_image()
+            ms, _ = time_launches(lambda: plan.backproject(pos, echo, image=img), steps, warmup)
+        upd = s.updates / (ms * 1e-3)
+        out[interp] = {"scene": s.name, "ms": ms, "G_updates_per_s": upd / 1e9,
+                       "TFLOPs_algorithmic": FLOPS_PER_UPDATE[interp] * upd / 1e12,
+                       "frac_fp32_peak": FLOPS_PER_UPDATE[interp] * upd / 1e12 / PEAK_FP32_TFLOPS}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +146,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-aux", action="store_true", help="skip the end-to-end (range compression) figures")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run a plain elementwise copy of MIB MiB (read once, write once) three times, "
+                         "to scale HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -148,6 +172,13 @@ def main():
         torch.cuda.synchronize()
         ms, wall = time_launches(lambda: plan.backproject(pos, echo, image=img), args.steps, args.warmup)
     log(f"bench: {args.steps} launches, {ms:.3f} ms per launch (HIP events), wall {wall:.3f} s")
+    if args.calibrate_copy:
+        a = torch.ones(args.calibrate_copy * 2**20 // 4, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        log(f"bench: copy calibration, {args.calibrate_copy} MiB read + {args.calibrate_copy} MiB written per launch")
 
     value = s.updates / (ms * 1e-3) / 1e9
     achieved = FLOPS_PER_UPDATE[s.interp] * s.updates / (ms * 1e-3) / 1e12
@@ -172,6 +203,7 @@ def main():
     }
     if not args.no_aux:
         line["aux"] = aux_end_to_end(sarbp, max(5, args.steps // 2), args.warmup)
+        line["aux"]["interpolators"] = aux_interpolators(sarbp, max(5, args.steps // 2), args.warmup)
         log(f"bench: end-to-end {line['aux']}")
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(s)

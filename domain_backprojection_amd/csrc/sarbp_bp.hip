@@ -11,9 +11,9 @@
 //
 // Design on gfx950 (not the page's one-thread-per-pixel CUDA kernel):
 //
-// * A workgroup of 4 wave64s owns a 64 (x) by 32 (y) pixel tile; each lane keeps
-//   8 pixels of one column (register blocking) and accumulates them in fp32
-//   registers across all pulses, so the image is written once.
+// * A workgroup of 16 wave64s owns a 64 (x) by 32 (y) pixel tile; each lane
+//   keeps 2 pixels of one column (register blocking) and accumulates them in
+//   fp32 registers across all pulses, so the image is written once.
 // * Pulses are processed in chunks.  For each pulse of a chunk one lane
 //   computes, in fp64, the tile-centre range R_t and derived fp32 constants;
 //   the pixels then need only the fp32 range *difference* to the tile centre,
@@ -31,9 +31,9 @@
 //   kappa = 2 dr / lambda, so one v_sin_f32 / v_cos_f32 pair (inputs in
 //   revolutions) on a bounded argument replaces a large-argument reduction.
 // * Linear interpolation stages (A, D) = (s[k] E[k], (s[k+1] - s[k]) E[k]) per
-//   bin so a sample is one ds_read_b128 and two FMAs.  Floor and fraction come
-//   from the 2^23 magic-number rounding, whose float bits also give the LDS
-//   address.
+//   bin so a sample is one ds_read_b128 and two FMAs.  The window position ub
+//   is positive by construction, so v_cvt_u32_f32 (truncation) is its floor and
+//   v_fract_f32 its fraction; one shift-add turns the floor into the LDS address.
 // * Nearest interpolation rechecks lanes within tie_eps of a rounding tie in
 //   fp64, in the definition's operation order, so the chosen bin matches the
 //   double-precision definition exactly.
@@ -47,10 +47,6 @@
 
 namespace {
 
-constexpr float kMagicFloor = 8388607.5f; // 2^23 - 1/2: ub + this rounds to 2^23 + floor(ub) for ub >= 1
-constexpr float kMagicRound = 8388608.0f; // 2^23: ub + this rounds ub to the nearest integer
-constexpr float kTwo23 = 8388608.0f;
-constexpr uint32_t kTwo23Bits = 0x4B000000u;
 
 // cos(pi m / 4) and sin(pi m / 4) for the sinc8 tap offsets m = -3 .. 4
 constexpr float kH = 0.70710678118654752f;
@@ -85,7 +81,9 @@ __device__ int pulse_setup(const BpArgs& A, int n, double cx, double cy, double 
     }
     const double inv_r = 1.0 / Rt;
     const double idr = A.inv_dr;
-    cst[0] = make_float4((float)(2.0 * ux), (float)(2.0 * uy), (float)(uc - klo_d), (float)(0.5 * inv_r * idr));
+    // nearest rounds u: the +1/2 is folded into the window position
+    const double ft = uc - klo_d + (A.round_half ? 0.5 : 0.0);
+    cst[0] = make_float4((float)(2.0 * ux), (float)(2.0 * uy), (float)ft, (float)(0.5 * inv_r * idr));
     cst[1] = make_float4((float)(-0.125 * inv_r * inv_r * inv_r * idr),
                          (float)(0.0625 * inv_r * inv_r * inv_r * inv_r * inv_r * idr), (float)(inv_r * inv_r),
                          (float)(inv_r * idr));
@@ -142,19 +140,19 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
     const int eb = entry_bytes<INTERP>();
     const uint32_t wstride = (uint32_t)(A.win * eb);
     const float kappa = A.kappa;
+#pragma unroll BP_PUNROLL
     for (int p = 0; p < np; ++p) {
         const float4 c0 = cst[2 * p];
         const float4 c1 = cst[2 * p + 1];
         const float X = dxl * c0.x;
-        const uint32_t wbase = (uint32_t)p * wstride + A.addr_bias;
+        const uint32_t wbase = (uint32_t)p * wstride;
 #pragma unroll
         for (int m = 0; m < BP_PPT; ++m) {
             const float num = fmaf(dyv[m], c0.y, ddv[m] + X);
             const float ub = bin_position<MODE>(num, c0, c1);
             if constexpr (INTERP == SARBP_LINEAR) {
-                const float t = ub + kMagicFloor;
-                const float f = ub - (t - kTwo23);
-                const uint32_t addr = (__float_as_uint(t) << 4) + wbase;
+                const float f = __builtin_amdgcn_fractf(ub);
+                const uint32_t addr = ((uint32_t)ub << 4) + wbase;
                 const float4 ad = *reinterpret_cast<const float4*>(smem + addr);
                 const float vr = fmaf(f, ad.z, ad.x);
                 const float vi = fmaf(f, ad.w, ad.y);
@@ -165,31 +163,31 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
                 acci[m] = fmaf(vr, sn, acci[m]);
                 acci[m] = fmaf(vi, cs, acci[m]);
             } else if constexpr (INTERP == SARBP_NEAREST) {
-                const float t = ub + kMagicRound;
-                float f = ub - (t - kTwo23);
-                uint32_t tb = __float_as_uint(t); // 2^23 bits + window entry
-                if (fabsf(f) > 0.5f - A.tie_eps) {
+                // ub carries u + 1/2: its floor is the nearest bin, g - 1/2 = u - bin
+                float g = __builtin_amdgcn_fractf(ub);
+                uint32_t kb = (uint32_t)ub;
+                if (fabsf(g - 0.5f) > 0.5f - A.tie_eps) {
                     // within tie_eps of a rounding tie: take the fp64 decision
                     const size_t pn = 3 * (size_t)(n0 + p);
                     const int kabs = nearest_bin_fp64(A.pos[pn], A.pos[pn + 1], A.pos[pn + 2], A.x0, A.y0, A.z0,
                                                       A.dx, A.dy, A.r0, A.dr, i_pix, j_pix0 + BP_WAVES * m);
                     int kr = kabs - klo_s[p];
                     kr = kr < 0 ? 0 : (kr > A.win - 1 ? A.win - 1 : kr);
-                    tb = kTwo23Bits + (uint32_t)kr;
-                    f = ub - (float)kr;
+                    kb = (uint32_t)kr;
+                    g = ub - (float)kr;
                 }
-                const float2 sv = *reinterpret_cast<const float2*>(smem + ((tb << 3) + wbase));
+                // the staged sample carries exp(-j pi kappa), so exp(j 2 pi kappa g) completes the phase
+                const float2 sv = *reinterpret_cast<const float2*>(smem + ((kb << 3) + wbase));
                 float sn, cs;
-                sincos_rev(kappa * f, &sn, &cs);
+                sincos_rev(kappa * g, &sn, &cs);
                 accr[m] = fmaf(sv.x, cs, accr[m]);
                 accr[m] = fmaf(-sv.y, sn, accr[m]);
                 acci[m] = fmaf(sv.x, sn, acci[m]);
                 acci[m] = fmaf(sv.y, cs, acci[m]);
             } else {
                 // 8-tap Hamming-windowed sinc around k = floor(ub), taps k-3 .. k+4
-                const float t = ub + kMagicFloor;
-                const float f = ub - (t - kTwo23);
-                const uint32_t addr = (__float_as_uint(t) << 4) + wbase - 3u * 16u;
+                const float f = __builtin_amdgcn_fractf(ub);
+                const uint32_t addr = ((uint32_t)ub << 4) + wbase - 3u * 16u;
                 const float4* e = reinterpret_cast<const float4*>(smem + addr);
                 const float sp = __builtin_amdgcn_sinf(0.5f * f);   // sin(pi f)
                 const float sq = __builtin_amdgcn_sinf(0.125f * f); // sin(pi f / 4)
@@ -252,7 +250,9 @@ __device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int n
                 if (bad) v = make_float4(NAN, NAN, NAN, NAN);
                 reinterpret_cast<float4*>(smem)[p * W + kk] = v;
             } else if constexpr (INTERP == SARBP_NEAREST) {
-                float2 v = make_float2(s0.x * e.x - s0.y * e.y, s0.x * e.y + s0.y * e.x);
+                const float2 er = make_float2(e.x * A.half_rot.x - e.y * A.half_rot.y,
+                                              e.x * A.half_rot.y + e.y * A.half_rot.x);
+                float2 v = make_float2(s0.x * er.x - s0.y * er.y, s0.x * er.y + s0.y * er.x);
                 if (bad) v = make_float2(NAN, NAN);
                 reinterpret_cast<float2*>(smem)[p * W + kk] = v;
             } else {
@@ -363,9 +363,14 @@ int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* ech
     A.half_span_bins = plan->half_span / p.dr;
     A.kappa = (float)(2.0 * p.dr / p.wavelength);
     A.tie_eps = 4e-5f;
-    // (float bits of 2^23 + k) << log2(entry bytes) wraps to k * entry bytes
-    // once this bias is added (mod 2^32)
-    A.addr_bias = p.interp == SARBP_NEAREST ? (uint32_t)0u - (0x4B000000u << 3) : (uint32_t)0u - (0x4B000000u << 4);
+    A.round_half = p.interp == SARBP_NEAREST ? 1 : 0;
+    {
+        // exp(-j pi kappa): the nearest path measures the phase from half a bin below the sample
+        const double k = 2.0 * p.dr / p.wavelength;
+        const double fr = 0.5 * k - floor(0.5 * k);
+        A.half_rot = make_float2((float)cos(-2.0 * 3.14159265358979323846 * fr),
+                                 (float)sin(-2.0 * 3.14159265358979323846 * fr));
+    }
     const dim3 grid(A.ntiles), block(BP_THREADS);
     switch (p.interp) {
         case SARBP_NEAREST:

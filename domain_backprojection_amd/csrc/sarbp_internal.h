@@ -9,14 +9,28 @@
 
 // Backprojection tiling (see sarbp_bp.hip): a workgroup of BP_WAVES wave64s
 // owns a tile of BP_TX (along x) by BP_WAVES * BP_PPT (along y) pixels; each
-// lane keeps BP_PPT pixels of one column in registers.
+// lane keeps BP_PPT pixels of one column in registers.  16 waves x 2 pixels
+// (64 x 32 tiles, 1024-lane workgroups) measured fastest on gfx950: the loop is
+// bound by VALU issue and needs many waves per SIMD to hide LDS and
+// transcendental latency.
 #define BP_TX 64
-#define BP_WAVES 4
-#define BP_PPT 8
+#ifndef BP_WAVES
+#define BP_WAVES 16
+#endif
+#ifndef BP_PPT
+#define BP_PPT 2
+#endif
 #define BP_TY (BP_WAVES * BP_PPT)
 #define BP_THREADS (64 * BP_WAVES)
-#define BP_MAX_CHUNK 64           // pulses staged in LDS per step
+#ifndef BP_MAX_CHUNK
+#define BP_MAX_CHUNK 64 // pulses staged in LDS per step
+#endif
+#ifndef BP_PUNROLL
+#define BP_PUNROLL 1 // pulses per unrolled hot-loop iteration
+#endif
+#ifndef BP_LDS_BUDGET
 #define BP_LDS_BUDGET (52 * 1024) // bytes per workgroup: three workgroups per CU
+#endif
 
 struct sarbp_plan {
     sarbp_params p;
@@ -50,7 +64,8 @@ struct BpArgs {
     double half_span_bins; // half_span / dr
     float kappa;           // 2 dr / lambda: phase cycles per bin
     float tie_eps;         // nearest: fp64 recheck band around a rounding tie [bins]
-    uint32_t addr_bias;    // LDS address bias that cancels the 2^23 exponent bits
+    int round_half;        // nearest: window positions carry u + 1/2
+    float2 half_rot;       // nearest: exp(-j pi kappa), folded into the staged samples
 };
 
 int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* echo, float2* image,

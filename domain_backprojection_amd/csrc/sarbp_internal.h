@@ -47,7 +47,6 @@ struct sarbp_plan {
     // range compression
     int rc_log2;       // log2(n_fast), 0 when disabled
     float2* rc_filter; // conj(FFT(ref)) * W / n_fast
-    float2* rc_twiddle;// exp(-2 pi i t / n_fast), t in [0, n_fast)
 };
 
 // Argument block of the backprojection kernels (passed by value).

@@ -80,7 +80,6 @@ void release(sarbp_plan* plan) {
     if (switch_dev) (void)hipSetDevice(plan->device);
     if (plan->phase_tab) (void)hipFree(plan->phase_tab);
     if (plan->rc_filter) (void)hipFree(plan->rc_filter);
-    if (plan->rc_twiddle) (void)hipFree(plan->rc_twiddle);
     if (switch_dev) (void)hipSetDevice(cur);
     delete plan;
 }
@@ -164,18 +163,15 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
             ref[(size_t)((m % N + N) % N)] = std::complex<double>(cos(ph), sin(ph));
         }
         fft_host(ref);
-        std::vector<float2> filt((size_t)N), tw((size_t)N);
+        std::vector<float2> filt((size_t)N);
         for (int m = 0; m < N; ++m) {
             const double f = (m < N / 2 ? (double)m : (double)(m - N)) * p.fs / (double)N; // fftfreq
             double w = 1.0;
             if (p.window == 1) w = fabs(f) <= 0.5 * p.chirp_B ? 0.54 + 0.46 * cos(2.0 * kPi * f / p.chirp_B) : 0.0;
             const std::complex<double> h = std::conj(ref[(size_t)m]) * (w / (double)N);
             filt[(size_t)m] = make_float2((float)h.real(), (float)h.imag());
-            const double a = -2.0 * kPi * (double)m / (double)N;
-            tw[(size_t)m] = make_float2((float)cos(a), (float)sin(a));
         }
         st = upload(filt, &plan->rc_filter);
-        if (st == SARBP_OK) st = upload(tw, &plan->rc_twiddle);
         if (st == SARBP_OK) st = sarbp_rc_prepare_device();
         if (st != SARBP_OK) {
             release(plan);

@@ -6,28 +6,26 @@
 // section 3.1: pulses are independent, so the batch is one launch with one
 // workgroup per pulse.
 //
-// Both transforms are radix-8 Stockham passes (radix 4 or 2 for the remaining
-// factor) over a single LDS buffer: each pass loads its butterfly inputs into
-// registers, synchronises, and stores the outputs in autosorted order.  The
-// first pass reads the raw record straight from global memory, the matched
-// filter multiply is fused into the first pass of the inverse transform
-// (computed as conj(FFT(conj(X H)))), and the last pass writes the conjugated
-// result straight to global memory, so the record crosses HBM once each way.
+// Both transforms are Stockham autosort passes of radix 8 or 16 over a single
+// LDS buffer, specialised at compile time for each record length N = 2^L
+// (64 .. 16384) with N/16 lanes, so a lane holds exactly one radix-16 butterfly
+// (or two radix-8 ones) in registers.  Twiddles exp(-2 pi i k r / (Ns R)) come
+// from v_sin_f32 / v_cos_f32, whose inputs are in revolutions: the dyadic angle
+// k r / (Ns R) is exact in fp32, so no table is read.  The first pass reads the
+// raw record straight from global memory, the matched-filter multiply is fused
+// into the first pass of the inverse transform (computed as
+// conj(FFT(conj(X H)))), and the last pass writes the conjugated result straight
+// to global memory, so the record crosses HBM once each way.
 #include "sarbp_internal.h"
 
 #pragma clang fp contract(off)
 
 namespace {
 
-constexpr int RC_THREADS = 256;
-constexpr int RC_MAX_N = 16384;
-
 struct RcArgs {
     const float2* raw;
     float2* out;
     const float2* filt; // H[m], 1/N included
-    const float2* tw;   // exp(-2 pi i t / N)
-    int log2n;
 };
 
 __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
@@ -36,146 +34,187 @@ __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
 __device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
 __device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
 __device__ __forceinline__ float2 cconj(float2 a) { return make_float2(a.x, -a.y); }
-// multiply by -i
-__device__ __forceinline__ float2 cmul_mi(float2 a) { return make_float2(a.y, -a.x); }
+__device__ __forceinline__ float2 cmul_mi(float2 a) { return make_float2(a.y, -a.x); } // times -i
 
-// Forward DFT of R points in natural order (exp(-2 pi i n k / R)).
+// In-register forward DFT of R points in natural order (exp(-2 pi i n k / R)).
 template <int R>
-__device__ __forceinline__ void dft(float2* v) {
-    if constexpr (R == 2) {
-        const float2 t = csub(v[0], v[1]);
-        v[0] = cadd(v[0], v[1]);
-        v[1] = t;
-    } else if constexpr (R == 4) {
-        const float2 a0 = cadd(v[0], v[2]), a1 = csub(v[0], v[2]);
-        const float2 b0 = cadd(v[1], v[3]), b1 = cmul_mi(csub(v[1], v[3]));
-        v[0] = cadd(a0, b0);
-        v[2] = csub(a0, b0);
-        v[1] = cadd(a1, b1);
-        v[3] = csub(a1, b1);
-    } else {
-        // split into even outputs (DFT4 of x_n + x_{n+4}) and odd outputs
-        // (DFT4 of (x_n - x_{n+4}) W8^n), W8 = exp(-2 pi i / 8)
-        constexpr float h = 0.70710678118654752f;
-        float2 a[4], b[4];
+__device__ __forceinline__ void dft(float2* v);
+
+template <>
+__device__ __forceinline__ void dft<4>(float2* v) {
+    const float2 a0 = cadd(v[0], v[2]), a1 = csub(v[0], v[2]);
+    const float2 b0 = cadd(v[1], v[3]), b1 = cmul_mi(csub(v[1], v[3]));
+    v[0] = cadd(a0, b0);
+    v[2] = csub(a0, b0);
+    v[1] = cadd(a1, b1);
+    v[3] = csub(a1, b1);
+}
+
+template <>
+__device__ __forceinline__ void dft<8>(float2* v) {
+    // even outputs: DFT4 of x_n + x_{n+4}; odd outputs: DFT4 of (x_n - x_{n+4}) W8^n
+    constexpr float h = 0.70710678118654752f;
+    float2 a[4], b[4];
 #pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            a[n] = cadd(v[n], v[n + 4]);
-            b[n] = csub(v[n], v[n + 4]);
-        }
-        b[1] = make_float2(h * (b[1].x + b[1].y), h * (b[1].y - b[1].x));
-        b[2] = cmul_mi(b[2]);
-        b[3] = make_float2(h * (b[3].y - b[3].x), -h * (b[3].x + b[3].y));
-        dft<4>(a);
-        dft<4>(b);
+    for (int n = 0; n < 4; ++n) {
+        a[n] = cadd(v[n], v[n + 4]);
+        b[n] = csub(v[n], v[n + 4]);
+    }
+    b[1] = make_float2(h * (b[1].x + b[1].y), h * (b[1].y - b[1].x));
+    b[2] = cmul_mi(b[2]);
+    b[3] = make_float2(h * (b[3].y - b[3].x), -h * (b[3].x + b[3].y));
+    dft<4>(a);
+    dft<4>(b);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            v[2 * k] = a[k];
-            v[2 * k + 1] = b[k];
-        }
+    for (int k = 0; k < 4; ++k) {
+        v[2 * k] = a[k];
+        v[2 * k + 1] = b[k];
+    }
+}
+
+template <>
+__device__ __forceinline__ void dft<16>(float2* v) {
+    // n = 4 n1 + n2, k = k1 + 4 k2:  X[k] = sum_n2 W4^{n2 k2} W16^{n2 k1} sum_n1 x[4 n1 + n2] W4^{n1 k1}
+    constexpr float c1 = 0.92387953251128674f, s1 = 0.38268343236508978f, h = 0.70710678118654752f;
+    float2 y[4][4]; // y[n2][k1]
+#pragma unroll
+    for (int n2 = 0; n2 < 4; ++n2) {
+        float2 t[4] = {v[n2], v[4 + n2], v[8 + n2], v[12 + n2]};
+        dft<4>(t);
+#pragma unroll
+        for (int k1 = 0; k1 < 4; ++k1) y[n2][k1] = t[k1];
+    }
+    // twiddles W16^{n2 k1}, W16 = exp(-2 pi i / 16)
+    y[1][1] = cmul(y[1][1], make_float2(c1, -s1));
+    y[1][2] = cmul(y[1][2], make_float2(h, -h));
+    y[1][3] = cmul(y[1][3], make_float2(s1, -c1));
+    y[2][1] = cmul(y[2][1], make_float2(h, -h));
+    y[2][2] = cmul_mi(y[2][2]);
+    y[2][3] = cmul(y[2][3], make_float2(-h, -h));
+    y[3][1] = cmul(y[3][1], make_float2(s1, -c1));
+    y[3][2] = cmul(y[3][2], make_float2(-h, -h));
+    y[3][3] = cmul(y[3][3], make_float2(-c1, s1));
+#pragma unroll
+    for (int k1 = 0; k1 < 4; ++k1) {
+        float2 t[4] = {y[0][k1], y[1][k1], y[2][k1], y[3][k1]};
+        dft<4>(t);
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) v[k1 + 4 * k2] = t[k2];
     }
 }
 
 enum Src { SRC_LDS = 0, SRC_RAW = 1, SRC_LDS_FILTER = 2 };
 enum Dst { DST_LDS = 0, DST_OUT_CONJ = 1 };
 
-// One Stockham pass of radix R over N points with current sub-transform length
-// Ns: butterfly j reads x[j + r N/R], twiddles input r by exp(-2 pi i k r/(Ns R))
-// (k = j mod Ns) and writes output r to (j / Ns) Ns R + k + r Ns.
-template <int R, int SRC, int DST>
-__device__ __forceinline__ void pass(const RcArgs& A, float2* buf, const float2* rin, float2* rout, int N, int Ns) {
-    constexpr int BMAX = RC_MAX_N / (R * RC_THREADS);
-    const int nb = N / R;
-    const int stride = N / R;
-    float2 v[BMAX][R];
+constexpr int rc_threads(int log2n) {
+    return (1 << log2n) / 16 < 64 ? 64 : ((1 << log2n) / 16 > 1024 ? 1024 : (1 << log2n) / 16);
+}
+
+// Radix of pass `p` for a transform of 2^L points: passes of 16 and up to three
+// of 8 so that every pass is radix 8 or 16.
+constexpr int rc_radix(int L, int p) {
+    const int n8 = (L % 4 == 1) ? 3 : (L % 4 == 2 ? 2 : (L % 4 == 3 ? 1 : 0));
+    return p < n8 ? 8 : 16;
+}
+constexpr int rc_passes(int L) {
+    return (L % 4 == 1) ? 3 + (L - 9) / 4 : (L % 4 == 2 ? 2 + (L - 6) / 4 : (L % 4 == 3 ? 1 + (L - 3) / 4 : L / 4));
+}
+
+// One Stockham pass: butterfly j reads x[j + r N/R], twiddles input r by
+// exp(-2 pi i k r/(Ns R)) (k = j mod Ns) and writes output r to
+// (j / Ns) Ns R + k + r Ns.
+template <int L, int R, int NS, int SRC, int DST>
+__device__ __forceinline__ void pass(const RcArgs& A, float2* buf, const float2* rin, float2* rout) {
+    constexpr int N = 1 << L, T = rc_threads(L), NB = N / R, BPT = (NB + T - 1) / T;
+    float2 v[BPT][R];
 #pragma unroll
-    for (int b = 0; b < BMAX; ++b) {
-        const int j = threadIdx.x + b * RC_THREADS;
-        if (j < nb) {
+    for (int b = 0; b < BPT; ++b) {
+        const int j = threadIdx.x + b * T;
+        if (NB % T == 0 || j < NB) {
 #pragma unroll
             for (int r = 0; r < R; ++r) {
-                const int idx = j + r * stride;
-                float2 x;
+                const int idx = j + r * NB;
                 if constexpr (SRC == SRC_RAW) {
-                    x = rin[idx];
+                    v[b][r] = rin[idx];
                 } else if constexpr (SRC == SRC_LDS_FILTER) {
-                    x = cconj(cmul(buf[idx], A.filt[idx]));
+                    v[b][r] = cconj(cmul(buf[idx], A.filt[idx]));
                 } else {
-                    x = buf[idx];
+                    v[b][r] = buf[idx];
                 }
-                v[b][r] = x;
             }
         }
     }
-    __syncthreads();
-    const int twstep = N / (Ns * R);
+    // every lane must have read its inputs before any output overwrites them
+    if constexpr (SRC != SRC_RAW && DST == DST_LDS) __syncthreads();
 #pragma unroll
-    for (int b = 0; b < BMAX; ++b) {
-        const int j = threadIdx.x + b * RC_THREADS;
-        if (j < nb) {
-            const int k = j & (Ns - 1);
+    for (int b = 0; b < BPT; ++b) {
+        const int j = threadIdx.x + b * T;
+        if (NB % T == 0 || j < NB) {
+            const int k = j & (NS - 1);
+            if constexpr (NS > 1) {
+                const float step = (float)k * (1.0f / (float)(NS * R)); // revolutions per input index
 #pragma unroll
-            for (int r = 1; r < R; ++r) v[b][r] = cmul(v[b][r], A.tw[k * r * twstep]);
+                for (int r = 1; r < R; ++r) {
+                    const float ang = step * (float)r; // exact: k r < 2^14, power-of-two divisor
+                    v[b][r] = cmul(v[b][r], make_float2(__builtin_amdgcn_cosf(ang), -__builtin_amdgcn_sinf(ang)));
+                }
+            }
             dft<R>(v[b]);
-            const int base = (j / Ns) * Ns * R + k;
+            const int base = (j / NS) * NS * R + k;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 if constexpr (DST == DST_OUT_CONJ) {
-                    rout[base + r * Ns] = cconj(v[b][r]);
+                    rout[base + r * NS] = cconj(v[b][r]);
                 } else {
-                    buf[base + r * Ns] = v[b][r];
+                    buf[base + r * NS] = v[b][r];
                 }
             }
         }
     }
-    __syncthreads();
+    if constexpr (DST == DST_LDS) __syncthreads();
 }
 
-// One full transform: radix-8 passes, then a radix-4 or radix-2 pass for the
-// remaining factor.  The first pass reads SRC0, the last writes DST_LAST.
-template <int SRC0, int DST_LAST>
-__device__ void fft(const RcArgs& A, float2* buf, const float2* rin, float2* rout) {
-    const int N = 1 << A.log2n;
-    int rem = A.log2n, Ns = 1;
-    bool first = true;
-    while (rem > 0) {
-        const int lr = rem >= 3 ? 3 : rem;
-        const bool last = (rem == lr);
-#define RC_PASS(R)                                                                  \
-    if (first && last) pass<R, SRC0, DST_LAST>(A, buf, rin, rout, N, Ns);          \
-    else if (first) pass<R, SRC0, DST_LDS>(A, buf, rin, rout, N, Ns);              \
-    else if (last) pass<R, SRC_LDS, DST_LAST>(A, buf, rin, rout, N, Ns);           \
-    else pass<R, SRC_LDS, DST_LDS>(A, buf, rin, rout, N, Ns);
-        if (lr == 3) {
-            RC_PASS(8)
-        } else if (lr == 2) {
-            RC_PASS(4)
-        } else {
-            RC_PASS(2)
-        }
-#undef RC_PASS
-        Ns <<= lr;
-        rem -= lr;
-        first = false;
+template <int L, int P, int NS, int SRC0, int DST_LAST>
+__device__ __forceinline__ void fft_from(const RcArgs& A, float2* buf, const float2* rin, float2* rout) {
+    if constexpr (P < rc_passes(L)) {
+        constexpr int R = rc_radix(L, P);
+        constexpr bool first = (P == 0), last = (P == rc_passes(L) - 1);
+        pass<L, R, NS, first ? SRC0 : SRC_LDS, last ? DST_LAST : DST_LDS>(A, buf, rin, rout);
+        fft_from<L, P + 1, NS * R, SRC0, DST_LAST>(A, buf, rin, rout);
     }
 }
 
-__global__ __launch_bounds__(RC_THREADS) void rc_kernel(RcArgs A) {
+template <int L>
+__global__ __launch_bounds__(rc_threads(L)) void rc_kernel(RcArgs A) {
     extern __shared__ __align__(16) float2 rc_buf[];
-    const size_t N = (size_t)1 << A.log2n;
+    constexpr size_t N = (size_t)1 << L;
     const float2* rin = A.raw + (size_t)blockIdx.x * N;
     float2* rout = A.out + (size_t)blockIdx.x * N;
-    fft<SRC_RAW, DST_LDS>(A, rc_buf, rin, rout);        // X = FFT(x)       -> LDS
-    fft<SRC_LDS_FILTER, DST_OUT_CONJ>(A, rc_buf, rin, rout); // y = conj(FFT(conj(X H)))
+    fft_from<L, 0, 1, SRC_RAW, DST_LDS>(A, rc_buf, rin, rout);             // X = FFT(x) -> LDS
+    fft_from<L, 0, 1, SRC_LDS_FILTER, DST_OUT_CONJ>(A, rc_buf, rin, rout); // y = conj(FFT(conj(X H)))
+}
+
+template <int L>
+int launch(const RcArgs& A, int n, hipStream_t stream) {
+    const size_t lds = ((size_t)1 << L) * sizeof(float2);
+    hipLaunchKernelGGL(rc_kernel<L>, dim3(n), dim3(rc_threads(L)), lds, stream, A);
+    return hipGetLastError() == hipSuccess ? SARBP_OK : SARBP_EDEVICE;
+}
+
+template <int L>
+int allow_lds() {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(rc_kernel<L>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)(((size_t)1 << L) * sizeof(float2))) == hipSuccess
+               ? SARBP_OK
+               : SARBP_EDEVICE;
 }
 
 } // namespace
 
 int sarbp_rc_prepare_device() {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(rc_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                               RC_MAX_N * (int)sizeof(float2)) == hipSuccess
-               ? SARBP_OK
-               : SARBP_EDEVICE;
+    // only the 16384-point record needs more than the default 64 KiB of dynamic LDS
+    return allow_lds<14>();
 }
 
 int sarbp_launch_rc(const sarbp_plan* plan, const float2* raw, float2* out, int n, hipStream_t stream) {
@@ -183,9 +222,16 @@ int sarbp_launch_rc(const sarbp_plan* plan, const float2* raw, float2* out, int 
     A.raw = raw;
     A.out = out;
     A.filt = plan->rc_filter;
-    A.tw = plan->rc_twiddle;
-    A.log2n = plan->rc_log2;
-    const size_t lds = ((size_t)1 << plan->rc_log2) * sizeof(float2);
-    hipLaunchKernelGGL(rc_kernel, dim3(n), dim3(RC_THREADS), lds, stream, A);
-    return hipGetLastError() == hipSuccess ? SARBP_OK : SARBP_EDEVICE;
+    switch (plan->rc_log2) {
+        case 6: return launch<6>(A, n, stream);
+        case 7: return launch<7>(A, n, stream);
+        case 8: return launch<8>(A, n, stream);
+        case 9: return launch<9>(A, n, stream);
+        case 10: return launch<10>(A, n, stream);
+        case 11: return launch<11>(A, n, stream);
+        case 12: return launch<12>(A, n, stream);
+        case 13: return launch<13>(A, n, stream);
+        case 14: return launch<14>(A, n, stream);
+        default: return SARBP_EINVAL;
+    }
 }

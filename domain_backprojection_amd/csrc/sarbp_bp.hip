@@ -48,10 +48,8 @@
 namespace {
 
 
-// cos(pi m / 4) and sin(pi m / 4) for the sinc8 tap offsets m = -3 .. 4
-constexpr float kH = 0.70710678118654752f;
-__device__ constexpr float kCosQuarter[8] = {-kH, 0.f, kH, 1.f, kH, 0.f, -kH, -1.f};
-__device__ constexpr float kSinQuarter[8] = {-kH, -1.f, -kH, 0.f, kH, 1.f, kH, 0.f};
+constexpr float kH = 0.70710678118654752f;       // 1/sqrt(2)
+constexpr float kInvPi = 0.31830988618379067f;
 
 template <int INTERP>
 __device__ constexpr int entry_bytes() {
@@ -146,11 +144,11 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
         const float4 c1 = cst[2 * p + 1];
         const float X = dxl * c0.x;
         const uint32_t wbase = (uint32_t)p * wstride;
+        if constexpr (INTERP == SARBP_LINEAR) {
 #pragma unroll
-        for (int m = 0; m < BP_PPT; ++m) {
-            const float num = fmaf(dyv[m], c0.y, ddv[m] + X);
-            const float ub = bin_position<MODE>(num, c0, c1);
-            if constexpr (INTERP == SARBP_LINEAR) {
+            for (int m = 0; m < BP_PPT; ++m) {
+                const float num = fmaf(dyv[m], c0.y, ddv[m] + X);
+                const float ub = bin_position<MODE>(num, c0, c1);
                 const float f = __builtin_amdgcn_fractf(ub);
                 const uint32_t addr = ((uint32_t)ub << 4) + wbase;
                 const float4 ad = *reinterpret_cast<const float4*>(smem + addr);
@@ -162,58 +160,107 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
                 accr[m] = fmaf(-vi, sn, accr[m]);
                 acci[m] = fmaf(vr, sn, acci[m]);
                 acci[m] = fmaf(vi, cs, acci[m]);
-            } else if constexpr (INTERP == SARBP_NEAREST) {
-                // ub carries u + 1/2: its floor is the nearest bin, g - 1/2 = u - bin
-                float g = __builtin_amdgcn_fractf(ub);
-                uint32_t kb = (uint32_t)ub;
-                if (fabsf(g - 0.5f) > 0.5f - A.tie_eps) {
-                    // within tie_eps of a rounding tie: take the fp64 decision
-                    const size_t pn = 3 * (size_t)(n0 + p);
-                    const int kabs = nearest_bin_fp64(A.pos[pn], A.pos[pn + 1], A.pos[pn + 2], A.x0, A.y0, A.z0,
-                                                      A.dx, A.dy, A.r0, A.dr, i_pix, j_pix0 + BP_WAVES * m);
-                    int kr = kabs - klo_s[p];
-                    kr = kr < 0 ? 0 : (kr > A.win - 1 ? A.win - 1 : kr);
-                    kb = (uint32_t)kr;
-                    g = ub - (float)kr;
+            }
+        } else if constexpr (INTERP == SARBP_NEAREST) {
+            // ub carries u + 1/2: its floor is the nearest bin and g - 1/2 = u - bin.
+            // All pixels first, then one rare branch for lanes near a rounding tie.
+            float g[BP_PPT];
+            uint32_t kb[BP_PPT];
+            bool tie = false;
+#pragma unroll
+            for (int m = 0; m < BP_PPT; ++m) {
+                const float num = fmaf(dyv[m], c0.y, ddv[m] + X);
+                const float ub = bin_position<MODE>(num, c0, c1);
+                g[m] = __builtin_amdgcn_fractf(ub);
+                kb[m] = (uint32_t)ub;
+                tie |= fabsf(g[m] - 0.5f) > 0.5f - A.tie_eps;
+            }
+            if (tie) {
+                // within tie_eps of a rounding tie: take the fp64 decision
+                const size_t pn = 3 * (size_t)(n0 + p);
+#pragma unroll
+                for (int m = 0; m < BP_PPT; ++m) {
+                    if (fabsf(g[m] - 0.5f) > 0.5f - A.tie_eps) {
+                        const int kabs = nearest_bin_fp64(A.pos[pn], A.pos[pn + 1], A.pos[pn + 2], A.x0, A.y0,
+                                                          A.z0, A.dx, A.dy, A.r0, A.dr, i_pix, j_pix0 + BP_WAVES * m);
+                        int kr = kabs - klo_s[p];
+                        kr = kr < 0 ? 0 : (kr > A.win - 1 ? A.win - 1 : kr);
+                        g[m] = g[m] + (float)((int)kb[m] - kr); // = ub - kr
+                        kb[m] = (uint32_t)kr;
+                    }
                 }
+            }
+#pragma unroll
+            for (int m = 0; m < BP_PPT; ++m) {
                 // the staged sample carries exp(-j pi kappa), so exp(j 2 pi kappa g) completes the phase
-                const float2 sv = *reinterpret_cast<const float2*>(smem + ((kb << 3) + wbase));
+                const float2 sv = *reinterpret_cast<const float2*>(smem + ((kb[m] << 3) + wbase));
                 float sn, cs;
-                sincos_rev(kappa * g, &sn, &cs);
+                sincos_rev(kappa * g[m], &sn, &cs);
                 accr[m] = fmaf(sv.x, cs, accr[m]);
                 accr[m] = fmaf(-sv.y, sn, accr[m]);
                 acci[m] = fmaf(sv.x, sn, acci[m]);
                 acci[m] = fmaf(sv.y, cs, acci[m]);
-            } else {
-                // 8-tap Hamming-windowed sinc around k = floor(ub), taps k-3 .. k+4
+            }
+        } else {
+            // 8-tap Hamming-windowed sinc around k = floor(ub), taps mo = -3 .. 4:
+            //   h(f - mo) = sinc(f - mo) (0.54 + 0.46 cos(pi (f - mo) / 4))
+            //             = (-1)^mo sin(pi f) / pi * (0.54 + 0.46 c_mo) / (f - mo),
+            //   c_mo = cos(pi f/4) cos(pi mo/4) + sin(pi f/4) sin(pi mo/4)
+            //        = -U, -S, V, C, U, S, -V, -C   (C = cos(pi f/4), S = sin(pi f/4),
+            //                                         U = (C + S)/sqrt2, V = (C - S)/sqrt2)
+            // The samples sit in a float2 array (S) and the bin carrier phases in a
+            // second one (E) of the same window.
+            const float2* sw = reinterpret_cast<const float2*>(smem) + (size_t)p * (2 * A.win);
+            const float2* ew = sw + A.win;
+#pragma unroll
+            for (int m = 0; m < BP_PPT; ++m) {
+                const float num = fmaf(dyv[m], c0.y, ddv[m] + X);
+                const float ub = bin_position<MODE>(num, c0, c1);
                 const float f = __builtin_amdgcn_fractf(ub);
-                const uint32_t addr = ((uint32_t)ub << 4) + wbase - 3u * 16u;
-                const float4* e = reinterpret_cast<const float4*>(smem + addr);
+                const uint32_t k = (uint32_t)ub;
                 const float sp = __builtin_amdgcn_sinf(0.5f * f);   // sin(pi f)
-                const float sq = __builtin_amdgcn_sinf(0.125f * f); // sin(pi f / 4)
-                const float cq = __builtin_amdgcn_cosf(0.125f * f); // cos(pi f / 4)
+                const float S = __builtin_amdgcn_sinf(0.125f * f);  // sin(pi f / 4)
+                const float C = __builtin_amdgcn_cosf(0.125f * f);  // cos(pi f / 4)
+                const float a = sp * (0.54f * kInvPi), b = sp * (0.46f * kInvPi);
+                const float bS = b * S, bC = b * C, bh = b * kH;
+                const float bU = bh * (C + S), bV = bh * (C - S);
+                // (-1)^mo (a + b c_mo) for mo = -3 .. 4
+                const float wn[8] = {bU - a, a - bS, -(a + bV), a + bC, -(a + bU), a + bS, bV - a, a - bC};
+                const float2* sk = sw + (k - 3);
                 float vr = 0.f, vi = 0.f;
 #pragma unroll
                 for (int tp = 0; tp < 8; ++tp) {
-                    const int mo = tp - 3; // tap offset -3 .. 4
-                    const float tt = f - (float)mo;
-                    // sin(pi (f - mo)) = (-1)^mo sin(pi f)
-                    const float sgn_sp = (mo & 1) ? -sp : sp;
-                    const float pt = 3.14159265358979f * tt;
-                    const float sinc = fabsf(tt) < 1e-4f ? fmaf(-pt * pt, 1.0f / 6.0f, 1.0f)
-                                                         : sgn_sp * __builtin_amdgcn_rcpf(pt);
-                    // cos(pi (f - mo) / 4) = cos(pi f/4) cos(pi mo/4) + sin(pi f/4) sin(pi mo/4)
-                    const float cm = kCosQuarter[tp], sm = kSinQuarter[tp];
-                    const float w = sinc * fmaf(0.46f, fmaf(cq, cm, sq * sm), 0.54f);
-                    const float4 s = e[tp];
-                    vr = fmaf(w, s.x, vr);
-                    vi = fmaf(w, s.y, vi);
+                    const float w = wn[tp] * __builtin_amdgcn_rcpf(f - (float)(tp - 3));
+                    const float2 smp = sk[tp];
+                    vr = fmaf(w, smp.x, vr);
+                    vi = fmaf(w, smp.y, vi);
                 }
-                const float4 ec = e[3]; // carrier phase of bin k
+                if (f < 1e-4f || f > 1.0f - 1e-4f) {
+                    // f - mo near 0 for the tap at k (f -> 0) or k + 1 (f -> 1): redo the sum with
+                    // sinc(t) = 1 - (pi t)^2 / 6 on that tap
+                    vr = 0.f;
+                    vi = 0.f;
+#pragma unroll
+                    for (int tp = 0; tp < 8; ++tp) {
+                        const float t = f - (float)(tp - 3);
+                        float w;
+                        if (fabsf(t) < 1e-4f) {
+                            const float pt = 3.14159265358979f * t;
+                            const float cw = (tp == 3) ? C : ((C + S) * kH);
+                            w = fmaf(-pt * pt, 1.0f / 6.0f, 1.0f) * fmaf(0.46f, cw, 0.54f);
+                        } else {
+                            w = wn[tp] * __builtin_amdgcn_rcpf(t);
+                        }
+                        const float2 smp = sk[tp];
+                        vr = fmaf(w, smp.x, vr);
+                        vi = fmaf(w, smp.y, vi);
+                    }
+                }
+                const float2 ec = ew[k]; // carrier phase of bin k
                 float sn, cs;
                 sincos_rev(kappa * f, &sn, &cs);
-                const float pr = ec.z * cs - ec.w * sn;
-                const float pi_ = ec.z * sn + ec.w * cs;
+                const float pr = ec.x * cs - ec.y * sn;
+                const float pi_ = ec.x * sn + ec.y * cs;
                 accr[m] = fmaf(vr, pr, accr[m]);
                 accr[m] = fmaf(-vi, pi_, accr[m]);
                 acci[m] = fmaf(vr, pi_, acci[m]);
@@ -256,16 +303,20 @@ __device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int n
                 if (bad) v = make_float2(NAN, NAN);
                 reinterpret_cast<float2*>(smem)[p * W + kk] = v;
             } else {
-                float4 v = make_float4(s0.x, s0.y, e.x, e.y);
-                if (bad) v = make_float4(NAN, NAN, NAN, NAN);
-                reinterpret_cast<float4*>(smem)[p * W + kk] = v;
+                float2 v = s0, ev = e;
+                if (bad) v = ev = make_float2(NAN, NAN);
+                float2* sw = reinterpret_cast<float2*>(smem) + (size_t)p * (2 * W);
+                sw[kk] = v;
+                sw[W + kk] = ev;
             }
         }
     }
 }
 
+// At most 64 VGPRs, so two 1024-lane workgroups (8 waves per SIMD) fit on a CU:
+// the loop needs that many waves to hide LDS and transcendental latency.
 template <int INTERP>
-__global__ __launch_bounds__(BP_THREADS) void bp_kernel(BpArgs A) {
+__global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void bp_kernel(BpArgs A) {
     extern __shared__ __align__(16) char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 

@@ -382,7 +382,23 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     }
 }
 
+template <int INTERP>
+int allow_lds(size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(bp_kernel<INTERP>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) == hipSuccess
+               ? SARBP_OK
+               : SARBP_EDEVICE;
+}
+
 } // namespace
+
+int sarbp_bp_allow_lds(int interp, size_t bytes) {
+    switch (interp) {
+        case SARBP_NEAREST: return allow_lds<SARBP_NEAREST>(bytes);
+        case SARBP_LINEAR: return allow_lds<SARBP_LINEAR>(bytes);
+        default: return allow_lds<SARBP_SINC8>(bytes);
+    }
+}
 
 int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* echo, float2* image, int n,
                     int accumulate, hipStream_t stream) {

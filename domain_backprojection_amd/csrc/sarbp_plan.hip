@@ -12,6 +12,7 @@
 #include "sarbp_internal.h"
 
 int sarbp_rc_prepare_device();
+int sarbp_bp_allow_lds(int interp, size_t bytes);
 
 namespace {
 
@@ -133,7 +134,10 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     plan->win = (int)span_bins + plan->margin_lo + 2 + taps_hi;
     const int eb = p.interp == SARBP_NEAREST ? 8 : 16;
     const int per_pulse = plan->win * eb + 2 * 16 + 4;
+    // Coarse grids (long windows) that would stage fewer than 8 pulses per step
+    // use up to 150 KiB of LDS: one workgroup per CU instead of two.
     int chunk = (BP_LDS_BUDGET - 64) / per_pulse;
+    if (chunk < 8) chunk = (150 * 1024 - 64) / per_pulse;
     if (chunk > BP_MAX_CHUNK) chunk = BP_MAX_CHUNK;
     if (chunk < 1) {
         release(plan);
@@ -141,6 +145,13 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     }
     plan->chunk = chunk;
     plan->lds_bytes = (size_t)chunk * per_pulse;
+    if (plan->lds_bytes > 64 * 1024) {
+        st = sarbp_bp_allow_lds(p.interp, plan->lds_bytes);
+        if (st != SARBP_OK) {
+            release(plan);
+            return st;
+        }
+    }
 
     st = upload(phase_table(p), &plan->phase_tab);
     if (st != SARBP_OK) {

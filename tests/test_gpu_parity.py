@@ -244,3 +244,43 @@ def test_end_to_end_sampled(sb):
     assert rel_l2(g, want) <= REL_L2, rel_l2(g, want)
     lut = {tuple(p): v for p, v in zip(ij.tolist(), want)}
     check_peaks(lambda w: got[w[:, 1], w[:, 0]], lambda w: np.array([lut[tuple(p)] for p in w.tolist()]), wins)
+
+
+# ----------------------------------------------------------------------------- geometry edge cases
+
+def _custom_scene(pos, nr, nx, ny, dx, dy, interp, seed):
+    """Random echo on an arbitrary geometry (range record centred on the scene centre)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    Rc = float(np.linalg.norm(pos[len(pos) // 2] - np.array([0.0, 0.0, 0.0])))
+    r0 = Rc - (nr // 2) * synth.DR
+    echo = (rng.standard_normal((len(pos), nr)) + 1j * rng.standard_normal((len(pos), nr))).astype(np.complex64)
+    return synth.Scene(cfg=0, name="custom", seed=seed, na=len(pos), nr=nr, nx=nx, ny=ny, x0=-(nx // 2) * dx,
+                       y0=-(ny // 2) * dy, z0=0.0, dx=dx, dy=dy, r0=r0, dr=synth.DR, wavelength=synth.WAVELENGTH,
+                       interp=interp, positions=pos, echo=echo, raw=None, targets=np.zeros((0, 2), np.int64))
+
+
+@pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
+def test_coarse_grid_uses_large_lds_windows(sb, interp):
+    """3 m pixels: each tile spans ~500 bins, so fewer than 8 pulses fit the default LDS
+    budget and the plan stages pulses in up to 150 KiB instead."""
+    pos = synth.track(40)
+    s = _custom_scene(pos, 4096, 70, 40, 3.0, 3.0, interp, 31)
+    _say(f"[coarse {interp}] {s.nx}x{s.ny} at 3 m")
+    got = _run_bp(sb, s)
+    want = oracle.scene_backproject(s)
+    assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
+
+
+@pytest.mark.parametrize("ground, height", [(400.0, 300.0), (1600.0, 1200.0)])
+@pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
+def test_short_range_series_modes(sb, interp, ground, height):
+    """500 m and 2 km slant ranges: the tile-centre series needs its exact form or its
+    third term there (bounds checked per pulse chunk in the kernel)."""
+    na = 48
+    t = (np.arange(na) - (na - 1) / 2) / synth.PRF
+    pos = np.stack([synth.V_PLATFORM * t, np.full(na, -ground), np.full(na, height)], 1)
+    s = _custom_scene(pos, 2048, 96, 64, synth.PIXEL, synth.PIXEL, interp, 37)
+    _say(f"[short range {interp}] R = {np.hypot(ground, height):.0f} m")
+    got = _run_bp(sb, s)
+    want = oracle.scene_backproject(s)
+    assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)

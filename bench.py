@@ -33,6 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBPS = 8000.0
 FLOPS_PER_UPDATE = {"nearest": 23, "linear": 29, "sinc8": 103}
 PAGE_RATE_G = 4096 * 1024 * 1024 / 0.8 / 1e9  # the page's 0.8 s per 4096 x 1024^2 frame
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bp_linear_std_traffic.json")
@@ -57,30 +58,53 @@ def traffic_bytes():
 
 
 def time_launches(fn, steps, warmup):
+    """Mean, median and minimum per-launch time [ms] of `steps` back-to-back calls,
+    from HIP events recorded between the launches on the launch stream."""
     import torch
 
-    for _ in range(warmup):
+    # At least `warmup` launches and 0.1 s of them: after an idle gap the clock
+    # takes a few tens of milliseconds of load to settle.
+    t0, n = time.perf_counter(), 0
+    while n < warmup or time.perf_counter() - t0 < 0.1:
         fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(steps):
+    ev[0].record(stream)
+    for k in range(steps):
         fn()
-    stop.record(stream)
+        ev[k + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return start.elapsed_time(stop) / steps, wall
+    per = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(steps))
+    med = per[steps // 2] if steps % 2 else 0.5 * (per[steps // 2 - 1] + per[steps // 2])
+    return {"mean": ev[0].elapsed_time(ev[steps]) / steps, "median": med, "min": per[0]}, wall
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(scene, target_s=12.0):
-    import numpy as np
-
+    """The fp64 oracle on host threads: a row band of the benchmark scene sized to
+    about target_s, plus single-thread runs on the tiny scene and on 1/64 of the rows."""
     import oracle
+    import synth
 
     threads = oracle.threads()
-    rows = 4
+    # Probe on a band large enough that thread start-up does not dominate, then
+    # size the timed band to about target_s (the whole frame if that is shorter).
+    rows = 32
     t = time.perf_counter()
     oracle.scene_backproject(scene, rows=(0, rows), nthreads=threads)
     dt = time.perf_counter() - t
@@ -90,10 +114,23 @@ def cpu_baseline(scene, target_s=12.0):
     oracle.scene_backproject(scene, rows=(j0, j0 + rows), nthreads=threads)
     dt = time.perf_counter() - t
     upd = rows * scene.nx * scene.na
-    del np
+
+    tiny = synth.make_scene(1)
+    t = time.perf_counter()
+    oracle.scene_backproject(tiny, nthreads=1)
+    dt_tiny = time.perf_counter() - t
+    r64 = max(1, scene.ny // 64)
+    j1 = (scene.ny - r64) // 2
+    t = time.perf_counter()
+    oracle.scene_backproject(scene, rows=(j1, j1 + r64), nthreads=1)
+    dt_64 = time.perf_counter() - t
     return {"value": upd / dt / 1e9, "unit": "G pixel-pulse updates/s", "cores": threads, "kind": "oracle",
-            "sample": f"rows {j0}..{j0 + rows - 1} of the 1024x1024 grid ({rows * scene.nx} px x {scene.na} pulses,"
-                      f" {upd:.3e} updates, {dt:.1f} s)"}
+            "sample": f"rows {j0}..{j0 + rows - 1} of the {scene.nx}x{scene.ny} grid ({rows * scene.nx} px x "
+                      f"{scene.na} pulses, {upd:.3e} updates, {dt:.1f} s)",
+            "cpu_model": cpu_model(),
+            "single_thread": {"tiny_full_G_per_s": tiny.updates / dt_tiny / 1e9,
+                              "std_1_64_rows_G_per_s": r64 * scene.nx * scene.na / dt_64 / 1e9,
+                              "std_1_64_rows_s": dt_64}}
 
 
 def aux_end_to_end(sb, steps, warmup):
@@ -108,42 +145,52 @@ def aux_end_to_end(sb, steps, warmup):
         pos = torch.from_numpy(s.positions).cuda()
         rc = torch.empty_like(raw)
         img = plan.new_image()
-        rc_ms, _ = time_launches(lambda: plan.range_compress(raw, out=rc), steps, warmup)
-        bp_ms, _ = time_launches(lambda: plan.backproject(pos, rc, image=img), steps, warmup)
-        e2e_ms, _ = time_launches(lambda: (plan.range_compress(raw, out=rc), plan.backproject(pos, rc, image=img)),
-                                  steps, warmup)
+        rc_t, _ = time_launches(lambda: plan.range_compress(raw, out=rc), steps, warmup)
+        bp_t, _ = time_launches(lambda: plan.backproject(pos, rc, image=img), steps, warmup)
+        e2e_t, _ = time_launches(lambda: (plan.range_compress(raw, out=rc), plan.backproject(pos, rc, image=img)),
+                                 steps, warmup)
+    rc_ms, bp_ms, e2e_ms = rc_t["mean"], bp_t["mean"], e2e_t["mean"]
     hbm = 2 * s.na * s.nr * 8  # read raw + write compressed record, bytes
     return {"workload": "end-to-end: raw LFM 4096 x 8192 -> FFT matched filter (Hamming) -> BP 1024x1024 linear",
-            "rc_ms": rc_ms, "rc_GBps_algorithmic": hbm / rc_ms / 1e6, "bp_ms": bp_ms, "e2e_ms": e2e_ms,
+            "rc_ms": rc_ms, "rc_ms_median": rc_t["median"], "rc_GBps_algorithmic": hbm / rc_ms / 1e6,
+            "rc_frac_hbm": hbm / rc_ms / 1e6 / PEAK_HBM_GBPS, "bp_ms": bp_ms, "e2e_ms": e2e_ms,
             "e2e_G_updates_per_s": s.updates / e2e_ms / 1e6}
 
 
-def aux_interpolators(sb, steps, warmup):
-    """Nearest on the standard geometry and sinc8 on the hi-fi (perturbed-track) scene."""
+def aux_scenes(sb, steps, warmup):
+    """Nearest on the standard geometry, sinc8 on the hi-fi (perturbed-track) scene and
+    linear on the large scene (16384 pulses x 8192 bins -> 2048 x 2048)."""
     import torch
 
     import synth
 
     out = {}
-    for cfg, interp in ((2, "nearest"), (4, "sinc8")):
+    for cfg, interp, key in ((2, "nearest", "nearest"), (4, "sinc8", "sinc8"), (3, "linear", "large_linear")):
+        t = time.perf_counter()
         s = synth.make_scene(cfg, interp=interp)
+        log(f"bench: generated the {s.name} scene ({s.na} x {s.nr} echo) in {time.perf_counter() - t:.1f} s")
         with sb.Plan.for_scene(s) as plan:
             pos = torch.from_numpy(s.positions).cuda()
             echo = torch.from_numpy(s.echo).cuda()
             img = plan.new_image()
-            ms, _ = time_launches(lambda: plan.backproject(pos, echo, image=img), steps, warmup)
-        upd = s.updates / (ms * 1e-3)
-        out[interp] = {"scene": s.name, "ms": ms, "G_updates_per_s": upd / 1e9,
-                       "TFLOPs_algorithmic": FLOPS_PER_UPDATE[interp] * upd / 1e12,
-                       "frac_fp32_peak": FLOPS_PER_UPDATE[interp] * upd / 1e12 / PEAK_FP32_TFLOPS}
+            k = steps if cfg != 3 else max(5, steps // 4)
+            tm, _ = time_launches(lambda: plan.backproject(pos, echo, image=img), k, warmup)
+            del echo
+        upd = s.updates / (tm["mean"] * 1e-3)
+        out[key] = {"scene": f"{s.name}: {s.na} pulses x {s.nr} bins -> {s.nx}x{s.ny}, {interp}",
+                    "ms": tm["mean"], "ms_median": tm["median"], "ms_min": tm["min"], "launches": k,
+                    "G_updates_per_s": upd / 1e9, "TFLOPs_algorithmic": FLOPS_PER_UPDATE[interp] * upd / 1e12,
+                    "frac_fp32_peak": FLOPS_PER_UPDATE[interp] * upd / 1e12 / PEAK_FP32_TFLOPS}
+        del s
     return out
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=25,
+                    help="untimed launches first; the clock takes ~20 back-to-back launches to settle")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-aux", action="store_true", help="skip the end-to-end (range compression) figures")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -170,8 +217,10 @@ def main():
         echo = torch.from_numpy(s.echo).cuda()
         img = plan.new_image()
         torch.cuda.synchronize()
-        ms, wall = time_launches(lambda: plan.backproject(pos, echo, image=img), args.steps, args.warmup)
-    log(f"bench: {args.steps} launches, {ms:.3f} ms per launch (HIP events), wall {wall:.3f} s")
+        tm, wall = time_launches(lambda: plan.backproject(pos, echo, image=img), args.steps, args.warmup)
+    ms = tm["mean"]
+    log(f"bench: {args.steps} launches, {ms:.3f} ms per launch (HIP events; median {tm['median']:.3f}, "
+        f"min {tm['min']:.3f}), wall {wall:.3f} s")
     if args.calibrate_copy:
         a = torch.ones(args.calibrate_copy * 2**20 // 4, dtype=torch.float32, device="cuda")
         b = torch.empty_like(a)
@@ -190,6 +239,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_median": tm["median"],
+        "ms_min": tm["min"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": value / PAGE_RATE_G,
@@ -202,8 +253,8 @@ def main():
                      "frac": achieved / PEAK_FP32_TFLOPS, "traffic": traffic_bytes()},
     }
     if not args.no_aux:
-        line["aux"] = aux_end_to_end(sarbp, max(5, args.steps // 2), args.warmup)
-        line["aux"]["interpolators"] = aux_interpolators(sarbp, max(5, args.steps // 2), args.warmup)
+        line["aux"] = aux_end_to_end(sarbp, max(5, args.steps // 2), max(10, args.warmup // 2))
+        line["aux"]["scenes"] = aux_scenes(sarbp, max(5, args.steps // 5), max(5, args.warmup // 5))
         log(f"bench: end-to-end {line['aux']}")
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(s)

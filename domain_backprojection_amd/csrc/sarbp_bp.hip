@@ -113,6 +113,33 @@ __device__ __forceinline__ void sincos_rev(float x, float* s, float* c) {
     *c = __builtin_amdgcn_cosf(x);
 }
 
+// Issue priority of this workgroup's waves for the next chunk.  Two workgroups
+// share each CU and the wave arbiter favours the older one, so left alone the
+// first finishes early and the second then runs by itself at half occupancy.
+// When every tile is resident at once (at most two per CU; the partner of
+// workgroup b is then b +- slots), each publishes its progress and whichever is
+// behind takes the higher priority.  Larger grids use a fixed schedule instead:
+// the priority drops by one with each quarter of the pulses done.  The values
+// only steer scheduling; stale or racing reads cannot change a result.
+__device__ int chunk_priority(const BpArgs& A, int n0) {
+    const int b = (int)blockIdx.x;
+    if (A.ntiles <= 2 * A.slots) {
+        __hip_atomic_store(A.progress + b, n0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int partner = b < A.slots ? b + A.slots : b - A.slots;
+        if (partner >= A.ntiles) return 0;
+        const int other = __hip_atomic_load(A.progress + partner, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return (n0 < other || (n0 == other && b >= A.slots)) ? 3 : 0;
+    }
+    return 3 - (int)((4 * (long long)n0) / A.n);
+}
+
+__device__ __forceinline__ void set_priority(int p) {
+    if (p >= 3) __builtin_amdgcn_s_setprio(3);
+    else if (p == 2) __builtin_amdgcn_s_setprio(2);
+    else if (p == 1) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
 // Exact nearest-bin decision for one pixel and pulse, in the definition's
 // double-precision operation order (no contraction): floor(u + 1/2).
 // Arguments by value so the rare call needs no stack.
@@ -346,15 +373,21 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     const int P = A.chunk, W = A.win;
     float4* cst = reinterpret_cast<float4*>(smem + (size_t)P * W * entry_bytes<INTERP>());
     int* klo_s = reinterpret_cast<int*>(cst + 2 * P);
+    int* prio_s = klo_s + P;
 
-    for (int n0 = 0; n0 < A.n; n0 += P) {
-        const int np = min(P, A.n - n0);
+    // The first chunk is half size on alternate workgroups: both placements of a
+    // CU's two workgroups (b, b + slots) and (b, b + 8) get opposite parities.
+    const int stagger = BP_STAGGER ? (((int)blockIdx.x / A.slots) ^ ((int)blockIdx.x >> 3)) & 1 : 0;
+    for (int n0 = 0, np = 0; n0 < A.n; n0 += np) {
+        np = min((n0 == 0 && stagger) ? max(1, P >> 1) : P, A.n - n0);
         int need = 0;
         if (tid < np) need = pulse_setup(A, n0 + tid, cx, cy, cz, cst + 2 * tid, klo_s + tid);
+        if (tid == 0) *prio_s = chunk_priority(A, n0);
         const int m1 = __syncthreads_or(need & 1);
         const int m2 = __syncthreads_or(need & 2);
         stage_chunk<INTERP>(A, smem, klo_s, np, n0, wave, lane);
         __syncthreads();
+        set_priority(*prio_s);
         if (m2)
             accumulate_chunk<INTERP, 2>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv, accr, acci);
         else if (m1)
@@ -418,6 +451,8 @@ int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* ech
     A.margin_lo = plan->margin_lo;
     A.chunk = plan->chunk;
     A.accumulate = accumulate;
+    A.slots = plan->n_cu;
+    A.progress = plan->progress;
     A.r0 = p.r0;
     A.dr = p.dr;
     A.inv_dr = 1.0 / p.dr;

@@ -28,6 +28,11 @@
 #ifndef BP_PUNROLL
 #define BP_PUNROLL 1 // pulses per unrolled hot-loop iteration
 #endif
+// Workgroups that share a CU start with a half-size pulse chunk on alternate
+// slots, so their chunk barriers (pulse set-up and echo staging) do not line up.
+#ifndef BP_STAGGER
+#define BP_STAGGER 1
+#endif
 #ifndef BP_LDS_BUDGET
 #define BP_LDS_BUDGET (52 * 1024) // bytes per workgroup: three workgroups per CU
 #endif
@@ -43,6 +48,8 @@ struct sarbp_plan {
     int margin_lo;    // bins below the tile's lowest range kept in the window
     int chunk;        // pulses per LDS step
     size_t lds_bytes; // dynamic LDS per workgroup
+    int n_cu;         // compute units of the plan's device
+    int* progress;    // [2 * n_cu] per-workgroup pulse progress (scheduling hints only)
     double half_span; // half tile diagonal [m]
     // range compression
     int rc_log2;       // log2(n_fast), 0 when disabled
@@ -58,6 +65,8 @@ struct BpArgs {
     int n, n_range, nx, ny;
     int tiles_x, ntiles;
     int win, margin_lo, chunk, accumulate;
+    int slots;             // compute units: workgroup b and b + slots usually share a CU
+    int* progress;         // [2 * slots] pulse progress per workgroup, read by its CU partner
     double r0, dr, inv_dr, x0, y0, z0, dx, dy;
     double half_span;      // half tile diagonal [m]
     double half_span_bins; // half_span / dr

@@ -81,6 +81,7 @@ void release(sarbp_plan* plan) {
     if (switch_dev) (void)hipSetDevice(plan->device);
     if (plan->phase_tab) (void)hipFree(plan->phase_tab);
     if (plan->rc_filter) (void)hipFree(plan->rc_filter);
+    if (plan->progress) (void)hipFree(plan->progress);
     if (switch_dev) (void)hipSetDevice(cur);
     delete plan;
 }
@@ -109,10 +110,12 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     memset(plan, 0, sizeof(*plan));
     plan->p = *params;
     const sarbp_params& p = plan->p;
-    if (hipGetDevice(&plan->device) != hipSuccess) {
+    if (hipGetDevice(&plan->device) != hipSuccess ||
+        hipDeviceGetAttribute(&plan->n_cu, hipDeviceAttributeMultiprocessorCount, plan->device) != hipSuccess) {
         delete plan;
         return SARBP_EDEVICE;
     }
+    if (plan->n_cu < 1) plan->n_cu = 1;
 
     // Backprojection tiling and LDS window size.  Every pixel of a tile lies
     // within half_span of the tile centre, so (triangle inequality) its range
@@ -144,7 +147,7 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
         return SARBP_EUNSUPPORTED;
     }
     plan->chunk = chunk;
-    plan->lds_bytes = (size_t)chunk * per_pulse;
+    plan->lds_bytes = (size_t)chunk * per_pulse + 16; // + the chunk's issue-priority word
     if (plan->lds_bytes > 64 * 1024) {
         st = sarbp_bp_allow_lds(p.interp, plan->lds_bytes);
         if (st != SARBP_OK) {
@@ -154,6 +157,7 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     }
 
     st = upload(phase_table(p), &plan->phase_tab);
+    if (st == SARBP_OK) st = upload(std::vector<int>((size_t)2 * plan->n_cu, 0), &plan->progress);
     if (st != SARBP_OK) {
         release(plan);
         return st;

@@ -23,11 +23,14 @@
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream).  Argument checks are synchronous and return SARBP_EINVAL
  *     before anything is enqueued; a failed launch returns SARBP_EDEVICE.
- *   - A plan is immutable after creation and owns only read-only device
- *     tables, so calls with one plan on different streams may run
- *     concurrently.  Calls that write the same image must be ordered by the
- *     caller.  No entry point allocates device memory except
- *     sarbp_plan_create.
+ *   - A plan's parameters and device tables are immutable after creation,
+ *     so calls with one plan on different streams may run concurrently.  The
+ *     plan also owns a small progress array that backprojection workgroups
+ *     write and read to balance issue priority between the two workgroups of
+ *     a compute unit; it steers scheduling only, so overlapping calls that
+ *     share it stay correct (they may run slightly slower).  Calls that write
+ *     the same image must be ordered by the caller.  No entry point allocates
+ *     device memory except sarbp_plan_create.
  */
 #ifndef SARBP_H
 #define SARBP_H
@@ -74,7 +77,8 @@ typedef struct {
 
 typedef struct sarbp_plan sarbp_plan; /* opaque */
 
-/* Validate `params`, build the plan's read-only device tables on the current
+/* Validate `params`, build the plan's device tables (read-only phase and
+ * filter tables, plus the 2 x compute-unit progress array) on the current
  * HIP device and return the plan in *out (set to NULL on failure).
  * Returns SARBP_EINVAL for invalid parameters, SARBP_ENOMEM if an allocation
  * fails, SARBP_EDEVICE if the HIP runtime fails. */

@@ -57,9 +57,13 @@ __device__ constexpr int entry_bytes() {
 }
 
 // Per-pulse constants of the current tile, two float4 per pulse:
-//   c0 = (2 ux, 2 uy, ft, a)   c1 = (b, c, 1/R_t^2, 1/(R_t dr))
+//   c0 = (2 ux, 2 uy, ft, a)   c1 = (b, c, 1/R_t^2, a2)
 // with u = c - a_n, ft = u_c - k_lo (fractional bin of the tile centre within
 // the window), a = 1/(2 R_t dr), b = -1/(8 R_t^3 dr), c = 1/(16 R_t^5 dr).
+// In q = num / R_t^2, (R - R_t) / R_t = q/2 - q^2/8 + q^3/16 - 5 q^4/128 + ...
+// The two-term form replaces the cubic by its Chebyshev-economised linear fit
+// over |q| <= q_m, (3/4) q_m^2 q, so its linear coefficient is
+// a2 = a (1 + 3 q_m^2 / 32) and its error at most R_t (q_m^3/64 + 5 q_m^4/128).
 // Returns the accuracy mode this pulse needs (0: 2 terms, 1: 3 terms, 2: exact).
 __device__ int pulse_setup(const BpArgs& A, int n, double cx, double cy, double cz, float4* cst, int* klo_out) {
     const double ax = A.pos[3 * (size_t)n], ay = A.pos[3 * (size_t)n + 1], az = A.pos[3 * (size_t)n + 2];
@@ -81,15 +85,18 @@ __device__ int pulse_setup(const BpArgs& A, int n, double cx, double cy, double 
     const double idr = A.inv_dr;
     // nearest rounds u: the +1/2 is folded into the window position
     const double ft = uc - klo_d + (A.round_half ? 0.5 : 0.0);
-    cst[0] = make_float4((float)(2.0 * ux), (float)(2.0 * uy), (float)ft, (float)(0.5 * inv_r * idr));
-    cst[1] = make_float4((float)(-0.125 * inv_r * inv_r * inv_r * idr),
-                         (float)(0.0625 * inv_r * inv_r * inv_r * inv_r * inv_r * idr), (float)(inv_r * inv_r),
-                         (float)(inv_r * idr));
-    *klo_out = (int)klo_d;
-    // Truncation error of the series for the worst pixel of the tile, in bins.
+    // q_m bounds |q| over the tile: |d| <= half_span and |u| = R_t.
     const double hs = A.half_span;
     const double q = (hs * hs + 2.0 * hs * Rt) * inv_r * inv_r;
-    const double e2 = Rt * q * q * q * (1.0 / 16.0) * idr;
+    const double a = 0.5 * inv_r * idr;
+    cst[0] = make_float4((float)(2.0 * ux), (float)(2.0 * uy), (float)ft, (float)a);
+    cst[1] = make_float4((float)(-0.125 * inv_r * inv_r * inv_r * idr),
+                         (float)(0.0625 * inv_r * inv_r * inv_r * inv_r * inv_r * idr), (float)(inv_r * inv_r),
+                         (float)(a * (1.0 + (3.0 / 32.0) * q * q)));
+    *klo_out = (int)klo_d;
+    // Truncation error of each series for the worst pixel of the tile, in bins,
+    // against 1e-6 bins (below the fp32 rounding of the window position).
+    const double e2 = Rt * (q * q * q * (1.0 / 64.0) + q * q * q * q * (5.0 / 128.0)) * idr;
     const double e3 = Rt * q * q * q * q * (5.0 / 128.0) * idr;
     return (q > 0.25 || e3 > 1e-6) ? 2 : (e2 > 1e-6 ? 1 : 0);
 }
@@ -98,12 +105,13 @@ __device__ int pulse_setup(const BpArgs& A, int n, double cx, double cy, double 
 template <int MODE>
 __device__ __forceinline__ float bin_position(float num, const float4& c0, const float4& c1) {
     if constexpr (MODE == 0) {
-        return fmaf(num, fmaf(num, c1.x, c0.w), c0.z);
+        return fmaf(num, fmaf(num, c1.x, c1.w), c0.z);
     } else if constexpr (MODE == 1) {
         return fmaf(num, fmaf(num, fmaf(num, c1.y, c1.x), c0.w), c0.z);
     } else {
+        // (R - R_t) / dr = (num / (R_t dr)) / (1 + s) = a num / (1/2 + s/2),  s = sqrt(1 + q)
         const float s = __builtin_amdgcn_sqrtf(fmaxf(fmaf(num, c1.z, 1.0f), 0.0f));
-        return fmaf(num * c1.w, __builtin_amdgcn_rcpf(1.0f + s), c0.z);
+        return fmaf(num * c0.w, __builtin_amdgcn_rcpf(fmaf(0.5f, s, 0.5f)), c0.z);
     }
 }
 

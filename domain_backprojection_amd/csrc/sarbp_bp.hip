@@ -48,12 +48,10 @@
 namespace {
 
 
-constexpr float kH = 0.70710678118654752f;       // 1/sqrt(2)
-constexpr float kInvPi = 0.31830988618379067f;
 
 template <int INTERP>
 __device__ constexpr int entry_bytes() {
-    return INTERP == SARBP_NEAREST ? 8 : 16;
+    return INTERP == SARBP_NEAREST ? 8 : (INTERP == SARBP_LINEAR ? 16 : 64);
 }
 
 // Per-pulse constants of the current tile, two float4 per pulse:
@@ -237,76 +235,46 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
                 acci[m] = fmaf(sv.y, cs, acci[m]);
             }
         } else {
-            // 8-tap Hamming-windowed sinc around k = floor(ub), taps mo = -3 .. 4:
-            //   h(f - mo) = sinc(f - mo) (0.54 + 0.46 cos(pi (f - mo) / 4))
-            //             = (-1)^mo sin(pi f) / pi * (0.54 + 0.46 c_mo) / (f - mo),
-            //   c_mo = cos(pi f/4) cos(pi mo/4) + sin(pi f/4) sin(pi mo/4)
-            //        = -U, -S, V, C, U, S, -V, -C   (C = cos(pi f/4), S = sin(pi f/4),
-            //                                         U = (C + S)/sqrt2, V = (C - S)/sqrt2)
-            // The samples sit in a float2 array (S) and the bin carrier phases in a
-            // second one (E) of the same window.
-            const float2* sw = reinterpret_cast<const float2*>(smem) + (size_t)p * (2 * A.win);
-            const float2* ew = sw + A.win;
+            // 8-tap windowed sinc: entry k of the window holds the coefficients of the
+            // degree-7 polynomial v(g) = sum_j C_j g^j, g = f - 1/2, that gives the
+            // interpolated sample at k + f, already multiplied by the carrier of bin k
+            // (built by stage_chunk).  Stored highest degree first, two per float4.
 #pragma unroll
             for (int m = 0; m < BP_PPT; ++m) {
                 const float num = fmaf(dyv[m], c0.y, ddv[m] + X);
                 const float ub = bin_position<MODE>(num, c0, c1);
                 const float f = __builtin_amdgcn_fractf(ub);
-                const uint32_t k = (uint32_t)ub;
-                const float sp = __builtin_amdgcn_sinf(0.5f * f);   // sin(pi f)
-                const float S = __builtin_amdgcn_sinf(0.125f * f);  // sin(pi f / 4)
-                const float C = __builtin_amdgcn_cosf(0.125f * f);  // cos(pi f / 4)
-                const float a = sp * (0.54f * kInvPi), b = sp * (0.46f * kInvPi);
-                const float bS = b * S, bC = b * C, bh = b * kH;
-                const float bU = bh * (C + S), bV = bh * (C - S);
-                // (-1)^mo (a + b c_mo) for mo = -3 .. 4
-                const float wn[8] = {bU - a, a - bS, -(a + bV), a + bC, -(a + bU), a + bS, bV - a, a - bC};
-                const float2* sk = sw + (k - 3);
-                float vr = 0.f, vi = 0.f;
-#pragma unroll
-                for (int tp = 0; tp < 8; ++tp) {
-                    const float w = wn[tp] * __builtin_amdgcn_rcpf(f - (float)(tp - 3));
-                    const float2 smp = sk[tp];
-                    vr = fmaf(w, smp.x, vr);
-                    vi = fmaf(w, smp.y, vi);
-                }
-                if (f < 1e-4f || f > 1.0f - 1e-4f) {
-                    // f - mo near 0 for the tap at k (f -> 0) or k + 1 (f -> 1): redo the sum with
-                    // sinc(t) = 1 - (pi t)^2 / 6 on that tap
-                    vr = 0.f;
-                    vi = 0.f;
-#pragma unroll
-                    for (int tp = 0; tp < 8; ++tp) {
-                        const float t = f - (float)(tp - 3);
-                        float w;
-                        if (fabsf(t) < 1e-4f) {
-                            const float pt = 3.14159265358979f * t;
-                            const float cw = (tp == 3) ? C : ((C + S) * kH);
-                            w = fmaf(-pt * pt, 1.0f / 6.0f, 1.0f) * fmaf(0.46f, cw, 0.54f);
-                        } else {
-                            w = wn[tp] * __builtin_amdgcn_rcpf(t);
-                        }
-                        const float2 smp = sk[tp];
-                        vr = fmaf(w, smp.x, vr);
-                        vi = fmaf(w, smp.y, vi);
-                    }
-                }
-                const float2 ec = ew[k]; // carrier phase of bin k
+                const float g = f - 0.5f;
+                const float4* e = reinterpret_cast<const float4*>(smem + (((uint32_t)ub << 6) + wbase));
+                const float4 q0 = e[0], q1 = e[1], q2 = e[2], q3 = e[3];
+                float vr = fmaf(q0.x, g, q0.z), vi = fmaf(q0.y, g, q0.w);
+                vr = fmaf(vr, g, q1.x);
+                vi = fmaf(vi, g, q1.y);
+                vr = fmaf(vr, g, q1.z);
+                vi = fmaf(vi, g, q1.w);
+                vr = fmaf(vr, g, q2.x);
+                vi = fmaf(vi, g, q2.y);
+                vr = fmaf(vr, g, q2.z);
+                vi = fmaf(vi, g, q2.w);
+                vr = fmaf(vr, g, q3.x);
+                vi = fmaf(vi, g, q3.y);
+                vr = fmaf(vr, g, q3.z);
+                vi = fmaf(vi, g, q3.w);
                 float sn, cs;
                 sincos_rev(kappa * f, &sn, &cs);
-                const float pr = ec.x * cs - ec.y * sn;
-                const float pi_ = ec.x * sn + ec.y * cs;
-                accr[m] = fmaf(vr, pr, accr[m]);
-                accr[m] = fmaf(-vi, pi_, accr[m]);
-                acci[m] = fmaf(vr, pi_, acci[m]);
-                acci[m] = fmaf(vi, pr, acci[m]);
+                accr[m] = fmaf(vr, cs, accr[m]);
+                accr[m] = fmaf(-vi, sn, accr[m]);
+                acci[m] = fmaf(vr, sn, acci[m]);
+                acci[m] = fmaf(vi, cs, acci[m]);
             }
         }
     }
 }
 
-// Stage the echo windows of one chunk into LDS: wave w takes pulses w, w+4, ...;
-// lanes take consecutive bins (coalesced loads of the echo row).
+// Stage the echo windows of one chunk into LDS: wave w takes pulses w, w+16, ...;
+// lanes take consecutive bins (coalesced loads of the echo row).  Samples
+// outside the record are zero; the carrier table covers bins -4 .. n_range + 3,
+// every bin whose taps can reach the record.
 template <int INTERP>
 __device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int np, int n0, int wave, int lane) {
     const int W = A.win, nr = A.n_range;
@@ -316,13 +284,14 @@ __device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int n
         const bool bad = (klo == INT32_MIN);
         for (int kk = lane; kk < W; kk += 64) {
             const int k = klo + kk;
-            float2 s0 = make_float2(0.f, 0.f), s1 = make_float2(0.f, 0.f), e = make_float2(0.f, 0.f);
-            if (!bad) {
-                if (k >= 0 && k < nr) s0 = row[k];
-                if (k + 1 >= 0 && k + 1 < nr) s1 = row[k + 1];
-                if (k >= -1 && k <= nr) e = A.phase[k + 1];
-            }
+            float2 e = make_float2(0.f, 0.f);
+            if (!bad && k >= -4 && k <= nr + 3) e = A.phase[k + 4];
             if constexpr (INTERP == SARBP_LINEAR) {
+                float2 s0 = make_float2(0.f, 0.f), s1 = make_float2(0.f, 0.f);
+                if (!bad) {
+                    if (k >= 0 && k < nr) s0 = row[k];
+                    if (k + 1 >= 0 && k + 1 < nr) s1 = row[k + 1];
+                }
                 float4 v;
                 v.x = s0.x * e.x - s0.y * e.y;
                 v.y = s0.x * e.y + s0.y * e.x;
@@ -332,17 +301,46 @@ __device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int n
                 if (bad) v = make_float4(NAN, NAN, NAN, NAN);
                 reinterpret_cast<float4*>(smem)[p * W + kk] = v;
             } else if constexpr (INTERP == SARBP_NEAREST) {
+                float2 s0 = make_float2(0.f, 0.f);
+                if (!bad && k >= 0 && k < nr) s0 = row[k];
                 const float2 er = make_float2(e.x * A.half_rot.x - e.y * A.half_rot.y,
                                               e.x * A.half_rot.y + e.y * A.half_rot.x);
                 float2 v = make_float2(s0.x * er.x - s0.y * er.y, s0.x * er.y + s0.y * er.x);
                 if (bad) v = make_float2(NAN, NAN);
                 reinterpret_cast<float2*>(smem)[p * W + kk] = v;
             } else {
-                float2 v = s0, ev = e;
-                if (bad) v = ev = make_float2(NAN, NAN);
-                float2* sw = reinterpret_cast<float2*>(smem) + (size_t)p * (2 * W);
-                sw[kk] = v;
-                sw[W + kk] = ev;
+                // Taps k-3 .. k+4 pair up as (k+t-3, k+4-t), t = 0..3: tap k+4-t's weight
+                // polynomial is tap k+t-3's with g -> -g, so coefficient j takes the
+                // pair's sum (j even) or difference (j odd) times sinc_poly[4 j + t].
+                float2 ps[4], pd[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int ka = k + t - 3, kb = k + 4 - t;
+                    float2 sa = make_float2(0.f, 0.f), sb = make_float2(0.f, 0.f);
+                    if (!bad && ka >= 0 && ka < nr) sa = row[ka];
+                    if (!bad && kb >= 0 && kb < nr) sb = row[kb];
+                    ps[t] = make_float2(sa.x + sb.x, sa.y + sb.y);
+                    pd[t] = make_float2(sa.x - sb.x, sa.y - sb.y);
+                }
+                float cr[8], ci[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float2* src = (j & 1) ? pd : ps;
+                    float r = 0.f, i = 0.f;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        r = fmaf(A.sinc_poly[4 * j + t], src[t].x, r);
+                        i = fmaf(A.sinc_poly[4 * j + t], src[t].y, i);
+                    }
+                    cr[j] = r * e.x - i * e.y;
+                    ci[j] = r * e.y + i * e.x;
+                    if (bad) cr[j] = ci[j] = NAN;
+                }
+                float4* dst = reinterpret_cast<float4*>(smem) + ((size_t)p * W + kk) * 4;
+                dst[0] = make_float4(cr[7], ci[7], cr[6], ci[6]);
+                dst[1] = make_float4(cr[5], ci[5], cr[4], ci[4]);
+                dst[2] = make_float4(cr[3], ci[3], cr[2], ci[2]);
+                dst[3] = make_float4(cr[1], ci[1], cr[0], ci[0]);
             }
         }
     }
@@ -470,6 +468,7 @@ int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* ech
     A.dx = p.dx;
     A.dy = p.dy;
     A.half_span = plan->half_span;
+    for (int i = 0; i < 32; ++i) A.sinc_poly[i] = plan->sinc_poly[i];
     A.half_span_bins = plan->half_span / p.dr;
     A.kappa = (float)(2.0 * p.dr / p.wavelength);
     A.tie_eps = 4e-5f;

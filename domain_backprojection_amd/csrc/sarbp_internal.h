@@ -34,13 +34,13 @@
 #define BP_STAGGER 1
 #endif
 #ifndef BP_LDS_BUDGET
-#define BP_LDS_BUDGET (52 * 1024) // bytes per workgroup: three workgroups per CU
+#define BP_LDS_BUDGET 76000 // bytes per workgroup: two 1024-lane workgroups per CU fit in 160 KiB
 #endif
 
 struct sarbp_plan {
     sarbp_params p;
     int device;
-    // exp(+j 4 pi (r0 + k dr) / lambda) for k = -1 .. n_range, stored at [k + 1]
+    // exp(+j 4 pi (r0 + k dr) / lambda) for k = -4 .. n_range + 3, stored at [k + 4]
     float2* phase_tab;
     // backprojection launch geometry
     int tiles_x, tiles_y;
@@ -50,6 +50,9 @@ struct sarbp_plan {
     size_t lds_bytes; // dynamic LDS per workgroup
     int n_cu;         // compute units of the plan's device
     int* progress;    // [2 * n_cu] per-workgroup pulse progress (scheduling hints only)
+    // sinc8: monomial coefficients in g = f - 1/2 of the degree-7 interpolant of
+    // tap t - 3 (t = 0..3) of the windowed sinc, coefficient j at [4 j + t]
+    float sinc_poly[32];
     double half_span; // half tile diagonal [m]
     // range compression
     int rc_log2;       // log2(n_fast), 0 when disabled
@@ -70,6 +73,7 @@ struct BpArgs {
     double r0, dr, inv_dr, x0, y0, z0, dx, dy;
     double half_span;      // half tile diagonal [m]
     double half_span_bins; // half_span / dr
+    float sinc_poly[32];   // see sarbp_plan::sinc_poly
     float kappa;           // 2 dr / lambda: phase cycles per bin
     float tie_eps;         // nearest: fp64 recheck band around a rounding tie [bins]
     int round_half;        // nearest: window positions carry u + 1/2

@@ -86,16 +86,57 @@ void release(sarbp_plan* plan) {
     delete plan;
 }
 
-// Carrier phase of each range bin: exp(+j 4 pi (r0 + k dr) / lambda) at [k + 1],
-// k = -1 .. n_range, reduced modulo one cycle in double precision.
+// Carrier phase of each range bin: exp(+j 4 pi (r0 + k dr) / lambda) at [k + 4],
+// k = -4 .. n_range + 3 (every bin whose interpolation taps can reach the
+// record), reduced modulo one cycle in double precision.
 std::vector<float2> phase_table(const sarbp_params& p) {
-    std::vector<float2> t((size_t)p.n_range + 2);
-    for (int64_t k = -1; k <= p.n_range; ++k) {
+    std::vector<float2> t((size_t)p.n_range + 8);
+    for (int64_t k = -4; k <= (int64_t)p.n_range + 3; ++k) {
         const double cyc = 2.0 * (p.r0 + (double)k * p.dr) / p.wavelength;
         const double fr = cyc - floor(cyc);
-        t[(size_t)(k + 1)] = make_float2((float)cos(2.0 * kPi * fr), (float)sin(2.0 * kPi * fr));
+        t[(size_t)(k + 4)] = make_float2((float)cos(2.0 * kPi * fr), (float)sin(2.0 * kPi * fr));
     }
     return t;
+}
+
+// The 8-tap interpolation kernel of the page's sinc option: sinc(t) times a
+// Hamming-type taper over its 8-sample support, h(t) = sinc(t) (0.54 + 0.46
+// cos(pi t / 4)) for |t| < 4.
+double sinc8_kernel(double t) {
+    if (fabs(t) >= 4.0) return 0.0;
+    const double s = t == 0.0 ? 1.0 : sin(kPi * t) / (kPi * t);
+    return s * (0.54 + 0.46 * cos(kPi * t / 4.0));
+}
+
+// For taps mo = -3 .. 0 the weight h(f - mo), f in [0, 1), as a degree-7
+// polynomial in g = f - 1/2: interpolation at the 8 Chebyshev nodes of
+// [-1/2, 1/2] (largest deviation from h below 7e-7), solved in the monomial
+// basis by Gaussian elimination in double precision.  Taps 1 - mo are the
+// mirror images, h(f - (1 - mo)) = h(-g + 1/2 - mo), so they need no table.
+// Layout: coefficient j of tap mo = t - 3 at [4 j + t].
+void sinc8_polynomials(float* out) {
+    for (int t = 0; t < 4; ++t) {
+        const int mo = t - 3;
+        double V[8][9];
+        for (int i = 0; i < 8; ++i) {
+            const double x = 0.5 * cos(kPi * (2 * i + 1) / 16.0);
+            double xp = 1.0;
+            for (int j = 0; j < 8; ++j, xp *= x) V[i][j] = xp;
+            V[i][8] = sinc8_kernel(x + 0.5 - mo);
+        }
+        for (int c = 0; c < 8; ++c) {
+            int piv = c;
+            for (int r = c + 1; r < 8; ++r)
+                if (fabs(V[r][c]) > fabs(V[piv][c])) piv = r;
+            for (int j = 0; j < 9; ++j) std::swap(V[c][j], V[piv][j]);
+            for (int r = 0; r < 8; ++r) {
+                if (r == c) continue;
+                const double q = V[r][c] / V[c][c];
+                for (int j = c; j < 9; ++j) V[r][j] -= q * V[c][j];
+            }
+        }
+        for (int j = 0; j < 8; ++j) out[4 * j + t] = (float)(V[j][8] / V[j][j]);
+    }
 }
 
 } // namespace
@@ -128,14 +169,17 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     }
     plan->half_span = 0.5 * sqrt((BP_TX * p.dx) * (BP_TX * p.dx) + (BP_TY * p.dy) * (BP_TY * p.dy));
     const double span_bins = ceil(2.0 * plan->half_span / p.dr);
-    const int taps_hi = p.interp == SARBP_SINC8 ? 4 : 1;
-    plan->margin_lo = p.interp == SARBP_SINC8 ? 5 : 2;
+    // The window holds the bins floor(u) can take (the sinc8 taps are folded into
+    // each bin's polynomial), with a spare bin each side.
+    const int taps_hi = 1;
+    plan->margin_lo = 2;
     if (span_bins > 1.0e6) {
         release(plan);
         return SARBP_EUNSUPPORTED;
     }
     plan->win = (int)span_bins + plan->margin_lo + 2 + taps_hi;
-    const int eb = p.interp == SARBP_NEAREST ? 8 : 16;
+    const int eb = p.interp == SARBP_NEAREST ? 8 : (p.interp == SARBP_LINEAR ? 16 : 64);
+    if (p.interp == SARBP_SINC8) sinc8_polynomials(plan->sinc_poly);
     const int per_pulse = plan->win * eb + 2 * 16 + 4;
     // Coarse grids (long windows) that would stage fewer than 8 pulses per step
     // use up to 150 KiB of LDS: one workgroup per CU instead of two.

@@ -96,13 +96,18 @@ def test_linearity_and_pulse_order(sb, interp):
     assert np.linalg.norm(c - d) / np.linalg.norm(d) < 1e-5
 
 
-def test_zero_extension_and_far_pixels(sb):
+@pytest.mark.parametrize("first, nr", [(246, 48), (226, 36)], ids=["record-starts-in-scene", "record-ends-in-scene"])
+@pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
+def test_zero_extension_and_far_pixels(sb, interp, first, nr):
     """A short record that only part of the grid's ranges fall into: samples beyond
-    the record contribute zero, as in the oracle."""
-    s = synth.make_scene(1, na=40, nx=96, ny=96, interp="linear")
-    nr = 48
-    r0 = s.r0 + (s.nr // 2 - 10) * s.dr  # the record covers only the near half of the scene
-    sh = synth.Scene(**{**s.__dict__, "nr": nr, "r0": r0, "echo": np.ascontiguousarray(s.echo[:, 246:246 + nr])})
+    the record contribute zero, as in the oracle.  Pixels within the interpolator's
+    reach of either end of the record (sinc8: 4 bins) take the in-record taps only.
+    The scene spans bins 236..276 of the 512-bin record; the cut keeps bins
+    first .. first + nr - 1."""
+    s = synth.make_scene(1, na=40, nx=96, ny=96, interp=interp)
+    r0 = s.r0 + first * s.dr
+    sh = synth.Scene(**{**s.__dict__, "nr": nr, "r0": r0,
+                        "echo": np.ascontiguousarray(s.echo[:, first:first + nr])})
     got = _run_bp(sb, sh)
     want = oracle.scene_backproject(sh)
     assert np.count_nonzero(np.abs(want) == 0) > 0

@@ -171,16 +171,17 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
     const int eb = entry_bytes<INTERP>();
     const uint32_t wstride = (uint32_t)(A.win * eb);
     const float kappa = A.kappa;
-#pragma unroll BP_PUNROLL
+    constexpr int kUnroll = INTERP == SARBP_LINEAR ? BP_PUNROLL_LINEAR
+                                                   : (INTERP == SARBP_NEAREST ? BP_PUNROLL_NEAREST : BP_PUNROLL_SINC8);
+#pragma unroll kUnroll
     for (int p = 0; p < np; ++p) {
         const float4 c0 = cst[2 * p];
         const float4 c1 = cst[2 * p + 1];
-        const float X = dxl * c0.x;
         const uint32_t wbase = (uint32_t)p * wstride;
         if constexpr (INTERP == SARBP_LINEAR) {
 #pragma unroll
             for (int m = 0; m < BP_PPT; ++m) {
-                const float num = fmaf(dyv[m], c0.y, ddv[m] + X);
+                const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, ddv[m])); // |d|^2 + 2 d.u
                 const float ub = bin_position<MODE>(num, c0, c1);
                 const float f = __builtin_amdgcn_fractf(ub);
                 const uint32_t addr = ((uint32_t)ub << 4) + wbase;
@@ -202,7 +203,7 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
             bool tie = false;
 #pragma unroll
             for (int m = 0; m < BP_PPT; ++m) {
-                const float num = fmaf(dyv[m], c0.y, ddv[m] + X);
+                const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, ddv[m])); // |d|^2 + 2 d.u
                 const float ub = bin_position<MODE>(num, c0, c1);
                 g[m] = __builtin_amdgcn_fractf(ub);
                 kb[m] = (uint32_t)ub;
@@ -241,7 +242,7 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
             // (built by stage_chunk).  Stored highest degree first, two per float4.
 #pragma unroll
             for (int m = 0; m < BP_PPT; ++m) {
-                const float num = fmaf(dyv[m], c0.y, ddv[m] + X);
+                const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, ddv[m])); // |d|^2 + 2 d.u
                 const float ub = bin_position<MODE>(num, c0, c1);
                 const float f = __builtin_amdgcn_fractf(ub);
                 const float g = f - 0.5f;

@@ -25,8 +25,16 @@
 #ifndef BP_MAX_CHUNK
 #define BP_MAX_CHUNK 64 // pulses staged in LDS per step
 #endif
-#ifndef BP_PUNROLL
-#define BP_PUNROLL 1 // pulses per unrolled hot-loop iteration
+// Pulses per unrolled hot-loop iteration (measured best: linear four, sinc8
+// eight, nearest one, whose rare fp64 branch is large).
+#ifndef BP_PUNROLL_LINEAR
+#define BP_PUNROLL_LINEAR 4
+#endif
+#ifndef BP_PUNROLL_NEAREST
+#define BP_PUNROLL_NEAREST 1
+#endif
+#ifndef BP_PUNROLL_SINC8
+#define BP_PUNROLL_SINC8 8
 #endif
 // Workgroups that share a CU start with a half-size pulse chunk on alternate
 // slots, so their chunk barriers (pulse set-up and echo staging) do not line up.

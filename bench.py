@@ -37,24 +37,31 @@ PEAK_HBM_GBPS = 8000.0
 FLOPS_PER_UPDATE = {"nearest": 23, "linear": 29, "sinc8": 103}
 PAGE_RATE_G = 4096 * 1024 * 1024 / 0.8 / 1e9  # the page's 0.8 s per 4096 x 1024^2 frame
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bp_linear_std_traffic.json")
-BP_SOURCE = os.path.join(ROOT, "domain_backprojection_amd", "csrc", "sarbp_bp.hip")
+# Everything that shapes the backprojection kernel or its launch: a change to any
+# of these invalidates the committed counter readings.
+BP_SOURCES = [os.path.join(ROOT, "domain_backprojection_amd", "csrc", f)
+              for f in ("sarbp_bp.hip", "sarbp_internal.h", "sarbp_plan.hip")]
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def traffic_bytes():
-    """HBM bytes per launch from the committed rocprofv3 counter runs, or None when the
-    kernel source changed since they were taken."""
+def bp_source_hash():
+    h = hashlib.sha256()
+    for f in BP_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def counter_record():
+    """The committed rocprofv3 counter readings of the backprojection kernel on this
+    scene, or None when the kernel's sources changed since they were taken."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    sha = hashlib.sha256(open(BP_SOURCE, "rb").read()).hexdigest()
-    if rec.get("kernel_sha256") != sha:
-        return None
-    return rec.get("bytes_per_launch")
+    return rec if rec.get("kernel_sources_sha256") == bp_source_hash() else None
 
 
 def time_launches(fn, steps, warmup):
@@ -230,6 +237,7 @@ def main():
         log(f"bench: copy calibration, {args.calibrate_copy} MiB read + {args.calibrate_copy} MiB written per launch")
 
     value = s.updates / (ms * 1e-3) / 1e9
+    counters = counter_record()
     achieved = FLOPS_PER_UPDATE[s.interp] * s.updates / (ms * 1e-3) / 1e12
     line = {
         "metric": "giga pixel-pulse backprojections/s (1 GPU) + % of FP32 VALU roofline",
@@ -250,8 +258,13 @@ def main():
                                "25 targets + per-cell clutter", "na": s.na, "nr": s.nr, "nx": s.nx, "ny": s.ny,
                    "interp": s.interp, "parallelism": "single GPU"},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_FP32_TFLOPS, "traffic": traffic_bytes()},
+                     "frac": achieved / PEAK_FP32_TFLOPS,
+                     "traffic": counters["bytes_per_launch"] if counters else None},
     }
+    if counters:
+        line["counters"] = {k: counters[k] for k in ("valu_per_update", "fp32_flops_per_update_executed",
+                                                        "l2_hit_rate", "source")}
+        line["counters"]["frac_executed"] = counters["fp32_flops_per_update_executed"] * value / 1e3 / PEAK_FP32_TFLOPS
     if not args.no_aux:
         line["aux"] = aux_end_to_end(sarbp, max(5, args.steps // 2), max(10, args.warmup // 2))
         line["aux"]["scenes"] = aux_scenes(sarbp, max(5, args.steps // 5), max(5, args.warmup // 5))

@@ -192,6 +192,22 @@ def aux_scenes(sb, steps, warmup):
     return out
 
 
+def aux_accumulators(sb, scene, steps, warmup):
+    """The standard scene with the two compensated accumulators."""
+    import torch
+
+    out = {}
+    for accum in ("kahan", "chunk64"):
+        with sb.Plan.for_scene(scene, accum=accum) as plan:
+            pos = torch.from_numpy(scene.positions).cuda()
+            echo = torch.from_numpy(scene.echo).cuda()
+            img = plan.new_image()
+            tm, _ = time_launches(lambda: plan.backproject(pos, echo, image=img), steps, warmup)
+        out[accum] = {"ms": tm["mean"], "ms_median": tm["median"],
+                      "G_updates_per_s": scene.updates / (tm["mean"] * 1e-3) / 1e9}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -268,6 +284,7 @@ def main():
     if not args.no_aux:
         line["aux"] = aux_end_to_end(sarbp, max(5, args.steps // 2), max(10, args.warmup // 2))
         line["aux"]["scenes"] = aux_scenes(sarbp, max(5, args.steps // 5), max(5, args.warmup // 5))
+        line["aux"]["accumulators"] = aux_accumulators(sarbp, s, max(5, args.steps // 5), max(5, args.warmup // 5))
         log(f"bench: end-to-end {line['aux']}")
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(s)

@@ -163,11 +163,34 @@ __device__ __attribute__((noinline)) int nearest_bin_fp64(double ax, double ay, 
     return (int)floor(__dadd_rn(u, 0.5));
 }
 
-template <int INTERP, int MODE>
+// acc += v * (cs + j sn).  ACC_FP32 and ACC_CHUNK64 use four FMAs on the fp32
+// accumulator; ACC_KAHAN forms the product first and adds it with a compensation
+// term (Kahan summation: the low part lost by each add is carried to the next).
+template <int ACC>
+__device__ __forceinline__ void mac(float& ar, float& ai, float& cr, float& ci, float vr, float vi, float cs,
+                                    float sn) {
+    if constexpr (ACC == SARBP_ACC_KAHAN) {
+        const float tr = fmaf(vr, cs, -(vi * sn));
+        const float ti = fmaf(vr, sn, vi * cs);
+        const float yr = tr - cr, yi = ti - ci;
+        const float sr = ar + yr, si = ai + yi;
+        cr = (sr - ar) - yr;
+        ci = (si - ai) - yi;
+        ar = sr;
+        ai = si;
+    } else {
+        ar = fmaf(vr, cs, ar);
+        ar = fmaf(-vi, sn, ar);
+        ai = fmaf(vr, sn, ai);
+        ai = fmaf(vi, cs, ai);
+    }
+}
+
+template <int INTERP, int MODE, int ACC>
 __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* smem, const float4* cst,
                                                  const int* klo_s, int np, int n0, int i_pix, int j_pix0,
                                                  float dxl, const float* dyv, const float* ddv, float* accr,
-                                                 float* acci) {
+                                                 float* acci, float* cmpr, float* cmpi) {
     const int eb = entry_bytes<INTERP>();
     const uint32_t wstride = (uint32_t)(A.win * eb);
     const float kappa = A.kappa;
@@ -190,10 +213,7 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
                 const float vi = fmaf(f, ad.w, ad.y);
                 float sn, cs;
                 sincos_rev(kappa * f, &sn, &cs);
-                accr[m] = fmaf(vr, cs, accr[m]);
-                accr[m] = fmaf(-vi, sn, accr[m]);
-                acci[m] = fmaf(vr, sn, acci[m]);
-                acci[m] = fmaf(vi, cs, acci[m]);
+                mac<ACC>(accr[m], acci[m], cmpr[m], cmpi[m], vr, vi, cs, sn);
             }
         } else if constexpr (INTERP == SARBP_NEAREST) {
             // ub carries u + 1/2: its floor is the nearest bin and g - 1/2 = u - bin.
@@ -230,10 +250,7 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
                 const float2 sv = *reinterpret_cast<const float2*>(smem + ((kb[m] << 3) + wbase));
                 float sn, cs;
                 sincos_rev(kappa * g[m], &sn, &cs);
-                accr[m] = fmaf(sv.x, cs, accr[m]);
-                accr[m] = fmaf(-sv.y, sn, accr[m]);
-                acci[m] = fmaf(sv.x, sn, acci[m]);
-                acci[m] = fmaf(sv.y, cs, acci[m]);
+                mac<ACC>(accr[m], acci[m], cmpr[m], cmpi[m], sv.x, sv.y, cs, sn);
             }
         } else {
             // 8-tap windowed sinc: entry k of the window holds the coefficients of the
@@ -263,10 +280,7 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
                 vi = fmaf(vi, g, q3.w);
                 float sn, cs;
                 sincos_rev(kappa * f, &sn, &cs);
-                accr[m] = fmaf(vr, cs, accr[m]);
-                accr[m] = fmaf(-vi, sn, accr[m]);
-                acci[m] = fmaf(vr, sn, acci[m]);
-                acci[m] = fmaf(vi, cs, acci[m]);
+                mac<ACC>(accr[m], acci[m], cmpr[m], cmpi[m], vr, vi, cs, sn);
             }
         }
     }
@@ -349,7 +363,7 @@ __device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int n
 
 // At most 64 VGPRs, so two 1024-lane workgroups (8 waves per SIMD) fit on a CU:
 // the loop needs that many waves to hide LDS and transcendental latency.
-template <int INTERP>
+template <int INTERP, int ACC>
 __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void bp_kernel(BpArgs A) {
     extern __shared__ __align__(16) char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -368,6 +382,8 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     const double ddx = ((double)lane - 0.5 * (BP_TX - 1)) * A.dx;
     const float dxl = (float)ddx;
     float dyv[BP_PPT], ddv[BP_PPT], accr[BP_PPT], acci[BP_PPT];
+    float cmpr[BP_PPT], cmpi[BP_PPT]; // Kahan compensation (ACC_KAHAN)
+    double sumr[BP_PPT], sumi[BP_PPT]; // fp64 totals of the chunk partials (ACC_CHUNK64)
 #pragma unroll
     for (int m = 0; m < BP_PPT; ++m) {
         const double ddy = ((double)(wave + BP_WAVES * m) - 0.5 * (BP_TY - 1)) * A.dy;
@@ -375,6 +391,10 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         ddv[m] = (float)(ddx * ddx + ddy * ddy);
         accr[m] = 0.f;
         acci[m] = 0.f;
+        cmpr[m] = 0.f;
+        cmpi[m] = 0.f;
+        sumr[m] = 0.0;
+        sumi[m] = 0.0;
     }
 
     const int P = A.chunk, W = A.win;
@@ -396,11 +416,23 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         __syncthreads();
         set_priority(*prio_s);
         if (m2)
-            accumulate_chunk<INTERP, 2>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv, accr, acci);
+            accumulate_chunk<INTERP, 2, ACC>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv, accr,
+                                              acci, cmpr, cmpi);
         else if (m1)
-            accumulate_chunk<INTERP, 1>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv, accr, acci);
+            accumulate_chunk<INTERP, 1, ACC>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv, accr,
+                                              acci, cmpr, cmpi);
         else
-            accumulate_chunk<INTERP, 0>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv, accr, acci);
+            accumulate_chunk<INTERP, 0, ACC>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv, accr,
+                                              acci, cmpr, cmpi);
+        if constexpr (ACC == SARBP_ACC_CHUNK64) {
+#pragma unroll
+            for (int m = 0; m < BP_PPT; ++m) {
+                sumr[m] += (double)accr[m];
+                sumi[m] += (double)acci[m];
+                accr[m] = 0.f;
+                acci[m] = 0.f;
+            }
+        }
         __syncthreads();
     }
 
@@ -411,32 +443,72 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
             const int j = j0 + wave + BP_WAVES * m;
             if (j < A.ny) {
                 float2* o = A.image + (size_t)j * A.nx + i;
-                if (A.accumulate) {
-                    const float2 old = *o;
-                    *o = make_float2(old.x + accr[m], old.y + acci[m]);
+                if constexpr (ACC == SARBP_ACC_CHUNK64) {
+                    double r = sumr[m], im = sumi[m];
+                    if (A.accumulate) {
+                        const float2 old = *o;
+                        r += (double)old.x;
+                        im += (double)old.y;
+                    }
+                    *o = make_float2((float)r, (float)im);
                 } else {
-                    *o = make_float2(accr[m], acci[m]);
+                    float r = accr[m], im = acci[m];
+                    if constexpr (ACC == SARBP_ACC_KAHAN) {
+                        r -= cmpr[m];
+                        im -= cmpi[m];
+                    }
+                    if (A.accumulate) {
+                        const float2 old = *o;
+                        r = old.x + r;
+                        im = old.y + im;
+                    }
+                    *o = make_float2(r, im);
                 }
             }
         }
     }
 }
 
-template <int INTERP>
-int allow_lds(size_t bytes) {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(bp_kernel<INTERP>),
+template <int INTERP, int ACC>
+int allow_lds_one(size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(bp_kernel<INTERP, ACC>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) == hipSuccess
                ? SARBP_OK
                : SARBP_EDEVICE;
 }
 
+template <int INTERP>
+int allow_lds(int accum, size_t bytes) {
+    switch (accum) {
+        case SARBP_ACC_KAHAN: return allow_lds_one<INTERP, SARBP_ACC_KAHAN>(bytes);
+        case SARBP_ACC_CHUNK64: return allow_lds_one<INTERP, SARBP_ACC_CHUNK64>(bytes);
+        default: return allow_lds_one<INTERP, SARBP_ACC_FP32>(bytes);
+    }
+}
+
+template <int INTERP>
+void launch(const BpArgs& A, int accum, size_t lds, hipStream_t stream) {
+    const dim3 grid(A.ntiles), block(BP_THREADS);
+    switch (accum) {
+        case SARBP_ACC_KAHAN:
+            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_KAHAN>), grid, block, lds, stream, A);
+            break;
+        case SARBP_ACC_CHUNK64:
+            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_CHUNK64>), grid, block, lds, stream, A);
+            break;
+        default:
+            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_FP32>), grid, block, lds, stream, A);
+            break;
+    }
+}
+
 } // namespace
 
-int sarbp_bp_allow_lds(int interp, size_t bytes) {
+int sarbp_bp_allow_lds(int interp, int accum, size_t bytes) {
     switch (interp) {
-        case SARBP_NEAREST: return allow_lds<SARBP_NEAREST>(bytes);
-        case SARBP_LINEAR: return allow_lds<SARBP_LINEAR>(bytes);
-        default: return allow_lds<SARBP_SINC8>(bytes);
+        case SARBP_NEAREST: return allow_lds<SARBP_NEAREST>(accum, bytes);
+        case SARBP_LINEAR: return allow_lds<SARBP_LINEAR>(accum, bytes);
+        default: return allow_lds<SARBP_SINC8>(accum, bytes);
     }
 }
 
@@ -481,17 +553,10 @@ int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* ech
         A.half_rot = make_float2((float)cos(-2.0 * 3.14159265358979323846 * fr),
                                  (float)sin(-2.0 * 3.14159265358979323846 * fr));
     }
-    const dim3 grid(A.ntiles), block(BP_THREADS);
     switch (p.interp) {
-        case SARBP_NEAREST:
-            hipLaunchKernelGGL(bp_kernel<SARBP_NEAREST>, grid, block, plan->lds_bytes, stream, A);
-            break;
-        case SARBP_LINEAR:
-            hipLaunchKernelGGL(bp_kernel<SARBP_LINEAR>, grid, block, plan->lds_bytes, stream, A);
-            break;
-        default:
-            hipLaunchKernelGGL(bp_kernel<SARBP_SINC8>, grid, block, plan->lds_bytes, stream, A);
-            break;
+        case SARBP_NEAREST: launch<SARBP_NEAREST>(A, p.accum, plan->lds_bytes, stream); break;
+        case SARBP_LINEAR: launch<SARBP_LINEAR>(A, p.accum, plan->lds_bytes, stream); break;
+        default: launch<SARBP_SINC8>(A, p.accum, plan->lds_bytes, stream); break;
     }
     return hipGetLastError() == hipSuccess ? SARBP_OK : SARBP_EDEVICE;
 }

@@ -12,7 +12,7 @@
 #include "sarbp_internal.h"
 
 int sarbp_rc_prepare_device();
-int sarbp_bp_allow_lds(int interp, size_t bytes);
+int sarbp_bp_allow_lds(int interp, int accum, size_t bytes);
 
 namespace {
 
@@ -49,6 +49,7 @@ int validate(const sarbp_params* p) {
     if (p == nullptr) return SARBP_EINVAL;
     if (p->n_pulses < 1 || p->nx < 1 || p->ny < 1) return SARBP_EINVAL;
     if (p->interp < SARBP_NEAREST || p->interp > SARBP_SINC8) return SARBP_EINVAL;
+    if (p->accum < SARBP_ACC_FP32 || p->accum > SARBP_ACC_CHUNK64) return SARBP_EINVAL;
     if (p->n_range < (p->interp == SARBP_SINC8 ? 8 : 2)) return SARBP_EINVAL;
     if (!isfinite(p->r0) || !finite_pos(p->dr) || !finite_pos(p->dx) || !finite_pos(p->dy)) return SARBP_EINVAL;
     if (!isfinite(p->x0) || !isfinite(p->y0) || !isfinite(p->z0) || !finite_pos(p->wavelength)) return SARBP_EINVAL;
@@ -58,7 +59,11 @@ int validate(const sarbp_params* p) {
         if (!finite_pos(p->fs) || !finite_pos(p->chirp_T) || !finite_pos(p->chirp_B)) return SARBP_EINVAL;
         const double L = floor(p->chirp_T * p->fs + 0.5);
         if (L < 1.0 || L > (double)p->n_fast) return SARBP_EINVAL;
-        if (p->window != 0 && p->window != 1) return SARBP_EINVAL;
+        if (p->window < 0 || p->window > 2) return SARBP_EINVAL;
+        if (p->window == 2) {
+            if (p->taylor_nbar != 0 && (p->taylor_nbar < 2 || p->taylor_nbar > 64)) return SARBP_EINVAL;
+            if (p->taylor_sll != 0.0 && !(p->taylor_sll >= 13.0 && p->taylor_sll <= 150.0)) return SARBP_EINVAL;
+        }
     }
     return SARBP_OK;
 }
@@ -98,6 +103,34 @@ std::vector<float2> phase_table(const sarbp_params& p) {
     }
     return t;
 }
+
+// Taylor taper at x in [-1/2, 1/2] with nbar nearly equal sidelobes at sll dB
+// below the peak, scaled to 1 at x = 0 (the classical Taylor line-source
+// weighting: A = acosh(10^(sll/20)) / pi, sigma^2 = nbar^2 / (A^2 + (nbar - 1/2)^2),
+// w = 1 + 2 sum_m F_m cos(2 pi m x) with the F_m below).
+struct TaylorTaper {
+    double F[64];
+    int nbar;
+    double centre;
+    TaylorTaper(int nbar_, double sll) : nbar(nbar_), centre(1.0) {
+        const double A = acosh(pow(10.0, sll / 20.0)) / kPi;
+        const double s2 = (double)nbar * nbar / (A * A + (nbar - 0.5) * (nbar - 0.5));
+        for (int m = 1; m < nbar; ++m) {
+            double num = 1.0, den = 1.0;
+            for (int n = 1; n < nbar; ++n) {
+                num *= 1.0 - (double)m * m / (s2 * (A * A + (n - 0.5) * (n - 0.5)));
+                if (n != m) den *= 1.0 - (double)m * m / ((double)n * n);
+            }
+            F[m] = ((m & 1) ? 0.5 : -0.5) * num / den;
+            centre += 2.0 * F[m];
+        }
+    }
+    double operator()(double x) const {
+        double w = 1.0;
+        for (int m = 1; m < nbar; ++m) w += 2.0 * F[m] * cos(2.0 * kPi * m * x);
+        return w / centre;
+    }
+};
 
 // The 8-tap interpolation kernel of the page's sinc option: sinc(t) times a
 // Hamming-type taper over its 8-sample support, h(t) = sinc(t) (0.54 + 0.46
@@ -193,7 +226,7 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     plan->chunk = chunk;
     plan->lds_bytes = (size_t)chunk * per_pulse + 16; // + the chunk's issue-priority word
     if (plan->lds_bytes > 64 * 1024) {
-        st = sarbp_bp_allow_lds(p.interp, plan->lds_bytes);
+        st = sarbp_bp_allow_lds(p.interp, p.accum, plan->lds_bytes);
         if (st != SARBP_OK) {
             release(plan);
             return st;
@@ -223,10 +256,13 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
         }
         fft_host(ref);
         std::vector<float2> filt((size_t)N);
+        const TaylorTaper taylor(p.taylor_nbar ? p.taylor_nbar : 4, p.taylor_sll != 0.0 ? p.taylor_sll : 35.0);
         for (int m = 0; m < N; ++m) {
             const double f = (m < N / 2 ? (double)m : (double)(m - N)) * p.fs / (double)N; // fftfreq
+            const bool in_band = fabs(f) <= 0.5 * p.chirp_B;
             double w = 1.0;
-            if (p.window == 1) w = fabs(f) <= 0.5 * p.chirp_B ? 0.54 + 0.46 * cos(2.0 * kPi * f / p.chirp_B) : 0.0;
+            if (p.window == 1) w = in_band ? 0.54 + 0.46 * cos(2.0 * kPi * f / p.chirp_B) : 0.0;
+            if (p.window == 2) w = in_band ? taylor(f / p.chirp_B) : 0.0;
             const std::complex<double> h = std::conj(ref[(size_t)m]) * (w / (double)N);
             filt[(size_t)m] = make_float2((float)h.real(), (float)h.imag());
         }
@@ -283,4 +319,4 @@ extern "C" const char* sarbp_status_string(int status) {
     }
 }
 
-extern "C" int sarbp_version(void) { return 100; }
+extern "C" int sarbp_version(void) { return 200; }

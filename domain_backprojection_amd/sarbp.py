@@ -37,6 +37,8 @@ SARBP_NEAREST = 0
 SARBP_LINEAR = 1
 SARBP_SINC8 = 2
 INTERP = {"nearest": SARBP_NEAREST, "linear": SARBP_LINEAR, "sinc8": SARBP_SINC8}
+SARBP_ACC_FP32, SARBP_ACC_KAHAN, SARBP_ACC_CHUNK64 = 0, 1, 2
+ACCUM = {"fp32": SARBP_ACC_FP32, "kahan": SARBP_ACC_KAHAN, "chunk64": SARBP_ACC_CHUNK64}
 
 
 class sarbp_params(ctypes.Structure):
@@ -61,6 +63,9 @@ class sarbp_params(ctypes.Structure):
         ("chirp_T", ctypes.c_double),
         ("chirp_B", ctypes.c_double),
         ("window", ctypes.c_int32),
+        ("taylor_nbar", ctypes.c_int32),
+        ("taylor_sll", ctypes.c_double),
+        ("accum", ctypes.c_int32),
     ]
 
 
@@ -97,11 +102,12 @@ def sarbp_version() -> int:
 
 
 def make_params(n_pulses, n_range, r0, dr, nx, ny, x0, y0, z0, dx, dy, wavelength, interp="linear",
-                n_fast=0, fs=0.0, chirp_T=0.0, chirp_B=0.0, window=0) -> sarbp_params:
+                n_fast=0, fs=0.0, chirp_T=0.0, chirp_B=0.0, window=0, taylor_nbar=0, taylor_sll=0.0, accum="fp32") -> sarbp_params:
     return sarbp_params(int(n_pulses), int(n_range), float(r0), float(dr), int(nx), int(ny), float(x0),
                         float(y0), float(z0), float(dx), float(dy), float(wavelength),
                         INTERP[interp] if isinstance(interp, str) else int(interp), int(n_fast), float(fs),
-                        float(chirp_T), float(chirp_B), int(window))
+                        float(chirp_T), float(chirp_B), int(window), int(taylor_nbar), float(taylor_sll),
+                        ACCUM[accum] if isinstance(accum, str) else int(accum))
 
 
 def sarbp_plan_create(params: sarbp_params) -> int:

@@ -13,7 +13,7 @@
  * axis r0 and dr, the pixel grid x = x0 + i dx, y = y0 + j dy, and the image
  * indexed [j * nx + i]; section 4.2 for the carrier wavelength in the phase).
  * Range compression (section 3.1) is an FFT matched filter with an optional
- * Hamming window, batched over pulses.
+ * Hamming or Taylor window, batched over pulses.
  *
  * Conventions shared by every entry point:
  *   - Complex data are complex64: interleaved (re, im) float pairs.
@@ -56,6 +56,15 @@ extern "C" {
  * Samples outside [0, n_range - 1] are zero. */
 typedef enum { SARBP_NEAREST = 0, SARBP_LINEAR = 1, SARBP_SINC8 = 2 } sarbp_interp;
 
+/* How the sum over pulses is accumulated (section 4.3 of the page: fp32 sums over
+ * thousands of pulses lose precision; it offers a Kahan compensation term in the
+ * kernel, or partial sums folded into double precision).  The image stays complex64.
+ *   SARBP_ACC_FP32    fp32 registers (default, fastest)
+ *   SARBP_ACC_KAHAN   fp32 with a Kahan compensation term per pixel, per pulse
+ *   SARBP_ACC_CHUNK64 fp32 within each LDS pulse chunk (<= 64 pulses), chunk partial
+ *                     sums added in fp64 (nearly free) */
+typedef enum { SARBP_ACC_FP32 = 0, SARBP_ACC_KAHAN = 1, SARBP_ACC_CHUNK64 = 2 } sarbp_accum;
+
 /* Plan parameters.  Lengths in metres, frequencies in Hz, times in seconds. */
 typedef struct {
     int32_t n_pulses;   /* Na: the most pulses one sarbp_backproject call may take (>= 1)      */
@@ -72,7 +81,13 @@ typedef struct {
     double fs;          /* fast-time sampling rate (> 0)                                        */
     double chirp_T;     /* LFM pulse length (> 0); round(chirp_T * fs) samples, <= n_fast      */
     double chirp_B;     /* LFM bandwidth (> 0), up-chirp exp(j pi (B/T) t^2), -T/2 <= t < T/2   */
-    int32_t window;     /* 0: none; 1: Hamming 0.54 + 0.46 cos(2 pi f / B) over |f| <= B/2     */
+    int32_t window;     /* weight w(f / B) over |f| <= B/2, zero outside the band:
+                         *   0: none (w = 1 everywhere); 1: Hamming 0.54 + 0.46 cos(2 pi x);
+                         *   2: Taylor, 1 + 2 sum_{m<nbar} F_m cos(2 pi m x) scaled to w(0) = 1
+                         *      (the page's lower-widening alternative to Hamming, section 3.1) */
+    int32_t taylor_nbar; /* Taylor: nearly equal sidelobes, 2..64 (0: 4)                        */
+    double taylor_sll;   /* Taylor: design sidelobe level in dB below the peak, 13..150 (0: 35)  */
+    int32_t accum;       /* sarbp_accum of sarbp_backproject (0: SARBP_ACC_FP32)                 */
 } sarbp_params;
 
 typedef struct sarbp_plan sarbp_plan; /* opaque */

@@ -74,12 +74,31 @@ def _good(sb, **over):
     dict(n_fast=100, fs=1e6, chirp_T=1e-5, chirp_B=1e5), dict(n_fast=32, fs=1e6, chirp_T=1e-5, chirp_B=1e5),
     dict(n_fast=1024, fs=0.0, chirp_T=1e-5, chirp_B=1e5), dict(n_fast=64, fs=1e8, chirp_T=1e-5, chirp_B=1e5),
     dict(n_fast=1024, fs=1e6, chirp_T=1e-5, chirp_B=1e5, window=3),
+    dict(n_fast=1024, fs=1e6, chirp_T=1e-5, chirp_B=1e5, window=-1),
+    dict(n_fast=1024, fs=1e6, chirp_T=1e-5, chirp_B=1e5, window=2, taylor_nbar=1),
+    dict(n_fast=1024, fs=1e6, chirp_T=1e-5, chirp_B=1e5, window=2, taylor_nbar=65),
+    dict(n_fast=1024, fs=1e6, chirp_T=1e-5, chirp_B=1e5, window=2, taylor_sll=10.0),
+    dict(n_fast=1024, fs=1e6, chirp_T=1e-5, chirp_B=1e5, window=2, taylor_sll=float("nan")),
+    dict(accum=3), dict(accum=-1),
 ])
 def test_plan_create_rejects_invalid_parameters(sb, bad):
     h = ctypes.c_void_p(123)
     st = sb._lib.sarbp_plan_create(ctypes.byref(_good(sb, **bad)), ctypes.byref(h))
     assert st == sb.SARBP_EINVAL
     assert h.value is None
+
+
+@pytest.mark.parametrize("ok", [dict(window=2), dict(window=2, taylor_nbar=6, taylor_sll=45.0),
+                                dict(window=1, taylor_nbar=1), dict(window=0)])
+def test_plan_params_validate_window_fields(sb, ok):
+    """Validation of the window fields without touching a device: a valid set passes
+    validation and fails, if at all, only at the device step (no GPU here)."""
+    h = ctypes.c_void_p()
+    st = sb._lib.sarbp_plan_create(ctypes.byref(_good(sb, n_fast=1024, fs=1e6, chirp_T=1e-5, chirp_B=1e5, **ok)),
+                                   ctypes.byref(h))
+    assert st != sb.SARBP_EINVAL
+    if st == sb.SARBP_OK:
+        sb._lib.sarbp_destroy(h)
 
 
 def test_null_arguments(sb):

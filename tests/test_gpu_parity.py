@@ -123,6 +123,63 @@ def test_nonfinite_positions_propagate_nan(sb):
     assert np.isnan(got).all()
 
 
+# ----------------------------------------------------------------------------- accumulation modes
+
+@pytest.mark.parametrize("accum", ["kahan", "chunk64"])
+@pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
+def test_accumulation_modes_full_image(sb, interp, accum):
+    """The compensated accumulators give the same image as the oracle (tiny scene,
+    plus a ragged grid on the perturbed track with a pulse count that is not a
+    multiple of the chunk, and accumulate = 1 over two calls)."""
+    import torch
+
+    s = synth.make_scene(1, interp=interp)
+    got = _run_bp(sb, s, accum=accum)
+    want = oracle.scene_backproject(s)
+    assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
+    check_peaks(lambda w: got[w[:, 1], w[:, 0]], lambda w: want[w[:, 1], w[:, 0]], target_windows(s))
+    r = synth.make_scene(4, na=203, nr=1024, nx=70, ny=45, interp=interp, n_targets=1)
+    with sb.Plan.for_scene(r, accum=accum) as plan:
+        pos = torch.from_numpy(r.positions).cuda()
+        ech = torch.from_numpy(r.echo).cuda()
+        img = plan.backproject(pos[:120].contiguous(), ech[:120].contiguous())
+        plan.backproject(pos[120:].contiguous(), ech[120:].contiguous(), image=img, accumulate=1)
+        torch.cuda.synchronize()
+        got = img.cpu().numpy().astype(np.complex128)
+    assert rel_l2(got, oracle.scene_backproject(r)) <= REL_L2
+
+
+def test_compensated_accumulation_reduces_summation_error(sb):
+    """16384 pulses from one antenna position with an echo that is constant along range:
+    every pulse's term is s_n times the same rotation, so |I| = |sum_n s_n| up to the
+    accumulation error (plus ~1e-7 from the rotation's fp32 magnitude).  A slowly rising
+    s_n = 1 + n/N + 0.3j biases plain fp32 rounding (a CPU emulation of the three
+    accumulators gives 8e-5, 3e-8 and 5e-7): the compensated modes must stay below
+    1e-6 and the plain one must lose over ten times more."""
+    import torch
+
+    na, nr, nx, ny = 16384, 64, 64, 32
+    g = np.array([[0.0, -synth.GROUND_RANGE, synth.ALTITUDE]])
+    pos = np.repeat(g, na, axis=0)
+    s_n = 1.0 + np.arange(na) / na + 0.3j
+    echo = np.repeat(s_n.astype(np.complex64)[:, None], nr, axis=1)
+    r0 = synth.RC_CENTRE - (nr // 2) * synth.DR
+    kw = dict(n_pulses=na, n_range=nr, r0=r0, dr=synth.DR, nx=nx, ny=ny, x0=-(nx // 2) * synth.PIXEL,
+              y0=-(ny // 2) * synth.PIXEL, z0=0.0, dx=synth.PIXEL, dy=synth.PIXEL, wavelength=synth.WAVELENGTH,
+              interp="linear")
+    exact = abs(np.sum(echo.astype(np.complex128)[:, 0]))
+    errs = {}
+    for accum in ("fp32", "kahan", "chunk64"):
+        with sb.Plan(accum=accum, **kw) as plan:
+            img = plan.backproject(torch.from_numpy(pos).cuda(), torch.from_numpy(echo).cuda())
+            torch.cuda.synchronize()
+            mag = np.abs(img.cpu().numpy().astype(np.complex128))
+        errs[accum] = float(np.sqrt(np.mean((mag - exact) ** 2)) / exact)
+    _say(f"[accumulation] relative RMS error of |I|: {errs}")
+    assert errs["kahan"] < 1e-6 and errs["chunk64"] < 1e-6, errs
+    assert errs["fp32"] > 10 * max(errs["kahan"], errs["chunk64"]), errs
+
+
 # ----------------------------------------------------------------------------- nearest: bit-exact index
 
 def _index_probe(sb, scene, pulses):
@@ -183,7 +240,7 @@ def test_range_compression_matches_oracle(sb):
 
 
 @pytest.mark.parametrize("n_fast", [64, 128, 512, 1024, 2048, 4096, 16384])
-@pytest.mark.parametrize("window", [0, 1])
+@pytest.mark.parametrize("window", [0, 1, 2])
 def test_range_compression_sizes(sb, n_fast, window):
     import torch
 
@@ -197,6 +254,23 @@ def test_range_compression_sizes(sb, n_fast, window):
         torch.cuda.synchronize()
         got = out.cpu().numpy().astype(np.complex128)
     want = oracle.rc.range_compress(x, synth.FS, T, synth.BANDWIDTH, window)
+    assert rel_l2(got, want) < 1e-5
+
+
+@pytest.mark.parametrize("nbar, sll", [(4, 35.0), (6, 45.0), (3, 25.0)])
+def test_range_compression_taylor_parameters(sb, nbar, sll):
+    """The Taylor taper's parameters reach the filter (end-to-end scene's chirp, 8192 samples)."""
+    import torch
+
+    rng = np.random.Generator(np.random.PCG64(nbar))
+    x = (rng.standard_normal((3, 8192)) + 1j * rng.standard_normal((3, 8192))).astype(np.complex64)
+    with sb.Plan(n_pulses=1, n_range=8192, r0=0.0, dr=1.0, nx=1, ny=1, x0=0, y0=0, z0=0, dx=1, dy=1,
+                 wavelength=0.03, interp="linear", n_fast=8192, fs=synth.FS, chirp_T=synth.CHIRP_T,
+                 chirp_B=synth.BANDWIDTH, window=2, taylor_nbar=nbar, taylor_sll=sll) as plan:
+        out = plan.range_compress(torch.from_numpy(x).cuda())
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.complex128)
+    want = oracle.rc.range_compress(x, synth.FS, synth.CHIRP_T, synth.BANDWIDTH, 2, nbar, sll)
     assert rel_l2(got, want) < 1e-5
 
 

@@ -208,6 +208,41 @@ def aux_accumulators(sb, scene, steps, warmup):
     return out
 
 
+def aux_host_stream(sb, scene, steps, warmup):
+    """Frames fed from page-locked host memory through the two-buffer pipeline
+    (PCIe-inclusive; the headline value keeps its inputs resident in HBM):
+    the standard scene's echo, and the end-to-end scene's raw pulses compressed on
+    the device chunk by chunk.  A plain host-to-device copy gives the link rate."""
+    import torch
+
+    import synth
+
+    out = {}
+    pos_h = torch.from_numpy(scene.positions).pin_memory()
+    echo_h = torch.from_numpy(scene.echo).pin_memory()
+    dev = torch.empty(echo_h.shape, dtype=echo_h.dtype, device="cuda")
+    tm, _ = time_launches(lambda: dev.copy_(echo_h, non_blocking=True), steps, warmup)
+    out["h2d_GBps"] = echo_h.numel() * 8 / (tm["mean"] * 1e-3) / 1e9
+    del dev
+    with sb.Plan.for_scene(scene, n_pulses=1024) as plan, sb.HostStream(plan, chunk=1024) as hs:
+        img = plan.new_image()
+        tm, _ = time_launches(lambda: hs.backproject(pos_h, echo_h, image=img), steps, warmup)
+    out["std_linear"] = {"chunk": 1024, "ms": tm["mean"], "ms_median": tm["median"],
+                         "G_updates_per_s": scene.updates / (tm["mean"] * 1e-3) / 1e9,
+                         "input_MB": echo_h.numel() * 8 / 1e6}
+    e = synth.make_scene(5)
+    pos_h = torch.from_numpy(e.positions).pin_memory()
+    raw_h = torch.from_numpy(e.raw).pin_memory()
+    with sb.Plan.for_scene(e, n_fast=e.nr, n_pulses=1024) as plan, \
+            sb.HostStream(plan, chunk=1024, compress=True) as hs:
+        img = plan.new_image()
+        tm, _ = time_launches(lambda: hs.backproject(pos_h, raw_h, image=img), steps, warmup)
+    out["e2e_raw_compress"] = {"chunk": 1024, "ms": tm["mean"], "ms_median": tm["median"],
+                               "G_updates_per_s": e.updates / (tm["mean"] * 1e-3) / 1e9,
+                               "input_MB": raw_h.numel() * 8 / 1e6}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,6 +320,7 @@ def main():
         line["aux"] = aux_end_to_end(sarbp, max(5, args.steps // 2), max(10, args.warmup // 2))
         line["aux"]["scenes"] = aux_scenes(sarbp, max(5, args.steps // 5), max(5, args.warmup // 5))
         line["aux"]["accumulators"] = aux_accumulators(sarbp, s, max(5, args.steps // 5), max(5, args.warmup // 5))
+        line["aux"]["host_stream"] = aux_host_stream(sarbp, s, max(5, args.steps // 5), max(5, args.warmup // 5))
         log(f"bench: end-to-end {line['aux']}")
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(s)

@@ -82,9 +82,16 @@ _lib.sarbp_status_string.argtypes = [ctypes.c_int]
 _lib.sarbp_status_string.restype = ctypes.c_char_p
 _lib.sarbp_version.argtypes = []
 _lib.sarbp_version.restype = ctypes.c_int
+_lib.sarbp_stream_create.argtypes = [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_vp)]
+_lib.sarbp_stream_create.restype = ctypes.c_int
+_lib.sarbp_backproject_host.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp]
+_lib.sarbp_backproject_host.restype = ctypes.c_int
+_lib.sarbp_stream_destroy.argtypes = [_vp]
+_lib.sarbp_stream_destroy.restype = None
 
 EXPORTS = ("sarbp_plan_create", "sarbp_backproject", "sarbp_range_compress", "sarbp_destroy",
-           "sarbp_status_string", "sarbp_version")
+           "sarbp_status_string", "sarbp_version", "sarbp_stream_create", "sarbp_backproject_host",
+           "sarbp_stream_destroy")
 
 
 class SarbpError(RuntimeError):
@@ -167,6 +174,44 @@ def sarbp_range_compress(handle, raw: torch.Tensor, out: torch.Tensor, n: int | 
         raise SarbpError(st, "sarbp_range_compress")
 
 
+def _host_ptr(t: torch.Tensor, dtype, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or t.is_cuda:
+        raise TypeError(f"{name} must be a host tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def sarbp_stream_create(plan_handle, chunk: int, compress: int = 0) -> int:
+    h = _vp()
+    st = _lib.sarbp_stream_create(plan_handle, int(chunk), int(compress), ctypes.byref(h))
+    if st != SARBP_OK:
+        raise SarbpError(st, "sarbp_stream_create")
+    return h.value
+
+
+def sarbp_backproject_host(stream_handle, positions: torch.Tensor, data: torch.Tensor, image: torch.Tensor,
+                           n: int | None = None, accumulate: int = 0, stream=None) -> None:
+    """positions float64 (n, 3) and data complex64 (n, row) in host memory (page-locked for
+    overlap), image complex64 (ny, nx) on the device."""
+    if n is None:
+        n = positions.shape[0]
+    if positions.dim() != 2 or positions.shape[1] != 3 or positions.shape[0] < n or data.shape[0] < n:
+        raise ValueError("positions must be (>= n, 3) and data (>= n, row)")
+    st = _lib.sarbp_backproject_host(stream_handle, _host_ptr(positions, torch.float64, "positions"),
+                                     _host_ptr(data, torch.complex64, "data"),
+                                     _dev_ptr(image, torch.complex64, "image"), int(n), int(accumulate),
+                                     _stream(stream))
+    if st != SARBP_OK:
+        raise SarbpError(st, "sarbp_backproject_host")
+
+
+def sarbp_stream_destroy(stream_handle) -> None:
+    _lib.sarbp_stream_destroy(stream_handle)
+
+
 class Plan:
     """Owns one plan handle; checks tensor shapes against the plan's sizes."""
 
@@ -219,3 +264,39 @@ class Plan:
             raise ValueError("raw must be (n, n_fast)")
         sarbp_range_compress(self.handle, raw, out, n=n, stream=stream)
         return out
+
+
+class HostStream:
+    """Owns one host-to-device pulse pipeline of a plan (``sarbp_stream_create``)."""
+
+    def __init__(self, plan: Plan, chunk: int, compress: bool = False):
+        self.plan = plan
+        self.row = plan.params.n_range
+        self.handle = sarbp_stream_create(plan.handle, chunk, 1 if compress else 0)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            sarbp_stream_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def backproject(self, positions, data, image=None, n=None, accumulate=0, stream=None) -> torch.Tensor:
+        if image is None:
+            image = torch.empty((self.plan.params.ny, self.plan.params.nx), dtype=torch.complex64, device="cuda")
+        if tuple(image.shape) != (self.plan.params.ny, self.plan.params.nx):
+            raise ValueError("image shape does not match the plan")
+        if data.dim() != 2 or data.shape[1] != self.row:
+            raise ValueError("data must be (n, n_range)")
+        sarbp_backproject_host(self.handle, positions, data, image, n=n, accumulate=accumulate, stream=stream)
+        return image

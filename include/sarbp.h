@@ -127,6 +127,42 @@ int sarbp_range_compress(const sarbp_plan* plan, const void* raw_d, void* out_d,
  * ensure no call using the plan is still running. */
 void sarbp_destroy(sarbp_plan* plan);
 
+/* ---- Streaming pulses from host memory (section 3.3 of the page: prefetch the
+ * echo with streams so that copies overlap computation). --------------------- */
+
+typedef struct sarbp_stream sarbp_stream; /* opaque */
+
+/* Create a host-to-device pipeline for `plan` on the plan's device: two device
+ * staging buffers of `chunk` pulses each, a copy stream and its events.
+ *   chunk    : pulses per staged step, 1 <= chunk <= plan n_pulses
+ *   compress : 0: host data is the range-compressed echo, [n][n_range];
+ *              1: host data is raw pulses, [n][n_fast], range-compressed on the
+ *                 device chunk by chunk (requires n_fast = n_range)
+ * The plan must outlive the stream object.  Returns SARBP_EINVAL (bad chunk,
+ * compress without a compatible plan, null pointers, wrong device),
+ * SARBP_ENOMEM, SARBP_EDEVICE. */
+int sarbp_stream_create(const sarbp_plan* plan, int32_t chunk, int32_t compress, sarbp_stream** out);
+
+/* Backproject n pulses held in host memory into a device image.
+ *   positions_h : host, float64 [n][3]
+ *   data_h      : host, complex64 pulses (see compress above)
+ *   image_d     : device, complex64 [ny][nx]; written (accumulate = 0) or added to
+ *   n           : any count >= 1 (it may exceed the plan's n_pulses: the pulses
+ *                 go through in chunks, each added to the image)
+ * Chunk c is copied on the object's copy stream while chunk c - 1 is processed
+ * on `stream`; the two staging buffers alternate, ordered by events.  The call
+ * returns once everything is enqueued; synchronise `stream` before reading the
+ * image or reusing the host buffers.  Overlap needs page-locked host memory
+ * (hipHostMalloc); pageable memory still works but copies synchronously.  One
+ * stream object must not be used by two threads at once; calls on it are
+ * ordered through its buffers' events.  Returns SARBP_EINVAL (null pointer,
+ * n < 1, accumulate not 0/1, wrong device), SARBP_EDEVICE. */
+int sarbp_backproject_host(sarbp_stream* s, const double* positions_h, const void* data_h, void* image_d,
+                           int32_t n, int32_t accumulate, void* stream);
+
+/* Release the stream object after its work has finished.  NULL is a no-op. */
+void sarbp_stream_destroy(sarbp_stream* s);
+
 /* Static description of a status code (never NULL). */
 const char* sarbp_status_string(int status);
 

@@ -108,3 +108,7 @@ def test_null_arguments(sb):
     assert sb._lib.sarbp_backproject(None, 8, 8, 8, 1, 0, None) == sb.SARBP_EINVAL
     assert sb._lib.sarbp_range_compress(None, 8, 16, 1, None) == sb.SARBP_EINVAL
     sb._lib.sarbp_destroy(None)  # no-op
+    assert sb._lib.sarbp_stream_create(None, 8, 0, ctypes.byref(h)) == sb.SARBP_EINVAL
+    assert sb._lib.sarbp_stream_create(None, 8, 0, None) == sb.SARBP_EINVAL
+    assert sb._lib.sarbp_backproject_host(None, 8, 8, 8, 1, 0, None) == sb.SARBP_EINVAL
+    sb._lib.sarbp_stream_destroy(None)  # no-op

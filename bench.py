@@ -243,6 +243,27 @@ def aux_host_stream(sb, scene, steps, warmup):
     return out
 
 
+def aux_terrain(sb, scene, steps, warmup):
+    """The standard scene's geometry and echo backprojected onto 20 m (peak to peak) of
+    seeded terrain (timing only: the per-pixel height, the wider echo windows and one
+    more FMA per update)."""
+    import numpy as np
+    import torch
+
+    import synth
+
+    dem = synth.terrain(scene.nx, scene.ny, scene.dx, scene.dy, np.random.Generator(np.random.PCG64(77)), 20.0)
+    relief = synth.block_relief(dem)
+    with sb.Plan.for_scene(scene, dem_relief=relief) as plan:
+        pos = torch.from_numpy(scene.positions).cuda()
+        echo = torch.from_numpy(scene.echo).cuda()
+        dem_d = torch.from_numpy(dem).cuda()
+        img = plan.new_image()
+        tm, _ = time_launches(lambda: plan.backproject(pos, echo, image=img, dem=dem_d), steps, warmup)
+    return {"relief_m": 20.0, "block_relief_m": relief, "ms": tm["mean"], "ms_median": tm["median"],
+            "G_updates_per_s": scene.updates / (tm["mean"] * 1e-3) / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -321,6 +342,7 @@ def main():
         line["aux"]["scenes"] = aux_scenes(sarbp, max(5, args.steps // 5), max(5, args.warmup // 5))
         line["aux"]["accumulators"] = aux_accumulators(sarbp, s, max(5, args.steps // 5), max(5, args.warmup // 5))
         line["aux"]["host_stream"] = aux_host_stream(sarbp, s, max(5, args.steps // 5), max(5, args.warmup // 5))
+        line["aux"]["terrain"] = aux_terrain(sarbp, s, max(5, args.steps // 5), max(5, args.warmup // 5))
         log(f"bench: end-to-end {line['aux']}")
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(s)

@@ -63,7 +63,9 @@ __device__ constexpr int entry_bytes() {
 // over |q| <= q_m, (3/4) q_m^2 q, so its linear coefficient is
 // a2 = a (1 + 3 q_m^2 / 32) and its error at most R_t (q_m^3/64 + 5 q_m^4/128).
 // Returns the accuracy mode this pulse needs (0: 2 terms, 1: 3 terms, 2: exact).
-__device__ int pulse_setup(const BpArgs& A, int n, double cx, double cy, double cz, float4* cst, int* klo_out) {
+// Terrain (dem) kernels also store c2 = (2 uz, 0, 0, 0), the vertical term of 2 d.u.
+__device__ int pulse_setup(const BpArgs& A, int n, double cx, double cy, double cz, float4* cst, int* klo_out,
+                           bool dem) {
     const double ax = A.pos[3 * (size_t)n], ay = A.pos[3 * (size_t)n + 1], az = A.pos[3 * (size_t)n + 2];
     const double ux = cx - ax, uy = cy - ay, uz = cz - az;
     const double R2 = ux * ux + uy * uy + uz * uz;
@@ -76,6 +78,7 @@ __device__ int pulse_setup(const BpArgs& A, int n, double cx, double cy, double 
         // let the staging fill the window with NaN, so NaN propagates.
         cst[0] = make_float4(0.f, 0.f, (float)A.margin_lo + 0.25f, 0.f);
         cst[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (dem) cst[2] = make_float4(0.f, 0.f, 0.f, 0.f);
         *klo_out = INT32_MIN;
         return 0;
     }
@@ -91,6 +94,7 @@ __device__ int pulse_setup(const BpArgs& A, int n, double cx, double cy, double 
     cst[1] = make_float4((float)(-0.125 * inv_r * inv_r * inv_r * idr),
                          (float)(0.0625 * inv_r * inv_r * inv_r * inv_r * inv_r * idr), (float)(inv_r * inv_r),
                          (float)(a * (1.0 + (3.0 / 32.0) * q * q)));
+    if (dem) cst[2] = make_float4((float)(2.0 * uz), 0.f, 0.f, 0.f);
     *klo_out = (int)klo_d;
     // Truncation error of each series for the worst pixel of the tile, in bins,
     // against 1e-6 bins (below the fp32 rounding of the window position).
@@ -186,11 +190,12 @@ __device__ __forceinline__ void mac(float& ar, float& ai, float& cr, float& ci, 
     }
 }
 
-template <int INTERP, int MODE, int ACC>
+template <int INTERP, int MODE, int ACC, bool DEM>
 __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* smem, const float4* cst,
                                                  const int* klo_s, int np, int n0, int i_pix, int j_pix0,
                                                  float dxl, const float* dyv, const float* ddv, float* accr,
-                                                 float* acci, float* cmpr, float* cmpi) {
+                                                 float* acci, float* cmpr, float* cmpi, const float* dzv,
+                                                 const float* hv) {
     const int eb = entry_bytes<INTERP>();
     const uint32_t wstride = (uint32_t)(A.win * eb);
     const float kappa = A.kappa;
@@ -198,13 +203,15 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
                                                    : (INTERP == SARBP_NEAREST ? BP_PUNROLL_NEAREST : BP_PUNROLL_SINC8);
 #pragma unroll kUnroll
     for (int p = 0; p < np; ++p) {
-        const float4 c0 = cst[2 * p];
-        const float4 c1 = cst[2 * p + 1];
+        constexpr int CS = DEM ? 3 : 2; // float4 constants per pulse
+        const float4 c0 = cst[CS * p];
+        const float4 c1 = cst[CS * p + 1];
+        const float4 c2 = DEM ? cst[CS * p + 2] : c1;
         const uint32_t wbase = (uint32_t)p * wstride;
         if constexpr (INTERP == SARBP_LINEAR) {
 #pragma unroll
             for (int m = 0; m < BP_PPT; ++m) {
-                const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, ddv[m])); // |d|^2 + 2 d.u
+                const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
                 const float ub = bin_position<MODE>(num, c0, c1);
                 const float f = __builtin_amdgcn_fractf(ub);
                 const uint32_t addr = ((uint32_t)ub << 4) + wbase;
@@ -223,7 +230,7 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
             bool tie = false;
 #pragma unroll
             for (int m = 0; m < BP_PPT; ++m) {
-                const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, ddv[m])); // |d|^2 + 2 d.u
+                const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
                 const float ub = bin_position<MODE>(num, c0, c1);
                 g[m] = __builtin_amdgcn_fractf(ub);
                 kb[m] = (uint32_t)ub;
@@ -235,8 +242,9 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
 #pragma unroll
                 for (int m = 0; m < BP_PPT; ++m) {
                     if (fabsf(g[m] - 0.5f) > 0.5f - A.tie_eps) {
+                        const double zp = DEM ? A.z0 + (double)hv[m] : A.z0; // the pixel's height
                         const int kabs = nearest_bin_fp64(A.pos[pn], A.pos[pn + 1], A.pos[pn + 2], A.x0, A.y0,
-                                                          A.z0, A.dx, A.dy, A.r0, A.dr, i_pix, j_pix0 + BP_WAVES * m);
+                                                          zp, A.dx, A.dy, A.r0, A.dr, i_pix, j_pix0 + BP_WAVES * m);
                         int kr = kabs - klo_s[p];
                         kr = kr < 0 ? 0 : (kr > A.win - 1 ? A.win - 1 : kr);
                         g[m] = g[m] + (float)((int)kb[m] - kr); // = ub - kr
@@ -259,7 +267,7 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
             // (built by stage_chunk).  Stored highest degree first, two per float4.
 #pragma unroll
             for (int m = 0; m < BP_PPT; ++m) {
-                const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, ddv[m])); // |d|^2 + 2 d.u
+                const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
                 const float ub = bin_position<MODE>(num, c0, c1);
                 const float f = __builtin_amdgcn_fractf(ub);
                 const float g = f - 0.5f;
@@ -363,7 +371,7 @@ __device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int n
 
 // At most 64 VGPRs, so two 1024-lane workgroups (8 waves per SIMD) fit on a CU:
 // the loop needs that many waves to hide LDS and transcendental latency.
-template <int INTERP, int ACC>
+template <int INTERP, int ACC, bool DEM>
 __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void bp_kernel(BpArgs A) {
     extern __shared__ __align__(16) char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -378,7 +386,8 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
 
     // tile centre (fp64) and this lane's pixel offsets from it
     const double cxp = (double)i0 + 0.5 * (BP_TX - 1), cyp = (double)j0 + 0.5 * (BP_TY - 1);
-    const double cx = A.x0 + cxp * A.dx, cy = A.y0 + cyp * A.dy, cz = A.z0;
+    const double cx = A.x0 + cxp * A.dx, cy = A.y0 + cyp * A.dy;
+    double cz = A.z0;
     const double ddx = ((double)lane - 0.5 * (BP_TX - 1)) * A.dx;
     const float dxl = (float)ddx;
     float dyv[BP_PPT], ddv[BP_PPT], accr[BP_PPT], acci[BP_PPT];
@@ -397,18 +406,66 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         sumi[m] = 0.0;
     }
 
+    // Terrain: pixel heights h (z = z0 + h); the tile centre sits at the tile's
+    // mid-height, so |dz| <= half the tile's height range, which the plan's
+    // window allows for up to dem_relief.  A tile beyond that bound is NaN.
+    float dzv[BP_PPT], hv[BP_PPT];
+    bool bad_tile = false;
+#pragma unroll
+    for (int m = 0; m < BP_PPT; ++m) dzv[m] = hv[m] = 0.f;
+    if constexpr (DEM) {
+        float hmin = INFINITY, hmax = -INFINITY;
+#pragma unroll
+        for (int m = 0; m < BP_PPT; ++m) {
+            const int j = j0 + wave + BP_WAVES * m, i = i0 + lane;
+            if (i < A.nx && j < A.ny) {
+                hv[m] = A.dem[(size_t)j * A.nx + i];
+                hmin = fminf(hmin, hv[m]);
+                hmax = fmaxf(hmax, hv[m]);
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            hmin = fminf(hmin, __shfl_xor(hmin, off));
+            hmax = fmaxf(hmax, __shfl_xor(hmax, off));
+        }
+        float* red = reinterpret_cast<float*>(smem);
+        if (lane == 0) {
+            red[2 * wave] = hmin;
+            red[2 * wave + 1] = hmax;
+        }
+        __syncthreads();
+        hmin = red[0];
+        hmax = red[1];
+        for (int w = 1; w < BP_WAVES; ++w) {
+            hmin = fminf(hmin, red[2 * w]);
+            hmax = fmaxf(hmax, red[2 * w + 1]);
+        }
+        __syncthreads();
+        bad_tile = !((double)hmax - (double)hmin <= A.dem_relief);
+        const double hc = 0.5 * ((double)hmin + (double)hmax);
+        cz = A.z0 + hc;
+#pragma unroll
+        for (int m = 0; m < BP_PPT; ++m) {
+            const double ddy = ((double)(wave + BP_WAVES * m) - 0.5 * (BP_TY - 1)) * A.dy;
+            const double ddz = (double)hv[m] - hc;
+            dzv[m] = (float)ddz;
+            ddv[m] = (float)(ddx * ddx + ddy * ddy + ddz * ddz);
+        }
+    }
+
     const int P = A.chunk, W = A.win;
     float4* cst = reinterpret_cast<float4*>(smem + (size_t)P * W * entry_bytes<INTERP>());
-    int* klo_s = reinterpret_cast<int*>(cst + 2 * P);
+    int* klo_s = reinterpret_cast<int*>(cst + (DEM ? 3 : 2) * P);
     int* prio_s = klo_s + P;
 
     // The first chunk is half size on alternate workgroups: both placements of a
     // CU's two workgroups (b, b + slots) and (b, b + 8) get opposite parities.
     const int stagger = BP_STAGGER ? (((int)blockIdx.x / A.slots) ^ ((int)blockIdx.x >> 3)) & 1 : 0;
-    for (int n0 = 0, np = 0; n0 < A.n; n0 += np) {
+    for (int n0 = 0, np = 0; n0 < (bad_tile ? 0 : A.n); n0 += np) {
         np = min((n0 == 0 && stagger) ? max(1, P >> 1) : P, A.n - n0);
         int need = 0;
-        if (tid < np) need = pulse_setup(A, n0 + tid, cx, cy, cz, cst + 2 * tid, klo_s + tid);
+        if (tid < np) need = pulse_setup(A, n0 + tid, cx, cy, cz, cst + (DEM ? 3 : 2) * tid, klo_s + tid, DEM);
         if (tid == 0) *prio_s = chunk_priority(A, n0);
         const int m1 = __syncthreads_or(need & 1);
         const int m2 = __syncthreads_or(need & 2);
@@ -416,14 +473,14 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         __syncthreads();
         set_priority(*prio_s);
         if (m2)
-            accumulate_chunk<INTERP, 2, ACC>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv, accr,
-                                              acci, cmpr, cmpi);
+            accumulate_chunk<INTERP, 2, ACC, DEM>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv,
+                                                   accr, acci, cmpr, cmpi, dzv, hv);
         else if (m1)
-            accumulate_chunk<INTERP, 1, ACC>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv, accr,
-                                              acci, cmpr, cmpi);
+            accumulate_chunk<INTERP, 1, ACC, DEM>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv,
+                                                   accr, acci, cmpr, cmpi, dzv, hv);
         else
-            accumulate_chunk<INTERP, 0, ACC>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv, accr,
-                                              acci, cmpr, cmpi);
+            accumulate_chunk<INTERP, 0, ACC, DEM>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv,
+                                                   accr, acci, cmpr, cmpi, dzv, hv);
         if constexpr (ACC == SARBP_ACC_CHUNK64) {
 #pragma unroll
             for (int m = 0; m < BP_PPT; ++m) {
@@ -436,6 +493,10 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         __syncthreads();
     }
 
+    if (bad_tile) {
+#pragma unroll
+        for (int m = 0; m < BP_PPT; ++m) accr[m] = acci[m] = sumr[m] = sumi[m] = NAN;
+    }
     const int i = i0 + lane;
     if (i < A.nx) {
 #pragma unroll
@@ -469,51 +530,54 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     }
 }
 
-template <int INTERP, int ACC>
+template <int INTERP, int ACC, bool DEM>
 int allow_lds_one(size_t bytes) {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(bp_kernel<INTERP, ACC>),
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(bp_kernel<INTERP, ACC, DEM>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) == hipSuccess
                ? SARBP_OK
                : SARBP_EDEVICE;
 }
 
-template <int INTERP>
+template <int INTERP, bool DEM>
 int allow_lds(int accum, size_t bytes) {
     switch (accum) {
-        case SARBP_ACC_KAHAN: return allow_lds_one<INTERP, SARBP_ACC_KAHAN>(bytes);
-        case SARBP_ACC_CHUNK64: return allow_lds_one<INTERP, SARBP_ACC_CHUNK64>(bytes);
-        default: return allow_lds_one<INTERP, SARBP_ACC_FP32>(bytes);
+        case SARBP_ACC_KAHAN: return allow_lds_one<INTERP, SARBP_ACC_KAHAN, DEM>(bytes);
+        case SARBP_ACC_CHUNK64: return allow_lds_one<INTERP, SARBP_ACC_CHUNK64, DEM>(bytes);
+        default: return allow_lds_one<INTERP, SARBP_ACC_FP32, DEM>(bytes);
     }
 }
 
-template <int INTERP>
+template <int INTERP, bool DEM>
 void launch(const BpArgs& A, int accum, size_t lds, hipStream_t stream) {
     const dim3 grid(A.ntiles), block(BP_THREADS);
     switch (accum) {
         case SARBP_ACC_KAHAN:
-            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_KAHAN>), grid, block, lds, stream, A);
+            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_KAHAN, DEM>), grid, block, lds, stream, A);
             break;
         case SARBP_ACC_CHUNK64:
-            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_CHUNK64>), grid, block, lds, stream, A);
+            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_CHUNK64, DEM>), grid, block, lds, stream, A);
             break;
         default:
-            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_FP32>), grid, block, lds, stream, A);
+            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_FP32, DEM>), grid, block, lds, stream, A);
             break;
     }
 }
 
 } // namespace
 
-int sarbp_bp_allow_lds(int interp, int accum, size_t bytes) {
+int sarbp_bp_allow_lds(int interp, int accum, bool dem, size_t bytes) {
     switch (interp) {
-        case SARBP_NEAREST: return allow_lds<SARBP_NEAREST>(accum, bytes);
-        case SARBP_LINEAR: return allow_lds<SARBP_LINEAR>(accum, bytes);
-        default: return allow_lds<SARBP_SINC8>(accum, bytes);
+        case SARBP_NEAREST:
+            return dem ? allow_lds<SARBP_NEAREST, true>(accum, bytes) : allow_lds<SARBP_NEAREST, false>(accum, bytes);
+        case SARBP_LINEAR:
+            return dem ? allow_lds<SARBP_LINEAR, true>(accum, bytes) : allow_lds<SARBP_LINEAR, false>(accum, bytes);
+        default:
+            return dem ? allow_lds<SARBP_SINC8, true>(accum, bytes) : allow_lds<SARBP_SINC8, false>(accum, bytes);
     }
 }
 
-int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* echo, float2* image, int n,
-                    int accumulate, hipStream_t stream) {
+int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* echo, const float* dem,
+                    float2* image, int n, int accumulate, hipStream_t stream) {
     const sarbp_params& p = plan->p;
     BpArgs A;
     A.pos = pos;
@@ -541,6 +605,8 @@ int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* ech
     A.dx = p.dx;
     A.dy = p.dy;
     A.half_span = plan->half_span;
+    A.dem = dem;
+    A.dem_relief = p.dem_relief;
     for (int i = 0; i < 32; ++i) A.sinc_poly[i] = plan->sinc_poly[i];
     A.half_span_bins = plan->half_span / p.dr;
     A.kappa = (float)(2.0 * p.dr / p.wavelength);
@@ -553,10 +619,20 @@ int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* ech
         A.half_rot = make_float2((float)cos(-2.0 * 3.14159265358979323846 * fr),
                                  (float)sin(-2.0 * 3.14159265358979323846 * fr));
     }
+    const bool d = dem != nullptr;
     switch (p.interp) {
-        case SARBP_NEAREST: launch<SARBP_NEAREST>(A, p.accum, plan->lds_bytes, stream); break;
-        case SARBP_LINEAR: launch<SARBP_LINEAR>(A, p.accum, plan->lds_bytes, stream); break;
-        default: launch<SARBP_SINC8>(A, p.accum, plan->lds_bytes, stream); break;
+        case SARBP_NEAREST:
+            d ? launch<SARBP_NEAREST, true>(A, p.accum, plan->lds_bytes, stream)
+              : launch<SARBP_NEAREST, false>(A, p.accum, plan->lds_bytes, stream);
+            break;
+        case SARBP_LINEAR:
+            d ? launch<SARBP_LINEAR, true>(A, p.accum, plan->lds_bytes, stream)
+              : launch<SARBP_LINEAR, false>(A, p.accum, plan->lds_bytes, stream);
+            break;
+        default:
+            d ? launch<SARBP_SINC8, true>(A, p.accum, plan->lds_bytes, stream)
+              : launch<SARBP_SINC8, false>(A, p.accum, plan->lds_bytes, stream);
+            break;
     }
     return hipGetLastError() == hipSuccess ? SARBP_OK : SARBP_EDEVICE;
 }

@@ -82,12 +82,14 @@ struct BpArgs {
     double half_span;      // half tile diagonal [m]
     double half_span_bins; // half_span / dr
     float sinc_poly[32];   // see sarbp_plan::sinc_poly
+    const float* dem;      // [ny][nx] pixel heights above z0 (terrain kernels), else null
+    double dem_relief;     // bound on one tile's height range (terrain kernels)
     float kappa;           // 2 dr / lambda: phase cycles per bin
     float tie_eps;         // nearest: fp64 recheck band around a rounding tie [bins]
     int round_half;        // nearest: window positions carry u + 1/2
     float2 half_rot;       // nearest: exp(-j pi kappa), folded into the staged samples
 };
 
-int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* echo, float2* image,
-                    int n, int accumulate, hipStream_t stream);
+int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* echo, const float* dem,
+                    float2* image, int n, int accumulate, hipStream_t stream);
 int sarbp_launch_rc(const sarbp_plan* plan, const float2* raw, float2* out, int n, hipStream_t stream);

@@ -12,7 +12,7 @@
 #include "sarbp_internal.h"
 
 int sarbp_rc_prepare_device();
-int sarbp_bp_allow_lds(int interp, int accum, size_t bytes);
+int sarbp_bp_allow_lds(int interp, int accum, bool dem, size_t bytes);
 
 namespace {
 
@@ -50,6 +50,7 @@ int validate(const sarbp_params* p) {
     if (p->n_pulses < 1 || p->nx < 1 || p->ny < 1) return SARBP_EINVAL;
     if (p->interp < SARBP_NEAREST || p->interp > SARBP_SINC8) return SARBP_EINVAL;
     if (p->accum < SARBP_ACC_FP32 || p->accum > SARBP_ACC_CHUNK64) return SARBP_EINVAL;
+    if (!isfinite(p->dem_relief) || p->dem_relief < 0.0 || p->dem_relief > 1.0e4) return SARBP_EINVAL;
     if (p->n_range < (p->interp == SARBP_SINC8 ? 8 : 2)) return SARBP_EINVAL;
     if (!isfinite(p->r0) || !finite_pos(p->dr) || !finite_pos(p->dx) || !finite_pos(p->dy)) return SARBP_EINVAL;
     if (!isfinite(p->x0) || !isfinite(p->y0) || !isfinite(p->z0) || !finite_pos(p->wavelength)) return SARBP_EINVAL;
@@ -200,7 +201,9 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
         release(plan);
         return SARBP_EINVAL;
     }
-    plan->half_span = 0.5 * sqrt((BP_TX * p.dx) * (BP_TX * p.dx) + (BP_TY * p.dy) * (BP_TY * p.dy));
+    // (with terrain, the tile centre is at the tile's mid-height: |dz| <= dem_relief / 2)
+    plan->half_span = 0.5 * sqrt((BP_TX * p.dx) * (BP_TX * p.dx) + (BP_TY * p.dy) * (BP_TY * p.dy) +
+                                 p.dem_relief * p.dem_relief);
     const double span_bins = ceil(2.0 * plan->half_span / p.dr);
     // The window holds the bins floor(u) can take (the sinc8 taps are folded into
     // each bin's polynomial), with a spare bin each side.
@@ -213,7 +216,7 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     plan->win = (int)span_bins + plan->margin_lo + 2 + taps_hi;
     const int eb = p.interp == SARBP_NEAREST ? 8 : (p.interp == SARBP_LINEAR ? 16 : 64);
     if (p.interp == SARBP_SINC8) sinc8_polynomials(plan->sinc_poly);
-    const int per_pulse = plan->win * eb + 2 * 16 + 4;
+    const int per_pulse = plan->win * eb + (p.dem_relief > 0.0 ? 3 : 2) * 16 + 4;
     // Coarse grids (long windows) that would stage fewer than 8 pulses per step
     // use up to 150 KiB of LDS: one workgroup per CU instead of two.
     int chunk = (BP_LDS_BUDGET - 64) / per_pulse;
@@ -226,7 +229,8 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     plan->chunk = chunk;
     plan->lds_bytes = (size_t)chunk * per_pulse + 16; // + the chunk's issue-priority word
     if (plan->lds_bytes > 64 * 1024) {
-        st = sarbp_bp_allow_lds(p.interp, p.accum, plan->lds_bytes);
+        st = sarbp_bp_allow_lds(p.interp, p.accum, false, plan->lds_bytes);
+        if (st == SARBP_OK && p.dem_relief > 0.0) st = sarbp_bp_allow_lds(p.interp, p.accum, true, plan->lds_bytes);
         if (st != SARBP_OK) {
             release(plan);
             return st;
@@ -291,8 +295,22 @@ extern "C" int sarbp_backproject(const sarbp_plan* plan, const double* positions
     if (n < 1 || n > plan->p.n_pulses || (accumulate != 0 && accumulate != 1)) return SARBP_EINVAL;
     const int st = check_device(plan);
     if (st != SARBP_OK) return st;
-    return sarbp_launch_bp(plan, positions_d, static_cast<const float2*>(echo_d), static_cast<float2*>(image_d), n,
-                           accumulate, static_cast<hipStream_t>(stream));
+    return sarbp_launch_bp(plan, positions_d, static_cast<const float2*>(echo_d), nullptr,
+                           static_cast<float2*>(image_d), n, accumulate, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int sarbp_backproject_dem(const sarbp_plan* plan, const double* positions_d, const void* echo_d,
+                                     const float* dem_d, void* image_d, int32_t n, int32_t accumulate,
+                                     void* stream) {
+    if (plan == nullptr || !(plan->p.dem_relief > 0.0) || dem_d == nullptr ||
+        (reinterpret_cast<uintptr_t>(dem_d) & 3u) != 0 || !aligned8(positions_d) || !aligned8(echo_d) ||
+        !aligned8(image_d))
+        return SARBP_EINVAL;
+    if (n < 1 || n > plan->p.n_pulses || (accumulate != 0 && accumulate != 1)) return SARBP_EINVAL;
+    const int st = check_device(plan);
+    if (st != SARBP_OK) return st;
+    return sarbp_launch_bp(plan, positions_d, static_cast<const float2*>(echo_d), dem_d,
+                           static_cast<float2*>(image_d), n, accumulate, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int sarbp_range_compress(const sarbp_plan* plan, const void* raw_d, void* out_d, int32_t n, void* stream) {

@@ -135,7 +135,7 @@ extern "C" int sarbp_backproject_host(sarbp_stream* s, const double* positions_h
             if (st != SARBP_OK) return st;
             echo = s->rc_d;
         }
-        const int st = sarbp_launch_bp(s->plan, s->pos_d[b], echo, static_cast<float2*>(image_d), np,
+        const int st = sarbp_launch_bp(s->plan, s->pos_d[b], echo, nullptr, static_cast<float2*>(image_d), np,
                                        (c == 0) ? accumulate : 1, work);
         if (st != SARBP_OK) return st;
         if (hipEventRecord(s->released[b], work) != hipSuccess) return SARBP_EDEVICE;

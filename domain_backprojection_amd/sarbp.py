@@ -66,6 +66,7 @@ class sarbp_params(ctypes.Structure):
         ("taylor_nbar", ctypes.c_int32),
         ("taylor_sll", ctypes.c_double),
         ("accum", ctypes.c_int32),
+        ("dem_relief", ctypes.c_double),
     ]
 
 
@@ -88,10 +89,14 @@ _lib.sarbp_backproject_host.argtypes = [_vp, _vp, _vp, _vp, ctypes.c_int32, ctyp
 _lib.sarbp_backproject_host.restype = ctypes.c_int
 _lib.sarbp_stream_destroy.argtypes = [_vp]
 _lib.sarbp_stream_destroy.restype = None
+_lib.sarbp_interpolate_track.argtypes = [_vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp]
+_lib.sarbp_interpolate_track.restype = ctypes.c_int
+_lib.sarbp_backproject_dem.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp]
+_lib.sarbp_backproject_dem.restype = ctypes.c_int
 
 EXPORTS = ("sarbp_plan_create", "sarbp_backproject", "sarbp_range_compress", "sarbp_destroy",
            "sarbp_status_string", "sarbp_version", "sarbp_stream_create", "sarbp_backproject_host",
-           "sarbp_stream_destroy")
+           "sarbp_stream_destroy", "sarbp_interpolate_track", "sarbp_backproject_dem")
 
 
 class SarbpError(RuntimeError):
@@ -109,12 +114,12 @@ def sarbp_version() -> int:
 
 
 def make_params(n_pulses, n_range, r0, dr, nx, ny, x0, y0, z0, dx, dy, wavelength, interp="linear",
-                n_fast=0, fs=0.0, chirp_T=0.0, chirp_B=0.0, window=0, taylor_nbar=0, taylor_sll=0.0, accum="fp32") -> sarbp_params:
+                n_fast=0, fs=0.0, chirp_T=0.0, chirp_B=0.0, window=0, taylor_nbar=0, taylor_sll=0.0, accum="fp32", dem_relief=0.0) -> sarbp_params:
     return sarbp_params(int(n_pulses), int(n_range), float(r0), float(dr), int(nx), int(ny), float(x0),
                         float(y0), float(z0), float(dx), float(dy), float(wavelength),
                         INTERP[interp] if isinstance(interp, str) else int(interp), int(n_fast), float(fs),
                         float(chirp_T), float(chirp_B), int(window), int(taylor_nbar), float(taylor_sll),
-                        ACCUM[accum] if isinstance(accum, str) else int(accum))
+                        ACCUM[accum] if isinstance(accum, str) else int(accum), float(dem_relief))
 
 
 def sarbp_plan_create(params: sarbp_params) -> int:
@@ -160,6 +165,23 @@ def sarbp_backproject(handle, positions: torch.Tensor, echo: torch.Tensor, image
                                 int(n), int(accumulate), _stream(stream))
     if st != SARBP_OK:
         raise SarbpError(st, "sarbp_backproject")
+
+
+def sarbp_backproject_dem(handle, positions: torch.Tensor, echo: torch.Tensor, dem: torch.Tensor,
+                          image: torch.Tensor, n: int | None = None, accumulate: int = 0, stream=None) -> None:
+    """As :func:`sarbp_backproject`, with pixel heights dem float32 (ny, nx) on the device."""
+    if n is None:
+        n = positions.shape[0]
+    if positions.dim() != 2 or positions.shape[1] != 3 or positions.shape[0] < n or echo.shape[0] < n:
+        raise ValueError("positions must be (>= n, 3) and echo (>= n, n_range)")
+    if tuple(dem.shape) != tuple(image.shape):
+        raise ValueError("dem must have the image's shape (ny, nx)")
+    st = _lib.sarbp_backproject_dem(handle, _dev_ptr(positions, torch.float64, "positions"),
+                                    _dev_ptr(echo, torch.complex64, "echo"), _dev_ptr(dem, torch.float32, "dem"),
+                                    _dev_ptr(image, torch.complex64, "image"), int(n), int(accumulate),
+                                    _stream(stream))
+    if st != SARBP_OK:
+        raise SarbpError(st, "sarbp_backproject_dem")
 
 
 def sarbp_range_compress(handle, raw: torch.Tensor, out: torch.Tensor, n: int | None = None, stream=None) -> None:
@@ -212,6 +234,25 @@ def sarbp_stream_destroy(stream_handle) -> None:
     _lib.sarbp_stream_destroy(stream_handle)
 
 
+def sarbp_interpolate_track(nav_t: torch.Tensor, nav_xyz: torch.Tensor, t: torch.Tensor,
+                            out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Positions float64 (n, 3) at pulse times t (n,) from navigation samples nav_t (M,)
+    and nav_xyz (M, 3), all float64 on the device."""
+    if nav_t.dim() != 1 or nav_xyz.shape != (nav_t.shape[0], 3) or t.dim() != 1:
+        raise ValueError("nav_t must be (M,), nav_xyz (M, 3) and t (n,)")
+    if out is None:
+        out = torch.empty((t.shape[0], 3), dtype=torch.float64, device=t.device)
+    if tuple(out.shape) != (t.shape[0], 3):
+        raise ValueError("out must be (n, 3)")
+    st = _lib.sarbp_interpolate_track(_dev_ptr(nav_t, torch.float64, "nav_t"),
+                                      _dev_ptr(nav_xyz, torch.float64, "nav_xyz"), int(nav_t.shape[0]),
+                                      _dev_ptr(t, torch.float64, "t"), _dev_ptr(out, torch.float64, "out"),
+                                      int(t.shape[0]), _stream(stream))
+    if st != SARBP_OK:
+        raise SarbpError(st, "sarbp_interpolate_track")
+    return out
+
+
 class Plan:
     """Owns one plan handle; checks tensor shapes against the plan's sizes."""
 
@@ -247,14 +288,18 @@ class Plan:
     def new_image(self, device="cuda") -> torch.Tensor:
         return torch.zeros((self.params.ny, self.params.nx), dtype=torch.complex64, device=device)
 
-    def backproject(self, positions, echo, image=None, n=None, accumulate=0, stream=None) -> torch.Tensor:
+    def backproject(self, positions, echo, image=None, n=None, accumulate=0, stream=None, dem=None) -> torch.Tensor:
         if image is None:
             image = torch.empty((self.params.ny, self.params.nx), dtype=torch.complex64, device=echo.device)
         if tuple(image.shape) != (self.params.ny, self.params.nx):
             raise ValueError("image shape does not match the plan")
         if echo.dim() != 2 or echo.shape[1] != self.params.n_range:
             raise ValueError("echo must be (n, n_range)")
-        sarbp_backproject(self.handle, positions, echo, image, n=n, accumulate=accumulate, stream=stream)
+        if dem is None:
+            sarbp_backproject(self.handle, positions, echo, image, n=n, accumulate=accumulate, stream=stream)
+        else:
+            sarbp_backproject_dem(self.handle, positions, echo, dem, image, n=n, accumulate=accumulate,
+                                  stream=stream)
         return image
 
     def range_compress(self, raw, out=None, n=None, stream=None) -> torch.Tensor:

@@ -88,6 +88,10 @@ typedef struct {
     int32_t taylor_nbar; /* Taylor: nearly equal sidelobes, 2..64 (0: 4)                        */
     double taylor_sll;   /* Taylor: design sidelobe level in dB below the peak, 13..150 (0: 35)  */
     int32_t accum;       /* sarbp_accum of sarbp_backproject (0: SARBP_ACC_FP32)                 */
+    double dem_relief;   /* terrain (sarbp_backproject_dem): bound on the height range, max - min,
+                          * within any 64 x 32-pixel block of the grid aligned to pixel (0, 0)
+                          * (the whole map's range will do); 0 disables terrain.  The echo
+                          * windows grow with it.                                            */
 } sarbp_params;
 
 typedef struct sarbp_plan sarbp_plan; /* opaque */
@@ -112,6 +116,17 @@ int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out);
 int sarbp_backproject(const sarbp_plan* plan, const double* positions_d, const void* echo_d,
                       void* image_d, int32_t n, int32_t accumulate, void* stream);
 
+/* Backproject onto terrain (section 3.3 of the page: the pixel height may have to
+ * follow elevation data): as sarbp_backproject, with pixel (i, j) at
+ * (x0 + i dx, y0 + j dy, z0 + dem[j * nx + i]).
+ *   dem_d : device, float32 [ny][nx] heights above z0, 4-byte aligned
+ * The plan must have dem_relief > 0.  Pixels of a 64 x 32 block whose heights
+ * span more than dem_relief come out NaN, as does a pixel with a non-finite
+ * height.  Returns SARBP_EINVAL (as sarbp_backproject, or a null or misaligned
+ * dem, or a plan without terrain), SARBP_EDEVICE on a launch failure. */
+int sarbp_backproject_dem(const sarbp_plan* plan, const double* positions_d, const void* echo_d, const float* dem_d,
+                          void* image_d, int32_t n, int32_t accumulate, void* stream);
+
 /* Range-compress n raw pulses (section 3.1 of the page):
  *   out_n = IFFT( FFT(raw_n) * conj(FFT(ref)) * W ) with 1/n_fast on the inverse,
  *   ref[m mod n_fast] = p(m / fs), m = -L/2 .. L/2 - 1, L = round(chirp_T * fs).
@@ -126,6 +141,26 @@ int sarbp_range_compress(const sarbp_plan* plan, const void* raw_d, void* out_d,
 /* Release the plan and its device tables.  NULL is a no-op.  The caller must
  * ensure no call using the plan is still running. */
 void sarbp_destroy(sarbp_plan* plan);
+
+/* ---- Antenna positions from navigation samples (section 3.3 of the page: in
+ * practice the radar position of each pulse may have to be interpolated from the
+ * flight track). -------------------------------------------------------------- */
+
+/* Interpolate positions at n pulse times from n_nav navigation samples: per axis,
+ * the cubic Lagrange polynomial through the 4 samples around the time (two on each
+ * side where the record allows: samples j0 .. j0+3, j0 = clamp(i - 1, 0, n_nav - 4)
+ * for the interval i with nav_t[i] <= t < nav_t[i+1]), in double precision.
+ *   nav_t_d     : device, float64 [n_nav], strictly increasing sample times
+ *   nav_xyz_d   : device, float64 [n_nav][3] sampled positions
+ *   t_d         : device, float64 [n] pulse times
+ *   positions_d : device, float64 [n][3] output, ready for sarbp_backproject; must
+ *                 not overlap the inputs
+ * A time outside [nav_t[0], nav_t[n_nav-1]], a non-finite time, or a stencil whose
+ * times do not increase gives NaN for that pulse (which backprojection propagates).
+ * Returns SARBP_EINVAL (null or misaligned pointer, n_nav < 4, n < 1, overlap),
+ * SARBP_EDEVICE on a launch failure.  Asynchronous on `stream`. */
+int sarbp_interpolate_track(const double* nav_t_d, const double* nav_xyz_d, int32_t n_nav, const double* t_d,
+                            double* positions_d, int32_t n, void* stream);
 
 /* ---- Streaming pulses from host memory (section 3.3 of the page: prefetch the
  * echo with streams so that copies overlap computation). --------------------- */

@@ -8,6 +8,7 @@ library and its binding never import, link or call it, and share no code with it
   ``bp_oracle.c`` (plain IEEE double precision, gcc ``-O2 -ffp-contract=off``,
   OpenMP over image rows), the definition stated in that file's header.
 * :mod:`oracle.rc` holds the fp64 FFT matched filter (numpy).
+* :mod:`oracle.track` interpolates antenna positions from navigation samples (numpy).
 
 Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
 closed forms, textbook impulse-response figures, special cases and invariants
@@ -25,6 +26,7 @@ import threading
 import numpy as np
 
 from . import rc  # noqa: F401  (re-export)
+from . import track  # noqa: F401  (re-export)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "_bp_oracle.so")
@@ -56,9 +58,15 @@ def _load():
             lib.oracle_backproject_rows.argtypes = [i, i, dp, dp, d, d, i, i, d, d, d, d, d, d, i, i, i, dp, i]
             lib.oracle_backproject_pixels.argtypes = [i, i, dp, dp, d, d, d, d, d, d, d, d, i, i, lp, dp, i]
             lib.oracle_nearest_index.argtypes = [dp, d, d, d, d, d, d, d, i, lp, lp]
+            fp = ctypes.POINTER(ctypes.c_float)
+            lib.oracle_backproject_rows_dem.argtypes = [i, i, dp, dp, d, d, i, i, d, d, d, d, d, fp, d, i, i, i,
+                                                        dp, i]
+            lib.oracle_backproject_pixels_dem.argtypes = [i, i, dp, dp, d, d, d, d, d, d, d, i, fp, d, i, i, lp,
+                                                          dp, i]
             lib.oracle_sinc8_weight.argtypes = [d]
             lib.oracle_sinc8_weight.restype = d
-            for f in (lib.oracle_backproject_rows, lib.oracle_backproject_pixels, lib.oracle_nearest_index):
+            for f in (lib.oracle_backproject_rows, lib.oracle_backproject_pixels, lib.oracle_nearest_index,
+                      lib.oracle_backproject_rows_dem, lib.oracle_backproject_pixels_dem):
                 f.restype = ctypes.c_int
             _lib = lib
     return _lib
@@ -83,9 +91,17 @@ def _interp(interp):
     return INTERP[interp] if isinstance(interp, str) else int(interp)
 
 
+def _dem32(dem, ny, nx):
+    d = np.ascontiguousarray(dem, dtype=np.float32)
+    if d.shape != (ny, nx):
+        raise ValueError("dem must be (ny, nx)")
+    return d, d.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
 def backproject(positions, echo, r0, dr, nx, ny, x0, y0, z0, dx, dy, wavelength, interp,
-                rows=None, nthreads=None) -> np.ndarray:
-    """Image (ny, nx) complex128, or rows [j0, j1) of it when ``rows=(j0, j1)``."""
+                rows=None, nthreads=None, dem=None) -> np.ndarray:
+    """Image (ny, nx) complex128, or rows [j0, j1) of it when ``rows=(j0, j1)``.  With
+    ``dem`` (float32 (ny, nx)), pixel (i, j) lies at height z0 + dem[j, i]."""
     lib = _load()
     pos, pp = _f64(positions)
     e, ep = _echo128(echo)
@@ -93,29 +109,41 @@ def backproject(positions, echo, r0, dr, nx, ny, x0, y0, z0, dx, dy, wavelength,
     assert pos.shape == (na, 3)
     j0, j1 = (0, ny) if rows is None else rows
     out = np.zeros((j1 - j0, nx), dtype=np.complex128)
-    rc_ = lib.oracle_backproject_rows(na, nr, pp, ep, r0, dr, nx, ny, x0, y0, z0, dx, dy, wavelength,
-                                      _interp(interp), j0, j1,
-                                      out.view(np.float64).ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
-                                      nthreads or threads())
+    op = out.view(np.float64).ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    if dem is None:
+        rc_ = lib.oracle_backproject_rows(na, nr, pp, ep, r0, dr, nx, ny, x0, y0, z0, dx, dy, wavelength,
+                                          _interp(interp), j0, j1, op, nthreads or threads())
+    else:
+        d, dp_ = _dem32(dem, ny, nx)
+        rc_ = lib.oracle_backproject_rows_dem(na, nr, pp, ep, r0, dr, nx, ny, x0, y0, z0, dx, dy, dp_, wavelength,
+                                              _interp(interp), j0, j1, op, nthreads or threads())
     if rc_ != 0:
         raise ValueError("oracle_backproject_rows rejected its arguments")
     return out
 
 
 def backproject_pixels(positions, echo, r0, dr, x0, y0, z0, dx, dy, wavelength, interp, ij,
-                       nthreads=None) -> np.ndarray:
-    """Values at grid pixels ``ij`` ((P, 2) int: i along x, j along y), complex128 (P,)."""
+                       nthreads=None, dem=None) -> np.ndarray:
+    """Values at grid pixels ``ij`` ((P, 2) int: i along x, j along y), complex128 (P,).
+    With ``dem`` (float32 (ny, nx)), pixel (i, j) lies at height z0 + dem[j, i]."""
     lib = _load()
     pos, pp = _f64(positions)
     e, ep = _echo128(echo)
     na, nr = e.shape
     ij = np.ascontiguousarray(ij, dtype=np.int64).reshape(-1, 2)
     out = np.zeros(ij.shape[0], dtype=np.complex128)
-    rc_ = lib.oracle_backproject_pixels(na, nr, pp, ep, r0, dr, x0, y0, z0, dx, dy, wavelength,
-                                        _interp(interp), ij.shape[0],
-                                        ij.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
-                                        out.view(np.float64).ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
-                                        nthreads or threads())
+    ijp = ij.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    op = out.view(np.float64).ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    if dem is None:
+        rc_ = lib.oracle_backproject_pixels(na, nr, pp, ep, r0, dr, x0, y0, z0, dx, dy, wavelength,
+                                            _interp(interp), ij.shape[0], ijp, op, nthreads or threads())
+    else:
+        d = np.ascontiguousarray(dem, dtype=np.float32)
+        if ij.size and (ij[:, 0].max() >= d.shape[1] or ij[:, 1].max() >= d.shape[0] or ij.min() < 0):
+            raise ValueError("pixel outside the dem")
+        rc_ = lib.oracle_backproject_pixels_dem(na, nr, pp, ep, r0, dr, x0, y0, z0, dx, dy, d.shape[1],
+                                                d.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), wavelength,
+                                                _interp(interp), ij.shape[0], ijp, op, nthreads or threads())
     if rc_ != 0:
         raise ValueError("oracle_backproject_pixels rejected its arguments")
     return out
@@ -141,14 +169,15 @@ def sinc8_weight(t: float) -> float:
 
 
 def scene_backproject(scene, echo=None, rows=None, nthreads=None) -> np.ndarray:
-    """:func:`backproject` with the geometry of a ``synth.Scene``."""
+    """:func:`backproject` with the geometry of a ``synth.Scene`` (and its dem, if any)."""
     return backproject(scene.positions, scene.echo if echo is None else echo, scene.r0, scene.dr,
                        scene.nx, scene.ny, scene.x0, scene.y0, scene.z0, scene.dx, scene.dy,
-                       scene.wavelength, scene.interp, rows=rows, nthreads=nthreads)
+                       scene.wavelength, scene.interp, rows=rows, nthreads=nthreads,
+                       dem=getattr(scene, "dem", None))
 
 
 def scene_pixels(scene, ij, echo=None, nthreads=None) -> np.ndarray:
-    """:func:`backproject_pixels` with the geometry of a ``synth.Scene``."""
+    """:func:`backproject_pixels` with the geometry of a ``synth.Scene`` (and its dem, if any)."""
     return backproject_pixels(scene.positions, scene.echo if echo is None else echo, scene.r0, scene.dr,
                               scene.x0, scene.y0, scene.z0, scene.dx, scene.dy, scene.wavelength,
-                              scene.interp, ij, nthreads=nthreads)
+                              scene.interp, ij, nthreads=nthreads, dem=getattr(scene, "dem", None))

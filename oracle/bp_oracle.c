@@ -33,6 +33,10 @@
  *
  * The sinc8 kernel shape is a reading (the page names sinc interpolation but
  * does not define it): eight taps, Hamming-windowed, not normalised.
+ *
+ * Terrain (section 3.3 notes that terrain height may have to be taken into
+ * account): the *_dem variants place pixel (i, j) at height z0 + dem[j*nx + i]
+ * instead of the plane z = z0; dem is float32, each value taken exactly.
  */
 #include <math.h>
 #include <stdint.h>
@@ -184,6 +188,45 @@ int oracle_nearest_index(const double* a, double r0, double dr, double x0, doubl
         double R = sqrt(ddx * ddx + ddy * ddy + ddz * ddz);
         double u = (R - r0) / dr;
         k_out[p] = (int64_t)floor(u + 0.5);
+    }
+    return 0;
+}
+
+/* As oracle_backproject_rows, with pixel (i, j) at height z0 + dem[j * nx + i]. */
+int oracle_backproject_rows_dem(int na, int nr, const double* pos, const double* echo, double r0,
+                                double dr, int nx, int ny, double x0, double y0, double z0, double dx,
+                                double dy, const float* dem, double lam, int interp, int j0, int j1,
+                                double* image, int nthreads) {
+    if (check(na, nr, dr, lam, interp) || nx <= 0 || ny <= 0 || j0 < 0 || j1 > ny || j1 < j0 || !dem) return -1;
+    set_threads(nthreads);
+    orc_problem P = {na, nr, pos, echo, r0, dr, lam, interp};
+#pragma omp parallel for schedule(static)
+    for (int j = j0; j < j1; ++j) {
+        double y = y0 + (double)j * dy;
+        for (int i = 0; i < nx; ++i) {
+            double x = x0 + (double)i * dx;
+            double z = z0 + (double)dem[(size_t)j * nx + i];
+            double* o = image + (size_t)2 * ((size_t)(j - j0) * nx + i);
+            pixel_sum(&P, x, y, z, o, o + 1);
+        }
+    }
+    return 0;
+}
+
+/* As oracle_backproject_pixels, with pixel (i, j) at height z0 + dem[j * nx + i]. */
+int oracle_backproject_pixels_dem(int na, int nr, const double* pos, const double* echo, double r0,
+                                  double dr, double x0, double y0, double z0, double dx, double dy, int nx,
+                                  const float* dem, double lam, int interp, int npix, const int64_t* ij,
+                                  double* out, int nthreads) {
+    if (check(na, nr, dr, lam, interp) || npix < 0 || nx <= 0 || !dem) return -1;
+    set_threads(nthreads);
+    orc_problem P = {na, nr, pos, echo, r0, dr, lam, interp};
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int p = 0; p < npix; ++p) {
+        double x = x0 + (double)ij[2 * p] * dx;
+        double y = y0 + (double)ij[2 * p + 1] * dy;
+        double z = z0 + (double)dem[(size_t)ij[2 * p + 1] * nx + ij[2 * p]];
+        pixel_sum(&P, x, y, z, out + 2 * (size_t)p, out + 2 * (size_t)p + 1);
     }
     return 0;
 }

@@ -146,6 +146,7 @@ class Scene:
     chirp_T: float = CHIRP_T
     chirp_B: float = BANDWIDTH
     window: int = 1
+    dem: np.ndarray | None = None  # (ny, nx) float32 pixel heights above z0, or None (the plane z = z0)
 
     @property
     def updates(self) -> int:
@@ -170,25 +171,74 @@ class Scene:
                     wavelength=self.wavelength, interp=self.interp)
 
 
-def track(na: int, rng: np.random.Generator | None = None, perturbed: bool = False) -> np.ndarray:
-    """Antenna phase centres (na, 3): straight line at constant speed, plus an optional
-    seeded smooth deviation per axis, sum over m=1..3 of (0.5/3 m) sin(2 pi f_m t + psi_m),
-    f_m ~ U[0.02, 0.5] Hz, psi_m ~ U[0, 2 pi)."""
-    t = (np.arange(na, dtype=np.float64) - (na - 1) / 2.0) / PRF
-    pos = np.empty((na, 3), dtype=np.float64)
+def track_model(rng: np.random.Generator | None = None, perturbed: bool = False):
+    """Draw the seeded deviation of a track: frequencies f and phases psi, (3 axes, 3 terms)
+    each, or None for a straight track."""
+    if not perturbed:
+        return None
+    assert rng is not None
+    f = rng.uniform(0.02, 0.5, size=(3, 3))
+    psi = rng.uniform(0.0, 2.0 * np.pi, size=(3, 3))
+    return f, psi
+
+
+def track_at(t: np.ndarray, model=None) -> np.ndarray:
+    """Antenna phase centres (len(t), 3) at slow times t [s]: straight line at constant
+    speed through the origin's broadside point at t = 0, plus the drawn deviation per
+    axis, sum over m=1..3 of (0.5/3 m) sin(2 pi f_m t + psi_m)."""
+    t = np.asarray(t, dtype=np.float64)
+    pos = np.empty((t.size, 3), dtype=np.float64)
     pos[:, 0] = V_PLATFORM * t
     pos[:, 1] = -GROUND_RANGE
     pos[:, 2] = ALTITUDE
-    if perturbed:
-        assert rng is not None
-        f = rng.uniform(0.02, 0.5, size=(3, 3))
-        psi = rng.uniform(0.0, 2.0 * np.pi, size=(3, 3))
+    if model is not None:
+        f, psi = model
         for ax in range(3):
-            dev = np.zeros(na)
+            dev = np.zeros(t.size)
             for m in range(3):
                 dev += (TRACK_DEV_AMP / 3.0) * np.sin(2.0 * np.pi * f[ax, m] * t + psi[ax, m])
             pos[:, ax] += dev
     return pos
+
+
+def pulse_times(na: int) -> np.ndarray:
+    """Slow time of each pulse, centred on the aperture: (n - (na-1)/2) / PRF."""
+    return (np.arange(na, dtype=np.float64) - (na - 1) / 2.0) / PRF
+
+
+def track(na: int, rng: np.random.Generator | None = None, perturbed: bool = False) -> np.ndarray:
+    """Antenna phase centres (na, 3) at the pulse times: straight line at constant speed,
+    plus an optional seeded smooth deviation per axis, sum over m=1..3 of
+    (0.5/3 m) sin(2 pi f_m t + psi_m), f_m ~ U[0.02, 0.5] Hz, psi_m ~ U[0, 2 pi)."""
+    return track_at(pulse_times(na), track_model(rng, perturbed))
+
+
+def terrain(nx: int, ny: int, dx: float, dy: float, rng: np.random.Generator, relief: float,
+            hills: int = 8) -> np.ndarray:
+    """Smooth terrain heights (ny, nx) float32 above the reference plane: a sum of
+    seeded Gaussian hills and dips (centres over the scene, widths 15-40 % of its
+    smaller side), shifted and scaled to a peak-to-peak `relief` centred on zero."""
+    X, Y = np.meshgrid((np.arange(nx) - nx / 2) * dx, (np.arange(ny) - ny / 2) * dy)
+    side = min(nx * dx, ny * dy)
+    h = np.zeros((ny, nx))
+    for _ in range(hills):
+        cx, cy = rng.uniform(-0.5, 0.5) * nx * dx, rng.uniform(-0.5, 0.5) * ny * dy
+        sig = rng.uniform(0.15, 0.4) * side
+        h += rng.uniform(-1.0, 1.0) * np.exp(-((X - cx) ** 2 + (Y - cy) ** 2) / (2.0 * sig * sig))
+    h = (h - h.min()) / max(h.max() - h.min(), 1e-30) * relief - 0.5 * relief
+    return h.astype(np.float32)
+
+
+def block_relief(dem: np.ndarray, bx: int = 64, by: int = 32) -> float:
+    """Largest height range (max - min) within the bx x by blocks aligned to pixel (0, 0):
+    the bound a terrain plan needs."""
+    ny, nx = dem.shape
+    worst = 0.0
+    for j in range(0, ny, by):
+        for i in range(0, nx, bx):
+            b = dem[j:j + by, i:i + bx].astype(np.float64)
+            worst = max(worst, float(b.max() - b.min()))
+    return worst
 
 
 def target_pixels(nx: int, ny: int, k: int, rng: np.random.Generator) -> np.ndarray:
@@ -275,9 +325,12 @@ def complex_normal(rng: np.random.Generator, shape, var: float) -> np.ndarray:
 
 def make_scene(cfg: int, seed: int | None = None, **over) -> Scene:
     """Build configuration ``cfg`` (1..5).  Keyword overrides (na, nr, nx, ny, interp,
-    n_targets, clutter, noise_var, track, clutter_half) give reduced variants for tests."""
+    n_targets, clutter, noise_var, track, clutter_half) give reduced variants for tests;
+    ``dem_relief`` (metres, peak to peak) puts the grid, targets and clutter on seeded
+    terrain (drawn right after the targets)."""
     spec = dict(CONFIGS[cfg])
     clutter_half = over.pop("clutter_half", CLUTTER_HALF_TAPS)
+    dem_relief = over.pop("dem_relief", None)
     spec.update(over)
     seed = 1000 + cfg if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -287,7 +340,9 @@ def make_scene(cfg: int, seed: int | None = None, **over) -> Scene:
     r0 = RC_CENTRE - (nr // 2) * DR
     positions = track(na, rng, perturbed=(spec["track"] == "perturbed"))
     tg = target_pixels(nx, ny, spec["n_targets"], rng)
-    pts = np.stack([x0 + tg[:, 0] * dx, y0 + tg[:, 1] * dy, np.full(len(tg), z0)], axis=1)
+    dem = None if dem_relief is None else terrain(nx, ny, dx, dy, rng, float(dem_relief))
+    tz = np.full(len(tg), z0) if dem is None else z0 + dem[tg[:, 1], tg[:, 0]].astype(np.float64)
+    pts = np.stack([x0 + tg[:, 0] * dx, y0 + tg[:, 1] * dy, tz], axis=1)
     amp = np.ones(len(tg), dtype=np.complex128)
     echo = raw = None
     if spec["raw"]:
@@ -300,18 +355,19 @@ def make_scene(cfg: int, seed: int | None = None, **over) -> Scene:
         acc = render_points(positions, nr, r0, DR, pts, amp, half=half)
         if spec["clutter"]:
             sigma = complex_normal(rng, (ny, nx), CLUTTER_VAR)
-            if spec["track"] == "straight":
+            if spec["track"] == "straight" and dem is None:
                 render_grid_straight(na, nr, r0, DR, nx, ny, x0, y0, z0, dx, dy, sigma, clutter_half, acc)
             else:
                 jj, ii = np.meshgrid(np.arange(ny), np.arange(nx), indexing="ij")
-                cells = np.stack([x0 + ii.ravel() * dx, y0 + jj.ravel() * dy, np.full(ii.size, z0)], axis=1)
+                cz = np.full(ii.size, z0) if dem is None else z0 + dem.ravel().astype(np.float64)
+                cells = np.stack([x0 + ii.ravel() * dx, y0 + jj.ravel() * dy, cz], axis=1)
                 render_points(positions, nr, r0, DR, cells, sigma.ravel(), half=clutter_half, out=acc)
         if spec["noise_var"] > 0:
             acc += complex_normal(rng, (na, nr), spec["noise_var"])
         echo = acc.astype(np.complex64)
     return Scene(cfg=cfg, name=spec["name"], seed=seed, na=na, nr=nr, nx=nx, ny=ny, x0=x0, y0=y0,
                  z0=z0, dx=dx, dy=dy, r0=r0, dr=DR, wavelength=WAVELENGTH, interp=spec["interp"],
-                 positions=positions, echo=echo, raw=raw, targets=tg)
+                 positions=positions, echo=echo, raw=raw, targets=tg, dem=dem)
 
 
 def resolution(scene: Scene) -> tuple[float, float]:

@@ -80,6 +80,7 @@ def _good(sb, **over):
     dict(n_fast=1024, fs=1e6, chirp_T=1e-5, chirp_B=1e5, window=2, taylor_sll=10.0),
     dict(n_fast=1024, fs=1e6, chirp_T=1e-5, chirp_B=1e5, window=2, taylor_sll=float("nan")),
     dict(accum=3), dict(accum=-1),
+    dict(dem_relief=-1.0), dict(dem_relief=float("nan")), dict(dem_relief=1e5),
 ])
 def test_plan_create_rejects_invalid_parameters(sb, bad):
     h = ctypes.c_void_p(123)
@@ -112,3 +113,9 @@ def test_null_arguments(sb):
     assert sb._lib.sarbp_stream_create(None, 8, 0, None) == sb.SARBP_EINVAL
     assert sb._lib.sarbp_backproject_host(None, 8, 8, 8, 1, 0, None) == sb.SARBP_EINVAL
     sb._lib.sarbp_stream_destroy(None)  # no-op
+    assert sb._lib.sarbp_backproject_dem(None, 8, 8, 8, 8, 1, 0, None) == sb.SARBP_EINVAL
+    assert sb._lib.sarbp_interpolate_track(None, 8, 10, 8, 8, 4, None) == sb.SARBP_EINVAL
+    assert sb._lib.sarbp_interpolate_track(8, 8, 3, 8, 8, 4, None) == sb.SARBP_EINVAL  # fewer than 4 samples
+    assert sb._lib.sarbp_interpolate_track(8, 8, 10, 8, 8, 0, None) == sb.SARBP_EINVAL
+    # output overlapping the sample positions
+    assert sb._lib.sarbp_interpolate_track(4096, 8192, 10, 65536, 8192, 4, None) == sb.SARBP_EINVAL

@@ -258,6 +258,141 @@ def test_image_tiling_by_sub_image_plans(sb):
     assert np.linalg.norm(tiled - whole) / np.linalg.norm(whole) < 3e-4, (e_whole, e_tiled)
 
 
+# ----------------------------------------------------------------------------- track interpolation
+
+def test_track_interpolation_matches_oracle(sb):
+    """Non-uniform navigation samples; pulse times inside, at the ends, at sample
+    times, outside the span and not finite."""
+    import torch
+
+    rng = np.random.Generator(np.random.PCG64(21))
+    M = 300
+    nav_t = np.sort(rng.uniform(-4.0, 4.0, M))
+    nav_p = np.stack([100.0 * nav_t + rng.normal(0, 0.2, M), -1e4 + rng.normal(0, 0.3, M),
+                      5e3 + rng.normal(0, 0.3, M)], 1)
+    t = np.concatenate([rng.uniform(-4.0, 4.0, 5000), nav_t[[0, 1, 150, M - 1]], [-4.5, 4.5, np.nan, np.inf]])
+    got = sb.sarbp_interpolate_track(torch.from_numpy(nav_t).cuda(), torch.from_numpy(nav_p).cuda(),
+                                     torch.from_numpy(t).cuda())
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    want = oracle.track.interpolate_track(nav_t, nav_p, t)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.max(np.abs(got[ok] - want[ok])) < 1e-8
+
+
+def test_backprojection_from_interpolated_track(sb):
+    """Hi-fi geometry: navigation samples at 100 Hz of the perturbed track, positions
+    interpolated on the device, then backprojected; parity with the oracle using its
+    own interpolated positions, and the same image as from the exact positions."""
+    import torch
+
+    s = synth.make_scene(4, na=400, nr=1024, nx=96, ny=64, n_targets=2)
+    model = synth.track_model(np.random.Generator(np.random.PCG64(1004)), perturbed=True)
+    tp = synth.pulse_times(s.na)
+    nav_t = np.arange(tp[0] - 0.05, tp[-1] + 0.05, 0.01)
+    nav_p = synth.track_at(nav_t, model)
+    exact = synth.track_at(tp, model)
+    assert np.array_equal(exact, s.positions)  # the scene's echo was rendered from this track
+    pos_o = oracle.track.interpolate_track(nav_t, nav_p, tp)
+    assert np.max(np.abs(pos_o - exact)) < 1e-8
+    pos_d = sb.sarbp_interpolate_track(torch.from_numpy(nav_t).cuda(), torch.from_numpy(nav_p).cuda(),
+                                       torch.from_numpy(tp).cuda())
+    with sb.Plan.for_scene(s) as plan:
+        img = plan.backproject(pos_d, torch.from_numpy(s.echo).cuda())
+        torch.cuda.synchronize()
+        got = img.cpu().numpy().astype(np.complex128)
+    want = oracle.scene_backproject(synth.Scene(**{**s.__dict__, "positions": pos_o}))
+    assert rel_l2(got, want) <= REL_L2
+    ref = _run_bp(sb, s, positions=exact)
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 1e-5
+
+
+# ----------------------------------------------------------------------------- terrain (DEM)
+
+def _run_bp_dem(sb, scene, dem, relief, **over):
+    import torch
+
+    with sb.Plan.for_scene(scene, dem_relief=relief, **over) as plan:
+        img = plan.backproject(torch.from_numpy(scene.positions).cuda(), torch.from_numpy(scene.echo).cuda(),
+                               dem=torch.from_numpy(np.ascontiguousarray(dem)).cuda())
+        torch.cuda.synchronize()
+        return img.cpu().numpy().astype(np.complex128)
+
+
+@pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
+def test_terrain_full_image(sb, interp):
+    """Targets and clutter on 25 m of seeded terrain (steep on this small grid: a
+    64 x 32 block spans up to 20+ m), straight track; the plan's bound is the
+    terrain's largest block range."""
+    s = synth.make_scene(2, na=256, nr=1024, nx=150, ny=70, interp=interp, n_targets=3, dem_relief=25.0)
+    relief = synth.block_relief(s.dem)
+    _say(f"[terrain {interp}] block relief {relief:.1f} m")
+    got = _run_bp_dem(sb, s, s.dem, relief)
+    want = oracle.scene_backproject(s)
+    assert np.isfinite(got).all()
+    assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
+    check_peaks(lambda w: got[w[:, 1], w[:, 0]], lambda w: want[w[:, 1], w[:, 0]], target_windows(s))
+
+
+def test_terrain_perturbed_track_and_chunk64(sb):
+    s = synth.make_scene(4, na=203, nr=1024, nx=96, ny=64, interp="sinc8", n_targets=2, dem_relief=12.0)
+    got = _run_bp_dem(sb, s, s.dem, synth.block_relief(s.dem), accum="chunk64")
+    assert rel_l2(got, oracle.scene_backproject(s)) <= REL_L2
+
+
+def test_flat_terrain_equals_the_plane(sb):
+    s = synth.make_scene(2, na=128, nr=1024, nx=96, ny=64, n_targets=2)
+    got = _run_bp_dem(sb, s, np.zeros((s.ny, s.nx), np.float32), 5.0)
+    ref = _run_bp(sb, s)
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 3e-4
+
+
+def test_terrain_beyond_the_bound_is_nan(sb):
+    """Blocks whose height range exceeds the plan's bound come out NaN; the rest match
+    the oracle."""
+    s = synth.make_scene(2, na=96, nr=1024, nx=150, ny=70, n_targets=2, dem_relief=25.0)
+    bound = 0.5 * synth.block_relief(s.dem)
+    got = _run_bp_dem(sb, s, s.dem, bound)
+    want = oracle.scene_backproject(s)
+    expect_nan = np.zeros((s.ny, s.nx), bool)
+    for j in range(0, s.ny, 32):
+        for i in range(0, s.nx, 64):
+            b = s.dem[j:j + 32, i:i + 64].astype(np.float64)
+            expect_nan[j:j + 32, i:i + 64] = b.max() - b.min() > bound
+    assert expect_nan.any() and not expect_nan.all()
+    assert np.array_equal(np.isnan(got.real), expect_nan)
+    ok = ~expect_nan
+    assert np.linalg.norm(got[ok] - want[ok]) / np.linalg.norm(want[ok]) <= REL_L2
+
+
+def test_terrain_nearest_index_bit_exact(sb):
+    """One pulse at a time with echo s[k] = k + 1: |I| - 1 is the chosen bin, against
+    floor(u + 1/2) computed in fp64 in the definition's operation order."""
+    import torch
+
+    s = synth.make_scene(2, na=64, nr=1024, nx=150, ny=70, interp="nearest", n_targets=1, dem_relief=25.0)
+    relief = synth.block_relief(s.dem)
+    ramp = torch.arange(1, s.nr + 1, dtype=torch.float32).to(torch.complex64).cuda()[None, :].contiguous()
+    jj, ii = np.meshgrid(np.arange(s.ny), np.arange(s.nx), indexing="ij")
+    x = s.x0 + ii * s.dx
+    y = s.y0 + jj * s.dy
+    z = s.z0 + s.dem.astype(np.float64)
+    dem_d = torch.from_numpy(s.dem).cuda()
+    bad = 0
+    with sb.Plan.for_scene(s, interp="nearest", n_pulses=1, dem_relief=relief) as plan:
+        img = plan.new_image()
+        for n in range(0, s.na, 3):
+            a = s.positions[n]
+            plan.backproject(torch.from_numpy(s.positions[n:n + 1].copy()).cuda(), ramp, image=img, dem=dem_d)
+            mag = img.abs().cpu().numpy().astype(np.float64)
+            ddx, ddy, ddz = x - a[0], y - a[1], z - a[2]
+            R = np.sqrt(ddx * ddx + ddy * ddy + ddz * ddz)
+            k = np.floor((R - s.r0) / s.dr + 0.5)
+            bad += int(np.count_nonzero(np.rint(mag) - 1 != k))
+    assert bad == 0
+
+
 # ----------------------------------------------------------------------------- nearest: bit-exact index
 
 def _index_probe(sb, scene, pulses):

@@ -30,7 +30,7 @@ def _h(t):
     return s * (mp.mpf("0.54") + mp.mpf("0.46") * mp.cos(mp.pi * t / 4))
 
 
-def _brute(pos, echo, r0, dr, nx, ny, x0, y0, z0, dx, dy, interp):
+def _brute(pos, echo, r0, dr, nx, ny, x0, y0, z0, dx, dy, interp, dem=None):
     na, nr = echo.shape
     S = [[mp.mpc(complex(echo[n, k])) for k in range(nr)] for n in range(na)]
 
@@ -43,10 +43,11 @@ def _brute(pos, echo, r0, dr, nx, ny, x0, y0, z0, dx, dy, interp):
         for i in range(nx):
             x = mp.mpf(x0) + i * mp.mpf(dx)
             y = mp.mpf(y0) + j * mp.mpf(dy)
+            z = mp.mpf(z0) + (0 if dem is None else mp.mpf(float(dem[j, i])))
             acc = mp.mpc(0)
             for n in range(na):
                 ax, ay, az = (mp.mpf(float(c)) for c in pos[n])
-                R = mp.sqrt((x - ax) ** 2 + (y - ay) ** 2 + (mp.mpf(z0) - az) ** 2)
+                R = mp.sqrt((x - ax) ** 2 + (y - ay) ** 2 + (z - az) ** 2)
                 u = (R - r0) / dr
                 if interp == "nearest":
                     v = s(n, int(mp.floor(u + mp.mpf("0.5"))))
@@ -95,3 +96,15 @@ def test_oracle_matches_40_digit_definition(interp, R_centre):
                              wavelength=LAM, interp=interp)
     err = np.linalg.norm(got - want) / np.linalg.norm(want)
     assert err <= tol, err
+
+
+@pytest.mark.parametrize("interp", ["nearest", "linear", "sinc8"])
+def test_oracle_terrain_matches_40_digit_definition(interp):
+    """The same with a random terrain height per pixel (float32, +-5 m) at 11 km."""
+    pos, echo, r0, dr, nx, ny, x0, y0, z0, dx, dy = _case(11180.0, 13)
+    dem = np.random.Generator(np.random.PCG64(14)).uniform(-5, 5, (ny, nx)).astype(np.float32)
+    want = _brute(pos, echo, r0, dr, nx, ny, x0, y0, z0, dx, dy, interp, dem=dem)
+    got = oracle.backproject(pos, echo, r0=r0, dr=dr, nx=nx, ny=ny, x0=x0, y0=y0, z0=z0, dx=dx, dy=dy,
+                             wavelength=LAM, interp=interp, dem=dem)
+    err = np.linalg.norm(got - want) / np.linalg.norm(want)
+    assert err <= 4 * 2.0 ** -53 * 4 * np.pi * 11180.0 / LAM, err

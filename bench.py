@@ -264,6 +264,34 @@ def aux_terrain(sb, scene, steps, warmup):
             "G_updates_per_s": scene.updates / (tm["mean"] * 1e-3) / 1e9}
 
 
+def aux_volume(sb, steps, warmup):
+    """3-D backprojection: 8 parallel passes (40 m apart in height) of 512 pulses each
+    onto 256 x 256 x 16 voxels (0.2 m, 0.5 m layers) -- as many updates as the
+    standard scene; 5 unit targets."""
+    import numpy as np
+    import torch
+
+    import synth
+
+    pos = synth.multipass_track(8, 512, 40.0)
+    nr, nx, ny, nz = 4096, 256, 256, 16
+    r0 = synth.RC_CENTRE - (nr // 2) * synth.DR
+    x0, y0, z0, dz = -(nx // 2) * synth.PIXEL, -(ny // 2) * synth.PIXEL, -4.0, 0.5
+    rng = np.random.Generator(np.random.PCG64(55))
+    pts = np.stack([x0 + rng.integers(20, nx - 20, 5) * synth.PIXEL, y0 + rng.integers(20, ny - 20, 5) * synth.PIXEL,
+                    z0 + rng.integers(0, nz, 5) * dz], 1)
+    echo = synth.render_points(pos, nr, r0, synth.DR, pts, np.ones(5), half=256).astype(np.complex64)
+    with sb.Plan(n_pulses=len(pos), n_range=nr, r0=r0, dr=synth.DR, nx=nx, ny=ny, x0=x0, y0=y0, z0=z0,
+                 dx=synth.PIXEL, dy=synth.PIXEL, wavelength=synth.WAVELENGTH, interp="linear", nz=nz, dz=dz) as plan:
+        p_d = torch.from_numpy(pos).cuda()
+        e_d = torch.from_numpy(echo).cuda()
+        img = plan.new_image()
+        tm, _ = time_launches(lambda: plan.backproject(p_d, e_d, image=img), steps, warmup)
+    upd = len(pos) * nx * ny * nz
+    return {"voxels": [nz, ny, nx], "pulses": len(pos), "ms": tm["mean"], "ms_median": tm["median"],
+            "G_updates_per_s": upd / (tm["mean"] * 1e-3) / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -343,6 +371,7 @@ def main():
         line["aux"]["accumulators"] = aux_accumulators(sarbp, s, max(5, args.steps // 5), max(5, args.warmup // 5))
         line["aux"]["host_stream"] = aux_host_stream(sarbp, s, max(5, args.steps // 5), max(5, args.warmup // 5))
         line["aux"]["terrain"] = aux_terrain(sarbp, s, max(5, args.steps // 5), max(5, args.warmup // 5))
+        line["aux"]["volume"] = aux_volume(sarbp, max(5, args.steps // 5), max(5, args.warmup // 5))
         log(f"bench: end-to-end {line['aux']}")
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(s)

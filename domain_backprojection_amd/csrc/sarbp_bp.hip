@@ -133,10 +133,10 @@ __device__ __forceinline__ void sincos_rev(float x, float* s, float* c) {
 // only steer scheduling; stale or racing reads cannot change a result.
 __device__ int chunk_priority(const BpArgs& A, int n0) {
     const int b = (int)blockIdx.x;
-    if (A.ntiles <= 2 * A.slots) {
+    if (A.nblocks <= 2 * A.slots) {
         __hip_atomic_store(A.progress + b, n0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int partner = b < A.slots ? b + A.slots : b - A.slots;
-        if (partner >= A.ntiles) return 0;
+        if (partner >= A.nblocks) return 0;
         const int other = __hip_atomic_load(A.progress + partner, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return (n0 < other || (n0 == other && b >= A.slots)) ? 3 : 0;
     }
@@ -195,7 +195,7 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
                                                  const int* klo_s, int np, int n0, int i_pix, int j_pix0,
                                                  float dxl, const float* dyv, const float* ddv, float* accr,
                                                  float* acci, float* cmpr, float* cmpi, const float* dzv,
-                                                 const float* hv) {
+                                                 const float* hv, double zl) {
     const int eb = entry_bytes<INTERP>();
     const uint32_t wstride = (uint32_t)(A.win * eb);
     const float kappa = A.kappa;
@@ -242,7 +242,7 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
 #pragma unroll
                 for (int m = 0; m < BP_PPT; ++m) {
                     if (fabsf(g[m] - 0.5f) > 0.5f - A.tie_eps) {
-                        const double zp = DEM ? A.z0 + (double)hv[m] : A.z0; // the pixel's height
+                        const double zp = DEM ? A.z0 + (double)hv[m] : zl; // the pixel's height
                         const int kabs = nearest_bin_fp64(A.pos[pn], A.pos[pn + 1], A.pos[pn + 2], A.x0, A.y0,
                                                           zp, A.dx, A.dy, A.r0, A.dr, i_pix, j_pix0 + BP_WAVES * m);
                         int kr = kabs - klo_s[p];
@@ -378,7 +378,10 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
 
     // XCD-aware tile order: workgroup b runs on XCD (b mod 8); give each XCD a
     // contiguous range of tiles (rows of tiles share echo bins in its L2).
-    int tile = blockIdx.x;
+    // Workgroup b handles tile (b mod ntiles) of voxel layer b / ntiles (one layer,
+    // z = z0, for a 2-D image).
+    const int layer = (int)blockIdx.x / A.ntiles;
+    int tile = (int)blockIdx.x - layer * A.ntiles;
     const int nt8 = (A.ntiles / 8) * 8;
     if (tile < nt8) tile = (tile & 7) * (nt8 / 8) + (tile >> 3);
     const int tx = tile % A.tiles_x, ty = tile / A.tiles_x;
@@ -387,7 +390,8 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     // tile centre (fp64) and this lane's pixel offsets from it
     const double cxp = (double)i0 + 0.5 * (BP_TX - 1), cyp = (double)j0 + 0.5 * (BP_TY - 1);
     const double cx = A.x0 + cxp * A.dx, cy = A.y0 + cyp * A.dy;
-    double cz = A.z0;
+    const double zl = A.z0 + (double)layer * A.dz; // this layer's height
+    double cz = zl;
     const double ddx = ((double)lane - 0.5 * (BP_TX - 1)) * A.dx;
     const float dxl = (float)ddx;
     float dyv[BP_PPT], ddv[BP_PPT], accr[BP_PPT], acci[BP_PPT];
@@ -474,13 +478,13 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         set_priority(*prio_s);
         if (m2)
             accumulate_chunk<INTERP, 2, ACC, DEM>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv,
-                                                   accr, acci, cmpr, cmpi, dzv, hv);
+                                                   accr, acci, cmpr, cmpi, dzv, hv, zl);
         else if (m1)
             accumulate_chunk<INTERP, 1, ACC, DEM>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv,
-                                                   accr, acci, cmpr, cmpi, dzv, hv);
+                                                   accr, acci, cmpr, cmpi, dzv, hv, zl);
         else
             accumulate_chunk<INTERP, 0, ACC, DEM>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv,
-                                                   accr, acci, cmpr, cmpi, dzv, hv);
+                                                   accr, acci, cmpr, cmpi, dzv, hv, zl);
         if constexpr (ACC == SARBP_ACC_CHUNK64) {
 #pragma unroll
             for (int m = 0; m < BP_PPT; ++m) {
@@ -503,7 +507,7 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         for (int m = 0; m < BP_PPT; ++m) {
             const int j = j0 + wave + BP_WAVES * m;
             if (j < A.ny) {
-                float2* o = A.image + (size_t)j * A.nx + i;
+                float2* o = A.image + ((size_t)layer * A.ny + j) * A.nx + i;
                 if constexpr (ACC == SARBP_ACC_CHUNK64) {
                     double r = sumr[m], im = sumi[m];
                     if (A.accumulate) {
@@ -549,7 +553,7 @@ int allow_lds(int accum, size_t bytes) {
 
 template <int INTERP, bool DEM>
 void launch(const BpArgs& A, int accum, size_t lds, hipStream_t stream) {
-    const dim3 grid(A.ntiles), block(BP_THREADS);
+    const dim3 grid(A.nblocks), block(BP_THREADS);
     switch (accum) {
         case SARBP_ACC_KAHAN:
             hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_KAHAN, DEM>), grid, block, lds, stream, A);
@@ -590,6 +594,8 @@ int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* ech
     A.ny = p.ny;
     A.tiles_x = plan->tiles_x;
     A.ntiles = plan->tiles_x * plan->tiles_y;
+    A.nblocks = A.ntiles * (p.nz > 1 ? p.nz : 1);
+    A.dz = p.nz > 1 ? p.dz : 0.0;
     A.win = plan->win;
     A.margin_lo = plan->margin_lo;
     A.chunk = plan->chunk;

@@ -75,10 +75,12 @@ struct BpArgs {
     const float2* phase;   // phase_tab
     int n, n_range, nx, ny;
     int tiles_x, ntiles;
+    int nblocks;           // ntiles * voxel layers: the launch's workgroups
     int win, margin_lo, chunk, accumulate;
     int slots;             // compute units: workgroup b and b + slots usually share a CU
     int* progress;         // [2 * slots] pulse progress per workgroup, read by its CU partner
     double r0, dr, inv_dr, x0, y0, z0, dx, dy;
+    double dz;             // voxel layer spacing (3-D images), else 0
     double half_span;      // half tile diagonal [m]
     double half_span_bins; // half_span / dr
     float sinc_poly[32];   // see sarbp_plan::sinc_poly

@@ -51,6 +51,8 @@ int validate(const sarbp_params* p) {
     if (p->interp < SARBP_NEAREST || p->interp > SARBP_SINC8) return SARBP_EINVAL;
     if (p->accum < SARBP_ACC_FP32 || p->accum > SARBP_ACC_CHUNK64) return SARBP_EINVAL;
     if (!isfinite(p->dem_relief) || p->dem_relief < 0.0 || p->dem_relief > 1.0e4) return SARBP_EINVAL;
+    if (p->nz < 0 || p->nz > 65535) return SARBP_EINVAL;
+    if (p->nz > 1 && (!finite_pos(p->dz) || p->dem_relief > 0.0)) return SARBP_EINVAL; // volume xor terrain
     if (p->n_range < (p->interp == SARBP_SINC8 ? 8 : 2)) return SARBP_EINVAL;
     if (!isfinite(p->r0) || !finite_pos(p->dr) || !finite_pos(p->dx) || !finite_pos(p->dy)) return SARBP_EINVAL;
     if (!isfinite(p->x0) || !isfinite(p->y0) || !isfinite(p->z0) || !finite_pos(p->wavelength)) return SARBP_EINVAL;
@@ -197,7 +199,7 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     // lies within R_t +- half_span and its bin within the window below.
     plan->tiles_x = (p.nx + BP_TX - 1) / BP_TX;
     plan->tiles_y = (p.ny + BP_TY - 1) / BP_TY;
-    if ((int64_t)plan->tiles_x * plan->tiles_y > INT32_MAX) {
+    if ((int64_t)plan->tiles_x * plan->tiles_y * (p.nz > 1 ? p.nz : 1) > INT32_MAX) {
         release(plan);
         return SARBP_EINVAL;
     }

@@ -67,6 +67,8 @@ class sarbp_params(ctypes.Structure):
         ("taylor_sll", ctypes.c_double),
         ("accum", ctypes.c_int32),
         ("dem_relief", ctypes.c_double),
+        ("nz", ctypes.c_int32),
+        ("dz", ctypes.c_double),
     ]
 
 
@@ -114,12 +116,14 @@ def sarbp_version() -> int:
 
 
 def make_params(n_pulses, n_range, r0, dr, nx, ny, x0, y0, z0, dx, dy, wavelength, interp="linear",
-                n_fast=0, fs=0.0, chirp_T=0.0, chirp_B=0.0, window=0, taylor_nbar=0, taylor_sll=0.0, accum="fp32", dem_relief=0.0) -> sarbp_params:
+                n_fast=0, fs=0.0, chirp_T=0.0, chirp_B=0.0, window=0, taylor_nbar=0, taylor_sll=0.0, accum="fp32", dem_relief=0.0, nz=0,
+                dz=0.0) -> sarbp_params:
     return sarbp_params(int(n_pulses), int(n_range), float(r0), float(dr), int(nx), int(ny), float(x0),
                         float(y0), float(z0), float(dx), float(dy), float(wavelength),
                         INTERP[interp] if isinstance(interp, str) else int(interp), int(n_fast), float(fs),
                         float(chirp_T), float(chirp_B), int(window), int(taylor_nbar), float(taylor_sll),
-                        ACCUM[accum] if isinstance(accum, str) else int(accum), float(dem_relief))
+                        ACCUM[accum] if isinstance(accum, str) else int(accum), float(dem_relief), int(nz),
+                        float(dz))
 
 
 def sarbp_plan_create(params: sarbp_params) -> int:
@@ -285,13 +289,19 @@ class Plan:
     def __exit__(self, *exc):
         self.close()
 
+    @property
+    def image_shape(self) -> tuple:
+        """(ny, nx), or (nz, ny, nx) for a volume."""
+        p = self.params
+        return (p.nz, p.ny, p.nx) if p.nz > 1 else (p.ny, p.nx)
+
     def new_image(self, device="cuda") -> torch.Tensor:
-        return torch.zeros((self.params.ny, self.params.nx), dtype=torch.complex64, device=device)
+        return torch.zeros(self.image_shape, dtype=torch.complex64, device=device)
 
     def backproject(self, positions, echo, image=None, n=None, accumulate=0, stream=None, dem=None) -> torch.Tensor:
         if image is None:
-            image = torch.empty((self.params.ny, self.params.nx), dtype=torch.complex64, device=echo.device)
-        if tuple(image.shape) != (self.params.ny, self.params.nx):
+            image = torch.empty(self.image_shape, dtype=torch.complex64, device=echo.device)
+        if tuple(image.shape) != self.image_shape:
             raise ValueError("image shape does not match the plan")
         if echo.dim() != 2 or echo.shape[1] != self.params.n_range:
             raise ValueError("echo must be (n, n_range)")
@@ -338,8 +348,8 @@ class HostStream:
 
     def backproject(self, positions, data, image=None, n=None, accumulate=0, stream=None) -> torch.Tensor:
         if image is None:
-            image = torch.empty((self.plan.params.ny, self.plan.params.nx), dtype=torch.complex64, device="cuda")
-        if tuple(image.shape) != (self.plan.params.ny, self.plan.params.nx):
+            image = torch.empty(self.plan.image_shape, dtype=torch.complex64, device="cuda")
+        if tuple(image.shape) != self.plan.image_shape:
             raise ValueError("image shape does not match the plan")
         if data.dim() != 2 or data.shape[1] != self.row:
             raise ValueError("data must be (n, n_range)")

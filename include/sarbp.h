@@ -92,6 +92,11 @@ typedef struct {
                           * within any 64 x 32-pixel block of the grid aligned to pixel (0, 0)
                           * (the whole map's range will do); 0 disables terrain.  The echo
                           * windows grow with it.                                            */
+    /* 3-D imaging (section 5 of the page names backprojection onto a volume as the
+     * next step): nz layers of the grid, layer l at height z0 + l dz; the image is
+     * complex64 [nz][ny][nx].  nz = 0 or 1 is the plane z = z0.                    */
+    int32_t nz;          /* voxel layers, 0..65535 (0 or 1: a 2-D image)                          */
+    double dz;           /* layer spacing (> 0 when nz > 1)                                       */
 } sarbp_params;
 
 typedef struct sarbp_plan sarbp_plan; /* opaque */
@@ -106,8 +111,8 @@ int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out);
 /* Backproject n pulses into the image (sections 1.1, 2.2 and 3.3 of the page).
  *   positions_d : device, float64 [n][3] antenna phase centres (x, y, z)
  *   echo_d      : device, complex64 [n][n_range] range-compressed echo, bin fastest
- *   image_d     : device, complex64 [ny][nx], x fastest; written (accumulate = 0)
- *                 or added to (accumulate = 1)
+ *   image_d     : device, complex64 [ny][nx], x fastest ([nz][ny][nx] for a volume);
+ *                 written (accumulate = 0) or added to (accumulate = 1)
  *   n           : pulses in this call, 1 <= n <= plan n_pulses
  * Because the sum is linear in the echo, a long aperture can be streamed in
  * pulse chunks with accumulate = 1.  Returns SARBP_EINVAL (null plan or
@@ -120,7 +125,7 @@ int sarbp_backproject(const sarbp_plan* plan, const double* positions_d, const v
  * follow elevation data): as sarbp_backproject, with pixel (i, j) at
  * (x0 + i dx, y0 + j dy, z0 + dem[j * nx + i]).
  *   dem_d : device, float32 [ny][nx] heights above z0, 4-byte aligned
- * The plan must have dem_relief > 0.  Pixels of a 64 x 32 block whose heights
+ * The plan must have dem_relief > 0 and nz <= 1.  Pixels of a 64 x 32 block whose heights
  * span more than dem_relief come out NaN, as does a pixel with a non-finite
  * height.  Returns SARBP_EINVAL (as sarbp_backproject, or a null or misaligned
  * dem, or a plan without terrain), SARBP_EDEVICE on a launch failure. */

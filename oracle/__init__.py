@@ -168,6 +168,14 @@ def sinc8_weight(t: float) -> float:
     return float(_load().oracle_sinc8_weight(float(t)))
 
 
+def backproject_volume(positions, echo, r0, dr, nx, ny, nz, x0, y0, z0, dx, dy, dz, wavelength, interp,
+                       nthreads=None) -> np.ndarray:
+    """Voxel image (nz, ny, nx) complex128: voxel (i, j, l) at (x0 + i dx, y0 + j dy, z0 + l dz)
+    -- the plane definition at each layer height (3-D backprojection, the page's section 5)."""
+    return np.stack([backproject(positions, echo, r0, dr, nx, ny, x0, y0, z0 + float(l) * dz, dx, dy, wavelength,
+                                 interp, nthreads=nthreads) for l in range(nz)])
+
+
 def scene_backproject(scene, echo=None, rows=None, nthreads=None) -> np.ndarray:
     """:func:`backproject` with the geometry of a ``synth.Scene`` (and its dem, if any)."""
     return backproject(scene.positions, scene.echo if echo is None else echo, scene.r0, scene.dr,

@@ -241,6 +241,19 @@ def block_relief(dem: np.ndarray, bx: int = 64, by: int = 32) -> float:
     return worst
 
 
+def multipass_track(passes: int, na_per_pass: int, dh: float) -> np.ndarray:
+    """Antenna positions (passes * na_per_pass, 3) of parallel straight passes at heights
+    ALTITUDE + (k - (passes - 1) / 2) dh: an aperture with extent in elevation, so that
+    backprojection onto a volume resolves height (a single pass does not)."""
+    one = track(na_per_pass)
+    out = []
+    for k in range(passes):
+        p = one.copy()
+        p[:, 2] += (k - (passes - 1) / 2.0) * dh
+        out.append(p)
+    return np.concatenate(out)
+
+
 def target_pixels(nx: int, ny: int, k: int, rng: np.random.Generator) -> np.ndarray:
     """K well-separated pixels: a ceil(sqrt K)^2 lattice over the central 80 % of the grid,
     K cells chosen at random, one pixel drawn from the middle half of each chosen cell."""

@@ -81,6 +81,7 @@ def _good(sb, **over):
     dict(n_fast=1024, fs=1e6, chirp_T=1e-5, chirp_B=1e5, window=2, taylor_sll=float("nan")),
     dict(accum=3), dict(accum=-1),
     dict(dem_relief=-1.0), dict(dem_relief=float("nan")), dict(dem_relief=1e5),
+    dict(nz=-1), dict(nz=70000), dict(nz=4, dz=0.0), dict(nz=4, dz=-0.5), dict(nz=4, dz=0.5, dem_relief=2.0),
 ])
 def test_plan_create_rejects_invalid_parameters(sb, bad):
     h = ctypes.c_void_p(123)

@@ -48,9 +48,15 @@ def log(msg):
 
 
 def bp_source_hash():
+    """sha256 of the kernel sources' code: comments and whitespace do not count."""
+    import re
+
     h = hashlib.sha256()
     for f in BP_SOURCES:
-        h.update(open(f, "rb").read())
+        text = open(f, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -11,32 +11,41 @@
 //
 // Design on gfx950 (not the page's one-thread-per-pixel CUDA kernel):
 //
-// * A workgroup of 16 wave64s owns a 64 (x) by 32 (y) pixel tile; each lane
-//   keeps 2 pixels of one column (register blocking) and accumulates them in
-//   fp32 registers across all pulses, so the image is written once.
+// * A workgroup of 16 wave64s owns a 64 (x) by 32 (y) pixel tile (of one voxel
+//   layer, for volumes); each lane keeps 2 pixels of one column (register
+//   blocking) and accumulates them across all pulses, so the image is written once.
 // * Pulses are processed in chunks.  For each pulse of a chunk one lane
 //   computes, in fp64, the tile-centre range R_t and derived fp32 constants;
 //   the pixels then need only the fp32 range *difference* to the tile centre,
 //      num = |d|^2 + 2 d.(c - a),   d = p - c,
 //      R - R_t = R_t (sqrt(1 + num / R_t^2) - 1)
-//   evaluated by its Taylor series in q = num / R_t^2 (2 or 3 terms, picked
-//   per chunk from a bound on the truncation error) or, when q is not small,
-//   by the exact form num / (R_t (1 + sqrt(1 + q))).  This keeps the bin
-//   position to ~1e-6 bins, which fp32 absolute ranges (~1e-3 m at 11 km)
-//   could not (section 2.2 warns about fp32 range precision).
-// * The echo window a tile can touch (the tile's range extent plus interpolator
-//   taps; bounded by the tile diagonal) is staged per pulse in LDS, already
-//   multiplied by the bin-centre carrier phase exp(+j 4 pi r_k / lambda).  For a
-//   pixel at u = k + f the remaining phase is exp(j 2 pi kappa f) with
-//   kappa = 2 dr / lambda, so one v_sin_f32 / v_cos_f32 pair (inputs in
-//   revolutions) on a bounded argument replaces a large-argument reduction.
-// * Linear interpolation stages (A, D) = (s[k] E[k], (s[k+1] - s[k]) E[k]) per
-//   bin so a sample is one ds_read_b128 and two FMAs.  The window position ub
-//   is positive by construction, so v_cvt_u32_f32 (truncation) is its floor and
-//   v_fract_f32 its fraction; one shift-add turns the floor into the LDS address.
+//   evaluated by a series in q = num / R_t^2 (two terms, with the dropped cubic
+//   Chebyshev-economised into the linear term, or three), picked per chunk from
+//   a bound on the truncation error, or when q is not small by the exact form
+//   num / (R_t (1 + sqrt(1 + q))).  This keeps the bin position to ~1e-6 bins,
+//   which fp32 absolute ranges (~1e-3 m at 11 km) could not (section 2.2 warns
+//   about fp32 range precision).
+// * The echo window a tile can touch (its range extent, bounded by the tile
+//   diagonal) is staged per pulse in LDS, already multiplied by the bin-centre
+//   carrier phase exp(+j 4 pi r_k / lambda).  For a pixel at u = k + f the
+//   remaining phase is exp(j 2 pi kappa f) with kappa = 2 dr / lambda, so one
+//   v_sin_f32 / v_cos_f32 pair (inputs in revolutions) on a bounded argument
+//   replaces a large-argument reduction.
+// * Staged per bin k: linear (A, D) = (s[k] E[k], (s[k+1] - s[k]) E[k]), a
+//   sample is one ds_read_b128 and two FMAs; nearest s[k] E[k] exp(-j pi kappa);
+//   sinc8 the 8 coefficients of the degree-7 polynomial in f that is the
+//   windowed-sinc interpolant at k + f, times E[k], so a sample is one complex
+//   Horner evaluation.  The window position is positive by construction, so
+//   v_cvt_u32_f32 (truncation) is its floor and v_fract_f32 its fraction.
 // * Nearest interpolation rechecks lanes within tie_eps of a rounding tie in
 //   fp64, in the definition's operation order, so the chosen bin matches the
 //   double-precision definition exactly.
+// * Template parameters select the accumulator (fp32, Kahan-compensated, or
+//   fp32 per chunk summed in fp64) and terrain (per-pixel heights: the tile is
+//   centred at its mid-height and the range term gains 2 u_z dz).
+// * The two workgroups that share a CU exchange pulse progress through a small
+//   array and the one behind raises its wave priority, so neither ends up
+//   running alone at half occupancy; larger grids lower the priority by quarter.
 // * Workgroups are remapped so each XCD (8 per GPU, round-robin dispatch) owns
 //   a contiguous band of tiles whose echo windows overlap in its L2.
 #include <math.h>

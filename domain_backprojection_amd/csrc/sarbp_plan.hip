@@ -1,5 +1,7 @@
-// Host side of the sarbp C ABI: argument validation, plan creation (read-only
-// device tables), dispatch and status strings.  See include/sarbp.h.
+// Host side of the sarbp C ABI: argument validation, plan creation (the
+// carrier-phase and matched-filter tables, the sinc8 polynomials, the progress
+// hints), the device entry points' dispatch and status strings.  See
+// include/sarbp.h.
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>

@@ -1,7 +1,8 @@
 // Range compression for gfx950: one workgroup per pulse, the whole record
 // resident in LDS.  Computes
 //   y = IFFT( FFT(x) * H ),  H = conj(FFT(ref)) * W / N,
-// the FFT matched filter with a Hamming window of the page
+// the FFT matched filter with a Hamming or Taylor window W (built into the
+// plan's table H) of the page
 // "基于GPU的SAR后向投影成像优化与CUDA加速实践" (GPU-based SAR backprojection),
 // section 3.1: pulses are independent, so the batch is one launch with one
 // workgroup per pulse.

@@ -6,9 +6,11 @@ the HIP library ``libsarbp.so`` built in this directory; importing this module
 raises if that library is missing -- there is no fallback.
 
 The functions keep the C names: :func:`sarbp_plan_create`,
-:func:`sarbp_backproject`, :func:`sarbp_range_compress`, :func:`sarbp_destroy`,
-:func:`sarbp_status_string`, :func:`sarbp_version`.  :class:`Plan` wraps a plan
-handle's lifetime.
+:func:`sarbp_backproject`, :func:`sarbp_backproject_dem`, :func:`sarbp_range_compress`,
+:func:`sarbp_interpolate_track`, :func:`sarbp_stream_create`,
+:func:`sarbp_backproject_host`, :func:`sarbp_stream_destroy`, :func:`sarbp_destroy`,
+:func:`sarbp_status_string`, :func:`sarbp_version`.  :class:`Plan` and
+:class:`HostStream` wrap the handles' lifetimes.
 """
 from __future__ import annotations
 

@@ -96,6 +96,32 @@ def test_linearity_and_pulse_order(sb, interp):
     assert np.linalg.norm(c - d) / np.linalg.norm(d) < 1e-5
 
 
+def test_one_plan_on_two_streams_concurrently(sb):
+    """Calls with one plan may overlap on different streams (they share only the
+    plan's progress hints, which steer scheduling): each result matches the same
+    call made alone."""
+    import torch
+
+    s = synth.make_scene(2, na=512, nr=1024, nx=300, ny=200, n_targets=2)
+    rng = np.random.Generator(np.random.PCG64(3))
+    e2 = (rng.standard_normal(s.echo.shape) + 1j * rng.standard_normal(s.echo.shape)).astype(np.complex64)
+    with sb.Plan.for_scene(s) as plan:
+        pos = torch.from_numpy(s.positions).cuda()
+        ea, eb = torch.from_numpy(s.echo).cuda(), torch.from_numpy(e2).cuda()
+        ref_a, ref_b = plan.backproject(pos, ea), plan.backproject(pos, eb)
+        torch.cuda.synchronize()
+        sa, sb_ = torch.cuda.Stream(), torch.cuda.Stream()
+        ia, ib = plan.new_image(), plan.new_image()
+        torch.cuda.synchronize()
+        for _ in range(3):
+            with torch.cuda.stream(sa):
+                plan.backproject(pos, ea, image=ia)
+            with torch.cuda.stream(sb_):
+                plan.backproject(pos, eb, image=ib)
+        torch.cuda.synchronize()
+        assert torch.equal(ia, ref_a) and torch.equal(ib, ref_b)
+
+
 @pytest.mark.parametrize("first, nr", [(246, 48), (226, 36)], ids=["record-starts-in-scene", "record-ends-in-scene"])
 @pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
 def test_zero_extension_and_far_pixels(sb, interp, first, nr):

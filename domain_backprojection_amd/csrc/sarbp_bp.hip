@@ -199,6 +199,65 @@ __device__ __forceinline__ void mac(float& ar, float& ai, float& cr, float& ci, 
     }
 }
 
+// Nearest interpolation over G consecutive pulses p0 .. p0+G-1: every bin
+// decision of the group first, then one (rare) branch that retakes the decisions
+// within tie_eps of a rounding tie in fp64, then the fetches and accumulations.
+// ub carries u + 1/2: its floor is the nearest bin and g - 1/2 = u - bin; the
+// staged sample carries exp(-j pi kappa), so exp(j 2 pi kappa g) completes the phase.
+template <int G, int MODE, int ACC, bool DEM>
+__device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem, const float4* cst, const int* klo_s,
+                                              int p0, int n0, int i_pix, int j_pix0, float dxl, const float* dyv,
+                                              const float* ddv, float* accr, float* acci, float* cmpr, float* cmpi,
+                                              const float* dzv, const float* hv, double zl, uint32_t wstride) {
+    constexpr int CS = DEM ? 3 : 2;
+    float g[G][BP_PPT];
+    uint32_t kb[G][BP_PPT];
+    bool tie = false;
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+        const float4 c0 = cst[CS * (p0 + q)];
+        const float4 c1 = cst[CS * (p0 + q) + 1];
+        const float4 c2 = DEM ? cst[CS * (p0 + q) + 2] : c1;
+#pragma unroll
+        for (int m = 0; m < BP_PPT; ++m) {
+            const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
+            const float ub = bin_position<MODE>(num, c0, c1);
+            g[q][m] = __builtin_amdgcn_fractf(ub);
+            kb[q][m] = (uint32_t)ub;
+            tie |= fabsf(g[q][m] - 0.5f) > 0.5f - A.tie_eps;
+        }
+    }
+    if (tie) {
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            const size_t pn = 3 * (size_t)(n0 + p0 + q);
+#pragma unroll
+            for (int m = 0; m < BP_PPT; ++m) {
+                if (fabsf(g[q][m] - 0.5f) > 0.5f - A.tie_eps) {
+                    const double zp = DEM ? A.z0 + (double)hv[m] : zl; // the pixel's height
+                    const int kabs = nearest_bin_fp64(A.pos[pn], A.pos[pn + 1], A.pos[pn + 2], A.x0, A.y0, zp, A.dx,
+                                                      A.dy, A.r0, A.dr, i_pix, j_pix0 + BP_WAVES * m);
+                    int kr = kabs - klo_s[p0 + q];
+                    kr = kr < 0 ? 0 : (kr > A.win - 1 ? A.win - 1 : kr);
+                    g[q][m] = g[q][m] + (float)((int)kb[q][m] - kr); // = ub - kr
+                    kb[q][m] = (uint32_t)kr;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+        const uint32_t wbase = (uint32_t)(p0 + q) * wstride;
+#pragma unroll
+        for (int m = 0; m < BP_PPT; ++m) {
+            const float2 sv = *reinterpret_cast<const float2*>(smem + ((kb[q][m] << 3) + wbase));
+            float sn, cs;
+            sincos_rev(A.kappa * g[q][m], &sn, &cs);
+            mac<ACC>(accr[m], acci[m], cmpr[m], cmpi[m], sv.x, sv.y, cs, sn);
+        }
+    }
+}
+
 template <int INTERP, int MODE, int ACC, bool DEM>
 __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* smem, const float4* cst,
                                                  const int* klo_s, int np, int n0, int i_pix, int j_pix0,
@@ -208,8 +267,17 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
     const int eb = entry_bytes<INTERP>();
     const uint32_t wstride = (uint32_t)(A.win * eb);
     const float kappa = A.kappa;
-    constexpr int kUnroll = INTERP == SARBP_LINEAR ? BP_PUNROLL_LINEAR
-                                                   : (INTERP == SARBP_NEAREST ? BP_PUNROLL_NEAREST : BP_PUNROLL_SINC8);
+    if constexpr (INTERP == SARBP_NEAREST) {
+        int p = 0;
+        for (; p + BP_NEAREST_GROUP <= np; p += BP_NEAREST_GROUP)
+            nearest_group<BP_NEAREST_GROUP, MODE, ACC, DEM>(A, smem, cst, klo_s, p, n0, i_pix, j_pix0, dxl, dyv, ddv,
+                                                              accr, acci, cmpr, cmpi, dzv, hv, zl, wstride);
+        for (; p < np; ++p)
+            nearest_group<1, MODE, ACC, DEM>(A, smem, cst, klo_s, p, n0, i_pix, j_pix0, dxl, dyv, ddv, accr, acci,
+                                             cmpr, cmpi, dzv, hv, zl, wstride);
+        return;
+    }
+    constexpr int kUnroll = INTERP == SARBP_LINEAR ? BP_PUNROLL_LINEAR : BP_PUNROLL_SINC8;
 #pragma unroll kUnroll
     for (int p = 0; p < np; ++p) {
         constexpr int CS = DEM ? 3 : 2; // float4 constants per pulse
@@ -230,44 +298,6 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
                 float sn, cs;
                 sincos_rev(kappa * f, &sn, &cs);
                 mac<ACC>(accr[m], acci[m], cmpr[m], cmpi[m], vr, vi, cs, sn);
-            }
-        } else if constexpr (INTERP == SARBP_NEAREST) {
-            // ub carries u + 1/2: its floor is the nearest bin and g - 1/2 = u - bin.
-            // All pixels first, then one rare branch for lanes near a rounding tie.
-            float g[BP_PPT];
-            uint32_t kb[BP_PPT];
-            bool tie = false;
-#pragma unroll
-            for (int m = 0; m < BP_PPT; ++m) {
-                const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
-                const float ub = bin_position<MODE>(num, c0, c1);
-                g[m] = __builtin_amdgcn_fractf(ub);
-                kb[m] = (uint32_t)ub;
-                tie |= fabsf(g[m] - 0.5f) > 0.5f - A.tie_eps;
-            }
-            if (tie) {
-                // within tie_eps of a rounding tie: take the fp64 decision
-                const size_t pn = 3 * (size_t)(n0 + p);
-#pragma unroll
-                for (int m = 0; m < BP_PPT; ++m) {
-                    if (fabsf(g[m] - 0.5f) > 0.5f - A.tie_eps) {
-                        const double zp = DEM ? A.z0 + (double)hv[m] : zl; // the pixel's height
-                        const int kabs = nearest_bin_fp64(A.pos[pn], A.pos[pn + 1], A.pos[pn + 2], A.x0, A.y0,
-                                                          zp, A.dx, A.dy, A.r0, A.dr, i_pix, j_pix0 + BP_WAVES * m);
-                        int kr = kabs - klo_s[p];
-                        kr = kr < 0 ? 0 : (kr > A.win - 1 ? A.win - 1 : kr);
-                        g[m] = g[m] + (float)((int)kb[m] - kr); // = ub - kr
-                        kb[m] = (uint32_t)kr;
-                    }
-                }
-            }
-#pragma unroll
-            for (int m = 0; m < BP_PPT; ++m) {
-                // the staged sample carries exp(-j pi kappa), so exp(j 2 pi kappa g) completes the phase
-                const float2 sv = *reinterpret_cast<const float2*>(smem + ((kb[m] << 3) + wbase));
-                float sn, cs;
-                sincos_rev(kappa * g[m], &sn, &cs);
-                mac<ACC>(accr[m], acci[m], cmpr[m], cmpi[m], sv.x, sv.y, cs, sn);
             }
         } else {
             // 8-tap windowed sinc: entry k of the window holds the coefficients of the

@@ -26,12 +26,12 @@
 #define BP_MAX_CHUNK 112 // pulses staged in LDS per step (measured: 64 -> 112 is 2-4 % faster)
 #endif
 // Pulses per unrolled hot-loop iteration (measured best: linear four, sinc8
-// eight, nearest one, whose rare fp64 branch is large).
+// eight).  Nearest works on groups of pulses, with one tie branch per group.
 #ifndef BP_PUNROLL_LINEAR
 #define BP_PUNROLL_LINEAR 4
 #endif
-#ifndef BP_PUNROLL_NEAREST
-#define BP_PUNROLL_NEAREST 1
+#ifndef BP_NEAREST_GROUP
+#define BP_NEAREST_GROUP 2
 #endif
 #ifndef BP_PUNROLL_SINC8
 #define BP_PUNROLL_SINC8 8

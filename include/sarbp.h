@@ -61,7 +61,7 @@ typedef enum { SARBP_NEAREST = 0, SARBP_LINEAR = 1, SARBP_SINC8 = 2 } sarbp_inte
  * kernel, or partial sums folded into double precision).  The image stays complex64.
  *   SARBP_ACC_FP32    fp32 registers (default, fastest)
  *   SARBP_ACC_KAHAN   fp32 with a Kahan compensation term per pixel, per pulse
- *   SARBP_ACC_CHUNK64 fp32 within each LDS pulse chunk (<= 64 pulses), chunk partial
+ *   SARBP_ACC_CHUNK64 fp32 within each LDS pulse chunk (<= 112 pulses), chunk partial
  *                     sums added in fp64 (nearly free) */
 typedef enum { SARBP_ACC_FP32 = 0, SARBP_ACC_KAHAN = 1, SARBP_ACC_CHUNK64 = 2 } sarbp_accum;
 

@@ -333,77 +333,82 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
     }
 }
 
-// Stage the echo windows of one chunk into LDS: wave w takes pulses w, w+16, ...;
-// lanes take consecutive bins (coalesced loads of the echo row).  Samples
-// outside the record are zero; the carrier table covers bins -4 .. n_range + 3,
-// every bin whose taps can reach the record.
+// Stage the echo windows of one chunk into LDS.  Entry e = p W + kk of the
+// chunk's np x W entries is bin kk of pulse p's window (the LDS order).  Lanes
+// take B consecutive bins of one window per step (B = 2 for linear and nearest,
+// whose windows have even W; 1 for sinc8), and the steps are spread evenly over
+// all lanes of the workgroup, so short windows leave no lane idle; the pulse
+// p = (e / B) / (W / B) is one multiply-high by the plan's ceil(2^32 B / W).
+// Samples outside the record are zero: the loads read a clamped index and a
+// select zeroes them.  The carrier table holds bins -4 .. n_range + 3 (every
+// bin whose taps can reach the record; beyond them the samples are zero, so the
+// clamped carrier is never seen) and then two NaN entries, which a pulse with
+// no finite geometry reads instead, so its whole window is NaN.
+__device__ __forceinline__ float2 sample_or_zero(const float2* row, int k, int nr) {
+    const bool in = (uint32_t)k < (uint32_t)nr;
+    const float2 v = row[in ? (uint32_t)k : 0u];
+    return make_float2(in ? v.x : 0.f, in ? v.y : 0.f);
+}
+
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+    return make_float2(fmaf(a.x, b.x, -(a.y * b.y)), fmaf(a.x, b.y, a.y * b.x));
+}
+
 template <int INTERP>
-__device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int np, int n0, int wave, int lane) {
-    const int W = A.win, nr = A.n_range;
-    for (int p = wave; p < np; p += BP_WAVES) {
+__device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int np, int n0, int tid) {
+    constexpr int B = INTERP == SARBP_SINC8 ? 1 : 2;
+    const int W = A.win, Wu = W / B, nr = A.n_range;
+    const int nu = np * Wu;
+    for (int u = tid; u < nu; u += BP_THREADS) {
+        const int p = (int)__umulhi((uint32_t)u, A.win_magic);
         const int klo = klo_s[p];
-        const float2* row = A.echo + (size_t)(n0 + p) * (size_t)nr;
         const bool bad = (klo == INT32_MIN);
-        for (int kk = lane; kk < W; kk += 64) {
-            const int k = klo + kk;
-            float2 e = make_float2(0.f, 0.f);
-            if (!bad && k >= -4 && k <= nr + 3) e = A.phase[k + 4];
-            if constexpr (INTERP == SARBP_LINEAR) {
-                float2 s0 = make_float2(0.f, 0.f), s1 = make_float2(0.f, 0.f);
-                if (!bad) {
-                    if (k >= 0 && k < nr) s0 = row[k];
-                    if (k + 1 >= 0 && k + 1 < nr) s1 = row[k + 1];
-                }
-                float4 v;
-                v.x = s0.x * e.x - s0.y * e.y;
-                v.y = s0.x * e.y + s0.y * e.x;
-                const float drx = s1.x - s0.x, dry = s1.y - s0.y;
-                v.z = drx * e.x - dry * e.y;
-                v.w = drx * e.y + dry * e.x;
-                if (bad) v = make_float4(NAN, NAN, NAN, NAN);
-                reinterpret_cast<float4*>(smem)[p * W + kk] = v;
-            } else if constexpr (INTERP == SARBP_NEAREST) {
-                float2 s0 = make_float2(0.f, 0.f);
-                if (!bad && k >= 0 && k < nr) s0 = row[k];
-                const float2 er = make_float2(e.x * A.half_rot.x - e.y * A.half_rot.y,
-                                              e.x * A.half_rot.y + e.y * A.half_rot.x);
-                float2 v = make_float2(s0.x * er.x - s0.y * er.y, s0.x * er.y + s0.y * er.x);
-                if (bad) v = make_float2(NAN, NAN);
-                reinterpret_cast<float2*>(smem)[p * W + kk] = v;
-            } else {
-                // Taps k-3 .. k+4 pair up as (k+t-3, k+4-t), t = 0..3: tap k+4-t's weight
-                // polynomial is tap k+t-3's with g -> -g, so coefficient j takes the
-                // pair's sum (j even) or difference (j odd) times sinc_poly[4 j + t].
-                float2 ps[4], pd[4];
+        const int k = (bad ? 0 : klo) + B * (u - (int)__umul24((uint32_t)p, (uint32_t)Wu));
+        const float2* row = A.echo + (size_t)(n0 + p) * (size_t)nr;
+        const int ke = bad ? nr + 8 : (k < -4 ? 0 : (k > nr + 4 - B ? nr + 8 - B : k + 4));
+        const float2 c0 = A.phase[ke];
+        if constexpr (INTERP == SARBP_LINEAR) {
+            const float2 c1 = A.phase[ke + 1];
+            const float2 s0 = sample_or_zero(row, k, nr), s1 = sample_or_zero(row, k + 1, nr),
+                         s2 = sample_or_zero(row, k + 2, nr);
+            const float2 a0 = cmul(s0, c0), d0 = cmul(make_float2(s1.x - s0.x, s1.y - s0.y), c0);
+            const float2 a1 = cmul(s1, c1), d1 = cmul(make_float2(s2.x - s1.x, s2.y - s1.y), c1);
+            float4* dst = reinterpret_cast<float4*>(smem) + 2 * u;
+            dst[0] = make_float4(a0.x, a0.y, d0.x, d0.y);
+            dst[1] = make_float4(a1.x, a1.y, d1.x, d1.y);
+        } else if constexpr (INTERP == SARBP_NEAREST) {
+            const float2 c1 = A.phase[ke + 1];
+            const float2 v0 = cmul(sample_or_zero(row, k, nr), cmul(c0, A.half_rot));
+            const float2 v1 = cmul(sample_or_zero(row, k + 1, nr), cmul(c1, A.half_rot));
+            reinterpret_cast<float4*>(smem)[u] = make_float4(v0.x, v0.y, v1.x, v1.y);
+        } else {
+            // Taps k-3 .. k+4 pair up as (k+t-3, k+4-t), t = 0..3: tap k+4-t's weight
+            // polynomial is tap k+t-3's with g -> -g, so coefficient j takes the
+            // pair's sum (j even) or difference (j odd) times sinc_poly[4 j + t].
+            float2 ps[4], pd[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const float2 sa = sample_or_zero(row, k + t - 3, nr), sb = sample_or_zero(row, k + 4 - t, nr);
+                ps[t] = make_float2(sa.x + sb.x, sa.y + sb.y);
+                pd[t] = make_float2(sa.x - sb.x, sa.y - sb.y);
+            }
+            float2 cj[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float2* src = (j & 1) ? pd : ps;
+                float r = 0.f, i = 0.f;
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    const int ka = k + t - 3, kb = k + 4 - t;
-                    float2 sa = make_float2(0.f, 0.f), sb = make_float2(0.f, 0.f);
-                    if (!bad && ka >= 0 && ka < nr) sa = row[ka];
-                    if (!bad && kb >= 0 && kb < nr) sb = row[kb];
-                    ps[t] = make_float2(sa.x + sb.x, sa.y + sb.y);
-                    pd[t] = make_float2(sa.x - sb.x, sa.y - sb.y);
+                    r = fmaf(A.sinc_poly[4 * j + t], src[t].x, r);
+                    i = fmaf(A.sinc_poly[4 * j + t], src[t].y, i);
                 }
-                float cr[8], ci[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float2* src = (j & 1) ? pd : ps;
-                    float r = 0.f, i = 0.f;
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        r = fmaf(A.sinc_poly[4 * j + t], src[t].x, r);
-                        i = fmaf(A.sinc_poly[4 * j + t], src[t].y, i);
-                    }
-                    cr[j] = r * e.x - i * e.y;
-                    ci[j] = r * e.y + i * e.x;
-                    if (bad) cr[j] = ci[j] = NAN;
-                }
-                float4* dst = reinterpret_cast<float4*>(smem) + ((size_t)p * W + kk) * 4;
-                dst[0] = make_float4(cr[7], ci[7], cr[6], ci[6]);
-                dst[1] = make_float4(cr[5], ci[5], cr[4], ci[4]);
-                dst[2] = make_float4(cr[3], ci[3], cr[2], ci[2]);
-                dst[3] = make_float4(cr[1], ci[1], cr[0], ci[0]);
+                cj[j] = cmul(make_float2(r, i), c0);
             }
+            float4* dst = reinterpret_cast<float4*>(smem) + (size_t)u * 4;
+            dst[0] = make_float4(cj[7].x, cj[7].y, cj[6].x, cj[6].y);
+            dst[1] = make_float4(cj[5].x, cj[5].y, cj[4].x, cj[4].y);
+            dst[2] = make_float4(cj[3].x, cj[3].y, cj[2].x, cj[2].y);
+            dst[3] = make_float4(cj[1].x, cj[1].y, cj[0].x, cj[0].y);
         }
     }
 }
@@ -512,7 +517,7 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         if (tid == 0) *prio_s = chunk_priority(A, n0);
         const int m1 = __syncthreads_or(need & 1);
         const int m2 = __syncthreads_or(need & 2);
-        stage_chunk<INTERP>(A, smem, klo_s, np, n0, wave, lane);
+        stage_chunk<INTERP>(A, smem, klo_s, np, n0, tid);
         __syncthreads();
         set_priority(*prio_s);
         if (m2)
@@ -636,6 +641,10 @@ int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* ech
     A.nblocks = A.ntiles * (p.nz > 1 ? p.nz : 1);
     A.dz = p.nz > 1 ? p.dz : 0.0;
     A.win = plan->win;
+    {
+        const uint64_t wu = (uint64_t)(plan->p.interp == SARBP_SINC8 ? plan->win : plan->win / 2);
+        A.win_magic = (uint32_t)(((1ull << 32) + wu - 1) / wu);
+    }
     A.margin_lo = plan->margin_lo;
     A.chunk = plan->chunk;
     A.accumulate = accumulate;

@@ -77,6 +77,7 @@ struct BpArgs {
     int tiles_x, ntiles;
     int nblocks;           // ntiles * voxel layers: the launch's workgroups
     int win, margin_lo, chunk, accumulate;
+    uint32_t win_magic;    // ceil(2^32 / wu), wu = win / (bins per staging step): u / wu = umulhi(u, win_magic)
     int slots;             // compute units: workgroup b and b + slots usually share a CU
     int* progress;         // [2 * slots] pulse progress per workgroup, read by its CU partner
     double r0, dr, inv_dr, x0, y0, z0, dx, dy;

@@ -100,7 +100,8 @@ void release(sarbp_plan* plan) {
 // k = -4 .. n_range + 3 (every bin whose interpolation taps can reach the
 // record), reduced modulo one cycle in double precision.
 std::vector<float2> phase_table(const sarbp_params& p) {
-    std::vector<float2> t((size_t)p.n_range + 8);
+    // bins -4 .. n_range + 3, then two NaN entries (the window of a pulse with no finite geometry)
+    std::vector<float2> t((size_t)p.n_range + 10, make_float2(NAN, NAN));
     for (int64_t k = -4; k <= (int64_t)p.n_range + 3; ++k) {
         const double cyc = 2.0 * (p.r0 + (double)k * p.dr) / p.wavelength;
         const double fr = cyc - floor(cyc);
@@ -218,6 +219,8 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
         return SARBP_EUNSUPPORTED;
     }
     plan->win = (int)span_bins + plan->margin_lo + 2 + taps_hi;
+    // linear and nearest windows are staged two bins per lane step: make W even
+    if (p.interp != SARBP_SINC8) plan->win += plan->win & 1;
     const int eb = p.interp == SARBP_NEAREST ? 8 : (p.interp == SARBP_LINEAR ? 16 : 64);
     if (p.interp == SARBP_SINC8) sinc8_polynomials(plan->sinc_poly);
     const int per_pulse = plan->win * eb + (p.dem_relief > 0.0 ? 3 : 2) * 16 + 4;
@@ -226,7 +229,10 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     int chunk = (BP_LDS_BUDGET - 64) / per_pulse;
     if (chunk < 8) chunk = (150 * 1024 - 64) / per_pulse;
     if (chunk > BP_MAX_CHUNK) chunk = BP_MAX_CHUNK;
-    if (chunk < 1) {
+    // (the staging divides step indices u < chunk * wu by wu <= win with a 32-bit
+    // multiply-high, exact while chunk * wu * wu < 2^32; the LDS bound keeps
+    // chunk * win below 19200, so this holds whenever a chunk fits)
+    if (chunk < 1 || (uint64_t)chunk * plan->win * plan->win >= (1ull << 32)) {
         release(plan);
         return SARBP_EUNSUPPORTED;
     }

@@ -506,20 +506,32 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     float4* cst = reinterpret_cast<float4*>(smem + (size_t)P * W * entry_bytes<INTERP>());
     int* klo_s = reinterpret_cast<int*>(cst + (DEM ? 3 : 2) * P);
     int* prio_s = klo_s + P;
+    // The accuracy mode of a chunk is the OR of its pulses' modes.  The words are
+    // double-buffered: chunk c ORs into mode_s[c & 1] and clears mode_s[(c + 1) & 1],
+    // which the previous chunk finished reading before its last barrier.
+    int* mode_s = prio_s + 1;
+    if (tid == 0) mode_s[0] = mode_s[1] = 0;
+    __syncthreads();
 
     // The first chunk is half size on alternate workgroups: both placements of a
     // CU's two workgroups (b, b + slots) and (b, b + 8) get opposite parities.
     const int stagger = BP_STAGGER ? (((int)blockIdx.x / A.slots) ^ ((int)blockIdx.x >> 3)) & 1 : 0;
-    for (int n0 = 0, np = 0; n0 < (bad_tile ? 0 : A.n); n0 += np) {
+    for (int n0 = 0, np = 0, c = 0; n0 < (bad_tile ? 0 : A.n); n0 += np, ++c) {
         np = min((n0 == 0 && stagger) ? max(1, P >> 1) : P, A.n - n0);
-        int need = 0;
-        if (tid < np) need = pulse_setup(A, n0 + tid, cx, cy, cz, cst + (DEM ? 3 : 2) * tid, klo_s + tid, DEM);
-        if (tid == 0) *prio_s = chunk_priority(A, n0);
-        const int m1 = __syncthreads_or(need & 1);
-        const int m2 = __syncthreads_or(need & 2);
+        if (tid < np) {
+            const int need = pulse_setup(A, n0 + tid, cx, cy, cz, cst + (DEM ? 3 : 2) * tid, klo_s + tid, DEM);
+            if (need) atomicOr(mode_s + (c & 1), need);
+        }
+        if (tid == 0) {
+            *prio_s = chunk_priority(A, n0);
+            mode_s[(c + 1) & 1] = 0;
+        }
+        __syncthreads();
         stage_chunk<INTERP>(A, smem, klo_s, np, n0, tid);
         __syncthreads();
         set_priority(*prio_s);
+        const int mode = __builtin_amdgcn_readfirstlane(mode_s[c & 1]); // the same word for every lane
+        const int m1 = mode & 1, m2 = mode & 2;
         if (m2)
             accumulate_chunk<INTERP, 2, ACC, DEM>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv,
                                                    accr, acci, cmpr, cmpi, dzv, hv, zl);

@@ -17,9 +17,16 @@
 // into the first pass of the inverse transform (computed as
 // conj(FFT(conj(X H)))), and the last pass writes the conjugated result straight
 // to global memory, so the record crosses HBM once each way.
+//
+// LDS layout: a pass with Ns < 32 writes each lane's outputs Ns apart, so the
+// lanes of a wave would land on a few banks.  Its output buffer is padded by Ns
+// entries after every group of Ns R (entry i is stored at i + Ns floor(i / (Ns R))):
+// R + 1 is odd, so the lanes' groups then start on distinct banks, and both the
+// writer's and the next reader's pad is one per-lane term plus compile-time
+// constants.  The padded buffer holds N (1 + 1/8) entries.
 #include "sarbp_internal.h"
 
-#pragma clang fp contract(off)
+#pragma clang fp contract(fast)
 
 namespace {
 
@@ -123,24 +130,29 @@ constexpr int rc_passes(int L) {
 
 // One Stockham pass: butterfly j reads x[j + r N/R], twiddles input r by
 // exp(-2 pi i k r/(Ns R)) (k = j mod Ns) and writes output r to
-// (j / Ns) Ns R + k + r Ns.
-template <int L, int R, int NS, int SRC, int DST>
+// (j / Ns) Ns R + k + r Ns.  PADR is the pad unit of the previous pass's writes
+// (0: unpadded), PADW this pass's (see the LDS layout above).
+template <int L, int R, int NS, int SRC, int DST, int PADR, int PADW>
 __device__ __forceinline__ void pass(const RcArgs& A, float2* buf, const float2* rin, float2* rout) {
     constexpr int N = 1 << L, T = rc_threads(L), NB = N / R, BPT = (NB + T - 1) / T;
+    static_assert(NB % NS == 0, "group size divides the butterfly stride");
     float2 v[BPT][R];
 #pragma unroll
     for (int b = 0; b < BPT; ++b) {
         const int j = threadIdx.x + b * T;
         if (NB % T == 0 || j < NB) {
+            // (j + r NB) / Ns = j / Ns + r NB / Ns: the previous writer's pad
+            const int rpad = PADR ? PADR * (j / NS) : 0;
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 const int idx = j + r * NB;
+                const int phys = idx + rpad + PADR * (r * NB / NS);
                 if constexpr (SRC == SRC_RAW) {
                     v[b][r] = rin[idx];
                 } else if constexpr (SRC == SRC_LDS_FILTER) {
-                    v[b][r] = cconj(cmul(buf[idx], A.filt[idx]));
+                    v[b][r] = cconj(cmul(buf[phys], A.filt[idx]));
                 } else {
-                    v[b][r] = buf[idx];
+                    v[b][r] = buf[phys];
                 }
             }
         }
@@ -161,7 +173,8 @@ __device__ __forceinline__ void pass(const RcArgs& A, float2* buf, const float2*
                 }
             }
             dft<R>(v[b]);
-            const int base = (j / NS) * NS * R + k;
+            // (base + r Ns) / (Ns R) = j / Ns: this pass's pad
+            const int base = (j / NS) * NS * R + k + (PADW ? PADW * (j / NS) : 0);
 #pragma unroll
             for (int r = 0; r < R; ++r) {
                 if constexpr (DST == DST_OUT_CONJ) {
@@ -175,15 +188,21 @@ __device__ __forceinline__ void pass(const RcArgs& A, float2* buf, const float2*
     if constexpr (DST == DST_LDS) __syncthreads();
 }
 
-template <int L, int P, int NS, int SRC0, int DST_LAST>
+// Passes P .. of one transform; PPREV is the pad unit of pass P - 1's writes.
+// Passes with Ns < 32 pad their output, except a transform's last pass.
+template <int L, int P, int NS, int SRC0, int DST_LAST, int PPREV>
 __device__ __forceinline__ void fft_from(const RcArgs& A, float2* buf, const float2* rin, float2* rout) {
     if constexpr (P < rc_passes(L)) {
         constexpr int R = rc_radix(L, P);
         constexpr bool first = (P == 0), last = (P == rc_passes(L) - 1);
-        pass<L, R, NS, first ? SRC0 : SRC_LDS, last ? DST_LAST : DST_LDS>(A, buf, rin, rout);
-        fft_from<L, P + 1, NS * R, SRC0, DST_LAST>(A, buf, rin, rout);
+        constexpr int PADW = (!last && NS < 32) ? NS : 0;
+        pass<L, R, NS, first ? SRC0 : SRC_LDS, last ? DST_LAST : DST_LDS, first ? 0 : PPREV, PADW>(A, buf, rin,
+                                                                                                   rout);
+        fft_from<L, P + 1, NS * R, SRC0, DST_LAST, PADW>(A, buf, rin, rout);
     }
 }
+
+constexpr size_t rc_lds_bytes(int L) { return ((size_t)1 << L) / 8 * 9 * sizeof(float2); }
 
 template <int L>
 __global__ __launch_bounds__(rc_threads(L)) void rc_kernel(RcArgs A) {
@@ -191,14 +210,13 @@ __global__ __launch_bounds__(rc_threads(L)) void rc_kernel(RcArgs A) {
     constexpr size_t N = (size_t)1 << L;
     const float2* rin = A.raw + (size_t)blockIdx.x * N;
     float2* rout = A.out + (size_t)blockIdx.x * N;
-    fft_from<L, 0, 1, SRC_RAW, DST_LDS>(A, rc_buf, rin, rout);             // X = FFT(x) -> LDS
-    fft_from<L, 0, 1, SRC_LDS_FILTER, DST_OUT_CONJ>(A, rc_buf, rin, rout); // y = conj(FFT(conj(X H)))
+    fft_from<L, 0, 1, SRC_RAW, DST_LDS, 0>(A, rc_buf, rin, rout);             // X = FFT(x) -> LDS
+    fft_from<L, 0, 1, SRC_LDS_FILTER, DST_OUT_CONJ, 0>(A, rc_buf, rin, rout); // y = conj(FFT(conj(X H)))
 }
 
 template <int L>
 int launch(const RcArgs& A, int n, hipStream_t stream) {
-    const size_t lds = ((size_t)1 << L) * sizeof(float2);
-    hipLaunchKernelGGL(rc_kernel<L>, dim3(n), dim3(rc_threads(L)), lds, stream, A);
+    hipLaunchKernelGGL(rc_kernel<L>, dim3(n), dim3(rc_threads(L)), rc_lds_bytes(L), stream, A);
     return hipGetLastError() == hipSuccess ? SARBP_OK : SARBP_EDEVICE;
 }
 
@@ -206,7 +224,7 @@ template <int L>
 int allow_lds() {
     return hipFuncSetAttribute(reinterpret_cast<const void*>(rc_kernel<L>),
                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)(((size_t)1 << L) * sizeof(float2))) == hipSuccess
+                               (int)rc_lds_bytes(L)) == hipSuccess
                ? SARBP_OK
                : SARBP_EDEVICE;
 }
@@ -214,8 +232,9 @@ int allow_lds() {
 } // namespace
 
 int sarbp_rc_prepare_device() {
-    // only the 16384-point record needs more than the default 64 KiB of dynamic LDS
-    return allow_lds<14>();
+    // the 8192- and 16384-point records need more than the default 64 KiB of dynamic LDS
+    const int st = allow_lds<13>();
+    return st == SARBP_OK ? allow_lds<14>() : st;
 }
 
 int sarbp_launch_rc(const sarbp_plan* plan, const float2* raw, float2* out, int n, hipStream_t stream) {

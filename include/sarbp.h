@@ -30,7 +30,7 @@
  *     a compute unit; it steers scheduling only, so overlapping calls that
  *     share it stay correct (they may run slightly slower).  Calls that write
  *     the same image must be ordered by the caller.  No entry point allocates
- *     device memory except sarbp_plan_create.
+ *     device memory except sarbp_plan_create and sarbp_stream_create.
  */
 #ifndef SARBP_H
 #define SARBP_H

@@ -122,6 +122,46 @@ def test_one_plan_on_two_streams_concurrently(sb):
         assert torch.equal(ia, ref_a) and torch.equal(ib, ref_b)
 
 
+def test_graph_capture_replays_match_eager(sb):
+    """Range compression and backprojection captured once in a HIP graph (the entry
+    points only enqueue kernels: they allocate and clear nothing) and replayed three
+    times, with eager work and synchronisation between the replays: every replay
+    reproduces the eager results bit for bit, also when accumulating into an image."""
+    import torch
+
+    s = synth.make_scene(5, na=256, nx=200, ny=96, n_targets=2)
+    with sb.Plan.for_scene(s, n_fast=s.nr) as plan:
+        raw = torch.from_numpy(s.raw).cuda()
+        pos = torch.from_numpy(s.positions).cuda()
+        rc_ref = plan.range_compress(raw)
+        ref = plan.backproject(pos, rc_ref)
+        torch.cuda.synchronize()
+        rc, img, acc = torch.empty_like(raw), plan.new_image(), plan.new_image()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):  # one eager pass on the capture's side stream first
+            plan.range_compress(raw, out=rc)
+            plan.backproject(pos, rc, image=img)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            plan.range_compress(raw, out=rc)
+            plan.backproject(pos, rc, image=img)
+            plan.backproject(pos, rc, image=acc, accumulate=1)
+        for k in range(3):
+            rc.fill_(7.0)
+            img.fill_(-3.0)
+            acc.zero_()
+            junk = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work between replays
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            _say(f"[graph] replay {k}: rc {torch.equal(rc, rc_ref)}, image {torch.equal(img, ref)}, "
+                 f"accumulated {torch.equal(acc, ref)} ({float(junk):.1f})")
+            assert torch.equal(rc, rc_ref) and torch.equal(img, ref) and torch.equal(acc, ref)
+
+
 @pytest.mark.parametrize("first, nr", [(246, 48), (226, 36)], ids=["record-starts-in-scene", "record-ends-in-scene"])
 @pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
 def test_zero_extension_and_far_pixels(sb, interp, first, nr):

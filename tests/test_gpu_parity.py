@@ -687,6 +687,22 @@ def test_coarse_grid_uses_large_lds_windows(sb, interp):
     assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
 
 
+@pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
+def test_anisotropic_squinted_grid(sb, interp):
+    """0.15 m x 0.35 m pixels (a 41-bin window, which linear and nearest stage as 42) on
+    a grid centred 300 m ahead of the track's middle (a squinted view), random echo:
+    the full image against the oracle."""
+    import dataclasses
+
+    nx, ny, dx, dy = 150, 70, 0.15, 0.35
+    s = _custom_scene(synth.track(160), 4096, nx, ny, dx, dy, interp, 41)
+    s = dataclasses.replace(s, x0=300.0 - (nx // 2) * dx)
+    _say(f"[anisotropic {interp}] {nx}x{ny} at {dx} x {dy} m, 300 m squint")
+    got = _run_bp(sb, s)
+    want = oracle.scene_backproject(s)
+    assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
+
+
 @pytest.mark.parametrize("ground, height", [(400.0, 300.0), (1600.0, 1200.0)])
 @pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
 def test_short_range_series_modes(sb, interp, ground, height):

@@ -113,6 +113,12 @@ extern "C" int sarbp_backproject_host(sarbp_stream* s, const double* positions_h
     for (int64_t n0 = 0, c = 0; n0 < n; n0 += s->chunk, ++c) {
         const int b = (int)(c & 1);
         const int np = (int)((int64_t)n - n0 < s->chunk ? (int64_t)n - n0 : s->chunk);
+        // The host waits until staging buffer b is free before queueing its next
+        // fill, so it runs at most two chunks ahead of the device.  Unbounded
+        // run-ahead queued hundreds of cross-stream waits, and the runtime then
+        // stalled the calling thread for 10-40 ms at a time, long enough to leave
+        // the device idle.  The device still orders the copy by the event below.
+        if (hipEventSynchronize(s->released[b]) != hipSuccess) return SARBP_EDEVICE;
         // copy stream: wait until the kernels that last read buffer b have run, then fill it.
         // The pulses go first: the runtime moves large copies with the DMA engines, which
         // run beside the kernel of the previous chunk, but small ones (here the positions,

@@ -188,13 +188,40 @@ def aux_scenes(sb, steps, warmup):
             img = plan.new_image()
             k = steps if cfg != 3 else max(5, steps // 4)
             tm, _ = time_launches(lambda: plan.backproject(pos, echo, image=img), k, warmup)
-            del echo
         upd = s.updates / (tm["mean"] * 1e-3)
         out[key] = {"scene": f"{s.name}: {s.na} pulses x {s.nr} bins -> {s.nx}x{s.ny}, {interp}",
                     "ms": tm["mean"], "ms_median": tm["median"], "ms_min": tm["min"], "launches": k,
                     "G_updates_per_s": upd / 1e9, "TFLOPs_algorithmic": FLOPS_PER_UPDATE[interp] * upd / 1e12,
                     "frac_fp32_peak": FLOPS_PER_UPDATE[interp] * upd / 1e12 / PEAK_FP32_TFLOPS}
-        del s
+        if cfg == 3:
+            out["large_shards"] = aux_shards(sb, s, pos, echo, max(5, steps // 4), warmup)
+        del echo, s
+    return out
+
+
+def aux_shards(sb, s, pos, echo, steps, warmup):
+    """One GPU's share of the large scene for G = 2, 4 and 8 GPUs, at its real shape:
+    a central band of ny/G image rows with every pulse (image-domain split), or the
+    whole image with the middle na/G pulses (pulse-domain split).  The projected rate
+    of G GPUs is the whole scene's updates over the share's time, communication
+    excluded (the pulse split would add one all-reduce of the complex image)."""
+    out = {}
+    for G in (2, 4, 8):
+        rows, npul = s.ny // G, s.na // G
+        j0, p0 = (s.ny - rows) // 2, (s.na - npul) // 2
+        row = {}
+        with sb.Plan.for_scene(s, ny=rows, y0=s.y0 + j0 * s.dy) as plan:
+            img = plan.new_image()
+            tm, _ = time_launches(lambda: plan.backproject(pos, echo, image=img), steps, warmup)
+        row["image_band"] = {"pixels": [rows, s.nx], "pulses": s.na, "ms": tm["mean"],
+                             "projected_G_updates_per_s": s.updates / (tm["mean"] * 1e-3) / 1e9}
+        with sb.Plan.for_scene(s, n_pulses=npul) as plan:
+            img = plan.new_image()
+            p, e = pos[p0:p0 + npul], echo[p0:p0 + npul]
+            tm, _ = time_launches(lambda: plan.backproject(p, e, image=img), steps, warmup)
+        row["pulse_share"] = {"pixels": [s.ny, s.nx], "pulses": npul, "ms": tm["mean"],
+                              "projected_G_updates_per_s": s.updates / (tm["mean"] * 1e-3) / 1e9}
+        out[f"G{G}"] = row
     return out
 
 

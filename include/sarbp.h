@@ -192,8 +192,9 @@ int sarbp_stream_create(const sarbp_plan* plan, int32_t chunk, int32_t compress,
  * Chunk c is copied on the object's copy stream while chunk c - 1 is processed
  * on `stream`; the two staging buffers alternate, ordered by events.  Before
  * refilling a staging buffer the calling thread waits until the device has
- * finished with it, so the host runs at most two chunks ahead; the call returns
- * once the last chunk is enqueued.  Synchronise `stream` before reading the
+ * finished with it, so the host runs at most two chunks ahead (and the call
+ * cannot be captured into a HIP graph); it returns once the last chunk is
+ * enqueued.  Synchronise `stream` before reading the
  * image or reusing the host buffers.  Overlap needs page-locked host memory
  * (hipHostMalloc); pageable memory still works but copies synchronously.  One
  * stream object must not be used by two threads at once; calls on it are

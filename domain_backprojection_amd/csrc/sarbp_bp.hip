@@ -204,14 +204,14 @@ __device__ __forceinline__ void mac(float& ar, float& ai, float& cr, float& ci, 
 // within tie_eps of a rounding tie in fp64, then the fetches and accumulations.
 // ub carries u + 1/2: its floor is the nearest bin and g - 1/2 = u - bin; the
 // staged sample carries exp(-j pi kappa), so exp(j 2 pi kappa g) completes the phase.
-template <int G, int MODE, int ACC, bool DEM>
+template <int G, int MODE, int ACC, bool DEM, int PPT>
 __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem, const float4* cst, const int* klo_s,
                                               int p0, int n0, int i_pix, int j_pix0, float dxl, const float* dyv,
                                               const float* ddv, float* accr, float* acci, float* cmpr, float* cmpi,
                                               const float* dzv, const float* hv, double zl, uint32_t wstride) {
     constexpr int CS = DEM ? 3 : 2;
-    float g[G][BP_PPT];
-    uint32_t kb[G][BP_PPT];
+    float g[G][PPT];
+    uint32_t kb[G][PPT];
     bool tie = false;
 #pragma unroll
     for (int q = 0; q < G; ++q) {
@@ -219,7 +219,7 @@ __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem,
         const float4 c1 = cst[CS * (p0 + q) + 1];
         const float4 c2 = DEM ? cst[CS * (p0 + q) + 2] : c1;
 #pragma unroll
-        for (int m = 0; m < BP_PPT; ++m) {
+        for (int m = 0; m < PPT; ++m) {
             const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
             const float ub = bin_position<MODE>(num, c0, c1);
             g[q][m] = __builtin_amdgcn_fractf(ub);
@@ -232,7 +232,7 @@ __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem,
         for (int q = 0; q < G; ++q) {
             const size_t pn = 3 * (size_t)(n0 + p0 + q);
 #pragma unroll
-            for (int m = 0; m < BP_PPT; ++m) {
+            for (int m = 0; m < PPT; ++m) {
                 if (fabsf(g[q][m] - 0.5f) > 0.5f - A.tie_eps) {
                     const double zp = DEM ? A.z0 + (double)hv[m] : zl; // the pixel's height
                     const int kabs = nearest_bin_fp64(A.pos[pn], A.pos[pn + 1], A.pos[pn + 2], A.x0, A.y0, zp, A.dx,
@@ -249,7 +249,7 @@ __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem,
     for (int q = 0; q < G; ++q) {
         const uint32_t wbase = (uint32_t)(p0 + q) * wstride;
 #pragma unroll
-        for (int m = 0; m < BP_PPT; ++m) {
+        for (int m = 0; m < PPT; ++m) {
             const float2 sv = *reinterpret_cast<const float2*>(smem + ((kb[q][m] << 3) + wbase));
             float sn, cs;
             sincos_rev(A.kappa * g[q][m], &sn, &cs);
@@ -258,7 +258,7 @@ __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem,
     }
 }
 
-template <int INTERP, int MODE, int ACC, bool DEM>
+template <int INTERP, int MODE, int ACC, bool DEM, int PPT>
 __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* smem, const float4* cst,
                                                  const int* klo_s, int np, int n0, int i_pix, int j_pix0,
                                                  float dxl, const float* dyv, const float* ddv, float* accr,
@@ -270,10 +270,10 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
     if constexpr (INTERP == SARBP_NEAREST) {
         int p = 0;
         for (; p + BP_NEAREST_GROUP <= np; p += BP_NEAREST_GROUP)
-            nearest_group<BP_NEAREST_GROUP, MODE, ACC, DEM>(A, smem, cst, klo_s, p, n0, i_pix, j_pix0, dxl, dyv, ddv,
+            nearest_group<BP_NEAREST_GROUP, MODE, ACC, DEM, PPT>(A, smem, cst, klo_s, p, n0, i_pix, j_pix0, dxl, dyv, ddv,
                                                               accr, acci, cmpr, cmpi, dzv, hv, zl, wstride);
         for (; p < np; ++p)
-            nearest_group<1, MODE, ACC, DEM>(A, smem, cst, klo_s, p, n0, i_pix, j_pix0, dxl, dyv, ddv, accr, acci,
+            nearest_group<1, MODE, ACC, DEM, PPT>(A, smem, cst, klo_s, p, n0, i_pix, j_pix0, dxl, dyv, ddv, accr, acci,
                                              cmpr, cmpi, dzv, hv, zl, wstride);
         return;
     }
@@ -287,7 +287,7 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
         const uint32_t wbase = (uint32_t)p * wstride;
         if constexpr (INTERP == SARBP_LINEAR) {
 #pragma unroll
-            for (int m = 0; m < BP_PPT; ++m) {
+            for (int m = 0; m < PPT; ++m) {
                 const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
                 const float ub = bin_position<MODE>(num, c0, c1);
                 const float f = __builtin_amdgcn_fractf(ub);
@@ -305,7 +305,7 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
             // interpolated sample at k + f, already multiplied by the carrier of bin k
             // (built by stage_chunk).  Stored highest degree first, two per float4.
 #pragma unroll
-            for (int m = 0; m < BP_PPT; ++m) {
+            for (int m = 0; m < PPT; ++m) {
                 const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
                 const float ub = bin_position<MODE>(num, c0, c1);
                 const float f = __builtin_amdgcn_fractf(ub);
@@ -415,7 +415,7 @@ __device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int n
 
 // At most 64 VGPRs, so two 1024-lane workgroups (8 waves per SIMD) fit on a CU:
 // the loop needs that many waves to hide LDS and transcendental latency.
-template <int INTERP, int ACC, bool DEM>
+template <int INTERP, int ACC, bool DEM, int PPT>
 __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void bp_kernel(BpArgs A) {
     extern __shared__ __align__(16) char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -429,21 +429,21 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     const int nt8 = (A.ntiles / 8) * 8;
     if (tile < nt8) tile = (tile & 7) * (nt8 / 8) + (tile >> 3);
     const int tx = tile % A.tiles_x, ty = tile / A.tiles_x;
-    const int i0 = tx * BP_TX, j0 = ty * BP_TY;
+    const int i0 = tx * BP_TX, j0 = ty * (BP_WAVES * PPT);
 
     // tile centre (fp64) and this lane's pixel offsets from it
-    const double cxp = (double)i0 + 0.5 * (BP_TX - 1), cyp = (double)j0 + 0.5 * (BP_TY - 1);
+    const double cxp = (double)i0 + 0.5 * (BP_TX - 1), cyp = (double)j0 + 0.5 * ((BP_WAVES * PPT) - 1);
     const double cx = A.x0 + cxp * A.dx, cy = A.y0 + cyp * A.dy;
     const double zl = A.z0 + (double)layer * A.dz; // this layer's height
     double cz = zl;
     const double ddx = ((double)lane - 0.5 * (BP_TX - 1)) * A.dx;
     const float dxl = (float)ddx;
-    float dyv[BP_PPT], ddv[BP_PPT], accr[BP_PPT], acci[BP_PPT];
-    float cmpr[BP_PPT], cmpi[BP_PPT]; // Kahan compensation (ACC_KAHAN)
-    double sumr[BP_PPT], sumi[BP_PPT]; // fp64 totals of the chunk partials (ACC_CHUNK64)
+    float dyv[PPT], ddv[PPT], accr[PPT], acci[PPT];
+    float cmpr[PPT], cmpi[PPT]; // Kahan compensation (ACC_KAHAN)
+    double sumr[PPT], sumi[PPT]; // fp64 totals of the chunk partials (ACC_CHUNK64)
 #pragma unroll
-    for (int m = 0; m < BP_PPT; ++m) {
-        const double ddy = ((double)(wave + BP_WAVES * m) - 0.5 * (BP_TY - 1)) * A.dy;
+    for (int m = 0; m < PPT; ++m) {
+        const double ddy = ((double)(wave + BP_WAVES * m) - 0.5 * ((BP_WAVES * PPT) - 1)) * A.dy;
         dyv[m] = (float)ddy;
         ddv[m] = (float)(ddx * ddx + ddy * ddy);
         accr[m] = 0.f;
@@ -457,14 +457,14 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     // Terrain: pixel heights h (z = z0 + h); the tile centre sits at the tile's
     // mid-height, so |dz| <= half the tile's height range, which the plan's
     // window allows for up to dem_relief.  A tile beyond that bound is NaN.
-    float dzv[BP_PPT], hv[BP_PPT];
+    float dzv[PPT], hv[PPT];
     bool bad_tile = false;
 #pragma unroll
-    for (int m = 0; m < BP_PPT; ++m) dzv[m] = hv[m] = 0.f;
+    for (int m = 0; m < PPT; ++m) dzv[m] = hv[m] = 0.f;
     if constexpr (DEM) {
         float hmin = INFINITY, hmax = -INFINITY;
 #pragma unroll
-        for (int m = 0; m < BP_PPT; ++m) {
+        for (int m = 0; m < PPT; ++m) {
             const int j = j0 + wave + BP_WAVES * m, i = i0 + lane;
             if (i < A.nx && j < A.ny) {
                 hv[m] = A.dem[(size_t)j * A.nx + i];
@@ -494,8 +494,8 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         const double hc = 0.5 * ((double)hmin + (double)hmax);
         cz = A.z0 + hc;
 #pragma unroll
-        for (int m = 0; m < BP_PPT; ++m) {
-            const double ddy = ((double)(wave + BP_WAVES * m) - 0.5 * (BP_TY - 1)) * A.dy;
+        for (int m = 0; m < PPT; ++m) {
+            const double ddy = ((double)(wave + BP_WAVES * m) - 0.5 * ((BP_WAVES * PPT) - 1)) * A.dy;
             const double ddz = (double)hv[m] - hc;
             dzv[m] = (float)ddz;
             ddv[m] = (float)(ddx * ddx + ddy * ddy + ddz * ddz);
@@ -533,17 +533,17 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         const int mode = __builtin_amdgcn_readfirstlane(mode_s[c & 1]); // the same word for every lane
         const int m1 = mode & 1, m2 = mode & 2;
         if (m2)
-            accumulate_chunk<INTERP, 2, ACC, DEM>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv,
+            accumulate_chunk<INTERP, 2, ACC, DEM, PPT>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv,
                                                    accr, acci, cmpr, cmpi, dzv, hv, zl);
         else if (m1)
-            accumulate_chunk<INTERP, 1, ACC, DEM>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv,
+            accumulate_chunk<INTERP, 1, ACC, DEM, PPT>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv,
                                                    accr, acci, cmpr, cmpi, dzv, hv, zl);
         else
-            accumulate_chunk<INTERP, 0, ACC, DEM>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv,
+            accumulate_chunk<INTERP, 0, ACC, DEM, PPT>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv,
                                                    accr, acci, cmpr, cmpi, dzv, hv, zl);
         if constexpr (ACC == SARBP_ACC_CHUNK64) {
 #pragma unroll
-            for (int m = 0; m < BP_PPT; ++m) {
+            for (int m = 0; m < PPT; ++m) {
                 sumr[m] += (double)accr[m];
                 sumi[m] += (double)acci[m];
                 accr[m] = 0.f;
@@ -555,12 +555,12 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
 
     if (bad_tile) {
 #pragma unroll
-        for (int m = 0; m < BP_PPT; ++m) accr[m] = acci[m] = sumr[m] = sumi[m] = NAN;
+        for (int m = 0; m < PPT; ++m) accr[m] = acci[m] = sumr[m] = sumi[m] = NAN;
     }
     const int i = i0 + lane;
     if (i < A.nx) {
 #pragma unroll
-        for (int m = 0; m < BP_PPT; ++m) {
+        for (int m = 0; m < PPT; ++m) {
             const int j = j0 + wave + BP_WAVES * m;
             if (j < A.ny) {
                 float2* o = A.image + ((size_t)layer * A.ny + j) * A.nx + i;
@@ -590,49 +590,63 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     }
 }
 
-template <int INTERP, int ACC, bool DEM>
+template <int INTERP, int ACC, bool DEM, int PPT>
 int allow_lds_one(size_t bytes) {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(bp_kernel<INTERP, ACC, DEM>),
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(bp_kernel<INTERP, ACC, DEM, PPT>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) == hipSuccess
                ? SARBP_OK
                : SARBP_EDEVICE;
 }
 
-template <int INTERP, bool DEM>
-int allow_lds(int accum, size_t bytes) {
+template <int INTERP, bool DEM, int PPT>
+int allow_lds_acc(int accum, size_t bytes) {
     switch (accum) {
-        case SARBP_ACC_KAHAN: return allow_lds_one<INTERP, SARBP_ACC_KAHAN, DEM>(bytes);
-        case SARBP_ACC_CHUNK64: return allow_lds_one<INTERP, SARBP_ACC_CHUNK64, DEM>(bytes);
-        default: return allow_lds_one<INTERP, SARBP_ACC_FP32, DEM>(bytes);
+        case SARBP_ACC_KAHAN: return allow_lds_one<INTERP, SARBP_ACC_KAHAN, DEM, PPT>(bytes);
+        case SARBP_ACC_CHUNK64: return allow_lds_one<INTERP, SARBP_ACC_CHUNK64, DEM, PPT>(bytes);
+        default: return allow_lds_one<INTERP, SARBP_ACC_FP32, DEM, PPT>(bytes);
     }
 }
 
 template <int INTERP, bool DEM>
-void launch(const BpArgs& A, int accum, size_t lds, hipStream_t stream) {
+int allow_lds(int accum, int ppt, size_t bytes) {
+    return ppt == 1 ? allow_lds_acc<INTERP, DEM, 1>(accum, bytes) : allow_lds_acc<INTERP, DEM, 2>(accum, bytes);
+}
+
+template <int INTERP, bool DEM, int PPT>
+void launch_acc(const BpArgs& A, int accum, size_t lds, hipStream_t stream) {
     const dim3 grid(A.nblocks), block(BP_THREADS);
     switch (accum) {
         case SARBP_ACC_KAHAN:
-            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_KAHAN, DEM>), grid, block, lds, stream, A);
+            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_KAHAN, DEM, PPT>), grid, block, lds, stream, A);
             break;
         case SARBP_ACC_CHUNK64:
-            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_CHUNK64, DEM>), grid, block, lds, stream, A);
+            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_CHUNK64, DEM, PPT>), grid, block, lds, stream, A);
             break;
         default:
-            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_FP32, DEM>), grid, block, lds, stream, A);
+            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_FP32, DEM, PPT>), grid, block, lds, stream, A);
             break;
     }
+}
+
+template <int INTERP, bool DEM>
+void launch(const BpArgs& A, int accum, int ppt, size_t lds, hipStream_t stream) {
+    if (ppt == 1) launch_acc<INTERP, DEM, 1>(A, accum, lds, stream);
+    else launch_acc<INTERP, DEM, 2>(A, accum, lds, stream);
 }
 
 } // namespace
 
-int sarbp_bp_allow_lds(int interp, int accum, bool dem, size_t bytes) {
+int sarbp_bp_allow_lds(int interp, int accum, bool dem, int ppt, size_t bytes) {
     switch (interp) {
         case SARBP_NEAREST:
-            return dem ? allow_lds<SARBP_NEAREST, true>(accum, bytes) : allow_lds<SARBP_NEAREST, false>(accum, bytes);
+            return dem ? allow_lds<SARBP_NEAREST, true>(accum, ppt, bytes)
+                       : allow_lds<SARBP_NEAREST, false>(accum, ppt, bytes);
         case SARBP_LINEAR:
-            return dem ? allow_lds<SARBP_LINEAR, true>(accum, bytes) : allow_lds<SARBP_LINEAR, false>(accum, bytes);
+            return dem ? allow_lds<SARBP_LINEAR, true>(accum, ppt, bytes)
+                       : allow_lds<SARBP_LINEAR, false>(accum, ppt, bytes);
         default:
-            return dem ? allow_lds<SARBP_SINC8, true>(accum, bytes) : allow_lds<SARBP_SINC8, false>(accum, bytes);
+            return dem ? allow_lds<SARBP_SINC8, true>(accum, ppt, bytes)
+                       : allow_lds<SARBP_SINC8, false>(accum, ppt, bytes);
     }
 }
 
@@ -688,16 +702,16 @@ int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* ech
     const bool d = dem != nullptr;
     switch (p.interp) {
         case SARBP_NEAREST:
-            d ? launch<SARBP_NEAREST, true>(A, p.accum, plan->lds_bytes, stream)
-              : launch<SARBP_NEAREST, false>(A, p.accum, plan->lds_bytes, stream);
+            d ? launch<SARBP_NEAREST, true>(A, p.accum, plan->ppt, plan->lds_bytes, stream)
+              : launch<SARBP_NEAREST, false>(A, p.accum, plan->ppt, plan->lds_bytes, stream);
             break;
         case SARBP_LINEAR:
-            d ? launch<SARBP_LINEAR, true>(A, p.accum, plan->lds_bytes, stream)
-              : launch<SARBP_LINEAR, false>(A, p.accum, plan->lds_bytes, stream);
+            d ? launch<SARBP_LINEAR, true>(A, p.accum, plan->ppt, plan->lds_bytes, stream)
+              : launch<SARBP_LINEAR, false>(A, p.accum, plan->ppt, plan->lds_bytes, stream);
             break;
         default:
-            d ? launch<SARBP_SINC8, true>(A, p.accum, plan->lds_bytes, stream)
-              : launch<SARBP_SINC8, false>(A, p.accum, plan->lds_bytes, stream);
+            d ? launch<SARBP_SINC8, true>(A, p.accum, plan->ppt, plan->lds_bytes, stream)
+              : launch<SARBP_SINC8, false>(A, p.accum, plan->ppt, plan->lds_bytes, stream);
             break;
     }
     return hipGetLastError() == hipSuccess ? SARBP_OK : SARBP_EDEVICE;

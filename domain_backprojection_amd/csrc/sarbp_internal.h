@@ -8,19 +8,16 @@
 #include "sarbp.h"
 
 // Backprojection tiling (see sarbp_bp.hip): a workgroup of BP_WAVES wave64s
-// owns a tile of BP_TX (along x) by BP_WAVES * BP_PPT (along y) pixels; each
-// lane keeps BP_PPT pixels of one column in registers.  16 waves x 2 pixels
-// (64 x 32 tiles, 1024-lane workgroups) measured fastest on gfx950: the loop is
-// bound by VALU issue and needs many waves per SIMD to hide LDS and
-// transcendental latency.
+// owns a tile of BP_TX (along x) by BP_WAVES * ppt (along y) pixels; each lane
+// keeps ppt pixels of one column in registers.  16 waves x 2 pixels (64 x 32
+// tiles, 1024-lane workgroups) measured fastest on gfx950: the loop is bound by
+// VALU issue and needs many waves per SIMD to hide LDS and transcendental
+// latency.  Grids of fewer than two such tiles per CU use 1 pixel per lane
+// (64 x 16 tiles) instead, so that two workgroups still share each CU.
 #define BP_TX 64
 #ifndef BP_WAVES
 #define BP_WAVES 16
 #endif
-#ifndef BP_PPT
-#define BP_PPT 2
-#endif
-#define BP_TY (BP_WAVES * BP_PPT)
 #define BP_THREADS (64 * BP_WAVES)
 #ifndef BP_MAX_CHUNK
 #define BP_MAX_CHUNK 112 // pulses staged in LDS per step (measured: 64 -> 112 is 2-4 % faster)
@@ -52,6 +49,7 @@ struct sarbp_plan {
     float2* phase_tab;
     // backprojection launch geometry
     int tiles_x, tiles_y;
+    int ppt;          // backprojection pixels per lane (1 or 2): tiles of 64 x 16 ppt
     int win;          // LDS window entries per pulse
     int margin_lo;    // bins below the tile's lowest range kept in the window
     int chunk;        // pulses per LDS step

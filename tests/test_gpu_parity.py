@@ -703,6 +703,19 @@ def test_anisotropic_squinted_grid(sb, interp):
     assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
 
 
+@pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
+@pytest.mark.parametrize("ny", [1024, 96])
+def test_full_image_both_tile_heights(sb, interp, ny):
+    """A random echo over a 1024-wide grid: 1024 rows give 512 tiles of 64 x 32 (two
+    pixels per lane); 96 rows give too few for two per CU, so the plan takes 64 x 16
+    tiles (one pixel per lane).  The full image against the oracle."""
+    s = _custom_scene(synth.track(48), 2048, 1024, ny, synth.PIXEL, synth.PIXEL, interp, 43)
+    _say(f"[tile heights {interp}] 1024 x {ny}")
+    got = _run_bp(sb, s)
+    want = oracle.scene_backproject(s)
+    assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
+
+
 @pytest.mark.parametrize("ground, height", [(400.0, 300.0), (1600.0, 1200.0)])
 @pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
 def test_short_range_series_modes(sb, interp, ground, height):

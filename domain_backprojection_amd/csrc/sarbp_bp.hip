@@ -11,9 +11,10 @@
 //
 // Design on gfx950 (not the page's one-thread-per-pixel CUDA kernel):
 //
-// * A workgroup of 16 wave64s owns a 64 (x) by 32 (y) pixel tile (of one voxel
-//   layer, for volumes); each lane keeps 2 pixels of one column (register
-//   blocking) and accumulates them across all pulses, so the image is written once.
+// * A workgroup of 16 wave64s owns a 64 (x) by 16 PPT (y) pixel tile (of one
+//   voxel layer, for volumes); each lane keeps PPT pixels of one column (register
+//   blocking) and accumulates them across all pulses, so the image is written
+//   once.  PPT is 2, or 1 for grids too small to give each CU two tiles.
 // * Pulses are processed in chunks.  For each pulse of a chunk one lane
 //   computes, in fp64, the tile-centre range R_t and derived fp32 constants;
 //   the pixels then need only the fp32 range *difference* to the tile centre,

@@ -128,7 +128,7 @@ def cpu_baseline(scene, target_s=12.0):
     dt = time.perf_counter() - t
     upd = rows * scene.nx * scene.na
 
-    tiny = synth.make_scene(1)
+    tiny = synth.make_scene("tiny")
     t = time.perf_counter()
     oracle.scene_backproject(tiny, nthreads=1)
     dt_tiny = time.perf_counter() - t
@@ -152,7 +152,7 @@ def aux_end_to_end(sb, steps, warmup):
 
     import synth
 
-    s = synth.make_scene(5)
+    s = synth.make_scene("e2e")
     with sb.Plan.for_scene(s, n_fast=s.nr) as plan:
         raw = torch.from_numpy(s.raw).cuda()
         pos = torch.from_numpy(s.positions).cuda()
@@ -178,22 +178,22 @@ def aux_scenes(sb, steps, warmup):
     import synth
 
     out = {}
-    for cfg, interp, key in ((2, "nearest", "nearest"), (4, "sinc8", "sinc8"), (3, "linear", "large_linear")):
+    for scene, interp, key in (("std", "nearest", "nearest"), ("hifi", "sinc8", "sinc8"), ("large", "linear", "large_linear")):
         t = time.perf_counter()
-        s = synth.make_scene(cfg, interp=interp)
+        s = synth.make_scene(scene, interp=interp)
         log(f"bench: generated the {s.name} scene ({s.na} x {s.nr} echo) in {time.perf_counter() - t:.1f} s")
         with sb.Plan.for_scene(s) as plan:
             pos = torch.from_numpy(s.positions).cuda()
             echo = torch.from_numpy(s.echo).cuda()
             img = plan.new_image()
-            k = steps if cfg != 3 else max(5, steps // 4)
+            k = steps if scene != "large" else max(5, steps // 4)
             tm, _ = time_launches(lambda: plan.backproject(pos, echo, image=img), k, warmup)
         upd = s.updates / (tm["mean"] * 1e-3)
         out[key] = {"scene": f"{s.name}: {s.na} pulses x {s.nr} bins -> {s.nx}x{s.ny}, {interp}",
                     "ms": tm["mean"], "ms_median": tm["median"], "ms_min": tm["min"], "launches": k,
                     "G_updates_per_s": upd / 1e9, "TFLOPs_algorithmic": FLOPS_PER_UPDATE[interp] * upd / 1e12,
                     "frac_fp32_peak": FLOPS_PER_UPDATE[interp] * upd / 1e12 / PEAK_FP32_TFLOPS}
-        if cfg == 3:
+        if scene == "large":
             out["large_shards"] = aux_shards(sb, s, pos, echo, max(5, steps // 4), warmup)
         del echo, s
     return out
@@ -263,7 +263,7 @@ def aux_host_stream(sb, scene, steps, warmup):
     out["std_linear"] = {"chunk": 1024, "ms": tm["mean"], "ms_median": tm["median"],
                          "G_updates_per_s": scene.updates / (tm["mean"] * 1e-3) / 1e9,
                          "input_MB": echo_h.numel() * 8 / 1e6}
-    e = synth.make_scene(5)
+    e = synth.make_scene("e2e")
     pos_h = torch.from_numpy(e.positions).pin_memory()
     raw_h = torch.from_numpy(e.raw).pin_memory()
     with sb.Plan.for_scene(e, n_fast=e.nr, n_pulses=1024) as plan, \
@@ -338,8 +338,8 @@ def main():
                          "to scale HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU split is a design note, not an implemented path)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the library runs on one device; splitting a scene over several is not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -349,7 +349,7 @@ def main():
 
     torch.cuda.set_device(0)
     t = time.perf_counter()
-    s = synth.make_scene(2)
+    s = synth.make_scene("std")
     log(f"bench: generated the standard scene ({s.na} x {s.nr} echo, {s.nx} x {s.ny} grid) in "
         f"{time.perf_counter() - t:.1f} s")
     with sarbp.Plan.for_scene(s) as plan:

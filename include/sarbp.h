@@ -46,7 +46,7 @@ extern "C" {
 #define SARBP_EINVAL (-1)       /* an argument is out of range, null or misaligned */
 #define SARBP_ENOMEM (-2)       /* a device or host allocation failed (plan creation only) */
 #define SARBP_EDEVICE (-3)      /* a HIP runtime call or kernel launch failed */
-#define SARBP_EUNSUPPORTED (-4) /* valid request this build cannot serve (e.g. LDS too small) */
+#define SARBP_EUNSUPPORTED (-4) /* valid request the library cannot serve (e.g. LDS too small) */
 
 /* Interpolation of the range-compressed echo at a fractional bin u (section 2.2):
  *   NEAREST: s[floor(u + 1/2)]

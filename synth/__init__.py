@@ -52,17 +52,17 @@ RC_CENTRE = float(np.hypot(GROUND_RANGE, ALTITUDE))
 
 # Configurations: (name, pulses, range bins or raw samples, grid side, interpolation,
 # targets, clutter, noise variance, noise location, track)
-CONFIGS = {
-    1: dict(name="tiny", na=256, nr=512, nx=128, ny=128, interp="linear", n_targets=5,
-            clutter=False, noise_var=0.01, noise_on="rc", track="straight", raw=False),
-    2: dict(name="std", na=4096, nr=4096, nx=1024, ny=1024, interp="linear", n_targets=25,
-            clutter=True, noise_var=0.0, noise_on="rc", track="straight", raw=False),
-    3: dict(name="large", na=16384, nr=8192, nx=2048, ny=2048, interp="linear", n_targets=64,
-            clutter=True, noise_var=0.0, noise_on="rc", track="straight", raw=False),
-    4: dict(name="hifi", na=4096, nr=4096, nx=1024, ny=1024, interp="sinc8", n_targets=25,
-            clutter=True, noise_var=0.0, noise_on="rc", track="perturbed", raw=False),
-    5: dict(name="e2e", na=4096, nr=8192, nx=1024, ny=1024, interp="linear", n_targets=25,
-            clutter=False, noise_var=0.1, noise_on="raw", track="straight", raw=True),
+SCENES = {
+    "tiny": dict(seed=1001, na=256, nr=512, nx=128, ny=128, interp="linear", n_targets=5,
+                 clutter=False, noise_var=0.01, noise_on="rc", track="straight", raw=False),
+    "std": dict(seed=1002, na=4096, nr=4096, nx=1024, ny=1024, interp="linear", n_targets=25,
+                clutter=True, noise_var=0.0, noise_on="rc", track="straight", raw=False),
+    "large": dict(seed=1003, na=16384, nr=8192, nx=2048, ny=2048, interp="linear", n_targets=64,
+                  clutter=True, noise_var=0.0, noise_on="rc", track="straight", raw=False),
+    "hifi": dict(seed=1004, na=4096, nr=4096, nx=1024, ny=1024, interp="sinc8", n_targets=25,
+                 clutter=True, noise_var=0.0, noise_on="rc", track="perturbed", raw=False),
+    "e2e": dict(seed=1005, na=4096, nr=8192, nx=1024, ny=1024, interp="linear", n_targets=25,
+                clutter=False, noise_var=0.1, noise_on="raw", track="straight", raw=True),
 }
 
 CLUTTER_VAR = 0.01  # per-cell reflectivity variance: -20 dB relative to a unit target
@@ -122,7 +122,6 @@ def _threads() -> int:
 class Scene:
     """One seeded synthetic workload.  Arrays are host numpy arrays."""
 
-    cfg: int
     name: str
     seed: int
     na: int
@@ -336,16 +335,16 @@ def complex_normal(rng: np.random.Generator, shape, var: float) -> np.ndarray:
     return (g[..., 0] + 1j * g[..., 1]) * np.sqrt(var / 2.0)
 
 
-def make_scene(cfg: int, seed: int | None = None, **over) -> Scene:
-    """Build configuration ``cfg`` (1..5).  Keyword overrides (na, nr, nx, ny, interp,
+def make_scene(name: str, seed: int | None = None, **over) -> Scene:
+    """Build the scene ``name`` (a key of SCENES).  Keyword overrides (na, nr, nx, ny, interp,
     n_targets, clutter, noise_var, track, clutter_half) give reduced variants for tests;
     ``dem_relief`` (metres, peak to peak) puts the grid, targets and clutter on seeded
     terrain (drawn right after the targets)."""
-    spec = dict(CONFIGS[cfg])
+    spec = dict(SCENES[name])
     clutter_half = over.pop("clutter_half", CLUTTER_HALF_TAPS)
     dem_relief = over.pop("dem_relief", None)
     spec.update(over)
-    seed = 1000 + cfg if seed is None else seed
+    seed = spec["seed"] if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
     na, nr, nx, ny = spec["na"], spec["nr"], spec["nx"], spec["ny"]
     dx = dy = PIXEL
@@ -378,7 +377,7 @@ def make_scene(cfg: int, seed: int | None = None, **over) -> Scene:
         if spec["noise_var"] > 0:
             acc += complex_normal(rng, (na, nr), spec["noise_var"])
         echo = acc.astype(np.complex64)
-    return Scene(cfg=cfg, name=spec["name"], seed=seed, na=na, nr=nr, nx=nx, ny=ny, x0=x0, y0=y0,
+    return Scene(name=name, seed=seed, na=na, nr=nr, nx=nx, ny=ny, x0=x0, y0=y0,
                  z0=z0, dx=dx, dy=dy, r0=r0, dr=DR, wavelength=WAVELENGTH, interp=spec["interp"],
                  positions=positions, echo=echo, raw=raw, targets=tg, dem=dem)
 

@@ -44,7 +44,7 @@ def _run_bp(sb, scene, echo=None, positions=None, interp=None, **over):
 
 @pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
 def test_tiny_config_full_image(sb, interp):
-    s = synth.make_scene(1, interp=interp)
+    s = synth.make_scene("tiny", interp=interp)
     _say(f"[tiny {interp}] {s.nx}x{s.ny} na={s.na}")
     got = _run_bp(sb, s)
     want = oracle.scene_backproject(s)
@@ -58,7 +58,7 @@ def test_ragged_tiles_and_chunks(sb, interp, shape):
     """Grids that are not multiples of the 64x32 tile, pulse counts that are not
     multiples of the LDS chunk, perturbed track, clutter."""
     nx, ny, na = shape
-    s = synth.make_scene(4, na=na, nr=1024, nx=nx, ny=ny, interp=interp, n_targets=1)
+    s = synth.make_scene("hifi", na=na, nr=1024, nx=nx, ny=ny, interp=interp, n_targets=1)
     _say(f"[ragged {interp}] {nx}x{ny} na={na}")
     got = _run_bp(sb, s)
     want = oracle.scene_backproject(s)
@@ -69,7 +69,7 @@ def test_accumulate_over_pulse_chunks(sb):
     """image = BP(first half) then += BP(second half) equals one call over all pulses."""
     import torch
 
-    s = synth.make_scene(2, na=300, nr=1024, nx=96, ny=80)
+    s = synth.make_scene("std", na=300, nr=1024, nx=96, ny=80)
     with sb.Plan.for_scene(s) as plan:
         pos = torch.from_numpy(s.positions).cuda()
         ech = torch.from_numpy(s.echo).cuda()
@@ -83,7 +83,7 @@ def test_accumulate_over_pulse_chunks(sb):
 
 @pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
 def test_linearity_and_pulse_order(sb, interp):
-    s = synth.make_scene(4, na=200, nr=1024, nx=80, ny=64, interp=interp)
+    s = synth.make_scene("hifi", na=200, nr=1024, nx=80, ny=64, interp=interp)
     rng = np.random.Generator(np.random.PCG64(12))
     s2 = (rng.standard_normal(s.echo.shape) + 1j * rng.standard_normal(s.echo.shape)).astype(np.complex64)
     a, b = np.complex64(0.75 - 0.5j), np.complex64(-1.25 + 0.25j)
@@ -102,7 +102,7 @@ def test_one_plan_on_two_streams_concurrently(sb):
     call made alone."""
     import torch
 
-    s = synth.make_scene(2, na=512, nr=1024, nx=300, ny=200, n_targets=2)
+    s = synth.make_scene("std", na=512, nr=1024, nx=300, ny=200, n_targets=2)
     rng = np.random.Generator(np.random.PCG64(3))
     e2 = (rng.standard_normal(s.echo.shape) + 1j * rng.standard_normal(s.echo.shape)).astype(np.complex64)
     with sb.Plan.for_scene(s) as plan:
@@ -129,7 +129,7 @@ def test_graph_capture_replays_match_eager(sb):
     reproduces the eager results bit for bit, also when accumulating into an image."""
     import torch
 
-    s = synth.make_scene(5, na=256, nx=200, ny=96, n_targets=2)
+    s = synth.make_scene("e2e", na=256, nx=200, ny=96, n_targets=2)
     with sb.Plan.for_scene(s, n_fast=s.nr) as plan:
         raw = torch.from_numpy(s.raw).cuda()
         pos = torch.from_numpy(s.positions).cuda()
@@ -170,7 +170,7 @@ def test_zero_extension_and_far_pixels(sb, interp, first, nr):
     reach of either end of the record (sinc8: 4 bins) take the in-record taps only.
     The scene spans bins 236..276 of the 512-bin record; the cut keeps bins
     first .. first + nr - 1."""
-    s = synth.make_scene(1, na=40, nx=96, ny=96, interp=interp)
+    s = synth.make_scene("tiny", na=40, nx=96, ny=96, interp=interp)
     r0 = s.r0 + first * s.dr
     sh = synth.Scene(**{**s.__dict__, "nr": nr, "r0": r0,
                         "echo": np.ascontiguousarray(s.echo[:, first:first + nr])})
@@ -182,7 +182,7 @@ def test_zero_extension_and_far_pixels(sb, interp, first, nr):
 
 
 def test_nonfinite_positions_propagate_nan(sb):
-    s = synth.make_scene(1, na=16, nx=64, ny=32)
+    s = synth.make_scene("tiny", na=16, nx=64, ny=32)
     pos = s.positions.copy()
     pos[5, 0] = np.nan
     got = _run_bp(sb, s, positions=pos)
@@ -199,12 +199,12 @@ def test_accumulation_modes_full_image(sb, interp, accum):
     multiple of the chunk, and accumulate = 1 over two calls)."""
     import torch
 
-    s = synth.make_scene(1, interp=interp)
+    s = synth.make_scene("tiny", interp=interp)
     got = _run_bp(sb, s, accum=accum)
     want = oracle.scene_backproject(s)
     assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
     check_peaks(lambda w: got[w[:, 1], w[:, 0]], lambda w: want[w[:, 1], w[:, 0]], target_windows(s))
-    r = synth.make_scene(4, na=203, nr=1024, nx=70, ny=45, interp=interp, n_targets=1)
+    r = synth.make_scene("hifi", na=203, nr=1024, nx=70, ny=45, interp=interp, n_targets=1)
     with sb.Plan.for_scene(r, accum=accum) as plan:
         pos = torch.from_numpy(r.positions).cuda()
         ech = torch.from_numpy(r.echo).cuda()
@@ -262,7 +262,7 @@ def test_host_stream_matches_device_path(sb, interp):
     device-resident call over all pulses, and the oracle's."""
     import torch
 
-    s = synth.make_scene(4, na=500, nr=1024, nx=96, ny=80, interp=interp, n_targets=2)
+    s = synth.make_scene("hifi", na=500, nr=1024, nx=96, ny=80, interp=interp, n_targets=2)
     want = oracle.scene_backproject(s)
     ref = _run_bp(sb, s)
     pos_h, echo_h = _pinned(s.positions), _pinned(s.echo)
@@ -286,7 +286,7 @@ def test_host_stream_with_range_compression(sb):
     and as the oracle's compression followed by its backprojection."""
     import torch
 
-    s = synth.make_scene(5, na=300, nx=64, ny=96)
+    s = synth.make_scene("e2e", na=300, nx=64, ny=96)
     with sb.Plan.for_scene(s, n_fast=s.nr, n_pulses=96) as plan:
         raw_d = torch.from_numpy(s.raw).cuda()
         pos_d = torch.from_numpy(s.positions).cuda()
@@ -309,7 +309,7 @@ def test_image_tiling_by_sub_image_plans(sb):
     """A scene split into four row bands, one plan each (the page's tiling of images
     too large for memory): the bands reassemble the whole-image result.  Pixels are
     independent, so no overlap between bands is needed."""
-    s = synth.make_scene(2, na=256, nr=1024, nx=128, ny=200, n_targets=3)
+    s = synth.make_scene("std", na=256, nr=1024, nx=128, ny=200, n_targets=3)
     whole = _run_bp(sb, s)
     bands = []
     for j0, j1 in ((0, 37), (37, 100), (100, 163), (163, 200)):
@@ -353,7 +353,7 @@ def test_backprojection_from_interpolated_track(sb):
     own interpolated positions, and the same image as from the exact positions."""
     import torch
 
-    s = synth.make_scene(4, na=400, nr=1024, nx=96, ny=64, n_targets=2)
+    s = synth.make_scene("hifi", na=400, nr=1024, nx=96, ny=64, n_targets=2)
     model = synth.track_model(np.random.Generator(np.random.PCG64(1004)), perturbed=True)
     tp = synth.pulse_times(s.na)
     nav_t = np.arange(tp[0] - 0.05, tp[-1] + 0.05, 0.01)
@@ -391,7 +391,7 @@ def test_terrain_full_image(sb, interp):
     """Targets and clutter on 25 m of seeded terrain (steep on this small grid: a
     64 x 32 block spans up to 20+ m), straight track; the plan's bound is the
     terrain's largest block range."""
-    s = synth.make_scene(2, na=256, nr=1024, nx=150, ny=70, interp=interp, n_targets=3, dem_relief=25.0)
+    s = synth.make_scene("std", na=256, nr=1024, nx=150, ny=70, interp=interp, n_targets=3, dem_relief=25.0)
     relief = synth.block_relief(s.dem)
     _say(f"[terrain {interp}] block relief {relief:.1f} m")
     got = _run_bp_dem(sb, s, s.dem, relief)
@@ -402,13 +402,13 @@ def test_terrain_full_image(sb, interp):
 
 
 def test_terrain_perturbed_track_and_chunk64(sb):
-    s = synth.make_scene(4, na=203, nr=1024, nx=96, ny=64, interp="sinc8", n_targets=2, dem_relief=12.0)
+    s = synth.make_scene("hifi", na=203, nr=1024, nx=96, ny=64, interp="sinc8", n_targets=2, dem_relief=12.0)
     got = _run_bp_dem(sb, s, s.dem, synth.block_relief(s.dem), accum="chunk64")
     assert rel_l2(got, oracle.scene_backproject(s)) <= REL_L2
 
 
 def test_flat_terrain_equals_the_plane(sb):
-    s = synth.make_scene(2, na=128, nr=1024, nx=96, ny=64, n_targets=2)
+    s = synth.make_scene("std", na=128, nr=1024, nx=96, ny=64, n_targets=2)
     got = _run_bp_dem(sb, s, np.zeros((s.ny, s.nx), np.float32), 5.0)
     ref = _run_bp(sb, s)
     assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 3e-4
@@ -417,7 +417,7 @@ def test_flat_terrain_equals_the_plane(sb):
 def test_terrain_beyond_the_bound_is_nan(sb):
     """Blocks whose height range exceeds the plan's bound come out NaN; the rest match
     the oracle."""
-    s = synth.make_scene(2, na=96, nr=1024, nx=150, ny=70, n_targets=2, dem_relief=25.0)
+    s = synth.make_scene("std", na=96, nr=1024, nx=150, ny=70, n_targets=2, dem_relief=25.0)
     bound = 0.5 * synth.block_relief(s.dem)
     got = _run_bp_dem(sb, s, s.dem, bound)
     want = oracle.scene_backproject(s)
@@ -437,7 +437,7 @@ def test_terrain_nearest_index_bit_exact(sb):
     floor(u + 1/2) computed in fp64 in the definition's operation order."""
     import torch
 
-    s = synth.make_scene(2, na=64, nr=1024, nx=150, ny=70, interp="nearest", n_targets=1, dem_relief=25.0)
+    s = synth.make_scene("std", na=64, nr=1024, nx=150, ny=70, interp="nearest", n_targets=1, dem_relief=25.0)
     relief = synth.block_relief(s.dem)
     ramp = torch.arange(1, s.nr + 1, dtype=torch.float32).to(torch.complex64).cuda()[None, :].contiguous()
     jj, ii = np.meshgrid(np.arange(s.ny), np.arange(s.nx), indexing="ij")
@@ -474,7 +474,7 @@ def _volume_scene(interp, nx=70, ny=45, nz=5, passes=6, na_per=40, seed=31):
     pts = np.stack([x0 + vox[:, 0] * dx, y0 + vox[:, 1] * dy, z0 + vox[:, 2] * dz], 1)
     echo = synth.render_points(pos, nr, r0, synth.DR, pts, np.ones(len(vox)), half=256)
     echo = echo + synth.complex_normal(rng, echo.shape, 1e-3)
-    s = synth.Scene(cfg=0, name="volume", seed=seed, na=len(pos), nr=nr, nx=nx, ny=ny, x0=x0, y0=y0, z0=z0,
+    s = synth.Scene(name="volume", seed=seed, na=len(pos), nr=nr, nx=nx, ny=ny, x0=x0, y0=y0, z0=z0,
                     dx=dx, dy=dy, r0=r0, dr=synth.DR, wavelength=synth.WAVELENGTH, interp=interp, positions=pos,
                     echo=echo.astype(np.complex64), raw=None, targets=vox[:, :2])
     return s, nz, dz, vox
@@ -541,24 +541,24 @@ def _index_probe(sb, scene, pulses):
     return mismatches
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
-def test_nearest_index_bit_exact(sb, cfg):
+@pytest.mark.parametrize("scene", ["tiny", "std", "large", "hifi"])
+def test_nearest_index_bit_exact(sb, scene):
     """>= 64 evenly spaced pulses plus the first and last of each geometry, every pixel."""
-    spec = synth.CONFIGS[cfg]
+    spec = synth.SCENES[scene]
     # geometry only: the echo is replaced by the index probe
-    s = synth.make_scene(cfg, nr=spec["nr"], na=spec["na"], clutter=False, n_targets=1) if cfg == 1 else None
+    s = synth.make_scene(scene, nr=spec["nr"], na=spec["na"], clutter=False, n_targets=1) if scene == "tiny" else None
     if s is None:
-        rng = np.random.Generator(np.random.PCG64(1000 + cfg))
+        rng = np.random.Generator(np.random.PCG64(spec["seed"]))
         na = spec["na"]
         pos = synth.track(na, rng, perturbed=spec["track"] == "perturbed")
         nx, ny, nr = spec["nx"], spec["ny"], spec["nr"]
-        s = synth.Scene(cfg=cfg, name=spec["name"], seed=1000 + cfg, na=na, nr=nr, nx=nx, ny=ny,
+        s = synth.Scene(name=scene, seed=spec["seed"], na=na, nr=nr, nx=nx, ny=ny,
                         x0=-(nx // 2) * synth.PIXEL, y0=-(ny // 2) * synth.PIXEL, z0=0.0, dx=synth.PIXEL,
                         dy=synth.PIXEL, r0=synth.RC_CENTRE - (nr // 2) * synth.DR, dr=synth.DR,
                         wavelength=synth.WAVELENGTH, interp="nearest", positions=pos, echo=None, raw=None,
                         targets=np.zeros((0, 2), np.int64))
     pulses = sorted(set(np.linspace(0, s.na - 1, 64).astype(int).tolist()) | {0, s.na - 1})
-    _say(f"[index probe cfg {cfg}] {len(pulses)} pulses x {s.nx * s.ny} pixels")
+    _say(f"[index probe {scene}] {len(pulses)} pulses x {s.nx * s.ny} pixels")
     assert _index_probe(sb, s, pulses) == 0
 
 
@@ -567,7 +567,7 @@ def test_nearest_index_bit_exact(sb, cfg):
 def test_range_compression_matches_oracle(sb):
     import torch
 
-    s = synth.make_scene(5, na=64)
+    s = synth.make_scene("e2e", na=64)
     with sb.Plan.for_scene(s, n_fast=s.nr) as plan:
         out = plan.range_compress(torch.from_numpy(s.raw).cuda())
         torch.cuda.synchronize()
@@ -613,13 +613,13 @@ def test_range_compression_taylor_parameters(sb, nbar, sll):
 
 # ----------------------------------------------------------------------------- full-size configs, sampled
 
-@pytest.mark.parametrize("cfg", [2, 4, 3])
-def test_full_size_sampled(sb, cfg):
+@pytest.mark.parametrize("scene, sample_seed", [("std", 79), ("hifi", 81), ("large", 80)])
+def test_full_size_sampled(sb, scene, sample_seed):
     import time
 
     t = time.time()
-    s = synth.make_scene(cfg)
-    _say(f"[full cfg {cfg}] generated {s.na}x{s.nr} echo, {s.nx}x{s.ny} grid in {time.time() - t:.1f}s")
+    s = synth.make_scene(scene)
+    _say(f"[full {scene}] generated {s.na}x{s.nr} echo, {s.nx}x{s.ny} grid in {time.time() - t:.1f}s")
     import torch
 
     with sb.Plan.for_scene(s) as plan:
@@ -627,13 +627,13 @@ def test_full_size_sampled(sb, cfg):
         torch.cuda.synchronize()
         got = img.cpu().numpy()
     wins = target_windows(s)
-    ij = np.concatenate([sample_pixels(s, 1500, 77 + cfg)] + wins)
+    ij = np.concatenate([sample_pixels(s, 1500, sample_seed)] + wins)
     want = oracle.scene_pixels(s, ij)
     g = got[ij[:, 1], ij[:, 0]].astype(np.complex128)
     assert rel_l2(g, want) <= REL_L2, rel_l2(g, want)
     lut = {tuple(p): v for p, v in zip(ij.tolist(), want)}
     check_peaks(lambda w: got[w[:, 1], w[:, 0]], lambda w: np.array([lut[tuple(p)] for p in w.tolist()]), wins)
-    _say(f"[full cfg {cfg}] rel-L2 {rel_l2(g, want):.2e} on {len(ij)} pixels")
+    _say(f"[full {scene}] rel-L2 {rel_l2(g, want):.2e} on {len(ij)} pixels")
 
 
 def test_end_to_end_sampled(sb):
@@ -641,7 +641,7 @@ def test_end_to_end_sampled(sb):
     oracle chain (numpy matched filter, then the C oracle on sampled pixels)."""
     import torch
 
-    s = synth.make_scene(5)
+    s = synth.make_scene("e2e")
     _say(f"[e2e] raw {s.na}x{s.nr}")
     with sb.Plan.for_scene(s, n_fast=s.nr) as plan:
         raw = torch.from_numpy(s.raw).cuda()
@@ -670,7 +670,7 @@ def _custom_scene(pos, nr, nx, ny, dx, dy, interp, seed):
     Rc = float(np.linalg.norm(pos[len(pos) // 2] - np.array([0.0, 0.0, 0.0])))
     r0 = Rc - (nr // 2) * synth.DR
     echo = (rng.standard_normal((len(pos), nr)) + 1j * rng.standard_normal((len(pos), nr))).astype(np.complex64)
-    return synth.Scene(cfg=0, name="custom", seed=seed, na=len(pos), nr=nr, nx=nx, ny=ny, x0=-(nx // 2) * dx,
+    return synth.Scene(name="custom", seed=seed, na=len(pos), nr=nr, nx=nx, ny=ny, x0=-(nx // 2) * dx,
                        y0=-(ny // 2) * dy, z0=0.0, dx=dx, dy=dy, r0=r0, dr=synth.DR, wavelength=synth.WAVELENGTH,
                        interp=interp, positions=pos, echo=echo, raw=None, targets=np.zeros((0, 2), np.int64))
 

@@ -415,8 +415,8 @@ def test_page_work_model_numbers():
     for case in GOLDEN["work_model"]["cases"]:
         upd = case["na"] * case["nx"] * case["ny"]
         assert abs(upd / case["approx_updates"] - 1) < case["rel_tol"]
-    s2 = synth.CONFIGS[2]
-    s3 = synth.CONFIGS[3]
+    s2 = synth.SCENES["std"]
+    s3 = synth.SCENES["large"]
     assert s2["na"] * s2["nx"] * s2["ny"] == 4096 * 1024 * 1024
     assert s3["na"] * s3["nx"] * s3["ny"] == 16384 * 2048 * 2048
     t = GOLDEN["threads_for_1024_square"]

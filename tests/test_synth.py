@@ -5,10 +5,10 @@ import synth
 
 
 def test_same_seed_same_scene():
-    a = synth.make_scene(1)
-    b = synth.make_scene(1)
+    a = synth.make_scene("tiny")
+    b = synth.make_scene("tiny")
     assert a.sha256() == b.sha256()
-    c = synth.make_scene(1, seed=5)
+    c = synth.make_scene("tiny", seed=5)
     assert c.sha256()["echo"] != a.sha256()["echo"]
 
 
@@ -96,8 +96,8 @@ def test_targets_are_central_and_separated():
 
 
 def test_noise_power():
-    a = synth.make_scene(1)
-    b = synth.make_scene(1, noise_var=0.0)
+    a = synth.make_scene("tiny")
+    b = synth.make_scene("tiny", noise_var=0.0)
     n = (a.echo.astype(np.complex128) - b.echo.astype(np.complex128)).ravel()
     var = np.mean(np.abs(n) ** 2)
     se = 0.01 / np.sqrt(n.size)
@@ -115,7 +115,7 @@ def test_perturbed_track_is_smooth_and_bounded():
 
 
 def test_config_geometry():
-    s = synth.make_scene(1)
+    s = synth.make_scene("tiny")
     assert s.positions.shape == (256, 3) and s.echo.shape == (256, 512) and s.echo.dtype == np.complex64
     # scene centre (pixel nx/2, ny/2) is the origin; the record is centred on its range
     x, y = s.pixel_xy(s.nx // 2, s.ny // 2)

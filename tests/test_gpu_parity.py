@@ -676,6 +676,17 @@ def _custom_scene(pos, nr, nx, ny, dx, dy, interp, seed):
 
 
 @pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
+def test_window_beyond_lds_is_unsupported(sb, interp):
+    """200 m pixels: one tile's echo window (~32,000 bins, 250 KB or more) cannot be
+    staged even one pulse at a time in 150 KiB of LDS, so plan creation reports
+    SARBP_EUNSUPPORTED and nothing runs."""
+    with pytest.raises(sb.SarbpError) as err:
+        sb.Plan(n_pulses=16, n_range=65536, r0=5000.0, dr=synth.DR, nx=64, ny=64, x0=-6400.0, y0=-6400.0,
+                z0=0.0, dx=200.0, dy=200.0, wavelength=synth.WAVELENGTH, interp=interp)
+    assert err.value.status == sb.SARBP_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
 def test_coarse_grid_uses_large_lds_windows(sb, interp):
     """3 m pixels: each tile spans ~500 bins, so fewer than 8 pulses fit the default LDS
     budget and the plan stages pulses in up to 150 KiB instead."""

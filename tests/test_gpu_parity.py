@@ -664,14 +664,14 @@ def test_end_to_end_sampled(sb):
 
 # ----------------------------------------------------------------------------- geometry edge cases
 
-def _custom_scene(pos, nr, nx, ny, dx, dy, interp, seed):
+def _custom_scene(pos, nr, nx, ny, dx, dy, interp, seed, dr=synth.DR):
     """Random echo on an arbitrary geometry (range record centred on the scene centre)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     Rc = float(np.linalg.norm(pos[len(pos) // 2] - np.array([0.0, 0.0, 0.0])))
-    r0 = Rc - (nr // 2) * synth.DR
+    r0 = Rc - (nr // 2) * dr
     echo = (rng.standard_normal((len(pos), nr)) + 1j * rng.standard_normal((len(pos), nr))).astype(np.complex64)
     return synth.Scene(name="custom", seed=seed, na=len(pos), nr=nr, nx=nx, ny=ny, x0=-(nx // 2) * dx,
-                       y0=-(ny // 2) * dy, z0=0.0, dx=dx, dy=dy, r0=r0, dr=synth.DR, wavelength=synth.WAVELENGTH,
+                       y0=-(ny // 2) * dy, z0=0.0, dx=dx, dy=dy, r0=r0, dr=dr, wavelength=synth.WAVELENGTH,
                        interp=interp, positions=pos, echo=echo, raw=None, targets=np.zeros((0, 2), np.int64))
 
 
@@ -688,11 +688,14 @@ def test_window_beyond_lds_is_unsupported(sb, interp):
 
 @pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
 def test_coarse_grid_uses_large_lds_windows(sb, interp):
-    """3 m pixels: each tile spans ~500 bins, so fewer than 8 pulses fit the default LDS
-    budget and the plan stages pulses in up to 150 KiB instead."""
+    """3 m pixels sampled at 0.1 m range bins: each 64 x 16 tile (this small grid's
+    tile) spans ~1980 bins, so fewer than 8 pulses fit the default LDS budget for every
+    interpolator (16 KB per pulse for nearest, 32 KB linear, 127 KB sinc8) and the plan
+    stages pulses in up to 150 KiB instead.  (The tile's range extent, ~200 m, not its
+    bin count, sets the fp32 phase error.)"""
     pos = synth.track(40)
-    s = _custom_scene(pos, 4096, 70, 40, 3.0, 3.0, interp, 31)
-    _say(f"[coarse {interp}] {s.nx}x{s.ny} at 3 m")
+    s = _custom_scene(pos, 16384, 70, 40, 3.0, 3.0, interp, 31, dr=0.1)
+    _say(f"[coarse {interp}] {s.nx}x{s.ny} at 3 m, dr 0.1 m")
     got = _run_bp(sb, s)
     want = oracle.scene_backproject(s)
     assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)

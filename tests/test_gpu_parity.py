@@ -280,6 +280,28 @@ def test_host_stream_matches_device_path(sb, interp):
     assert rel_l2(got2, want + oracle.scene_backproject(s200)) <= REL_L2
 
 
+def test_host_stream_many_calls_back_to_back(sb):
+    """Twelve calls queued back to back on one stream object (8 chunks of 64 pulses
+    each, so its two staging buffers and their release events are reused 96 times
+    while the host waits for them): the accumulated image equals twelve times one
+    call, and one call equals the device-resident path."""
+    import torch
+
+    s = synth.make_scene("std", na=512, nr=1024, nx=128, ny=96, n_targets=2)
+    ref = _run_bp(sb, s)
+    pos_h, echo_h = _pinned(s.positions), _pinned(s.echo)
+    with sb.Plan.for_scene(s, n_pulses=64) as plan, sb.HostStream(plan, chunk=64) as hs:
+        one = hs.backproject(pos_h, echo_h)
+        img = plan.new_image()
+        for k in range(12):
+            hs.backproject(pos_h, echo_h, image=img, accumulate=1 if k else 0)
+        torch.cuda.synchronize()
+        one = one.cpu().numpy().astype(np.complex128)
+        got = img.cpu().numpy().astype(np.complex128)
+    assert np.linalg.norm(one - ref) / np.linalg.norm(ref) < 1e-5
+    assert np.linalg.norm(got - 12 * one) / np.linalg.norm(12 * one) < 1e-6
+
+
 def test_host_stream_with_range_compression(sb):
     """Raw pulses from host memory, range-compressed on the device chunk by chunk and
     backprojected: the same image as compressing and backprojecting on the device,

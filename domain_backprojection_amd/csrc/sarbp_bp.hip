@@ -113,6 +113,65 @@ __device__ int pulse_setup(const BpArgs& A, int n, double cx, double cy, double 
     return (q > 0.25 || e3 > 1e-6) ? 2 : (e2 > 1e-6 ? 1 : 0);
 }
 
+// Per-pulse constants of the fp64-range kernels (tiles whose range extent is too
+// large for the fp32 difference): three double2 per pulse,
+//   (2 ux, 2 uy), (ft, 1/R_t^2), (R_t/dr, 0),
+// and the window position ub = ft + (R_t/dr) (sqrt(1 + q) - 1), q = num / R_t^2,
+// by its binomial series through q^7 (mode 0) or, when the first omitted term
+// could exceed 1e-8 bins over the tile, exactly (mode 2).
+__device__ int pulse_setup_f64(const BpArgs& A, int n, double cx, double cy, double cz, float4* cst, int* klo_out) {
+    double2* cd = reinterpret_cast<double2*>(cst);
+    const double ax = A.pos[3 * (size_t)n], ay = A.pos[3 * (size_t)n + 1], az = A.pos[3 * (size_t)n + 2];
+    const double ux = cx - ax, uy = cy - ay, uz = cz - az;
+    const double Rt = sqrt(ux * ux + uy * uy + uz * uz);
+    const double uc = (Rt - A.r0) * A.inv_dr;
+    const double klo_d = floor(uc - A.half_span_bins) - (double)A.margin_lo;
+    if (!(isfinite(Rt) && Rt > 0.0 && isfinite(uc) && fabs(klo_d) < 1.0e9)) {
+        cd[0] = make_double2(0.0, 0.0);
+        cd[1] = make_double2((double)A.margin_lo + 0.25, 0.0);
+        cd[2] = make_double2(0.0, 0.0);
+        *klo_out = INT32_MIN;
+        return 0;
+    }
+    const double inv_r = 1.0 / Rt;
+    const double ft = uc - klo_d + (A.round_half ? 0.5 : 0.0);
+    const double hs = A.half_span;
+    const double q = (hs * hs + 2.0 * hs * Rt) * inv_r * inv_r;
+    cd[0] = make_double2(2.0 * ux, 2.0 * uy);
+    cd[1] = make_double2(ft, inv_r * inv_r);
+    cd[2] = make_double2(Rt * A.inv_dr, 0.0);
+    *klo_out = (int)klo_d;
+    const double q2 = q * q, q8 = q2 * q2 * q2 * q2;
+    return (q > 0.25 || Rt * (429.0 / 32768.0) * q8 * A.inv_dr > 1e-8) ? 2 : 0;
+}
+
+// Window position of one pixel for pulse p in the fp64-range kernels: the bin
+// k = floor(ub) and the fraction f = ub - k.
+template <int MODE>
+__device__ __forceinline__ void locate_f64(const float4* cst, int p, double dxd, double dyd, double ddd, float* f,
+                                           uint32_t* k) {
+    const double2* cd = reinterpret_cast<const double2*>(cst) + 3 * p;
+    const double2 d0 = cd[0], d1 = cd[1], d2 = cd[2];
+    const double num = fma(dxd, d0.x, fma(dyd, d0.y, ddd));
+    const double q = num * d1.y;
+    double s; // (sqrt(1 + q) - 1) / q
+    if constexpr (MODE == 2) {
+        s = 1.0 / (1.0 + sqrt(1.0 + q));
+    } else {
+        s = 33.0 / 2048.0;
+        s = fma(s, q, -21.0 / 1024.0);
+        s = fma(s, q, 7.0 / 256.0);
+        s = fma(s, q, -5.0 / 128.0);
+        s = fma(s, q, 1.0 / 16.0);
+        s = fma(s, q, -1.0 / 8.0);
+        s = fma(s, q, 0.5);
+    }
+    const double ub = fma(d2.x * q, s, d1.x);
+    const double kd = floor(ub);
+    *k = (uint32_t)kd;
+    *f = (float)(ub - kd);
+}
+
 // Bin position of a pixel within its pulse window: ub = ft + (R - R_t) / dr.
 template <int MODE>
 __device__ __forceinline__ float bin_position(float num, const float4& c0, const float4& c1) {
@@ -205,12 +264,13 @@ __device__ __forceinline__ void mac(float& ar, float& ai, float& cr, float& ci, 
 // within tie_eps of a rounding tie in fp64, then the fetches and accumulations.
 // ub carries u + 1/2: its floor is the nearest bin and g - 1/2 = u - bin; the
 // staged sample carries exp(-j pi kappa), so exp(j 2 pi kappa g) completes the phase.
-template <int G, int MODE, int ACC, bool DEM, int PPT>
+template <int G, int MODE, int ACC, bool DEM, int PPT, bool F64>
 __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem, const float4* cst, const int* klo_s,
                                               int p0, int n0, int i_pix, int j_pix0, float dxl, const float* dyv,
                                               const float* ddv, float* accr, float* acci, float* cmpr, float* cmpi,
-                                              const float* dzv, const float* hv, double zl, uint32_t wstride) {
-    constexpr int CS = DEM ? 3 : 2;
+                                              const float* dzv, const float* hv, double zl, uint32_t wstride,
+                                              const double* pxd) {
+    constexpr int CS = (DEM || F64) ? 3 : 2;
     float g[G][PPT];
     uint32_t kb[G][PPT];
     bool tie = false;
@@ -221,10 +281,14 @@ __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem,
         const float4 c2 = DEM ? cst[CS * (p0 + q) + 2] : c1;
 #pragma unroll
         for (int m = 0; m < PPT; ++m) {
-            const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
-            const float ub = bin_position<MODE>(num, c0, c1);
-            g[q][m] = __builtin_amdgcn_fractf(ub);
-            kb[q][m] = (uint32_t)ub;
+            if constexpr (F64) {
+                locate_f64<MODE>(cst, p0 + q, pxd[0], pxd[1 + m], pxd[1 + PPT + m], &g[q][m], &kb[q][m]);
+            } else {
+                const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
+                const float ub = bin_position<MODE>(num, c0, c1);
+                g[q][m] = __builtin_amdgcn_fractf(ub);
+                kb[q][m] = (uint32_t)ub;
+            }
             tie |= fabsf(g[q][m] - 0.5f) > 0.5f - A.tie_eps;
         }
     }
@@ -259,29 +323,31 @@ __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem,
     }
 }
 
-template <int INTERP, int MODE, int ACC, bool DEM, int PPT>
+template <int INTERP, int MODE, int ACC, bool DEM, int PPT, bool F64>
 __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* smem, const float4* cst,
                                                  const int* klo_s, int np, int n0, int i_pix, int j_pix0,
                                                  float dxl, const float* dyv, const float* ddv, float* accr,
                                                  float* acci, float* cmpr, float* cmpi, const float* dzv,
-                                                 const float* hv, double zl) {
+                                                 const float* hv, double zl, const double* pxd) {
     const int eb = entry_bytes<INTERP>();
     const uint32_t wstride = (uint32_t)(A.win * eb);
     const float kappa = A.kappa;
     if constexpr (INTERP == SARBP_NEAREST) {
         int p = 0;
-        for (; p + BP_NEAREST_GROUP <= np; p += BP_NEAREST_GROUP)
-            nearest_group<BP_NEAREST_GROUP, MODE, ACC, DEM, PPT>(A, smem, cst, klo_s, p, n0, i_pix, j_pix0, dxl, dyv, ddv,
-                                                              accr, acci, cmpr, cmpi, dzv, hv, zl, wstride);
+        constexpr int G = F64 ? 1 : BP_NEAREST_GROUP;
+        for (; p + G <= np; p += G)
+            nearest_group<G, MODE, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, p, n0, i_pix, j_pix0, dxl,
+                                                                   dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl,
+                                                                   wstride, pxd);
         for (; p < np; ++p)
-            nearest_group<1, MODE, ACC, DEM, PPT>(A, smem, cst, klo_s, p, n0, i_pix, j_pix0, dxl, dyv, ddv, accr, acci,
-                                             cmpr, cmpi, dzv, hv, zl, wstride);
+            nearest_group<1, MODE, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, p, n0, i_pix, j_pix0, dxl, dyv, ddv, accr,
+                                                  acci, cmpr, cmpi, dzv, hv, zl, wstride, pxd);
         return;
     }
-    constexpr int kUnroll = INTERP == SARBP_LINEAR ? BP_PUNROLL_LINEAR : BP_PUNROLL_SINC8;
+    constexpr int kUnroll = F64 ? BP_PUNROLL_F64 : (INTERP == SARBP_LINEAR ? BP_PUNROLL_LINEAR : BP_PUNROLL_SINC8);
 #pragma unroll kUnroll
     for (int p = 0; p < np; ++p) {
-        constexpr int CS = DEM ? 3 : 2; // float4 constants per pulse
+        constexpr int CS = (DEM || F64) ? 3 : 2; // float4 constants per pulse
         const float4 c0 = cst[CS * p];
         const float4 c1 = cst[CS * p + 1];
         const float4 c2 = DEM ? cst[CS * p + 2] : c1;
@@ -289,10 +355,17 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
         if constexpr (INTERP == SARBP_LINEAR) {
 #pragma unroll
             for (int m = 0; m < PPT; ++m) {
-                const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
-                const float ub = bin_position<MODE>(num, c0, c1);
-                const float f = __builtin_amdgcn_fractf(ub);
-                const uint32_t addr = ((uint32_t)ub << 4) + wbase;
+                float f;
+                uint32_t kw;
+                if constexpr (F64) {
+                    locate_f64<MODE>(cst, p, pxd[0], pxd[1 + m], pxd[1 + PPT + m], &f, &kw);
+                } else {
+                    const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
+                    const float ub = bin_position<MODE>(num, c0, c1);
+                    f = __builtin_amdgcn_fractf(ub);
+                    kw = (uint32_t)ub;
+                }
+                const uint32_t addr = (kw << 4) + wbase;
                 const float4 ad = *reinterpret_cast<const float4*>(smem + addr);
                 const float vr = fmaf(f, ad.z, ad.x);
                 const float vi = fmaf(f, ad.w, ad.y);
@@ -307,11 +380,18 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
             // (built by stage_chunk).  Stored highest degree first, two per float4.
 #pragma unroll
             for (int m = 0; m < PPT; ++m) {
-                const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
-                const float ub = bin_position<MODE>(num, c0, c1);
-                const float f = __builtin_amdgcn_fractf(ub);
+                float f;
+                uint32_t kw;
+                if constexpr (F64) {
+                    locate_f64<MODE>(cst, p, pxd[0], pxd[1 + m], pxd[1 + PPT + m], &f, &kw);
+                } else {
+                    const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
+                    const float ub = bin_position<MODE>(num, c0, c1);
+                    f = __builtin_amdgcn_fractf(ub);
+                    kw = (uint32_t)ub;
+                }
                 const float g = f - 0.5f;
-                const float4* e = reinterpret_cast<const float4*>(smem + (((uint32_t)ub << 6) + wbase));
+                const float4* e = reinterpret_cast<const float4*>(smem + ((kw << 6) + wbase));
                 const float4 q0 = e[0], q1 = e[1], q2 = e[2], q3 = e[3];
                 float vr = fmaf(q0.x, g, q0.z), vi = fmaf(q0.y, g, q0.w);
                 vr = fmaf(vr, g, q1.x);
@@ -416,8 +496,11 @@ __device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int n
 
 // At most 64 VGPRs, so two 1024-lane workgroups (8 waves per SIMD) fit on a CU:
 // the loop needs that many waves to hide LDS and transcendental latency.
-template <int INTERP, int ACC, bool DEM, int PPT>
+// F64: the fp64-range variant (pulse_setup_f64 / locate_f64) for tiles whose
+// range extent makes the fp32 difference too coarse; no terrain.
+template <int INTERP, int ACC, bool DEM, int PPT, bool F64>
 __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void bp_kernel(BpArgs A) {
+    static_assert(!(F64 && DEM), "the fp64-range kernels have no terrain variant");
     extern __shared__ __align__(16) char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -439,6 +522,8 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     double cz = zl;
     const double ddx = ((double)lane - 0.5 * (BP_TX - 1)) * A.dx;
     const float dxl = (float)ddx;
+    double pxd[1 + 2 * PPT]; // F64: ddx, then ddy and |d|^2 of each of the lane's pixels
+    pxd[0] = ddx;
     float dyv[PPT], ddv[PPT], accr[PPT], acci[PPT];
     float cmpr[PPT], cmpi[PPT]; // Kahan compensation (ACC_KAHAN)
     double sumr[PPT], sumi[PPT]; // fp64 totals of the chunk partials (ACC_CHUNK64)
@@ -447,6 +532,8 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         const double ddy = ((double)(wave + BP_WAVES * m) - 0.5 * ((BP_WAVES * PPT) - 1)) * A.dy;
         dyv[m] = (float)ddy;
         ddv[m] = (float)(ddx * ddx + ddy * ddy);
+        pxd[1 + m] = ddy;
+        pxd[1 + PPT + m] = ddx * ddx + ddy * ddy;
         accr[m] = 0.f;
         acci[m] = 0.f;
         cmpr[m] = 0.f;
@@ -504,8 +591,9 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     }
 
     const int P = A.chunk, W = A.win;
+    constexpr int CS = (DEM || F64) ? 3 : 2; // float4 constants per pulse
     float4* cst = reinterpret_cast<float4*>(smem + (size_t)P * W * entry_bytes<INTERP>());
-    int* klo_s = reinterpret_cast<int*>(cst + (DEM ? 3 : 2) * P);
+    int* klo_s = reinterpret_cast<int*>(cst + CS * P);
     int* prio_s = klo_s + P;
     // The accuracy mode of a chunk is the OR of its pulses' modes.  The words are
     // double-buffered: chunk c ORs into mode_s[c & 1] and clears mode_s[(c + 1) & 1],
@@ -520,7 +608,8 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     for (int n0 = 0, np = 0, c = 0; n0 < (bad_tile ? 0 : A.n); n0 += np, ++c) {
         np = min((n0 == 0 && stagger) ? max(1, P >> 1) : P, A.n - n0);
         if (tid < np) {
-            const int need = pulse_setup(A, n0 + tid, cx, cy, cz, cst + (DEM ? 3 : 2) * tid, klo_s + tid, DEM);
+            const int need = F64 ? pulse_setup_f64(A, n0 + tid, cx, cy, cz, cst + CS * tid, klo_s + tid)
+                                 : pulse_setup(A, n0 + tid, cx, cy, cz, cst + CS * tid, klo_s + tid, DEM);
             if (need) atomicOr(mode_s + (c & 1), need);
         }
         if (tid == 0) {
@@ -534,14 +623,14 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         const int mode = __builtin_amdgcn_readfirstlane(mode_s[c & 1]); // the same word for every lane
         const int m1 = mode & 1, m2 = mode & 2;
         if (m2)
-            accumulate_chunk<INTERP, 2, ACC, DEM, PPT>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv,
-                                                   accr, acci, cmpr, cmpi, dzv, hv, zl);
+            accumulate_chunk<INTERP, 2, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv,
+                                                        ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd);
         else if (m1)
-            accumulate_chunk<INTERP, 1, ACC, DEM, PPT>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv,
-                                                   accr, acci, cmpr, cmpi, dzv, hv, zl);
+            accumulate_chunk<INTERP, 1, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv,
+                                                        ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd);
         else
-            accumulate_chunk<INTERP, 0, ACC, DEM, PPT>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv, ddv,
-                                                   accr, acci, cmpr, cmpi, dzv, hv, zl);
+            accumulate_chunk<INTERP, 0, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv,
+                                                        ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd);
         if constexpr (ACC == SARBP_ACC_CHUNK64) {
 #pragma unroll
             for (int m = 0; m < PPT; ++m) {
@@ -591,63 +680,71 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     }
 }
 
-template <int INTERP, int ACC, bool DEM, int PPT>
+template <int INTERP, int ACC, bool DEM, int PPT, bool F64>
 int allow_lds_one(size_t bytes) {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(bp_kernel<INTERP, ACC, DEM, PPT>),
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(bp_kernel<INTERP, ACC, DEM, PPT, F64>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) == hipSuccess
                ? SARBP_OK
                : SARBP_EDEVICE;
 }
 
-template <int INTERP, bool DEM, int PPT>
+template <int INTERP, bool DEM, int PPT, bool F64>
 int allow_lds_acc(int accum, size_t bytes) {
     switch (accum) {
-        case SARBP_ACC_KAHAN: return allow_lds_one<INTERP, SARBP_ACC_KAHAN, DEM, PPT>(bytes);
-        case SARBP_ACC_CHUNK64: return allow_lds_one<INTERP, SARBP_ACC_CHUNK64, DEM, PPT>(bytes);
-        default: return allow_lds_one<INTERP, SARBP_ACC_FP32, DEM, PPT>(bytes);
+        case SARBP_ACC_KAHAN: return allow_lds_one<INTERP, SARBP_ACC_KAHAN, DEM, PPT, F64>(bytes);
+        case SARBP_ACC_CHUNK64: return allow_lds_one<INTERP, SARBP_ACC_CHUNK64, DEM, PPT, F64>(bytes);
+        default: return allow_lds_one<INTERP, SARBP_ACC_FP32, DEM, PPT, F64>(bytes);
     }
 }
 
+// Kernel variants: (DEM, ppt 1 or 2) with fp32 ranges, and (no DEM, ppt 2) with fp64 ranges.
 template <int INTERP, bool DEM>
-int allow_lds(int accum, int ppt, size_t bytes) {
-    return ppt == 1 ? allow_lds_acc<INTERP, DEM, 1>(accum, bytes) : allow_lds_acc<INTERP, DEM, 2>(accum, bytes);
+int allow_lds(int accum, int ppt, bool f64, size_t bytes) {
+    if constexpr (!DEM) {
+        if (f64) return allow_lds_acc<INTERP, false, 2, true>(accum, bytes);
+    }
+    return ppt == 1 ? allow_lds_acc<INTERP, DEM, 1, false>(accum, bytes)
+                    : allow_lds_acc<INTERP, DEM, 2, false>(accum, bytes);
 }
 
-template <int INTERP, bool DEM, int PPT>
+template <int INTERP, bool DEM, int PPT, bool F64>
 void launch_acc(const BpArgs& A, int accum, size_t lds, hipStream_t stream) {
     const dim3 grid(A.nblocks), block(BP_THREADS);
     switch (accum) {
         case SARBP_ACC_KAHAN:
-            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_KAHAN, DEM, PPT>), grid, block, lds, stream, A);
+            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_KAHAN, DEM, PPT, F64>), grid, block, lds, stream, A);
             break;
         case SARBP_ACC_CHUNK64:
-            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_CHUNK64, DEM, PPT>), grid, block, lds, stream, A);
+            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_CHUNK64, DEM, PPT, F64>), grid, block, lds, stream, A);
             break;
         default:
-            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_FP32, DEM, PPT>), grid, block, lds, stream, A);
+            hipLaunchKernelGGL((bp_kernel<INTERP, SARBP_ACC_FP32, DEM, PPT, F64>), grid, block, lds, stream, A);
             break;
     }
 }
 
 template <int INTERP, bool DEM>
-void launch(const BpArgs& A, int accum, int ppt, size_t lds, hipStream_t stream) {
-    if (ppt == 1) launch_acc<INTERP, DEM, 1>(A, accum, lds, stream);
-    else launch_acc<INTERP, DEM, 2>(A, accum, lds, stream);
+void launch(const BpArgs& A, int accum, int ppt, bool f64, size_t lds, hipStream_t stream) {
+    if constexpr (!DEM) {
+        if (f64) return launch_acc<INTERP, false, 2, true>(A, accum, lds, stream);
+    }
+    if (ppt == 1) launch_acc<INTERP, DEM, 1, false>(A, accum, lds, stream);
+    else launch_acc<INTERP, DEM, 2, false>(A, accum, lds, stream);
 }
 
 } // namespace
 
-int sarbp_bp_allow_lds(int interp, int accum, bool dem, int ppt, size_t bytes) {
+int sarbp_bp_allow_lds(int interp, int accum, bool dem, int ppt, bool f64, size_t bytes) {
     switch (interp) {
         case SARBP_NEAREST:
-            return dem ? allow_lds<SARBP_NEAREST, true>(accum, ppt, bytes)
-                       : allow_lds<SARBP_NEAREST, false>(accum, ppt, bytes);
+            return dem ? allow_lds<SARBP_NEAREST, true>(accum, ppt, false, bytes)
+                       : allow_lds<SARBP_NEAREST, false>(accum, ppt, f64, bytes);
         case SARBP_LINEAR:
-            return dem ? allow_lds<SARBP_LINEAR, true>(accum, ppt, bytes)
-                       : allow_lds<SARBP_LINEAR, false>(accum, ppt, bytes);
+            return dem ? allow_lds<SARBP_LINEAR, true>(accum, ppt, false, bytes)
+                       : allow_lds<SARBP_LINEAR, false>(accum, ppt, f64, bytes);
         default:
-            return dem ? allow_lds<SARBP_SINC8, true>(accum, ppt, bytes)
-                       : allow_lds<SARBP_SINC8, false>(accum, ppt, bytes);
+            return dem ? allow_lds<SARBP_SINC8, true>(accum, ppt, false, bytes)
+                       : allow_lds<SARBP_SINC8, false>(accum, ppt, f64, bytes);
     }
 }
 
@@ -703,16 +800,16 @@ int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* ech
     const bool d = dem != nullptr;
     switch (p.interp) {
         case SARBP_NEAREST:
-            d ? launch<SARBP_NEAREST, true>(A, p.accum, plan->ppt, plan->lds_bytes, stream)
-              : launch<SARBP_NEAREST, false>(A, p.accum, plan->ppt, plan->lds_bytes, stream);
+            d ? launch<SARBP_NEAREST, true>(A, p.accum, plan->ppt, false, plan->lds_bytes, stream)
+              : launch<SARBP_NEAREST, false>(A, p.accum, plan->ppt, plan->f64, plan->lds_bytes, stream);
             break;
         case SARBP_LINEAR:
-            d ? launch<SARBP_LINEAR, true>(A, p.accum, plan->ppt, plan->lds_bytes, stream)
-              : launch<SARBP_LINEAR, false>(A, p.accum, plan->ppt, plan->lds_bytes, stream);
+            d ? launch<SARBP_LINEAR, true>(A, p.accum, plan->ppt, false, plan->lds_bytes, stream)
+              : launch<SARBP_LINEAR, false>(A, p.accum, plan->ppt, plan->f64, plan->lds_bytes, stream);
             break;
         default:
-            d ? launch<SARBP_SINC8, true>(A, p.accum, plan->ppt, plan->lds_bytes, stream)
-              : launch<SARBP_SINC8, false>(A, p.accum, plan->ppt, plan->lds_bytes, stream);
+            d ? launch<SARBP_SINC8, true>(A, p.accum, plan->ppt, false, plan->lds_bytes, stream)
+              : launch<SARBP_SINC8, false>(A, p.accum, plan->ppt, plan->f64, plan->lds_bytes, stream);
             break;
     }
     return hipGetLastError() == hipSuccess ? SARBP_OK : SARBP_EDEVICE;

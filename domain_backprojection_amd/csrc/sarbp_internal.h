@@ -30,6 +30,9 @@
 #ifndef BP_NEAREST_GROUP
 #define BP_NEAREST_GROUP 2
 #endif
+#ifndef BP_PUNROLL_F64
+#define BP_PUNROLL_F64 1 // fp64-range kernels (measured: 1, 2 and 4 equal for linear and nearest; sinc8 5 % faster at 1)
+#endif
 #ifndef BP_PUNROLL_SINC8
 #define BP_PUNROLL_SINC8 8
 #endif
@@ -50,6 +53,7 @@ struct sarbp_plan {
     // backprojection launch geometry
     int tiles_x, tiles_y;
     int ppt;          // backprojection pixels per lane (1 or 2): tiles of 64 x 16 ppt
+    int f64;          // 1: range differences in fp64 (coarse grids, no terrain; ppt = 2)
     int win;          // LDS window entries per pulse
     int margin_lo;    // bins below the tile's lowest range kept in the window
     int chunk;        // pulses per LDS step

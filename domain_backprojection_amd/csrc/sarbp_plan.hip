@@ -14,7 +14,7 @@
 #include "sarbp_internal.h"
 
 int sarbp_rc_prepare_device();
-int sarbp_bp_allow_lds(int interp, int accum, bool dem, int ppt, size_t bytes);
+int sarbp_bp_allow_lds(int interp, int accum, bool dem, int ppt, bool f64, size_t bytes);
 
 namespace {
 
@@ -208,7 +208,14 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     const int64_t layers = p.nz > 1 ? p.nz : 1;
     plan->tiles_x = (p.nx + BP_TX - 1) / BP_TX;
     const int64_t tiles2 = (int64_t)plan->tiles_x * ((p.ny + 2 * BP_WAVES - 1) / (2 * BP_WAVES)) * layers;
-    plan->ppt = (tiles2 < 2 * (int64_t)plan->n_cu && !(p.dem_relief > 0.0)) ? 1 : 2;
+    // The fp32 kernels carry a pixel's range offset from the tile centre to about
+    // 2^-24 of the tile's half diagonal, a phase error of 4 pi 2^-24 half_span /
+    // lambda.  Beyond 1024 wavelengths of half diagonal (7.7e-4 rad) the plan uses
+    // the fp64-range kernels instead (64 x 32 tiles; terrain plans keep fp32).
+    const double hs32 = 0.5 * sqrt((BP_TX * p.dx) * (BP_TX * p.dx) +
+                                   (2.0 * BP_WAVES * p.dy) * (2.0 * BP_WAVES * p.dy));
+    plan->f64 = !(p.dem_relief > 0.0) && hs32 > 1024.0 * p.wavelength;
+    plan->ppt = (tiles2 < 2 * (int64_t)plan->n_cu && !(p.dem_relief > 0.0) && !plan->f64) ? 1 : 2;
     const int ty = BP_WAVES * plan->ppt;
     plan->tiles_y = (p.ny + ty - 1) / ty;
     if ((int64_t)plan->tiles_x * plan->tiles_y * layers > INT32_MAX) {
@@ -232,7 +239,7 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     if (p.interp != SARBP_SINC8) plan->win += plan->win & 1;
     const int eb = p.interp == SARBP_NEAREST ? 8 : (p.interp == SARBP_LINEAR ? 16 : 64);
     if (p.interp == SARBP_SINC8) sinc8_polynomials(plan->sinc_poly);
-    const int per_pulse = plan->win * eb + (p.dem_relief > 0.0 ? 3 : 2) * 16 + 4;
+    const int per_pulse = plan->win * eb + ((p.dem_relief > 0.0 || plan->f64) ? 3 : 2) * 16 + 4;
     // Coarse grids (long windows) that would stage fewer than 8 pulses per step
     // use up to 150 KiB of LDS: one workgroup per CU instead of two.
     int chunk = (BP_LDS_BUDGET - 64) / per_pulse;
@@ -248,9 +255,9 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     plan->chunk = chunk;
     plan->lds_bytes = (size_t)chunk * per_pulse + 16; // + the chunk's issue-priority word
     if (plan->lds_bytes > 64 * 1024) {
-        st = sarbp_bp_allow_lds(p.interp, p.accum, false, plan->ppt, plan->lds_bytes);
+        st = sarbp_bp_allow_lds(p.interp, p.accum, false, plan->ppt, plan->f64, plan->lds_bytes);
         if (st == SARBP_OK && p.dem_relief > 0.0)
-            st = sarbp_bp_allow_lds(p.interp, p.accum, true, plan->ppt, plan->lds_bytes);
+            st = sarbp_bp_allow_lds(p.interp, p.accum, true, plan->ppt, false, plan->lds_bytes);
         if (st != SARBP_OK) {
             release(plan);
             return st;

@@ -74,9 +74,10 @@ typedef struct {
     int32_t nx, ny;     /* image size (>= 1 each); image[j * nx + i]                           */
     double x0, y0, z0;  /* centre of pixel (0, 0); every pixel lies in the plane z = z0          */
     double dx, dy;      /* pixel spacing (> 0): pixel (i, j) centre = (x0 + i dx, y0 + j dy, z0);
-                         * the fp32 phase error grows with a pixel tile's range extent: keep
-                         * 64 dx x 32 dy (64 dx x 16 dy on grids under 512 such tiles) within
-                         * ~200 m at a 3 cm wavelength for a 2e-3 image error            */
+                         * a plan whose 64 dx x 32 dy tiles have a half diagonal beyond 1024
+                         * wavelengths takes range differences in fp64 (about 1.5x the time).
+                         * Plans with dem_relief > 0 keep fp32 ones, whose phase error grows
+                         * with that half diagonal: ~2e-3 of the image at 4000 wavelengths */
     double wavelength;  /* carrier wavelength lambda (> 0) of the phase term exp(+j 4 pi R / lambda) */
     int32_t interp;     /* sarbp_interp                                                         */
     /* Range compression (sarbp_range_compress); n_fast = 0 disables it. */

@@ -710,15 +710,33 @@ def test_window_beyond_lds_is_unsupported(sb, interp):
 
 @pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
 def test_coarse_grid_uses_large_lds_windows(sb, interp):
-    """3 m pixels sampled at 0.1 m range bins: each 64 x 16 tile (this small grid's
-    tile) spans ~1980 bins, so fewer than 8 pulses fit the default LDS budget for every
-    interpolator (16 KB per pulse for nearest, 32 KB linear, 127 KB sinc8) and the plan
-    stages pulses in up to 150 KiB instead.  (The tile's range extent, ~200 m, not its
-    bin count, sets the fp32 phase error.)"""
+    """3 m pixels sampled at 0.1 m range bins: each 64 x 32 tile spans ~2150 bins, so
+    fewer than 8 pulses fit the default LDS budget for every interpolator (17 KB per
+    pulse for nearest, 34 KB linear, 138 KB sinc8) and the plan stages pulses in up to
+    150 KiB instead.  (The tiles' 107 m half diagonal also puts the plan on fp64 range
+    differences.)"""
     pos = synth.track(40)
     s = _custom_scene(pos, 16384, 70, 40, 3.0, 3.0, interp, 31, dr=0.1)
     _say(f"[coarse {interp}] {s.nx}x{s.ny} at 3 m, dr 0.1 m")
     got = _run_bp(sb, s)
+    want = oracle.scene_backproject(s)
+    assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
+
+
+@pytest.mark.parametrize("interp, accum", [("linear", "fp32"), ("nearest", "fp32"), ("sinc8", "fp32"),
+                                           ("linear", "kahan"), ("linear", "chunk64")])
+@pytest.mark.parametrize("pixel", [0.8, 8.0])
+def test_coarse_grid_range_precision(sb, interp, accum, pixel):
+    """Fp32 range offsets from a tile centre carry about 2^-24 of the tile's half
+    diagonal, so the plan switches to fp64 range differences once that half diagonal
+    exceeds 1024 wavelengths (32 m at 3.125 cm).  0.8 m pixels (64 x 32 tiles, 28.6 m)
+    stay just under it, on the fp32 kernels; 8 m pixels (286 m, where fp32 differences
+    gave a relative error of 4.2e-3) go over, with the exact square root for every
+    pulse at 11 km.  Both must meet the fine grids' bar."""
+    pos = synth.track(40)
+    s = _custom_scene(pos, 4096, 70, 40, pixel, pixel, interp, 47)
+    _say(f"[range precision {interp} {accum}] {s.nx}x{s.ny} at {pixel} m")
+    got = _run_bp(sb, s, accum=accum)
     want = oracle.scene_backproject(s)
     assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
 

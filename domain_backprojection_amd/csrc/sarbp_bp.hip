@@ -25,7 +25,10 @@
 //   a bound on the truncation error, or when q is not small by the exact form
 //   num / (R_t (1 + sqrt(1 + q))).  This keeps the bin position to ~1e-6 bins,
 //   which fp32 absolute ranges (~1e-3 m at 11 km) could not (section 2.2 warns
-//   about fp32 range precision).
+//   about fp32 range precision).  The fp32 difference itself carries ~2^-24 of
+//   the tile's half diagonal, so plans with coarse pixels (half diagonal beyond
+//   1024 wavelengths) run the F64 variant: the same difference and series in
+//   fp64, with only the fraction within the bin back in fp32.
 // * The echo window a tile can touch (its range extent, bounded by the tile
 //   diagonal) is staged per pulse in LDS, already multiplied by the bin-centre
 //   carrier phase exp(+j 4 pi r_k / lambda).  For a pixel at u = k + f the
@@ -515,12 +518,21 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     const int tx = tile % A.tiles_x, ty = tile / A.tiles_x;
     const int i0 = tx * BP_TX, j0 = ty * (BP_WAVES * PPT);
 
-    // tile centre (fp64) and this lane's pixel offsets from it
-    const double cxp = (double)i0 + 0.5 * (BP_TX - 1), cyp = (double)j0 + 0.5 * ((BP_WAVES * PPT) - 1);
+    // Tile centre (fp64): the centre of the part of the tile inside the grid, which
+    // brings the pixels of a ragged edge tile (or of a grid smaller than a tile)
+    // closer to it than the full tile's half diagonal.  Lanes past the grid's edge
+    // take the offsets of the last column or row, so every lane's range stays
+    // within the staged window; their results are not stored.
+    const int i_last = min(i0 + BP_TX, A.nx) - 1, j_last = min(j0 + BP_WAVES * PPT, A.ny) - 1;
+    const double cxp = 0.5 * (double)(i0 + i_last), cyp = 0.5 * (double)(j0 + j_last);
     const double cx = A.x0 + cxp * A.dx, cy = A.y0 + cyp * A.dy;
     const double zl = A.z0 + (double)layer * A.dz; // this layer's height
     double cz = zl;
-    const double ddx = ((double)lane - 0.5 * (BP_TX - 1)) * A.dx;
+    const int i_off = min(i0 + lane, i_last); // the pixel column whose offsets this lane uses
+    int j_off[PPT];
+#pragma unroll
+    for (int m = 0; m < PPT; ++m) j_off[m] = min(j0 + wave + BP_WAVES * m, j_last);
+    const double ddx = ((double)i_off - cxp) * A.dx;
     const float dxl = (float)ddx;
     double pxd[1 + 2 * PPT]; // F64: ddx, then ddy and |d|^2 of each of the lane's pixels
     pxd[0] = ddx;
@@ -529,7 +541,7 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     double sumr[PPT], sumi[PPT]; // fp64 totals of the chunk partials (ACC_CHUNK64)
 #pragma unroll
     for (int m = 0; m < PPT; ++m) {
-        const double ddy = ((double)(wave + BP_WAVES * m) - 0.5 * ((BP_WAVES * PPT) - 1)) * A.dy;
+        const double ddy = ((double)j_off[m] - cyp) * A.dy;
         dyv[m] = (float)ddy;
         ddv[m] = (float)(ddx * ddx + ddy * ddy);
         pxd[1 + m] = ddy;
@@ -553,12 +565,9 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         float hmin = INFINITY, hmax = -INFINITY;
 #pragma unroll
         for (int m = 0; m < PPT; ++m) {
-            const int j = j0 + wave + BP_WAVES * m, i = i0 + lane;
-            if (i < A.nx && j < A.ny) {
-                hv[m] = A.dem[(size_t)j * A.nx + i];
-                hmin = fminf(hmin, hv[m]);
-                hmax = fmaxf(hmax, hv[m]);
-            }
+            hv[m] = A.dem[(size_t)j_off[m] * A.nx + i_off]; // lanes past the edge repeat an edge pixel
+            hmin = fminf(hmin, hv[m]);
+            hmax = fmaxf(hmax, hv[m]);
         }
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) {
@@ -583,7 +592,7 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         cz = A.z0 + hc;
 #pragma unroll
         for (int m = 0; m < PPT; ++m) {
-            const double ddy = ((double)(wave + BP_WAVES * m) - 0.5 * ((BP_WAVES * PPT) - 1)) * A.dy;
+            const double ddy = ((double)j_off[m] - cyp) * A.dy;
             const double ddz = (double)hv[m] - hc;
             dzv[m] = (float)ddz;
             ddv[m] = (float)(ddx * ddx + ddy * ddy + ddz * ddz);

@@ -59,6 +59,9 @@ int validate(const sarbp_params* p) {
     if (!isfinite(p->r0) || !finite_pos(p->dr) || !finite_pos(p->dx) || !finite_pos(p->dy)) return SARBP_EINVAL;
     if (!isfinite(p->x0) || !isfinite(p->y0) || !isfinite(p->z0) || !finite_pos(p->wavelength)) return SARBP_EINVAL;
     if ((int64_t)p->nx * p->ny > (int64_t)1 << 40) return SARBP_EINVAL;
+    // The per-sample rotation takes v_sin/v_cos of kappa f revolutions, kappa = 2 dr /
+    // lambda and f in [0, 1); those instructions accept at most 256 revolutions.
+    if (!(2.0 * p->dr / p->wavelength < 255.0)) return SARBP_EUNSUPPORTED;
     if (p->n_fast != 0) {
         if (p->n_fast < 64 || p->n_fast > 16384 || (p->n_fast & (p->n_fast - 1)) != 0) return SARBP_EINVAL;
         if (!finite_pos(p->fs) || !finite_pos(p->chirp_T) || !finite_pos(p->chirp_B)) return SARBP_EINVAL;

@@ -78,7 +78,10 @@ typedef struct {
                          * wavelengths takes range differences in fp64 (about 1.5x the time).
                          * Plans with dem_relief > 0 keep fp32 ones, whose phase error grows
                          * with that half diagonal: ~2e-3 of the image at 4000 wavelengths */
-    double wavelength;  /* carrier wavelength lambda (> 0) of the phase term exp(+j 4 pi R / lambda) */
+    double wavelength;  /* carrier wavelength lambda (> 0) of the phase term exp(+j 4 pi R / lambda);
+                         * 2 dr / lambda, the carrier cycles per range bin, must be below 255
+                         * (SARBP_EUNSUPPORTED otherwise): the kernels rotate each sample with
+                         * hardware sine and cosine, whose argument is limited to 256 cycles */
     int32_t interp;     /* sarbp_interp                                                         */
     /* Range compression (sarbp_range_compress); n_fast = 0 disables it. */
     int32_t n_fast;     /* samples per raw pulse = FFT length: a power of two in [64, 16384]    */

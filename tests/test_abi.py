@@ -90,6 +90,24 @@ def test_plan_create_rejects_invalid_parameters(sb, bad):
     assert h.value is None
 
 
+@pytest.mark.parametrize("dr, wavelength, unsupported", [(4.0, 0.03125, True), (7.97, 0.0625, True),
+                                                      (3.98, 0.03125, False), (0.41637, 0.0086, False)])
+def test_plan_create_bounds_cycles_per_bin(sb, dr, wavelength, unsupported):
+    """2 dr / lambda carrier cycles per range bin must stay below 255 (the hardware sine
+    and cosine take at most 256 cycles): 256 and 255.04 are refused before any device
+    call; 254.7 and a Ka-band 96.8 pass validation (and fail, if at all, only at the
+    device step, with no GPU here)."""
+    h = ctypes.c_void_p()
+    st = sb._lib.sarbp_plan_create(ctypes.byref(_good(sb, dr=dr, wavelength=wavelength, n_range=4096)),
+                                   ctypes.byref(h))
+    if unsupported:
+        assert st == sb.SARBP_EUNSUPPORTED and h.value is None
+    else:
+        assert st not in (sb.SARBP_EINVAL, sb.SARBP_EUNSUPPORTED)
+        if st == sb.SARBP_OK:
+            sb._lib.sarbp_destroy(h)
+
+
 @pytest.mark.parametrize("ok", [dict(window=2), dict(window=2, taylor_nbar=6, taylor_sll=45.0),
                                 dict(window=1, taylor_nbar=1), dict(window=0)])
 def test_plan_params_validate_window_fields(sb, ok):

@@ -423,6 +423,28 @@ def test_terrain_full_image(sb, interp):
     check_peaks(lambda w: got[w[:, 1], w[:, 0]], lambda w: want[w[:, 1], w[:, 0]], target_windows(s))
 
 
+@pytest.mark.parametrize("interp", ["linear", "nearest"])
+def test_terrain_far_above_reference_plane(sb, interp):
+    """Terrain 300 m above z0 (+-8 m) on a 150 x 70 grid, whose edge tiles are ragged in
+    both directions, with a random echo over the whole record (the pixels sit ~130 m
+    nearer than the reference plane): each tile is centred at its own mid-height and on
+    its pixels inside the grid, and lanes past the grid's edge repeat an edge pixel, so
+    none of them reaches outside its staged window.  The full image against the oracle."""
+    import dataclasses
+
+    s = synth.make_scene("std", na=128, nr=2048, nx=150, ny=70, interp=interp, n_targets=1, clutter=False,
+                         dem_relief=16.0)
+    rng = np.random.Generator(np.random.PCG64(59))
+    echo = (rng.standard_normal(s.echo.shape) + 1j * rng.standard_normal(s.echo.shape)).astype(np.complex64)
+    s = dataclasses.replace(s, dem=(s.dem + np.float32(300.0)).astype(np.float32), echo=echo)
+    relief = synth.block_relief(s.dem)
+    _say(f"[terrain +300 m {interp}] block relief {relief:.1f} m")
+    got = _run_bp_dem(sb, s, s.dem, relief)
+    want = oracle.scene_backproject(s)
+    assert np.isfinite(got).all()
+    assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
+
+
 def test_terrain_perturbed_track_and_chunk64(sb):
     s = synth.make_scene("hifi", na=203, nr=1024, nx=96, ny=64, interp="sinc8", n_targets=2, dem_relief=12.0)
     got = _run_bp_dem(sb, s, s.dem, synth.block_relief(s.dem), accum="chunk64")
@@ -737,6 +759,18 @@ def test_coarse_grid_range_precision(sb, interp, accum, pixel):
     s = _custom_scene(pos, 4096, 70, 40, pixel, pixel, interp, 47)
     _say(f"[range precision {interp} {accum}] {s.nx}x{s.ny} at {pixel} m")
     got = _run_bp(sb, s, accum=accum)
+    want = oracle.scene_backproject(s)
+    assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
+
+
+@pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
+def test_most_carrier_cycles_per_bin(sb, interp):
+    """3.98 m range bins at 3.125 cm: 254.7 carrier cycles per bin, just under the 255
+    that plan creation accepts (the hardware sine and cosine take at most 256 cycles).
+    The per-sample rotation then spans almost the whole argument range."""
+    s = _custom_scene(synth.track(40), 1024, 70, 40, synth.PIXEL, synth.PIXEL, interp, 53, dr=3.98)
+    _say(f"[cycles per bin {interp}] {2 * s.dr / s.wavelength:.1f}")
+    got = _run_bp(sb, s)
     want = oracle.scene_backproject(s)
     assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
 

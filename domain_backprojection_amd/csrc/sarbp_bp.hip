@@ -120,8 +120,9 @@ __device__ int pulse_setup(const BpArgs& A, int n, double cx, double cy, double 
 // large for the fp32 difference): three double2 per pulse,
 //   (2 ux, 2 uy), (ft, 1/R_t^2), (R_t/dr, 0),
 // and the window position ub = ft + (R_t/dr) (sqrt(1 + q) - 1), q = num / R_t^2,
-// by its binomial series through q^7 (mode 0) or, when the first omitted term
-// could exceed 1e-8 bins over the tile, exactly (mode 2).
+// by its binomial series through q^4 (mode 0) or q^7 (mode 1), the shorter one
+// whose first omitted term stays below 1e-7 bins over the tile, else exactly
+// (mode 2).  (1e-7 bins is below the fp32 rounding of the fraction returned.)
 __device__ int pulse_setup_f64(const BpArgs& A, int n, double cx, double cy, double cz, float4* cst, int* klo_out) {
     double2* cd = reinterpret_cast<double2*>(cst);
     const double ax = A.pos[3 * (size_t)n], ay = A.pos[3 * (size_t)n + 1], az = A.pos[3 * (size_t)n + 2];
@@ -144,8 +145,9 @@ __device__ int pulse_setup_f64(const BpArgs& A, int n, double cx, double cy, dou
     cd[1] = make_double2(ft, inv_r * inv_r);
     cd[2] = make_double2(Rt * A.inv_dr, 0.0);
     *klo_out = (int)klo_d;
-    const double q2 = q * q, q8 = q2 * q2 * q2 * q2;
-    return (q > 0.25 || Rt * (429.0 / 32768.0) * q8 * A.inv_dr > 1e-8) ? 2 : 0;
+    const double q2 = q * q, q4 = q2 * q2, rb = Rt * A.inv_dr; // R_t in bins
+    if (q > 0.25 || rb * (429.0 / 32768.0) * q4 * q4 > 1e-7) return 2;
+    return rb * (7.0 / 256.0) * q4 * q > 1e-7 ? 1 : 0;
 }
 
 // Window position of one pixel for pulse p in the fp64-range kernels: the bin
@@ -161,10 +163,12 @@ __device__ __forceinline__ void locate_f64(const float4* cst, int p, double dxd,
     if constexpr (MODE == 2) {
         s = 1.0 / (1.0 + sqrt(1.0 + q));
     } else {
-        s = 33.0 / 2048.0;
-        s = fma(s, q, -21.0 / 1024.0);
-        s = fma(s, q, 7.0 / 256.0);
-        s = fma(s, q, -5.0 / 128.0);
+        s = -5.0 / 128.0;
+        if constexpr (MODE == 1) {
+            s = fma(33.0 / 2048.0, q, -21.0 / 1024.0);
+            s = fma(s, q, 7.0 / 256.0);
+            s = fma(s, q, -5.0 / 128.0);
+        }
         s = fma(s, q, 1.0 / 16.0);
         s = fma(s, q, -1.0 / 8.0);
         s = fma(s, q, 0.5);

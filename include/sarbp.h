@@ -75,7 +75,7 @@ typedef struct {
     double x0, y0, z0;  /* centre of pixel (0, 0); every pixel lies in the plane z = z0          */
     double dx, dy;      /* pixel spacing (> 0): pixel (i, j) centre = (x0 + i dx, y0 + j dy, z0);
                          * a plan whose 64 dx x 32 dy tiles have a half diagonal beyond 1024
-                         * wavelengths takes range differences in fp64 (about 1.5x the time).
+                         * wavelengths takes range differences in fp64 (about 1.4x the time).
                          * Plans with dem_relief > 0 keep fp32 ones, whose phase error grows
                          * with that half diagonal: ~2e-3 of the image at 4000 wavelengths */
     double wavelength;  /* carrier wavelength lambda (> 0) of the phase term exp(+j 4 pi R / lambda);

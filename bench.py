@@ -263,6 +263,36 @@ def aux_coarse(sb, scene, steps, warmup):
     return out
 
 
+def aux_small_grids(sb, scene, steps, warmup):
+    """Grids with fewer tiles than the GPU has room for, plain and with the pulses split over
+    workgroups (sarbp_backproject_split): the tiny scene (128 x 128, 256 pulses) and the
+    standard echo onto the central 256 x 256 pixels (4096 pulses)."""
+    import torch
+
+    import synth
+
+    out = {}
+    t = synth.make_scene("tiny")
+    cases = (("tiny_128", t, dict()),
+             ("std_256", scene, dict(nx=256, ny=256, x0=scene.x0 + 384 * scene.dx, y0=scene.y0 + 384 * scene.dy)))
+    for key, s, grid in cases:
+        with sb.Plan.for_scene(s, **grid) as plan:
+            pos = torch.from_numpy(s.positions).cuda()
+            echo = torch.from_numpy(s.echo).cuda()
+            img = plan.new_image()
+            need = plan.split_workspace_bytes(s.na)
+            ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+            plain, _ = time_launches(lambda: plan.backproject(pos, echo, image=img), steps, warmup)
+            split, _ = time_launches(lambda: plan.backproject(pos, echo, image=img, split=True, workspace=ws),
+                                     steps, warmup)
+        upd = s.na * plan.image_shape[-1] * plan.image_shape[-2]
+        out[key] = {"pixels": list(plan.image_shape), "pulses": s.na, "workspace_MB": need / 1e6,
+                    "plain_ms": plain["mean"], "split_ms": split["mean"],
+                    "plain_G_updates_per_s": upd / plain["mean"] / 1e6,
+                    "split_G_updates_per_s": upd / split["mean"] / 1e6}
+    return out
+
+
 def aux_host_stream(sb, scene, steps, warmup):
     """Frames fed from page-locked host memory through the two-buffer pipeline
     (PCIe-inclusive; the headline value keeps its inputs resident in HBM):
@@ -425,6 +455,7 @@ def main():
         line["aux"]["scenes"] = aux_scenes(sarbp, max(5, args.steps // 5), max(5, args.warmup // 5))
         line["aux"]["accumulators"] = aux_accumulators(sarbp, s, max(5, args.steps // 5), max(5, args.warmup // 5))
         line["aux"]["coarse"] = aux_coarse(sarbp, s, max(5, args.steps // 5), max(5, args.warmup // 5))
+        line["aux"]["small_grids"] = aux_small_grids(sarbp, s, max(5, args.steps // 5), max(5, args.warmup // 5))
         line["aux"]["host_stream"] = aux_host_stream(sarbp, s, max(5, args.steps // 5), max(5, args.warmup // 5))
         line["aux"]["terrain"] = aux_terrain(sarbp, s, max(5, args.steps // 5), max(5, args.warmup // 5))
         line["aux"]["volume"] = aux_volume(sarbp, max(5, args.steps // 5), max(5, args.warmup // 5))

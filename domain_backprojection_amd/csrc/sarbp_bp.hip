@@ -207,7 +207,7 @@ __device__ __forceinline__ void sincos_rev(float x, float* s, float* c) {
 // behind takes the higher priority.  Larger grids use a fixed schedule instead:
 // the priority drops by one with each quarter of the pulses done.  The values
 // only steer scheduling; stale or racing reads cannot change a result.
-__device__ int chunk_priority(const BpArgs& A, int n0) {
+__device__ int chunk_priority(const BpArgs& A, int n0, int total) {
     const int b = (int)blockIdx.x;
     if (A.nblocks <= 2 * A.slots) {
         __hip_atomic_store(A.progress + b, n0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -216,7 +216,7 @@ __device__ int chunk_priority(const BpArgs& A, int n0) {
         const int other = __hip_atomic_load(A.progress + partner, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return (n0 < other || (n0 == other && b >= A.slots)) ? 3 : 0;
     }
-    return 3 - (int)((4 * (long long)n0) / A.n);
+    return 3 - (int)((4 * (long long)n0) / total);
 }
 
 __device__ __forceinline__ void set_priority(int p) {
@@ -515,8 +515,14 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     // contiguous range of tiles (rows of tiles share echo bins in its L2).
     // Workgroup b handles tile (b mod ntiles) of voxel layer b / ntiles (one layer,
     // z = z0, for a 2-D image).
-    const int layer = (int)blockIdx.x / A.ntiles;
-    int tile = (int)blockIdx.x - layer * A.ntiles;
+    // A split launch runs group_blocks workgroups per pulse group: group g takes
+    // pulses g split_len .. and writes its partial image split_stride further on.
+    const int group = (int)blockIdx.x / A.group_blocks;
+    const int gb = (int)blockIdx.x - group * A.group_blocks;
+    const int pb = group * A.split_len;             // this group's first pulse
+    const int pn = min(A.split_len, A.n - pb);      // its pulses (a trailing group may have none)
+    const int layer = gb / A.ntiles;
+    int tile = gb - layer * A.ntiles;
     const int nt8 = (A.ntiles / 8) * 8;
     if (tile < nt8) tile = (tile & 7) * (nt8 / 8) + (tile >> 3);
     const int tx = tile % A.tiles_x, ty = tile / A.tiles_x;
@@ -618,31 +624,31 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     // The first chunk is half size on alternate workgroups: both placements of a
     // CU's two workgroups (b, b + slots) and (b, b + 8) get opposite parities.
     const int stagger = BP_STAGGER ? (((int)blockIdx.x / A.slots) ^ ((int)blockIdx.x >> 3)) & 1 : 0;
-    for (int n0 = 0, np = 0, c = 0; n0 < (bad_tile ? 0 : A.n); n0 += np, ++c) {
-        np = min((n0 == 0 && stagger) ? max(1, P >> 1) : P, A.n - n0);
+    for (int n0 = 0, np = 0, c = 0; n0 < (bad_tile ? 0 : pn); n0 += np, ++c) {
+        np = min((n0 == 0 && stagger) ? max(1, P >> 1) : P, pn - n0);
         if (tid < np) {
-            const int need = F64 ? pulse_setup_f64(A, n0 + tid, cx, cy, cz, cst + CS * tid, klo_s + tid)
-                                 : pulse_setup(A, n0 + tid, cx, cy, cz, cst + CS * tid, klo_s + tid, DEM);
+            const int need = F64 ? pulse_setup_f64(A, pb + n0 + tid, cx, cy, cz, cst + CS * tid, klo_s + tid)
+                                 : pulse_setup(A, pb + n0 + tid, cx, cy, cz, cst + CS * tid, klo_s + tid, DEM);
             if (need) atomicOr(mode_s + (c & 1), need);
         }
         if (tid == 0) {
-            *prio_s = chunk_priority(A, n0);
+            *prio_s = chunk_priority(A, n0, pn);
             mode_s[(c + 1) & 1] = 0;
         }
         __syncthreads();
-        stage_chunk<INTERP>(A, smem, klo_s, np, n0, tid);
+        stage_chunk<INTERP>(A, smem, klo_s, np, pb + n0, tid);
         __syncthreads();
         set_priority(*prio_s);
         const int mode = __builtin_amdgcn_readfirstlane(mode_s[c & 1]); // the same word for every lane
         const int m1 = mode & 1, m2 = mode & 2;
         if (m2)
-            accumulate_chunk<INTERP, 2, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv,
+            accumulate_chunk<INTERP, 2, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, np, pb + n0, i0 + lane, j0 + wave, dxl, dyv,
                                                         ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd);
         else if (m1)
-            accumulate_chunk<INTERP, 1, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv,
+            accumulate_chunk<INTERP, 1, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, np, pb + n0, i0 + lane, j0 + wave, dxl, dyv,
                                                         ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd);
         else
-            accumulate_chunk<INTERP, 0, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, np, n0, i0 + lane, j0 + wave, dxl, dyv,
+            accumulate_chunk<INTERP, 0, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, np, pb + n0, i0 + lane, j0 + wave, dxl, dyv,
                                                         ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd);
         if constexpr (ACC == SARBP_ACC_CHUNK64) {
 #pragma unroll
@@ -666,7 +672,7 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         for (int m = 0; m < PPT; ++m) {
             const int j = j0 + wave + BP_WAVES * m;
             if (j < A.ny) {
-                float2* o = A.image + ((size_t)layer * A.ny + j) * A.nx + i;
+                float2* o = A.image + (size_t)group * A.split_stride + ((size_t)layer * A.ny + j) * A.nx + i;
                 if constexpr (ACC == SARBP_ACC_CHUNK64) {
                     double r = sumr[m], im = sumi[m];
                     if (A.accumulate) {
@@ -745,7 +751,39 @@ void launch(const BpArgs& A, int accum, int ppt, bool f64, size_t lds, hipStream
     else launch_acc<INTERP, DEM, 2, false>(A, accum, lds, stream);
 }
 
+// Sum of the pulse groups' partial images of a split backprojection, in group
+// order and in fp64, added to the image (accumulate = 1) or written over it.
+__global__ __launch_bounds__(256) void split_sum_kernel(const float2* __restrict__ part, int nsplit, size_t elems,
+                                                        float2* __restrict__ image, int accumulate) {
+    const size_t stride = (size_t)gridDim.x * 256;
+    for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < elems; e += stride) {
+        double r = 0.0, im = 0.0;
+        for (int g = 0; g < nsplit; ++g) {
+            const float2 v = part[(size_t)g * elems + e];
+            r += (double)v.x;
+            im += (double)v.y;
+        }
+        if (accumulate) {
+            const float2 old = image[e];
+            r += (double)old.x;
+            im += (double)old.y;
+        }
+        image[e] = make_float2((float)r, (float)im);
+    }
+}
+
 } // namespace
+
+int sarbp_split_count(const sarbp_plan* plan, int n) {
+    // Pulse groups so that the launch has about two workgroups per CU, at most 16,
+    // each of at least 32 pulses; grids that already fill the GPU are not split.
+    const int64_t layers = plan->p.nz > 1 ? plan->p.nz : 1;
+    const int64_t blocks = (int64_t)plan->tiles_x * plan->tiles_y * layers;
+    int64_t s = (2 * (int64_t)plan->n_cu) / blocks;
+    if (s > 16) s = 16;
+    if (s > n / 32) s = n / 32;
+    return s < 2 ? 1 : (int)s;
+}
 
 int sarbp_bp_allow_lds(int interp, int accum, bool dem, int ppt, bool f64, size_t bytes) {
     switch (interp) {
@@ -762,7 +800,7 @@ int sarbp_bp_allow_lds(int interp, int accum, bool dem, int ppt, bool f64, size_
 }
 
 int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* echo, const float* dem,
-                    float2* image, int n, int accumulate, hipStream_t stream) {
+                    float2* image, int n, int accumulate, hipStream_t stream, float2* workspace, int nsplit) {
     const sarbp_params& p = plan->p;
     BpArgs A;
     A.pos = pos;
@@ -775,7 +813,17 @@ int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* ech
     A.ny = p.ny;
     A.tiles_x = plan->tiles_x;
     A.ntiles = plan->tiles_x * plan->tiles_y;
-    A.nblocks = A.ntiles * (p.nz > 1 ? p.nz : 1);
+    A.group_blocks = A.ntiles * (p.nz > 1 ? p.nz : 1);
+    const size_t elems = (size_t)(p.nz > 1 ? p.nz : 1) * (size_t)p.ny * (size_t)p.nx;
+    const bool split = nsplit > 1 && workspace != nullptr;
+    if (!split) nsplit = 1;
+    A.nblocks = A.group_blocks * nsplit;
+    A.split_len = split ? (n + nsplit - 1) / nsplit : n;
+    A.split_stride = split ? elems : 0;
+    if (split) {
+        A.image = workspace; // partial images, written over; summed into `image` below
+        A.accumulate = 0;
+    }
     A.dz = p.nz > 1 ? p.dz : 0.0;
     A.win = plan->win;
     {
@@ -784,7 +832,7 @@ int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* ech
     }
     A.margin_lo = plan->margin_lo;
     A.chunk = plan->chunk;
-    A.accumulate = accumulate;
+    if (!split) A.accumulate = accumulate;
     A.slots = plan->n_cu;
     A.progress = plan->progress;
     A.r0 = p.r0;
@@ -825,5 +873,12 @@ int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* ech
               : launch<SARBP_SINC8, false>(A, p.accum, plan->ppt, plan->f64, plan->lds_bytes, stream);
             break;
     }
-    return hipGetLastError() == hipSuccess ? SARBP_OK : SARBP_EDEVICE;
+    if (hipGetLastError() != hipSuccess) return SARBP_EDEVICE;
+    if (split) {
+        const size_t blocks = (elems + 255) / 256;
+        hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)(blocks < 2048 ? blocks : 2048)), dim3(256), 0, stream,
+                           static_cast<const float2*>(workspace), nsplit, elems, image, accumulate);
+        if (hipGetLastError() != hipSuccess) return SARBP_EDEVICE;
+    }
+    return SARBP_OK;
 }

@@ -77,7 +77,10 @@ struct BpArgs {
     const float2* phase;   // phase_tab
     int n, n_range, nx, ny;
     int tiles_x, ntiles;
-    int nblocks;           // ntiles * voxel layers: the launch's workgroups
+    int nblocks;           // the launch's workgroups: group_blocks * pulse groups
+    int group_blocks;      // ntiles * voxel layers: the workgroups of one pulse group
+    int split_len;         // pulses per group (n when the pulses are not split)
+    size_t split_stride;   // complex64 elements between the groups' partial images (0 unsplit)
     int win, margin_lo, chunk, accumulate;
     uint32_t win_magic;    // ceil(2^32 / wu), wu = win / (bins per staging step): u / wu = umulhi(u, win_magic)
     int slots;             // compute units: workgroup b and b + slots usually share a CU
@@ -96,5 +99,8 @@ struct BpArgs {
 };
 
 int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* echo, const float* dem,
-                    float2* image, int n, int accumulate, hipStream_t stream);
+                    float2* image, int n, int accumulate, hipStream_t stream, float2* workspace = nullptr,
+                    int nsplit = 1);
+// Pulse groups of a split backprojection of n pulses (1: no split) and its workspace bytes.
+int sarbp_split_count(const sarbp_plan* plan, int n);
 int sarbp_launch_rc(const sarbp_plan* plan, const float2* raw, float2* out, int n, hipStream_t stream);

@@ -343,6 +343,37 @@ extern "C" int sarbp_backproject_dem(const sarbp_plan* plan, const double* posit
                            static_cast<float2*>(image_d), n, accumulate, static_cast<hipStream_t>(stream));
 }
 
+extern "C" size_t sarbp_split_workspace_bytes(const sarbp_plan* plan, int32_t n) {
+    if (plan == nullptr || n < 1 || n > plan->p.n_pulses) return 0;
+    const int s = sarbp_split_count(plan, n);
+    if (s < 2) return 0;
+    const size_t layers = plan->p.nz > 1 ? (size_t)plan->p.nz : 1;
+    return (size_t)s * layers * (size_t)plan->p.ny * (size_t)plan->p.nx * sizeof(float2);
+}
+
+extern "C" int sarbp_backproject_split(const sarbp_plan* plan, const double* positions_d, const void* echo_d,
+                                       const float* dem_d, void* image_d, int32_t n, int32_t accumulate,
+                                       void* workspace_d, size_t workspace_bytes, void* stream) {
+    if (plan == nullptr || !aligned8(positions_d) || !aligned8(echo_d) || !aligned8(image_d)) return SARBP_EINVAL;
+    if (n < 1 || n > plan->p.n_pulses || (accumulate != 0 && accumulate != 1)) return SARBP_EINVAL;
+    if (dem_d != nullptr && (!(plan->p.dem_relief > 0.0) || (reinterpret_cast<uintptr_t>(dem_d) & 3u) != 0))
+        return SARBP_EINVAL;
+    const size_t need = sarbp_split_workspace_bytes(plan, n);
+    if (need > 0) {
+        if (!aligned8(workspace_d) || workspace_bytes < need) return SARBP_EINVAL;
+        const size_t layers = plan->p.nz > 1 ? (size_t)plan->p.nz : 1;
+        const uintptr_t ib = (uintptr_t)(layers * (size_t)plan->p.ny * (size_t)plan->p.nx * sizeof(float2));
+        const uintptr_t i = reinterpret_cast<uintptr_t>(image_d), w = reinterpret_cast<uintptr_t>(workspace_d);
+        if (i < w + need && w < i + ib) return SARBP_EINVAL; // the workspace overlaps the image
+    }
+    const int st = check_device(plan);
+    if (st != SARBP_OK) return st;
+    return sarbp_launch_bp(plan, positions_d, static_cast<const float2*>(echo_d), dem_d,
+                           static_cast<float2*>(image_d), n, accumulate, static_cast<hipStream_t>(stream),
+                           need > 0 ? static_cast<float2*>(workspace_d) : nullptr,
+                           need > 0 ? sarbp_split_count(plan, n) : 1);
+}
+
 extern "C" int sarbp_range_compress(const sarbp_plan* plan, const void* raw_d, void* out_d, int32_t n, void* stream) {
     if (plan == nullptr || plan->p.n_fast == 0 || !aligned8(raw_d) || !aligned8(out_d) || n < 1) return SARBP_EINVAL;
     const uintptr_t bytes = (uintptr_t)n * (uintptr_t)plan->p.n_fast * sizeof(float2);

@@ -97,10 +97,16 @@ _lib.sarbp_interpolate_track.argtypes = [_vp, _vp, ctypes.c_int32, _vp, _vp, cty
 _lib.sarbp_interpolate_track.restype = ctypes.c_int
 _lib.sarbp_backproject_dem.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp]
 _lib.sarbp_backproject_dem.restype = ctypes.c_int
+_lib.sarbp_split_workspace_bytes.argtypes = [_vp, ctypes.c_int32]
+_lib.sarbp_split_workspace_bytes.restype = ctypes.c_size_t
+_lib.sarbp_backproject_split.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_size_t,
+                                         _vp]
+_lib.sarbp_backproject_split.restype = ctypes.c_int
 
 EXPORTS = ("sarbp_plan_create", "sarbp_backproject", "sarbp_range_compress", "sarbp_destroy",
            "sarbp_status_string", "sarbp_version", "sarbp_stream_create", "sarbp_backproject_host",
-           "sarbp_stream_destroy", "sarbp_interpolate_track", "sarbp_backproject_dem")
+           "sarbp_stream_destroy", "sarbp_interpolate_track", "sarbp_backproject_dem",
+           "sarbp_split_workspace_bytes", "sarbp_backproject_split")
 
 
 class SarbpError(RuntimeError):
@@ -188,6 +194,39 @@ def sarbp_backproject_dem(handle, positions: torch.Tensor, echo: torch.Tensor, d
                                     _stream(stream))
     if st != SARBP_OK:
         raise SarbpError(st, "sarbp_backproject_dem")
+
+
+def sarbp_split_workspace_bytes(handle, n: int) -> int:
+    """Bytes of workspace :func:`sarbp_backproject_split` needs for n pulses (0: the call runs unsplit)."""
+    return int(_lib.sarbp_split_workspace_bytes(handle, int(n)))
+
+
+def sarbp_backproject_split(handle, positions: torch.Tensor, echo: torch.Tensor, image: torch.Tensor,
+                            workspace: torch.Tensor | None, n: int | None = None, accumulate: int = 0,
+                            stream=None, dem: torch.Tensor | None = None) -> None:
+    """As :func:`sarbp_backproject` (or with dem, :func:`sarbp_backproject_dem`), with the pulses split
+    over several workgroups per pixel tile; workspace is a device tensor of at least
+    :func:`sarbp_split_workspace_bytes` bytes (None when that is 0)."""
+    if n is None:
+        n = positions.shape[0]
+    if positions.dim() != 2 or positions.shape[1] != 3 or positions.shape[0] < n or echo.shape[0] < n:
+        raise ValueError("positions must be (>= n, 3) and echo (>= n, n_range)")
+    dem_p = None
+    if dem is not None:
+        if tuple(dem.shape) != tuple(image.shape):
+            raise ValueError("dem must have the image's shape (ny, nx)")
+        dem_p = _dev_ptr(dem, torch.float32, "dem")
+    ws_p, ws_bytes = None, 0
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
+            raise TypeError("workspace must be a contiguous device tensor")
+        ws_p, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = _lib.sarbp_backproject_split(handle, _dev_ptr(positions, torch.float64, "positions"),
+                                      _dev_ptr(echo, torch.complex64, "echo"), dem_p,
+                                      _dev_ptr(image, torch.complex64, "image"), int(n), int(accumulate), ws_p,
+                                      ws_bytes, _stream(stream))
+    if st != SARBP_OK:
+        raise SarbpError(st, "sarbp_backproject_split")
 
 
 def sarbp_range_compress(handle, raw: torch.Tensor, out: torch.Tensor, n: int | None = None, stream=None) -> None:
@@ -300,14 +339,27 @@ class Plan:
     def new_image(self, device="cuda") -> torch.Tensor:
         return torch.zeros(self.image_shape, dtype=torch.complex64, device=device)
 
-    def backproject(self, positions, echo, image=None, n=None, accumulate=0, stream=None, dem=None) -> torch.Tensor:
+    def split_workspace_bytes(self, n: int) -> int:
+        return sarbp_split_workspace_bytes(self.handle, n)
+
+    def backproject(self, positions, echo, image=None, n=None, accumulate=0, stream=None, dem=None,
+                    split=False, workspace=None) -> torch.Tensor:
+        """split=True calls sarbp_backproject_split, with `workspace` or, when it is None, a
+        workspace allocated here by torch (device memory is torch's; the kernels are the library's)."""
         if image is None:
             image = torch.empty(self.image_shape, dtype=torch.complex64, device=echo.device)
         if tuple(image.shape) != self.image_shape:
             raise ValueError("image shape does not match the plan")
         if echo.dim() != 2 or echo.shape[1] != self.params.n_range:
             raise ValueError("echo must be (n, n_range)")
-        if dem is None:
+        if split:
+            npulses = positions.shape[0] if n is None else n
+            if workspace is None:
+                need = self.split_workspace_bytes(npulses)
+                workspace = torch.empty(need, dtype=torch.uint8, device=echo.device) if need else None
+            sarbp_backproject_split(self.handle, positions, echo, image, workspace, n=n, accumulate=accumulate,
+                                    stream=stream, dem=dem)
+        elif dem is None:
             sarbp_backproject(self.handle, positions, echo, image, n=n, accumulate=accumulate, stream=stream)
         else:
             sarbp_backproject_dem(self.handle, positions, echo, dem, image, n=n, accumulate=accumulate,

@@ -35,6 +35,7 @@
 #ifndef SARBP_H
 #define SARBP_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -138,6 +139,39 @@ int sarbp_backproject(const sarbp_plan* plan, const double* positions_d, const v
  * dem, or a plan without terrain), SARBP_EDEVICE on a launch failure. */
 int sarbp_backproject_dem(const sarbp_plan* plan, const double* positions_d, const void* echo_d, const float* dem_d,
                           void* image_d, int32_t n, int32_t accumulate, void* stream);
+
+/* ---- Small grids: the pulses split over several workgroups per pixel tile. ----
+ * A grid with fewer than two 64 x 32 (or 64 x 16) pixel tiles per compute unit
+ * leaves most of the GPU idle in sarbp_backproject, whose workgroups each own one
+ * tile for every pulse (the sum of section 1.1 runs over the pulses of one
+ * pixel).  The sum is linear in the pulses, so it can run as S groups of
+ * consecutive pulses, each into a partial image, followed by the sum of the
+ * partials. */
+
+/* Workspace for sarbp_backproject_split of n pulses with this plan: S partial
+ * images of complex64 [nz][ny][nx], S = 2 .. 16 chosen so that the launch holds
+ * about two workgroups per compute unit with at least 32 pulses per group.
+ * Returns 0 when the plan's grid already fills the GPU (or for a null plan or n
+ * out of range): such calls run unsplit and need no workspace. */
+size_t sarbp_split_workspace_bytes(const sarbp_plan* plan, int32_t n);
+
+/* As sarbp_backproject (dem_d = NULL) or sarbp_backproject_dem (dem_d not NULL),
+ * with the pulses split into S groups as above.
+ *   workspace_d     : device memory of at least sarbp_split_workspace_bytes(plan, n)
+ *                     bytes, 8-byte aligned, not overlapping the image; caller-owned,
+ *                     written by the call (its contents afterwards are unspecified).
+ *                     May be NULL when that size is 0.
+ * Each group sums its pulses as sarbp_backproject does (with the plan's
+ * accumulator) into an fp32 partial image; a second kernel adds the S partials
+ * in group order in fp64, plus the old image when accumulate = 1, and rounds once
+ * to complex64.  The result equals sarbp_backproject's up to that summation order
+ * (about 1e-7 relative).  Two calls must not share a workspace while both may
+ * run.  Returns SARBP_EINVAL as sarbp_backproject / sarbp_backproject_dem, or for
+ * a missing, short, misaligned or overlapping workspace; SARBP_EDEVICE on a launch
+ * failure. */
+int sarbp_backproject_split(const sarbp_plan* plan, const double* positions_d, const void* echo_d,
+                            const float* dem_d, void* image_d, int32_t n, int32_t accumulate, void* workspace_d,
+                            size_t workspace_bytes, void* stream);
 
 /* Range-compress n raw pulses (section 3.1 of the page):
  *   out_n = IFFT( FFT(raw_n) * conj(FFT(ref)) * W ) with 1/n_fast on the inverse,

@@ -136,5 +136,7 @@ def test_null_arguments(sb):
     assert sb._lib.sarbp_interpolate_track(None, 8, 10, 8, 8, 4, None) == sb.SARBP_EINVAL
     assert sb._lib.sarbp_interpolate_track(8, 8, 3, 8, 8, 4, None) == sb.SARBP_EINVAL  # fewer than 4 samples
     assert sb._lib.sarbp_interpolate_track(8, 8, 10, 8, 8, 0, None) == sb.SARBP_EINVAL
+    assert sb._lib.sarbp_split_workspace_bytes(None, 16) == 0
+    assert sb._lib.sarbp_backproject_split(None, 8, 8, None, 8, 1, 0, None, 0, None) == sb.SARBP_EINVAL
     # output overlapping the sample positions
     assert sb._lib.sarbp_interpolate_track(4096, 8192, 10, 65536, 8192, 4, None) == sb.SARBP_EINVAL

@@ -763,6 +763,106 @@ def test_coarse_grid_range_precision(sb, interp, accum, pixel):
     assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
 
 
+# ----------------------------------------------------------------------------- pulses split over workgroups
+
+def _rel(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+@pytest.mark.parametrize("interp, accum", [("linear", "fp32"), ("nearest", "fp32"), ("sinc8", "fp32"),
+                                           ("linear", "kahan"), ("linear", "chunk64")])
+def test_split_small_grid(sb, interp, accum):
+    """The tiny scene (128 x 128 pixels in 16 tiles of 64 x 16, 256 pulses) through
+    sarbp_backproject_split: 8 pulse groups of 32, so 128 workgroups instead of 16.  The
+    image equals the unsplit call's up to the summation order (1e-5) and the oracle's
+    within the bar; then 250 pulses (ragged groups) with accumulate = 1 onto the first
+    image equals the unsplit calls' sum."""
+    import torch
+
+    s = synth.make_scene("tiny", interp=interp)
+    with sb.Plan.for_scene(s, accum=accum) as plan:
+        need = plan.split_workspace_bytes(s.na)
+        assert need == 8 * s.nx * s.ny * 8, need
+        pos = torch.from_numpy(s.positions).cuda()
+        ech = torch.from_numpy(s.echo).cuda()
+        a = plan.backproject(pos, ech)
+        b = plan.backproject(pos, ech, split=True)
+        a2 = plan.backproject(pos[:250].contiguous(), ech[:250].contiguous(), image=a.clone(), accumulate=1)
+        b2 = plan.backproject(pos[:250].contiguous(), ech[:250].contiguous(), image=b.clone(), accumulate=1,
+                              split=True)
+        torch.cuda.synchronize()
+        a, b, a2, b2 = (t.cpu().numpy().astype(np.complex128) for t in (a, b, a2, b2))
+    want = oracle.scene_backproject(s)
+    _say(f"[split {interp} {accum}] vs unsplit {_rel(b, a):.1e}, vs oracle {rel_l2(b, want):.1e}, "
+         f"accumulated {_rel(b2, a2):.1e}")
+    assert _rel(b, a) <= 1e-5
+    assert rel_l2(b, want) <= REL_L2
+    assert _rel(b2, a2) <= 1e-5
+
+
+def test_split_terrain_and_volume(sb):
+    """Small terrain (150 x 70 pixels, 6 tiles of 64 x 32) and volume (96 x 40 x 3 layers)
+    grids, split against unsplit."""
+    import torch
+
+    s = synth.make_scene("std", na=300, nr=1024, nx=150, ny=70, interp="linear", n_targets=3, dem_relief=20.0)
+    relief = synth.block_relief(s.dem)
+    dem = torch.from_numpy(np.ascontiguousarray(s.dem)).cuda()
+    with sb.Plan.for_scene(s, dem_relief=relief) as plan:
+        assert plan.split_workspace_bytes(s.na) > 0
+        pos = torch.from_numpy(s.positions).cuda()
+        ech = torch.from_numpy(s.echo).cuda()
+        a = plan.backproject(pos, ech, dem=dem)
+        b = plan.backproject(pos, ech, dem=dem, split=True)
+        torch.cuda.synchronize()
+        a, b = a.cpu().numpy(), b.cpu().numpy()
+    assert np.isfinite(b).all() and _rel(b, a) <= 1e-5, _rel(b, a)
+
+    v = synth.make_scene("std", na=256, nr=1024, nx=96, ny=40, interp="linear", n_targets=2)
+    with sb.Plan.for_scene(v, nz=3, dz=1.5) as plan:
+        assert plan.split_workspace_bytes(v.na) > 0
+        pos = torch.from_numpy(v.positions).cuda()
+        ech = torch.from_numpy(v.echo).cuda()
+        a = plan.backproject(pos, ech)
+        b = plan.backproject(pos, ech, split=True)
+        torch.cuda.synchronize()
+        a, b = a.cpu().numpy(), b.cpu().numpy()
+    assert b.shape == (3, 40, 96) and _rel(b, a) <= 1e-5, _rel(b, a)
+
+
+def test_split_workspace_rules(sb):
+    """A grid that fills the GPU needs no workspace and runs unsplit (bit for bit the plain
+    call); a short or overlapping workspace is refused before anything runs; fewer than 64
+    pulses are not split."""
+    import torch
+
+    s = synth.make_scene("std", na=64, nr=1024, nx=1024, ny=1024, interp="linear", n_targets=2, clutter=False)
+    with sb.Plan.for_scene(s) as plan:
+        assert plan.split_workspace_bytes(s.na) == 0
+        pos = torch.from_numpy(s.positions).cuda()
+        ech = torch.from_numpy(s.echo).cuda()
+        a = plan.backproject(pos, ech)
+        b = plan.backproject(pos, ech, split=True)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+    t = synth.make_scene("tiny")
+    with sb.Plan.for_scene(t) as plan:
+        assert plan.split_workspace_bytes(63) == 0 and plan.split_workspace_bytes(64) > 0
+        need = plan.split_workspace_bytes(t.na)
+        pos = torch.from_numpy(t.positions).cuda()
+        ech = torch.from_numpy(t.echo).cuda()
+        img = torch.zeros(plan.image_shape, dtype=torch.complex64, device="cuda")
+        short = torch.empty(need - 8, dtype=torch.uint8, device="cuda")
+        with pytest.raises(sb.SarbpError) as err:
+            plan.backproject(pos, ech, image=img, split=True, workspace=short)
+        assert err.value.status == sb.SARBP_EINVAL
+        big = torch.empty(need + img.numel() * 8, dtype=torch.uint8, device="cuda")
+        overlap = big[8:].view(torch.complex64)[: img.numel()].view(plan.image_shape)
+        with pytest.raises(sb.SarbpError) as err:
+            plan.backproject(pos, ech, image=overlap, split=True, workspace=big)
+        assert err.value.status == sb.SARBP_EINVAL
+
+
 @pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
 def test_most_carrier_cycles_per_bin(sb, interp):
     """3.98 m range bins at 3.125 cm: 254.7 carrier cycles per bin, just under the 255

@@ -126,7 +126,8 @@ def test_graph_capture_replays_match_eager(sb):
     """Range compression and backprojection captured once in a HIP graph (the entry
     points only enqueue kernels: they allocate and clear nothing) and replayed three
     times, with eager work and synchronisation between the replays: every replay
-    reproduces the eager results bit for bit, also when accumulating into an image."""
+    reproduces the eager results bit for bit, also when accumulating into an image and
+    for the pulse-group call (this 200 x 96 grid is split in 8 groups)."""
     import torch
 
     s = synth.make_scene("e2e", na=256, nx=200, ny=96, n_targets=2)
@@ -135,13 +136,17 @@ def test_graph_capture_replays_match_eager(sb):
         pos = torch.from_numpy(s.positions).cuda()
         rc_ref = plan.range_compress(raw)
         ref = plan.backproject(pos, rc_ref)
+        ws = torch.empty(plan.split_workspace_bytes(s.na), dtype=torch.uint8, device="cuda")
+        assert ws.numel() > 0
+        ref_split = plan.backproject(pos, rc_ref, split=True, workspace=ws)
         torch.cuda.synchronize()
-        rc, img, acc = torch.empty_like(raw), plan.new_image(), plan.new_image()
+        rc, img, acc, spl = torch.empty_like(raw), plan.new_image(), plan.new_image(), plan.new_image()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):  # one eager pass on the capture's side stream first
             plan.range_compress(raw, out=rc)
             plan.backproject(pos, rc, image=img)
+            plan.backproject(pos, rc, image=spl, split=True, workspace=ws)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
@@ -149,17 +154,20 @@ def test_graph_capture_replays_match_eager(sb):
             plan.range_compress(raw, out=rc)
             plan.backproject(pos, rc, image=img)
             plan.backproject(pos, rc, image=acc, accumulate=1)
+            plan.backproject(pos, rc, image=spl, split=True, workspace=ws)
         for k in range(3):
             rc.fill_(7.0)
             img.fill_(-3.0)
             acc.zero_()
+            spl.fill_(5.0)
             junk = torch.randn(1 << 20, device="cuda").sum()  # unrelated eager work between replays
             torch.cuda.synchronize()
             graph.replay()
             torch.cuda.synchronize()
             _say(f"[graph] replay {k}: rc {torch.equal(rc, rc_ref)}, image {torch.equal(img, ref)}, "
-                 f"accumulated {torch.equal(acc, ref)} ({float(junk):.1f})")
+                 f"accumulated {torch.equal(acc, ref)}, split {torch.equal(spl, ref_split)} ({float(junk):.1f})")
             assert torch.equal(rc, rc_ref) and torch.equal(img, ref) and torch.equal(acc, ref)
+            assert torch.equal(spl, ref_split)
 
 
 @pytest.mark.parametrize("first, nr", [(246, 48), (226, 36)], ids=["record-starts-in-scene", "record-ends-in-scene"])

@@ -17,6 +17,9 @@ Each case draws, from its own seed:
   wavelengths) for the fp32 terrain kernels;
 * for half of the cases, two calls that split the pulses, the second accumulating.
 
+Every case also runs through sarbp_backproject_split (pulse groups for small grids;
+most of these grids are small), against the oracle and against the plain call.
+
 The bar is the fine grids' one (relative L2 error at most REL_L2).  A case whose record
 misses the whole scene must give exactly zero.
 """
@@ -97,7 +100,7 @@ def random_case(seed):
     return scene, accum, split
 
 
-def _run(sb, scene, accum, split):
+def _run(sb, scene, accum, split, groups=False):
     import torch
 
     kw = dict(accum=accum)
@@ -109,10 +112,11 @@ def _run(sb, scene, accum, split):
         pos = torch.from_numpy(np.ascontiguousarray(scene.positions)).cuda()
         ech = torch.from_numpy(np.ascontiguousarray(scene.echo)).cuda()
         if split:
-            img = plan.backproject(pos[:split].contiguous(), ech[:split].contiguous(), dem=dem_d)
-            plan.backproject(pos[split:].contiguous(), ech[split:].contiguous(), image=img, accumulate=1, dem=dem_d)
+            img = plan.backproject(pos[:split].contiguous(), ech[:split].contiguous(), dem=dem_d, split=groups)
+            plan.backproject(pos[split:].contiguous(), ech[split:].contiguous(), image=img, accumulate=1, dem=dem_d,
+                             split=groups)
         else:
-            img = plan.backproject(pos, ech, dem=dem_d)
+            img = plan.backproject(pos, ech, dem=dem_d, split=groups)
         torch.cuda.synchronize()
         return img.cpu().numpy().astype(np.complex128)
 
@@ -134,11 +138,14 @@ def test_random_geometry_matches_oracle(sb, seed):
           f"terrain {scene.dem is not None}, split {split}", flush=True)
     sys.stdout.flush()
     got = _run(sb, scene, accum, split)
+    grouped = _run(sb, scene, accum, split, groups=True)
     want = oracle.scene_backproject(scene)
-    assert np.isfinite(got).all()
+    assert np.isfinite(got).all() and np.isfinite(grouped).all()
     if np.linalg.norm(want) == 0.0:
-        assert np.all(got == 0)
+        assert np.all(got == 0) and np.all(grouped == 0)
     else:
-        err = rel_l2(got, want)
-        print(f"[random {seed}] rel-L2 {err:.2e}", flush=True)
+        err, err_g = rel_l2(got, want), rel_l2(grouped, want)
+        print(f"[random {seed}] rel-L2 {err:.2e} (pulse groups {err_g:.2e})", flush=True)
         assert err <= REL_L2, err
+        assert err_g <= REL_L2, err_g
+        assert np.linalg.norm(grouped - got) <= 1e-5 * np.linalg.norm(got)

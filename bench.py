@@ -243,10 +243,10 @@ def aux_accumulators(sb, scene, steps, warmup):
 
 def aux_coarse(sb, scene, steps, warmup):
     """The standard echo onto 1024 x 1024 pixels of 0.8 m and of 1 m (linear): the
-    first grid's 64 x 32 tiles (28.6 m half diagonal) stay on fp32 range
-    differences, the second's (35.8 m) are past the 1024-wavelength limit and use
-    the fp64-range kernels.  Both windows (~140 and ~175 bins) are far longer than
-    the standard grid's (~38), so the staging work per pulse grows too."""
+    first grid's echo windows (144 bins, 3837 carrier cycles) stay on fp32 range
+    differences, the second's (178 bins, 4743 cycles) are past the 4096-cycle limit
+    and use the fp64-range kernels.  Both windows are far longer than the standard
+    grid's (41 bins), so the staging work per pulse grows too."""
     import torch
 
     out = {}

@@ -25,10 +25,11 @@
 //   a bound on the truncation error, or when q is not small by the exact form
 //   num / (R_t (1 + sqrt(1 + q))).  This keeps the bin position to ~1e-6 bins,
 //   which fp32 absolute ranges (~1e-3 m at 11 km) could not (section 2.2 warns
-//   about fp32 range precision).  The fp32 difference itself carries ~2^-24 of
-//   the tile's half diagonal, so plans with coarse pixels (half diagonal beyond
-//   1024 wavelengths) run the F64 variant: the same difference and series in
-//   fp64, with only the fraction within the bin back in fp32.
+//   about fp32 range precision).  The fp32 window position itself carries ~2^-24
+//   of the window, i.e. of the carrier cycles across it, so plans whose window
+//   spans more than 4096 cycles (coarse pixels, or many cycles per range bin) run
+//   the F64 variant: the same difference and series in fp64, with only the
+//   fraction within the bin back in fp32.
 // * The echo window a tile can touch (its range extent, bounded by the tile
 //   diagonal) is staged per pulse in LDS, already multiplied by the bin-centre
 //   carrier phase exp(+j 4 pi r_k / lambda).  For a pixel at u = k + f the

@@ -211,13 +211,15 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     const int64_t layers = p.nz > 1 ? p.nz : 1;
     plan->tiles_x = (p.nx + BP_TX - 1) / BP_TX;
     const int64_t tiles2 = (int64_t)plan->tiles_x * ((p.ny + 2 * BP_WAVES - 1) / (2 * BP_WAVES)) * layers;
-    // The fp32 kernels carry a pixel's range offset from the tile centre to about
-    // 2^-24 of the tile's half diagonal, a phase error of 4 pi 2^-24 half_span /
-    // lambda.  Beyond 1024 wavelengths of half diagonal (7.7e-4 rad) the plan uses
-    // the fp64-range kernels instead (64 x 32 tiles; terrain plans keep fp32).
+    // The fp32 kernels carry a pixel's window position (0 .. W bins) to about 2^-24
+    // of the window, and its phase to 2^-24 of the kappa W carrier cycles across
+    // the window (kappa = 2 dr / lambda; W ~ 4 half_span / lambda for large tiles).
+    // Past 4096 cycles (about 7.7e-4 rad per rounding) the plan uses the fp64-range
+    // kernels instead (64 x 32 tiles; terrain plans keep fp32).
     const double hs32 = 0.5 * sqrt((BP_TX * p.dx) * (BP_TX * p.dx) +
                                    (2.0 * BP_WAVES * p.dy) * (2.0 * BP_WAVES * p.dy));
-    plan->f64 = !(p.dem_relief > 0.0) && hs32 > 1024.0 * p.wavelength;
+    const double win32 = ceil(2.0 * hs32 / p.dr) + 6.0; // the window of 64 x 32 tiles, margins included
+    plan->f64 = !(p.dem_relief > 0.0) && (2.0 * p.dr / p.wavelength) * win32 > 4096.0;
     plan->ppt = (tiles2 < 2 * (int64_t)plan->n_cu && !(p.dem_relief > 0.0) && !plan->f64) ? 1 : 2;
     const int ty = BP_WAVES * plan->ppt;
     plan->tiles_y = (p.ny + ty - 1) / ty;

@@ -757,12 +757,12 @@ def test_coarse_grid_uses_large_lds_windows(sb, interp):
                                            ("linear", "kahan"), ("linear", "chunk64")])
 @pytest.mark.parametrize("pixel", [0.8, 8.0])
 def test_coarse_grid_range_precision(sb, interp, accum, pixel):
-    """Fp32 range offsets from a tile centre carry about 2^-24 of the tile's half
-    diagonal, so the plan switches to fp64 range differences once that half diagonal
-    exceeds 1024 wavelengths (32 m at 3.125 cm).  0.8 m pixels (64 x 32 tiles, 28.6 m)
-    stay just under it, on the fp32 kernels; 8 m pixels (286 m, where fp32 differences
-    gave a relative error of 4.2e-3) go over, with the exact square root for every
-    pulse at 11 km.  Both must meet the fine grids' bar."""
+    """Fp32 window positions carry about 2^-24 of the window, i.e. of the carrier cycles
+    across it, so the plan switches to fp64 range differences once a 64 x 32 tile's
+    window spans more than 4096 cycles.  0.8 m pixels (3837 cycles at 3.125 cm and
+    0.416 m bins) stay just under it, on the fp32 kernels; 8 m pixels (~37000 cycles,
+    where fp32 differences gave a relative error of 4.2e-3) go over, with the
+    seven-term series for every pulse at 11 km.  Both must meet the fine grids' bar."""
     pos = synth.track(40)
     s = _custom_scene(pos, 4096, 70, 40, pixel, pixel, interp, 47)
     _say(f"[range precision {interp} {accum}] {s.nx}x{s.ny} at {pixel} m")

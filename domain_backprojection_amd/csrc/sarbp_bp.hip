@@ -119,7 +119,7 @@ __device__ int pulse_setup(const BpArgs& A, int n, double cx, double cy, double 
 
 // Per-pulse constants of the fp64-range kernels (tiles whose range extent is too
 // large for the fp32 difference): three double2 per pulse,
-//   (2 ux, 2 uy), (ft, 1/R_t^2), (R_t/dr, 0),
+//   (2 ux, 2 uy), (ft, 1/R_t^2), (R_t/dr, 2 uz),
 // and the window position ub = ft + (R_t/dr) (sqrt(1 + q) - 1), q = num / R_t^2,
 // by its binomial series through q^4 (mode 0) or q^7 (mode 1), the shorter one
 // whose first omitted term stays below 1e-7 bins over the tile, else exactly
@@ -144,7 +144,7 @@ __device__ int pulse_setup_f64(const BpArgs& A, int n, double cx, double cy, dou
     const double q = (hs * hs + 2.0 * hs * Rt) * inv_r * inv_r;
     cd[0] = make_double2(2.0 * ux, 2.0 * uy);
     cd[1] = make_double2(ft, inv_r * inv_r);
-    cd[2] = make_double2(Rt * A.inv_dr, 0.0);
+    cd[2] = make_double2(Rt * A.inv_dr, 2.0 * uz); // 2 uz: the terrain kernels' vertical term
     *klo_out = (int)klo_d;
     const double q2 = q * q, q4 = q2 * q2, rb = Rt * A.inv_dr; // R_t in bins
     if (q > 0.25 || rb * (429.0 / 32768.0) * q4 * q4 > 1e-7) return 2;
@@ -153,12 +153,12 @@ __device__ int pulse_setup_f64(const BpArgs& A, int n, double cx, double cy, dou
 
 // Window position of one pixel for pulse p in the fp64-range kernels: the bin
 // k = floor(ub) and the fraction f = ub - k.
-template <int MODE>
-__device__ __forceinline__ void locate_f64(const float4* cst, int p, double dxd, double dyd, double ddd, float* f,
-                                           uint32_t* k) {
+template <int MODE, bool DEM>
+__device__ __forceinline__ void locate_f64(const float4* cst, int p, double dxd, double dyd, double ddd, double dzd,
+                                           float* f, uint32_t* k) {
     const double2* cd = reinterpret_cast<const double2*>(cst) + 3 * p;
     const double2 d0 = cd[0], d1 = cd[1], d2 = cd[2];
-    const double num = fma(dxd, d0.x, fma(dyd, d0.y, ddd));
+    const double num = fma(dxd, d0.x, fma(dyd, d0.y, DEM ? fma(dzd, d2.y, ddd) : ddd));
     const double q = num * d1.y;
     double s; // (sqrt(1 + q) - 1) / q
     if constexpr (MODE == 2) {
@@ -290,7 +290,8 @@ __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem,
 #pragma unroll
         for (int m = 0; m < PPT; ++m) {
             if constexpr (F64) {
-                locate_f64<MODE>(cst, p0 + q, pxd[0], pxd[1 + m], pxd[1 + PPT + m], &g[q][m], &kb[q][m]);
+                locate_f64<MODE, DEM>(cst, p0 + q, pxd[0], pxd[1 + m], pxd[1 + PPT + m], pxd[1 + 2 * PPT + m], &g[q][m],
+                                      &kb[q][m]);
             } else {
                 const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
                 const float ub = bin_position<MODE>(num, c0, c1);
@@ -366,7 +367,7 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
                 float f;
                 uint32_t kw;
                 if constexpr (F64) {
-                    locate_f64<MODE>(cst, p, pxd[0], pxd[1 + m], pxd[1 + PPT + m], &f, &kw);
+                    locate_f64<MODE, DEM>(cst, p, pxd[0], pxd[1 + m], pxd[1 + PPT + m], pxd[1 + 2 * PPT + m], &f, &kw);
                 } else {
                     const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
                     const float ub = bin_position<MODE>(num, c0, c1);
@@ -391,7 +392,7 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
                 float f;
                 uint32_t kw;
                 if constexpr (F64) {
-                    locate_f64<MODE>(cst, p, pxd[0], pxd[1 + m], pxd[1 + PPT + m], &f, &kw);
+                    locate_f64<MODE, DEM>(cst, p, pxd[0], pxd[1 + m], pxd[1 + PPT + m], pxd[1 + 2 * PPT + m], &f, &kw);
                 } else {
                     const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
                     const float ub = bin_position<MODE>(num, c0, c1);
@@ -504,11 +505,10 @@ __device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int n
 
 // At most 64 VGPRs, so two 1024-lane workgroups (8 waves per SIMD) fit on a CU:
 // the loop needs that many waves to hide LDS and transcendental latency.
-// F64: the fp64-range variant (pulse_setup_f64 / locate_f64) for tiles whose
-// range extent makes the fp32 difference too coarse; no terrain.
+// F64: the fp64-range variant (pulse_setup_f64 / locate_f64) for plans whose echo
+// window spans too many carrier cycles for the fp32 window position.
 template <int INTERP, int ACC, bool DEM, int PPT, bool F64>
 __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8))) void bp_kernel(BpArgs A) {
-    static_assert(!(F64 && DEM), "the fp64-range kernels have no terrain variant");
     extern __shared__ __align__(16) char smem[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -545,7 +545,7 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     for (int m = 0; m < PPT; ++m) j_off[m] = min(j0 + wave + BP_WAVES * m, j_last);
     const double ddx = ((double)i_off - cxp) * A.dx;
     const float dxl = (float)ddx;
-    double pxd[1 + 2 * PPT]; // F64: ddx, then ddy and |d|^2 of each of the lane's pixels
+    double pxd[1 + 3 * PPT]; // F64: ddx, then ddy, |d|^2 and (terrain) dz of each of the lane's pixels
     pxd[0] = ddx;
     float dyv[PPT], ddv[PPT], accr[PPT], acci[PPT];
     float cmpr[PPT], cmpi[PPT]; // Kahan compensation (ACC_KAHAN)
@@ -557,6 +557,7 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         ddv[m] = (float)(ddx * ddx + ddy * ddy);
         pxd[1 + m] = ddy;
         pxd[1 + PPT + m] = ddx * ddx + ddy * ddy;
+        pxd[1 + 2 * PPT + m] = 0.0;
         accr[m] = 0.f;
         acci[m] = 0.f;
         cmpr[m] = 0.f;
@@ -607,6 +608,8 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
             const double ddz = (double)hv[m] - hc;
             dzv[m] = (float)ddz;
             ddv[m] = (float)(ddx * ddx + ddy * ddy + ddz * ddz);
+            pxd[1 + PPT + m] = ddx * ddx + ddy * ddy + ddz * ddz;
+            pxd[1 + 2 * PPT + m] = ddz;
         }
     }
 
@@ -717,12 +720,10 @@ int allow_lds_acc(int accum, size_t bytes) {
     }
 }
 
-// Kernel variants: (DEM, ppt 1 or 2) with fp32 ranges, and (no DEM, ppt 2) with fp64 ranges.
+// Kernel variants: ppt 1 or 2 with fp32 ranges, and ppt 2 with fp64 ranges.
 template <int INTERP, bool DEM>
 int allow_lds(int accum, int ppt, bool f64, size_t bytes) {
-    if constexpr (!DEM) {
-        if (f64) return allow_lds_acc<INTERP, false, 2, true>(accum, bytes);
-    }
+    if (f64) return allow_lds_acc<INTERP, DEM, 2, true>(accum, bytes);
     return ppt == 1 ? allow_lds_acc<INTERP, DEM, 1, false>(accum, bytes)
                     : allow_lds_acc<INTERP, DEM, 2, false>(accum, bytes);
 }
@@ -745,9 +746,7 @@ void launch_acc(const BpArgs& A, int accum, size_t lds, hipStream_t stream) {
 
 template <int INTERP, bool DEM>
 void launch(const BpArgs& A, int accum, int ppt, bool f64, size_t lds, hipStream_t stream) {
-    if constexpr (!DEM) {
-        if (f64) return launch_acc<INTERP, false, 2, true>(A, accum, lds, stream);
-    }
+    if (f64) return launch_acc<INTERP, DEM, 2, true>(A, accum, lds, stream);
     if (ppt == 1) launch_acc<INTERP, DEM, 1, false>(A, accum, lds, stream);
     else launch_acc<INTERP, DEM, 2, false>(A, accum, lds, stream);
 }
@@ -789,13 +788,13 @@ int sarbp_split_count(const sarbp_plan* plan, int n) {
 int sarbp_bp_allow_lds(int interp, int accum, bool dem, int ppt, bool f64, size_t bytes) {
     switch (interp) {
         case SARBP_NEAREST:
-            return dem ? allow_lds<SARBP_NEAREST, true>(accum, ppt, false, bytes)
+            return dem ? allow_lds<SARBP_NEAREST, true>(accum, ppt, f64, bytes)
                        : allow_lds<SARBP_NEAREST, false>(accum, ppt, f64, bytes);
         case SARBP_LINEAR:
-            return dem ? allow_lds<SARBP_LINEAR, true>(accum, ppt, false, bytes)
+            return dem ? allow_lds<SARBP_LINEAR, true>(accum, ppt, f64, bytes)
                        : allow_lds<SARBP_LINEAR, false>(accum, ppt, f64, bytes);
         default:
-            return dem ? allow_lds<SARBP_SINC8, true>(accum, ppt, false, bytes)
+            return dem ? allow_lds<SARBP_SINC8, true>(accum, ppt, f64, bytes)
                        : allow_lds<SARBP_SINC8, false>(accum, ppt, f64, bytes);
     }
 }
@@ -862,15 +861,15 @@ int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* ech
     const bool d = dem != nullptr;
     switch (p.interp) {
         case SARBP_NEAREST:
-            d ? launch<SARBP_NEAREST, true>(A, p.accum, plan->ppt, false, plan->lds_bytes, stream)
+            d ? launch<SARBP_NEAREST, true>(A, p.accum, plan->ppt, plan->f64, plan->lds_bytes, stream)
               : launch<SARBP_NEAREST, false>(A, p.accum, plan->ppt, plan->f64, plan->lds_bytes, stream);
             break;
         case SARBP_LINEAR:
-            d ? launch<SARBP_LINEAR, true>(A, p.accum, plan->ppt, false, plan->lds_bytes, stream)
+            d ? launch<SARBP_LINEAR, true>(A, p.accum, plan->ppt, plan->f64, plan->lds_bytes, stream)
               : launch<SARBP_LINEAR, false>(A, p.accum, plan->ppt, plan->f64, plan->lds_bytes, stream);
             break;
         default:
-            d ? launch<SARBP_SINC8, true>(A, p.accum, plan->ppt, false, plan->lds_bytes, stream)
+            d ? launch<SARBP_SINC8, true>(A, p.accum, plan->ppt, plan->f64, plan->lds_bytes, stream)
               : launch<SARBP_SINC8, false>(A, p.accum, plan->ppt, plan->f64, plan->lds_bytes, stream);
             break;
     }

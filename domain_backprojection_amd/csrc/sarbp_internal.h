@@ -53,7 +53,7 @@ struct sarbp_plan {
     // backprojection launch geometry
     int tiles_x, tiles_y;
     int ppt;          // backprojection pixels per lane (1 or 2): tiles of 64 x 16 ppt
-    int f64;          // 1: range differences in fp64 (coarse grids, no terrain; ppt = 2)
+    int f64;          // 1: range differences in fp64 (windows of many carrier cycles; ppt = 2)
     int win;          // LDS window entries per pulse
     int margin_lo;    // bins below the tile's lowest range kept in the window
     int chunk;        // pulses per LDS step

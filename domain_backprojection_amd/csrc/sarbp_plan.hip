@@ -215,11 +215,11 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     // of the window, and its phase to 2^-24 of the kappa W carrier cycles across
     // the window (kappa = 2 dr / lambda; W ~ 4 half_span / lambda for large tiles).
     // Past 4096 cycles (about 7.7e-4 rad per rounding) the plan uses the fp64-range
-    // kernels instead (64 x 32 tiles; terrain plans keep fp32).
+    // kernels instead (64 x 32 tiles).
     const double hs32 = 0.5 * sqrt((BP_TX * p.dx) * (BP_TX * p.dx) +
-                                   (2.0 * BP_WAVES * p.dy) * (2.0 * BP_WAVES * p.dy));
+                                   (2.0 * BP_WAVES * p.dy) * (2.0 * BP_WAVES * p.dy) + p.dem_relief * p.dem_relief);
     const double win32 = ceil(2.0 * hs32 / p.dr) + 6.0; // the window of 64 x 32 tiles, margins included
-    plan->f64 = !(p.dem_relief > 0.0) && (2.0 * p.dr / p.wavelength) * win32 > 4096.0;
+    plan->f64 = (2.0 * p.dr / p.wavelength) * win32 > 4096.0;
     plan->ppt = (tiles2 < 2 * (int64_t)plan->n_cu && !(p.dem_relief > 0.0) && !plan->f64) ? 1 : 2;
     const int ty = BP_WAVES * plan->ppt;
     plan->tiles_y = (p.ny + ty - 1) / ty;
@@ -262,7 +262,7 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     if (plan->lds_bytes > 64 * 1024) {
         st = sarbp_bp_allow_lds(p.interp, p.accum, false, plan->ppt, plan->f64, plan->lds_bytes);
         if (st == SARBP_OK && p.dem_relief > 0.0)
-            st = sarbp_bp_allow_lds(p.interp, p.accum, true, plan->ppt, false, plan->lds_bytes);
+            st = sarbp_bp_allow_lds(p.interp, p.accum, true, plan->ppt, plan->f64, plan->lds_bytes);
         if (st != SARBP_OK) {
             release(plan);
             return st;

@@ -77,9 +77,8 @@ typedef struct {
     double dx, dy;      /* pixel spacing (> 0): pixel (i, j) centre = (x0 + i dx, y0 + j dy, z0);
                          * a plan whose LDS echo window spans more than 4096 carrier cycles,
                          * (2 dr / lambda) x (window bins) ~ 4 x (tile half diagonal) / lambda
-                         * for 64 dx x 32 dy tiles, takes range differences in fp64 (about
-                         * 1.4x the time).  Plans with dem_relief > 0 keep fp32 ones, whose
-                         * phase error grows with those cycles: ~2e-3 of the image near 8000 */
+                         * for 64 dx x 32 dy tiles (relief included), takes range differences
+                         * in fp64 (about 1.4x the time)                                      */
     double wavelength;  /* carrier wavelength lambda (> 0) of the phase term exp(+j 4 pi R / lambda);
                          * 2 dr / lambda, the carrier cycles per range bin, must be below 255
                          * (SARBP_EUNSUPPORTED otherwise): the kernels rotate each sample with

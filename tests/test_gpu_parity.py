@@ -453,6 +453,25 @@ def test_terrain_far_above_reference_plane(sb, interp):
     assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
 
 
+@pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
+def test_terrain_coarse_grid_fp64_ranges(sb, interp):
+    """2 m pixels on up to 20 m of seeded terrain: a 64 x 32 tile's window (with the
+    relief) spans about 9400 carrier cycles, past the 4096 up to which plans keep fp32
+    window positions, so the terrain kernels take their range differences in fp64.
+    Random echo; the full image against the oracle, within the fine grids' bar."""
+    import dataclasses
+
+    s = _custom_scene(synth.track(40), 4096, 70, 40, 2.0, 2.0, interp, 61)
+    dem = synth.terrain(s.nx, s.ny, s.dx, s.dy, np.random.Generator(np.random.PCG64(62)), 20.0)
+    s = dataclasses.replace(s, dem=dem)
+    relief = synth.block_relief(dem)
+    _say(f"[terrain 2 m {interp}] block relief {relief:.1f} m")
+    got = _run_bp_dem(sb, s, dem, relief)
+    want = oracle.scene_backproject(s)
+    assert np.isfinite(got).all()
+    assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
+
+
 def test_terrain_perturbed_track_and_chunk64(sb):
     s = synth.make_scene("hifi", na=203, nr=1024, nx=96, ny=64, interp="sinc8", n_targets=2, dem_relief=12.0)
     got = _run_bp_dem(sb, s, s.dem, synth.block_relief(s.dem), accum="chunk64")

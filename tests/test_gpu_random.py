@@ -12,9 +12,8 @@ Each case draws, from its own seed:
   cycles per bin, and widened where a tile's window would not fit in LDS);
 * a record of 8-4096 bins placed anywhere from well before to well after the
   scene, so pixels often fall partly or wholly outside it (zero extension);
-* for a quarter of the cases, rough terrain of up to 30 m peak to peak, with pixels,
-  relief and bins kept such that a tile's echo window spans at most 6000 carrier
-  cycles, within what the fp32 terrain kernels resolve;
+* for a quarter of the cases, rough terrain of up to 30 m peak to peak (on the fp32
+  or, for windows of many carrier cycles, the fp64-range terrain kernels);
 * for half of the cases, two calls that split the pulses, the second accumulating.
 
 Every case also runs through sarbp_backproject_split (pulse groups for small grids;
@@ -88,11 +87,6 @@ def random_case(seed):
     dem = None
     if terrain:
         h = rng.uniform(0.0, 15.0)
-        # window cycles: (2 dr / lambda) x (bins spanned by the tile's range extent + margins)
-        cycles = lambda: 2.0 * dr / lam * (math.ceil(math.sqrt(4 * half_diag() ** 2 + 4 * h * h) / dr) + 6)
-        while cycles() > 6000.0:
-            dx, dy, h = 0.7 * dx, 0.7 * dy, 0.7 * h
-        x0, y0 = -(nx // 2) * dx, -(ny // 2) * dy
         dem = rng.uniform(-1.0, 1.0, (ny, nx)).astype(np.float32) * np.float32(h)
     echo = (rng.standard_normal((na, nr)) + 1j * rng.standard_normal((na, nr))).astype(np.complex64)
     scene = synth.Scene(name=f"random{seed}", seed=seed, na=na, nr=nr, nx=nx, ny=ny, x0=x0, y0=y0, z0=0.0,

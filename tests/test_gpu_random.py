@@ -14,7 +14,8 @@ Each case draws, from its own seed:
   scene, so pixels often fall partly or wholly outside it (zero extension);
 * for a quarter of the cases, rough terrain of up to 30 m peak to peak (on the fp32
   or, for windows of many carrier cycles, the fp64-range terrain kernels);
-* for half of the cases, two calls that split the pulses, the second accumulating.
+* for half of the cases, two calls that split the pulses, the second accumulating;
+* for about a tenth (flat ones), a volume of 2-6 layers 0.1-20 m apart.
 
 Every case also runs through sarbp_backproject_split (pulse groups for small grids;
 most of these grids are small), against the oracle and against the plain call.
@@ -48,8 +49,9 @@ def _loguniform(rng, lo, hi):
 
 
 def random_case(seed):
-    """One random problem: (scene, accum, split) with split = 0 for a single call, else the
-    number of pulses in the first of two calls."""
+    """One random problem: (scene, accum, split, layers) with split = 0 for a single call,
+    else the number of pulses in the first of two calls, and layers = (nz, dz) for a
+    volume, else None."""
     rng = np.random.Generator(np.random.PCG64(seed))
     interp = ("nearest", "linear", "sinc8")[int(rng.integers(3))]
     accum = ("fp32", "kahan", "chunk64")[int(rng.integers(3))]
@@ -93,13 +95,27 @@ def random_case(seed):
                         dx=dx, dy=dy, r0=r0, dr=dr, wavelength=lam, interp=interp, positions=pos, echo=echo,
                         raw=None, targets=np.zeros((0, 2), np.int64), dem=dem)
     split = int(rng.integers(1, na)) if (na > 1 and rng.uniform() < 0.5) else 0
-    return scene, accum, split
+    layers = None
+    if dem is None and rng.uniform() < 0.15:
+        layers = (int(rng.integers(2, 7)), _loguniform(rng, 0.1, 20.0))
+    return scene, accum, split, layers
 
 
-def _run(sb, scene, accum, split, groups=False):
+def expected(scene, layers):
+    """The oracle's image: the plane (or terrain) definition, or each layer of a volume."""
+    if layers is None:
+        return oracle.scene_backproject(scene)
+    return oracle.backproject_volume(scene.positions, scene.echo, scene.r0, scene.dr, scene.nx, scene.ny, layers[0],
+                                     scene.x0, scene.y0, scene.z0, scene.dx, scene.dy, layers[1], scene.wavelength,
+                                     scene.interp)
+
+
+def _run(sb, scene, accum, split, layers=None, groups=False):
     import torch
 
     kw = dict(accum=accum)
+    if layers is not None:
+        kw.update(nz=layers[0], dz=layers[1])
     dem_d = None
     if scene.dem is not None:
         kw["dem_relief"] = max(synth.block_relief(scene.dem), 1e-3)
@@ -119,23 +135,23 @@ def _run(sb, scene, accum, split, groups=False):
 
 def test_random_case_generator_is_seeded():
     """The generator itself (no GPU use): the same seed gives the same case."""
-    a, acc_a, split_a = random_case(5)
-    b, acc_b, split_b = random_case(5)
-    assert (acc_a, split_a, a.interp, a.nx, a.ny, a.na) == (acc_b, split_b, b.interp, b.nx, b.ny, b.na)
+    a, acc_a, split_a, lay_a = random_case(5)
+    b, acc_b, split_b, lay_b = random_case(5)
+    assert (acc_a, split_a, lay_a, a.interp, a.nx, a.ny, a.na) == (acc_b, split_b, lay_b, b.interp, b.nx, b.ny, b.na)
     assert np.array_equal(a.echo, b.echo) and np.array_equal(a.positions, b.positions)
 
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("seed", range(7000, 7000 + N_CASES))
 def test_random_geometry_matches_oracle(sb, seed):
-    scene, accum, split = random_case(seed)
+    scene, accum, split, layers = random_case(seed)
     print(f"[random {seed}] {scene.interp} {accum} {scene.nx}x{scene.ny} px {scene.dx:.3g}x{scene.dy:.3g} m, "
           f"{scene.na} pulses x {scene.nr} bins of {scene.dr:.3g} m, lambda {scene.wavelength}, "
-          f"terrain {scene.dem is not None}, split {split}", flush=True)
+          f"terrain {scene.dem is not None}, split {split}, layers {layers}", flush=True)
     sys.stdout.flush()
-    got = _run(sb, scene, accum, split)
-    grouped = _run(sb, scene, accum, split, groups=True)
-    want = oracle.scene_backproject(scene)
+    got = _run(sb, scene, accum, split, layers)
+    grouped = _run(sb, scene, accum, split, layers, groups=True)
+    want = expected(scene, layers)
     assert np.isfinite(got).all() and np.isfinite(grouped).all()
     if np.linalg.norm(want) == 0.0:
         assert np.all(got == 0) and np.all(grouped == 0)

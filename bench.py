@@ -266,7 +266,7 @@ def aux_coarse(sb, scene, steps, warmup):
 def aux_small_grids(sb, scene, steps, warmup):
     """Grids with fewer tiles than the GPU has room for, plain and with the pulses split over
     workgroups (sarbp_backproject_split): the tiny scene (128 x 128, 256 pulses) and the
-    standard echo onto the central 256 x 256 pixels (4096 pulses)."""
+    standard echo onto the central 256 x 256 and 512 x 512 pixels (4096 pulses)."""
     import torch
 
     import synth
@@ -274,7 +274,8 @@ def aux_small_grids(sb, scene, steps, warmup):
     out = {}
     t = synth.make_scene("tiny")
     cases = (("tiny_128", t, dict()),
-             ("std_256", scene, dict(nx=256, ny=256, x0=scene.x0 + 384 * scene.dx, y0=scene.y0 + 384 * scene.dy)))
+             ("std_256", scene, dict(nx=256, ny=256, x0=scene.x0 + 384 * scene.dx, y0=scene.y0 + 384 * scene.dy)),
+             ("std_512", scene, dict(nx=512, ny=512, x0=scene.x0 + 256 * scene.dx, y0=scene.y0 + 256 * scene.dy)))
     for key, s, grid in cases:
         with sb.Plan.for_scene(s, **grid) as plan:
             pos = torch.from_numpy(s.positions).cuda()

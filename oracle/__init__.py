@@ -58,6 +58,8 @@ def _load():
             lib.oracle_backproject_rows.argtypes = [i, i, dp, dp, d, d, i, i, d, d, d, d, d, d, i, i, i, dp, i]
             lib.oracle_backproject_pixels.argtypes = [i, i, dp, dp, d, d, d, d, d, d, d, d, i, i, lp, dp, i]
             lib.oracle_nearest_index.argtypes = [dp, d, d, d, d, d, d, d, i, lp, lp]
+            fp_ = ctypes.POINTER(ctypes.c_float)
+            lib.oracle_nearest_index_dem.argtypes = [dp, d, d, d, d, d, d, d, i, i, fp_, i, lp, lp]
             fp = ctypes.POINTER(ctypes.c_float)
             lib.oracle_backproject_rows_dem.argtypes = [i, i, dp, dp, d, d, i, i, d, d, d, d, d, fp, d, i, i, i,
                                                         dp, i]
@@ -66,6 +68,7 @@ def _load():
             lib.oracle_sinc8_weight.argtypes = [d]
             lib.oracle_sinc8_weight.restype = d
             for f in (lib.oracle_backproject_rows, lib.oracle_backproject_pixels, lib.oracle_nearest_index,
+                      lib.oracle_nearest_index_dem,
                       lib.oracle_backproject_rows_dem, lib.oracle_backproject_pixels_dem):
                 f.restype = ctypes.c_int
             _lib = lib
@@ -149,15 +152,22 @@ def backproject_pixels(positions, echo, r0, dr, x0, y0, z0, dx, dy, wavelength, 
     return out
 
 
-def nearest_index(antenna, r0, dr, x0, y0, z0, dx, dy, ij) -> np.ndarray:
-    """floor(u + 1/2) for one antenna position at grid pixels ``ij``: int64 (P,)."""
+def nearest_index(antenna, r0, dr, x0, y0, z0, dx, dy, ij, dem=None) -> np.ndarray:
+    """floor(u + 1/2) for one antenna position at grid pixels ``ij``: int64 (P,).  With ``dem``
+    (float32 (ny, nx)), pixel (i, j) lies at height z0 + dem[j, i]."""
     lib = _load()
     a, ap = _f64(np.asarray(antenna).reshape(3))
     ij = np.ascontiguousarray(ij, dtype=np.int64).reshape(-1, 2)
     out = np.zeros(ij.shape[0], dtype=np.int64)
-    rc_ = lib.oracle_nearest_index(ap, r0, dr, x0, y0, z0, dx, dy, ij.shape[0],
-                                   ij.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
-                                   out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+    ijp = ij.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    op = out.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    if dem is None:
+        rc_ = lib.oracle_nearest_index(ap, r0, dr, x0, y0, z0, dx, dy, ij.shape[0], ijp, op)
+    else:
+        d = np.ascontiguousarray(dem, dtype=np.float32)
+        ny, nx = d.shape
+        rc_ = lib.oracle_nearest_index_dem(ap, r0, dr, x0, y0, z0, dx, dy, nx, ny,
+                                           d.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), ij.shape[0], ijp, op)
     if rc_ != 0:
         raise ValueError("oracle_nearest_index rejected its arguments")
     return out

@@ -192,6 +192,26 @@ int oracle_nearest_index(const double* a, double r0, double dr, double x0, doubl
     return 0;
 }
 
+/* As oracle_nearest_index, with pixel (i, j) at height z0 + dem[j * nx + i]
+ * (terrain: the pixel height of the definition above). */
+int oracle_nearest_index_dem(const double* a, double r0, double dr, double x0, double y0, double z0,
+                             double dx, double dy, int nx, int ny, const float* dem, int npix, const int64_t* ij,
+                             int64_t* k_out) {
+    if (!(dr > 0.0) || npix < 0 || !dem || nx <= 0 || ny <= 0) return -1;
+    for (int p = 0; p < npix; ++p) {
+        const int64_t i = ij[2 * p], j = ij[2 * p + 1];
+        if (i < 0 || i >= nx || j < 0 || j >= ny) return -1;
+        double x = x0 + (double)i * dx;
+        double y = y0 + (double)j * dy;
+        double z = z0 + (double)dem[j * nx + i];
+        double ddx = x - a[0], ddy = y - a[1], ddz = z - a[2];
+        double R = sqrt(ddx * ddx + ddy * ddy + ddz * ddz);
+        double u = (R - r0) / dr;
+        k_out[p] = (int64_t)floor(u + 0.5);
+    }
+    return 0;
+}
+
 /* As oracle_backproject_rows, with pixel (i, j) at height z0 + dem[j * nx + i]. */
 int oracle_backproject_rows_dem(int na, int nr, const double* pos, const double* echo, double r0,
                                 double dr, int nx, int ny, double x0, double y0, double z0, double dx,

@@ -144,3 +144,32 @@ def test_volume_layers_are_planes():
     plane = oracle.backproject(pos, echo, r0, synth.DR, 8, 6, -0.8, -0.6, 2.0 + 2 * 0.5, 0.2, 0.2,
                                synth.WAVELENGTH, "sinc8")
     assert np.array_equal(vol[2], plane)
+
+
+def test_nearest_index_on_terrain_is_the_ramp_probe():
+    """oracle.nearest_index with per-pixel heights equals the bin the terrain definition selects:
+    one pulse with echo s[k] = k + 1 gives |I| - 1 = floor(u + 1/2) exactly (the backprojection's
+    terrain variant is pinned against the 40-digit brute force); a flat map equals the plane
+    index, and a constant height h equals the plane at z0 + h."""
+    g = _geom(na=1, nr=512, nx=24, ny=20)
+    rng = np.random.Generator(np.random.PCG64(9))
+    dem = rng.uniform(-6.0, 9.0, (g["ny"], g["nx"])).astype(np.float32)
+    echo = (np.arange(g["nr"]) + 1.0).astype(np.complex128)[None, :]
+    img = _dem_bp(g, echo, "nearest", dem)
+    jj, ii = np.meshgrid(np.arange(g["ny"]), np.arange(g["nx"]), indexing="ij")
+    ij = np.stack([ii.ravel(), jj.ravel()], 1)
+    k = oracle.nearest_index(g["pos"][0], g["r0"], g["dr"], g["x0"], g["y0"], g["z0"], g["dx"], g["dy"], ij, dem=dem)
+    got = np.abs(img).ravel() - 1.0
+    assert np.max(np.abs(got - np.rint(got))) < 1e-9
+    assert np.array_equal(np.rint(got).astype(np.int64), k)
+    assert len(np.unique(k)) > 3  # the heights move the selected bin
+    flat = oracle.nearest_index(g["pos"][0], g["r0"], g["dr"], g["x0"], g["y0"], g["z0"], g["dx"], g["dy"], ij,
+                                dem=np.zeros_like(dem))
+    plane = oracle.nearest_index(g["pos"][0], g["r0"], g["dr"], g["x0"], g["y0"], g["z0"], g["dx"], g["dy"], ij)
+    assert np.array_equal(flat, plane)
+    h = np.float32(3.5)
+    lifted = oracle.nearest_index(g["pos"][0], g["r0"], g["dr"], g["x0"], g["y0"], g["z0"], g["dx"], g["dy"], ij,
+                                  dem=np.full_like(dem, h))
+    plane_h = oracle.nearest_index(g["pos"][0], g["r0"], g["dr"], g["x0"], g["y0"], g["z0"] + float(h), g["dx"],
+                                   g["dy"], ij)
+    assert np.array_equal(lifted, plane_h)

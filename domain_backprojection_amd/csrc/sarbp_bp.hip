@@ -55,6 +55,7 @@
 //   a contiguous band of tiles whose echo windows overlap in its L2.
 #include <math.h>
 
+#include "sarbp_geom.h"
 #include "sarbp_internal.h"
 
 #pragma clang fp contract(off)
@@ -62,137 +63,6 @@
 namespace {
 
 
-
-template <int INTERP>
-__device__ constexpr int entry_bytes() {
-    return INTERP == SARBP_NEAREST ? 8 : (INTERP == SARBP_LINEAR ? 16 : 64);
-}
-
-// Per-pulse constants of the current tile, two float4 per pulse:
-//   c0 = (2 ux, 2 uy, ft, a)   c1 = (b, c, 1/R_t^2, a2)
-// with u = c - a_n, ft = u_c - k_lo (fractional bin of the tile centre within
-// the window), a = 1/(2 R_t dr), b = -1/(8 R_t^3 dr), c = 1/(16 R_t^5 dr).
-// In q = num / R_t^2, (R - R_t) / R_t = q/2 - q^2/8 + q^3/16 - 5 q^4/128 + ...
-// The two-term form replaces the cubic by its Chebyshev-economised linear fit
-// over |q| <= q_m, (3/4) q_m^2 q, so its linear coefficient is
-// a2 = a (1 + 3 q_m^2 / 32) and its error at most R_t (q_m^3/64 + 5 q_m^4/128).
-// Returns the accuracy mode this pulse needs (0: 2 terms, 1: 3 terms, 2: exact).
-// Terrain (dem) kernels also store c2 = (2 uz, 0, 0, 0), the vertical term of 2 d.u.
-__device__ int pulse_setup(const BpArgs& A, int n, double cx, double cy, double cz, float4* cst, int* klo_out,
-                           bool dem) {
-    const double ax = A.pos[3 * (size_t)n], ay = A.pos[3 * (size_t)n + 1], az = A.pos[3 * (size_t)n + 2];
-    const double ux = cx - ax, uy = cy - ay, uz = cz - az;
-    const double R2 = ux * ux + uy * uy + uz * uz;
-    const double Rt = sqrt(R2);
-    const double uc = (Rt - A.r0) * A.inv_dr;
-    const double klo_d = floor(uc - A.half_span_bins) - (double)A.margin_lo;
-    const bool ok = isfinite(Rt) && Rt > 0.0 && isfinite(uc) && fabs(klo_d) < 1.0e9;
-    if (!ok) {
-        // Non-finite geometry: park every pixel on window entry margin_lo and
-        // let the staging fill the window with NaN, so NaN propagates.
-        cst[0] = make_float4(0.f, 0.f, (float)A.margin_lo + 0.25f, 0.f);
-        cst[1] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (dem) cst[2] = make_float4(0.f, 0.f, 0.f, 0.f);
-        *klo_out = INT32_MIN;
-        return 0;
-    }
-    const double inv_r = 1.0 / Rt;
-    const double idr = A.inv_dr;
-    // nearest rounds u: the +1/2 is folded into the window position
-    const double ft = uc - klo_d + (A.round_half ? 0.5 : 0.0);
-    // q_m bounds |q| over the tile: |d| <= half_span and |u| = R_t.
-    const double hs = A.half_span;
-    const double q = (hs * hs + 2.0 * hs * Rt) * inv_r * inv_r;
-    const double a = 0.5 * inv_r * idr;
-    cst[0] = make_float4((float)(2.0 * ux), (float)(2.0 * uy), (float)ft, (float)a);
-    cst[1] = make_float4((float)(-0.125 * inv_r * inv_r * inv_r * idr),
-                         (float)(0.0625 * inv_r * inv_r * inv_r * inv_r * inv_r * idr), (float)(inv_r * inv_r),
-                         (float)(a * (1.0 + (3.0 / 32.0) * q * q)));
-    if (dem) cst[2] = make_float4((float)(2.0 * uz), 0.f, 0.f, 0.f);
-    *klo_out = (int)klo_d;
-    // Truncation error of each series for the worst pixel of the tile, in bins,
-    // against 1e-6 bins (below the fp32 rounding of the window position).
-    const double e2 = Rt * (q * q * q * (1.0 / 64.0) + q * q * q * q * (5.0 / 128.0)) * idr;
-    const double e3 = Rt * q * q * q * q * (5.0 / 128.0) * idr;
-    return (q > 0.25 || e3 > 1e-6) ? 2 : (e2 > 1e-6 ? 1 : 0);
-}
-
-// Per-pulse constants of the fp64-range kernels (tiles whose range extent is too
-// large for the fp32 difference): three double2 per pulse,
-//   (2 ux, 2 uy), (ft, 1/R_t^2), (R_t/dr, 2 uz),
-// and the window position ub = ft + (R_t/dr) (sqrt(1 + q) - 1), q = num / R_t^2,
-// by its binomial series through q^4 (mode 0) or q^7 (mode 1), the shorter one
-// whose first omitted term stays below 1e-7 bins over the tile, else exactly
-// (mode 2).  (1e-7 bins is below the fp32 rounding of the fraction returned.)
-__device__ int pulse_setup_f64(const BpArgs& A, int n, double cx, double cy, double cz, float4* cst, int* klo_out) {
-    double2* cd = reinterpret_cast<double2*>(cst);
-    const double ax = A.pos[3 * (size_t)n], ay = A.pos[3 * (size_t)n + 1], az = A.pos[3 * (size_t)n + 2];
-    const double ux = cx - ax, uy = cy - ay, uz = cz - az;
-    const double Rt = sqrt(ux * ux + uy * uy + uz * uz);
-    const double uc = (Rt - A.r0) * A.inv_dr;
-    const double klo_d = floor(uc - A.half_span_bins) - (double)A.margin_lo;
-    if (!(isfinite(Rt) && Rt > 0.0 && isfinite(uc) && fabs(klo_d) < 1.0e9)) {
-        cd[0] = make_double2(0.0, 0.0);
-        cd[1] = make_double2((double)A.margin_lo + 0.25, 0.0);
-        cd[2] = make_double2(0.0, 0.0);
-        *klo_out = INT32_MIN;
-        return 0;
-    }
-    const double inv_r = 1.0 / Rt;
-    const double ft = uc - klo_d + (A.round_half ? 0.5 : 0.0);
-    const double hs = A.half_span;
-    const double q = (hs * hs + 2.0 * hs * Rt) * inv_r * inv_r;
-    cd[0] = make_double2(2.0 * ux, 2.0 * uy);
-    cd[1] = make_double2(ft, inv_r * inv_r);
-    cd[2] = make_double2(Rt * A.inv_dr, 2.0 * uz); // 2 uz: the terrain kernels' vertical term
-    *klo_out = (int)klo_d;
-    const double q2 = q * q, q4 = q2 * q2, rb = Rt * A.inv_dr; // R_t in bins
-    if (q > 0.25 || rb * (429.0 / 32768.0) * q4 * q4 > 1e-7) return 2;
-    return rb * (7.0 / 256.0) * q4 * q > 1e-7 ? 1 : 0;
-}
-
-// Window position of one pixel for pulse p in the fp64-range kernels: the bin
-// k = floor(ub) and the fraction f = ub - k.
-template <int MODE, bool DEM>
-__device__ __forceinline__ void locate_f64(const float4* cst, int p, double dxd, double dyd, double ddd, double dzd,
-                                           float* f, uint32_t* k) {
-    const double2* cd = reinterpret_cast<const double2*>(cst) + 3 * p;
-    const double2 d0 = cd[0], d1 = cd[1], d2 = cd[2];
-    const double num = fma(dxd, d0.x, fma(dyd, d0.y, DEM ? fma(dzd, d2.y, ddd) : ddd));
-    const double q = num * d1.y;
-    double s; // (sqrt(1 + q) - 1) / q
-    if constexpr (MODE == 2) {
-        s = 1.0 / (1.0 + sqrt(1.0 + q));
-    } else {
-        s = -5.0 / 128.0;
-        if constexpr (MODE == 1) {
-            s = fma(33.0 / 2048.0, q, -21.0 / 1024.0);
-            s = fma(s, q, 7.0 / 256.0);
-            s = fma(s, q, -5.0 / 128.0);
-        }
-        s = fma(s, q, 1.0 / 16.0);
-        s = fma(s, q, -1.0 / 8.0);
-        s = fma(s, q, 0.5);
-    }
-    const double ub = fma(d2.x * q, s, d1.x);
-    const double kd = floor(ub);
-    *k = (uint32_t)kd;
-    *f = (float)(ub - kd);
-}
-
-// Bin position of a pixel within its pulse window: ub = ft + (R - R_t) / dr.
-template <int MODE>
-__device__ __forceinline__ float bin_position(float num, const float4& c0, const float4& c1) {
-    if constexpr (MODE == 0) {
-        return fmaf(num, fmaf(num, c1.x, c1.w), c0.z);
-    } else if constexpr (MODE == 1) {
-        return fmaf(num, fmaf(num, fmaf(num, c1.y, c1.x), c0.w), c0.z);
-    } else {
-        // (R - R_t) / dr = (num / (R_t dr)) / (1 + s) = a num / (1/2 + s/2),  s = sqrt(1 + q)
-        const float s = __builtin_amdgcn_sqrtf(fmaxf(fmaf(num, c1.z, 1.0f), 0.0f));
-        return fmaf(num * c0.w, __builtin_amdgcn_rcpf(fmaf(0.5f, s, 0.5f)), c0.z);
-    }
-}
 
 // Rotation of a complex sample by exp(j 2 pi x), x in revolutions (|x| < 256).
 __device__ __forceinline__ void sincos_rev(float x, float* s, float* c) {
@@ -225,23 +95,6 @@ __device__ __forceinline__ void set_priority(int p) {
     else if (p == 2) __builtin_amdgcn_s_setprio(2);
     else if (p == 1) __builtin_amdgcn_s_setprio(1);
     else __builtin_amdgcn_s_setprio(0);
-}
-
-// Exact nearest-bin decision for one pixel and pulse, in the definition's
-// double-precision operation order (no contraction): floor(u + 1/2).  Inlined:
-// an out-of-line call made the hot loop keep its live registers across the call
-// boundary, 2 % slower although the call itself is rare.
-__device__ __forceinline__ int nearest_bin_fp64(double ax, double ay, double az, double x0, double y0, double z0,
-                                                double dx, double dy, double r0, double dr, int i, int j) {
-    const double x = __dadd_rn(x0, __dmul_rn((double)i, dx));
-    const double y = __dadd_rn(y0, __dmul_rn((double)j, dy));
-    const double ddx = __dsub_rn(x, ax);
-    const double ddy = __dsub_rn(y, ay);
-    const double ddz = __dsub_rn(z0, az);
-    const double s2 = __dadd_rn(__dadd_rn(__dmul_rn(ddx, ddx), __dmul_rn(ddy, ddy)), __dmul_rn(ddz, ddz));
-    const double R = __dsqrt_rn(s2);
-    const double u = __ddiv_rn(__dsub_rn(R, r0), dr);
-    return (int)floor(__dadd_rn(u, 0.5));
 }
 
 // acc += v * (cs + j sn).  ACC_FP32 and ACC_CHUNK64 use four FMAs on the fp32
@@ -277,7 +130,7 @@ __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem,
                                               int p0, int n0, int i_pix, int j_pix0, float dxl, const float* dyv,
                                               const float* ddv, float* accr, float* acci, float* cmpr, float* cmpi,
                                               const float* dzv, const float* hv, double zl, uint32_t wstride,
-                                              const double* pxd) {
+                                              const double* pxd, float tie_lim) {
     constexpr int CS = (DEM || F64) ? 3 : 2;
     float g[G][PPT];
     uint32_t kb[G][PPT];
@@ -293,12 +146,12 @@ __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem,
                 locate_f64<MODE, DEM>(cst, p0 + q, pxd[0], pxd[1 + m], pxd[1 + PPT + m], pxd[1 + 2 * PPT + m], &g[q][m],
                                       &kb[q][m]);
             } else {
-                const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
-                const float ub = bin_position<MODE>(num, c0, c1);
-                g[q][m] = __builtin_amdgcn_fractf(ub);
-                kb[q][m] = (uint32_t)ub;
+                const float num = pixel_num(dxl, dyv[m], ddv[m], dzv[m], c0, c2, DEM);
+                const float ub = bin_position<MODE, DevMath>(num, c0, c1);
+                g[q][m] = DevMath::fract(ub);
+                kb[q][m] = DevMath::to_u32(ub);
             }
-            tie |= fabsf(g[q][m] - 0.5f) > 0.5f - A.tie_eps;
+            tie |= fabsf(g[q][m] - 0.5f) > tie_lim;
         }
     }
     if (tie) {
@@ -307,10 +160,10 @@ __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem,
             const size_t pn = 3 * (size_t)(n0 + p0 + q);
 #pragma unroll
             for (int m = 0; m < PPT; ++m) {
-                if (fabsf(g[q][m] - 0.5f) > 0.5f - A.tie_eps) {
+                if (fabsf(g[q][m] - 0.5f) > tie_lim) {
                     const double zp = DEM ? A.z0 + (double)hv[m] : zl; // the pixel's height
-                    const int kabs = nearest_bin_fp64(A.pos[pn], A.pos[pn + 1], A.pos[pn + 2], A.x0, A.y0, zp, A.dx,
-                                                      A.dy, A.r0, A.dr, i_pix, j_pix0 + BP_WAVES * m);
+                    const int kabs = nearest_bin_fp64<DevMath>(A.pos[pn], A.pos[pn + 1], A.pos[pn + 2], A.x0, A.y0, zp,
+                                                               A.dx, A.dy, A.r0, A.dr, i_pix, j_pix0 + BP_WAVES * m);
                     int kr = kabs - klo_s[p0 + q];
                     kr = kr < 0 ? 0 : (kr > A.win - 1 ? A.win - 1 : kr);
                     g[q][m] = g[q][m] + (float)((int)kb[q][m] - kr); // = ub - kr
@@ -337,7 +190,7 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
                                                  const int* klo_s, int np, int n0, int i_pix, int j_pix0,
                                                  float dxl, const float* dyv, const float* ddv, float* accr,
                                                  float* acci, float* cmpr, float* cmpi, const float* dzv,
-                                                 const float* hv, double zl, const double* pxd) {
+                                                 const float* hv, double zl, const double* pxd, float tie_lim) {
     const int eb = entry_bytes<INTERP>();
     const uint32_t wstride = (uint32_t)(A.win * eb);
     const float kappa = A.kappa;
@@ -347,10 +200,10 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
         for (; p + G <= np; p += G)
             nearest_group<G, MODE, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, p, n0, i_pix, j_pix0, dxl,
                                                                    dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl,
-                                                                   wstride, pxd);
+                                                                   wstride, pxd, tie_lim);
         for (; p < np; ++p)
             nearest_group<1, MODE, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, p, n0, i_pix, j_pix0, dxl, dyv, ddv, accr,
-                                                  acci, cmpr, cmpi, dzv, hv, zl, wstride, pxd);
+                                                  acci, cmpr, cmpi, dzv, hv, zl, wstride, pxd, tie_lim);
         return;
     }
     constexpr int kUnroll = F64 ? BP_PUNROLL_F64 : (INTERP == SARBP_LINEAR ? BP_PUNROLL_LINEAR : BP_PUNROLL_SINC8);
@@ -369,10 +222,10 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
                 if constexpr (F64) {
                     locate_f64<MODE, DEM>(cst, p, pxd[0], pxd[1 + m], pxd[1 + PPT + m], pxd[1 + 2 * PPT + m], &f, &kw);
                 } else {
-                    const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
-                    const float ub = bin_position<MODE>(num, c0, c1);
-                    f = __builtin_amdgcn_fractf(ub);
-                    kw = (uint32_t)ub;
+                    const float num = pixel_num(dxl, dyv[m], ddv[m], dzv[m], c0, c2, DEM);
+                    const float ub = bin_position<MODE, DevMath>(num, c0, c1);
+                    f = DevMath::fract(ub);
+                    kw = DevMath::to_u32(ub);
                 }
                 const uint32_t addr = (kw << 4) + wbase;
                 const float4 ad = *reinterpret_cast<const float4*>(smem + addr);
@@ -394,10 +247,10 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
                 if constexpr (F64) {
                     locate_f64<MODE, DEM>(cst, p, pxd[0], pxd[1 + m], pxd[1 + PPT + m], pxd[1 + 2 * PPT + m], &f, &kw);
                 } else {
-                    const float num = fmaf(dxl, c0.x, fmaf(dyv[m], c0.y, DEM ? fmaf(dzv[m], c2.x, ddv[m]) : ddv[m]));
-                    const float ub = bin_position<MODE>(num, c0, c1);
-                    f = __builtin_amdgcn_fractf(ub);
-                    kw = (uint32_t)ub;
+                    const float num = pixel_num(dxl, dyv[m], ddv[m], dzv[m], c0, c2, DEM);
+                    const float ub = bin_position<MODE, DevMath>(num, c0, c1);
+                    f = DevMath::fract(ub);
+                    kw = DevMath::to_u32(ub);
                 }
                 const float g = f - 0.5f;
                 const float4* e = reinterpret_cast<const float4*>(smem + ((kw << 6) + wbase));
@@ -450,12 +303,11 @@ __device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int n
     const int W = A.win, Wu = W / B, nr = A.n_range;
     const int nu = np * Wu;
     for (int u = tid; u < nu; u += BP_THREADS) {
-        const int p = (int)__umulhi((uint32_t)u, A.win_magic);
-        const int klo = klo_s[p];
-        const bool bad = (klo == INT32_MIN);
-        const int k = (bad ? 0 : klo) + B * (u - (int)__umul24((uint32_t)p, (uint32_t)Wu));
+        int p, k;
+        bool bad;
+        stage_step<DevMath, B>(A, klo_s, u, Wu, &p, &k, &bad);
         const float2* row = A.echo + (size_t)(n0 + p) * (size_t)nr;
-        const int ke = bad ? nr + 8 : (k < -4 ? 0 : (k > nr + 4 - B ? nr + 8 - B : k + 4));
+        const int ke = carrier_index<B>(k, nr, bad);
         const float2 c0 = A.phase[ke];
         if constexpr (INTERP == SARBP_LINEAR) {
             const float2 c1 = A.phase[ke + 1];
@@ -522,22 +374,18 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     const int gb = (int)blockIdx.x - group * A.group_blocks;
     const int pb = group * A.split_len;             // this group's first pulse
     const int pn = min(A.split_len, A.n - pb);      // its pulses (a trailing group may have none)
-    const int layer = gb / A.ntiles;
-    int tile = gb - layer * A.ntiles;
-    const int nt8 = (A.ntiles / 8) * 8;
-    if (tile < nt8) tile = (tile & 7) * (nt8 / 8) + (tile >> 3);
-    const int tx = tile % A.tiles_x, ty = tile / A.tiles_x;
-    const int i0 = tx * BP_TX, j0 = ty * (BP_WAVES * PPT);
+    const TileFrame T = tile_frame<PPT>(A, gb);
+    const int layer = T.layer, i0 = T.i0, j0 = T.j0;
 
     // Tile centre (fp64): the centre of the part of the tile inside the grid, which
     // brings the pixels of a ragged edge tile (or of a grid smaller than a tile)
     // closer to it than the full tile's half diagonal.  Lanes past the grid's edge
     // take the offsets of the last column or row, so every lane's range stays
     // within the staged window; their results are not stored.
-    const int i_last = min(i0 + BP_TX, A.nx) - 1, j_last = min(j0 + BP_WAVES * PPT, A.ny) - 1;
-    const double cxp = 0.5 * (double)(i0 + i_last), cyp = 0.5 * (double)(j0 + j_last);
-    const double cx = A.x0 + cxp * A.dx, cy = A.y0 + cyp * A.dy;
-    const double zl = A.z0 + (double)layer * A.dz; // this layer's height
+    const int i_last = T.i_last, j_last = T.j_last;
+    const double cxp = T.cxp, cyp = T.cyp;
+    const double cx = T.cx, cy = T.cy;
+    const double zl = T.zl; // this layer's height
     double cz = zl;
     const int i_off = min(i0 + lane, i_last); // the pixel column whose offsets this lane uses
     int j_off[PPT];
@@ -618,11 +466,14 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     float4* cst = reinterpret_cast<float4*>(smem + (size_t)P * W * entry_bytes<INTERP>());
     int* klo_s = reinterpret_cast<int*>(cst + CS * P);
     int* prio_s = klo_s + P;
-    // The accuracy mode of a chunk is the OR of its pulses' modes.  The words are
-    // double-buffered: chunk c ORs into mode_s[c & 1] and clears mode_s[(c + 1) & 1],
-    // which the previous chunk finished reading before its last barrier.
+    // The accuracy mode of a chunk is the OR of its pulses' modes, and its nearest
+    // tie band follows from the largest of their range-term sizes rho.  The words
+    // are double-buffered: chunk c writes mode_s[c & 1] and rho_s[c & 1] and clears
+    // the other pair, which the previous chunk finished reading before its last
+    // barrier.  (rho >= 0, so its float bits order as integers.)
     int* mode_s = prio_s + 1;
-    if (tid == 0) mode_s[0] = mode_s[1] = 0;
+    int* rho_s = mode_s + 2;
+    if (tid == 0) mode_s[0] = mode_s[1] = rho_s[0] = rho_s[1] = 0;
     __syncthreads();
 
     // The first chunk is half size on alternate workgroups: both placements of a
@@ -631,13 +482,18 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     for (int n0 = 0, np = 0, c = 0; n0 < (bad_tile ? 0 : pn); n0 += np, ++c) {
         np = min((n0 == 0 && stagger) ? max(1, P >> 1) : P, pn - n0);
         if (tid < np) {
-            const int need = F64 ? pulse_setup_f64(A, pb + n0 + tid, cx, cy, cz, cst + CS * tid, klo_s + tid)
-                                 : pulse_setup(A, pb + n0 + tid, cx, cy, cz, cst + CS * tid, klo_s + tid, DEM);
+            const size_t pa = 3 * (size_t)(pb + n0 + tid);
+            const double ax = A.pos[pa], ay = A.pos[pa + 1], az = A.pos[pa + 2];
+            float rho = 0.f;
+            const int need = F64 ? pulse_setup_f64(A, ax, ay, az, cx, cy, cz, cst + CS * tid, klo_s + tid)
+                                 : pulse_setup(A, ax, ay, az, cx, cy, cz, cst + CS * tid, klo_s + tid, &rho, DEM);
             if (need) atomicOr(mode_s + (c & 1), need);
+            if constexpr (INTERP == SARBP_NEAREST && !F64) atomicMax(rho_s + (c & 1), __float_as_int(rho));
         }
         if (tid == 0) {
             *prio_s = chunk_priority(A, n0, pn);
             mode_s[(c + 1) & 1] = 0;
+            rho_s[(c + 1) & 1] = 0;
         }
         __syncthreads();
         stage_chunk<INTERP>(A, smem, klo_s, np, pb + n0, tid);
@@ -645,15 +501,22 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         set_priority(*prio_s);
         const int mode = __builtin_amdgcn_readfirstlane(mode_s[c & 1]); // the same word for every lane
         const int m1 = mode & 1, m2 = mode & 2;
+        const int mi = m2 ? 2 : (m1 ? 1 : 0);
+        // nearest: |fract(ub) - 1/2| beyond tie_lim means ub is within the tie band of an integer
+        float tie_lim = 0.f;
+        if constexpr (INTERP == SARBP_NEAREST) {
+            const float rho = __int_as_float(__builtin_amdgcn_readfirstlane(rho_s[c & 1]));
+            tie_lim = 0.5f - fmaf(A.tie_rho[mi], rho, A.tie_base[mi]);
+        }
         if (m2)
             accumulate_chunk<INTERP, 2, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, np, pb + n0, i0 + lane, j0 + wave, dxl, dyv,
-                                                        ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd);
+                                                        ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, tie_lim);
         else if (m1)
             accumulate_chunk<INTERP, 1, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, np, pb + n0, i0 + lane, j0 + wave, dxl, dyv,
-                                                        ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd);
+                                                        ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, tie_lim);
         else
             accumulate_chunk<INTERP, 0, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, np, pb + n0, i0 + lane, j0 + wave, dxl, dyv,
-                                                        ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd);
+                                                        ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, tie_lim);
         if constexpr (ACC == SARBP_ACC_CHUNK64) {
 #pragma unroll
             for (int m = 0; m < PPT; ++m) {
@@ -778,8 +641,8 @@ int sarbp_split_count(const sarbp_plan* plan, int n) {
     // Pulse groups so that the launch has about two workgroups per CU, at most 16,
     // each of at least 32 pulses; grids that already fill the GPU are not split.
     const int64_t layers = plan->p.nz > 1 ? plan->p.nz : 1;
-    const int64_t blocks = (int64_t)plan->tiles_x * plan->tiles_y * layers;
-    int64_t s = (2 * (int64_t)plan->n_cu) / blocks;
+    const int64_t blocks = (int64_t)plan->L.tiles_x * plan->L.tiles_y * layers;
+    int64_t s = (2 * (int64_t)plan->L.n_cu) / blocks;
     if (s > 16) s = 16;
     if (s > n / 32) s = n / 32;
     return s < 2 ? 1 : (int)s;
@@ -802,18 +665,16 @@ int sarbp_bp_allow_lds(int interp, int accum, bool dem, int ppt, bool f64, size_
 int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* echo, const float* dem,
                     float2* image, int n, int accumulate, hipStream_t stream, float2* workspace, int nsplit) {
     const sarbp_params& p = plan->p;
+    const BpLayout& L = plan->L;
     BpArgs A;
+    sarbp_bp_args(p, L, &A);
     A.pos = pos;
     A.echo = echo;
     A.image = image;
     A.phase = plan->phase_tab;
+    A.progress = plan->progress;
+    A.dem = dem;
     A.n = n;
-    A.n_range = p.n_range;
-    A.nx = p.nx;
-    A.ny = p.ny;
-    A.tiles_x = plan->tiles_x;
-    A.ntiles = plan->tiles_x * plan->tiles_y;
-    A.group_blocks = A.ntiles * (p.nz > 1 ? p.nz : 1);
     const size_t elems = (size_t)(p.nz > 1 ? p.nz : 1) * (size_t)p.ny * (size_t)p.nx;
     const bool split = nsplit > 1 && workspace != nullptr;
     if (!split) nsplit = 1;
@@ -823,54 +684,22 @@ int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* ech
     if (split) {
         A.image = workspace; // partial images, written over; summed into `image` below
         A.accumulate = 0;
-    }
-    A.dz = p.nz > 1 ? p.dz : 0.0;
-    A.win = plan->win;
-    {
-        const uint64_t wu = (uint64_t)(plan->p.interp == SARBP_SINC8 ? plan->win : plan->win / 2);
-        A.win_magic = (uint32_t)(((1ull << 32) + wu - 1) / wu);
-    }
-    A.margin_lo = plan->margin_lo;
-    A.chunk = plan->chunk;
-    if (!split) A.accumulate = accumulate;
-    A.slots = plan->n_cu;
-    A.progress = plan->progress;
-    A.r0 = p.r0;
-    A.dr = p.dr;
-    A.inv_dr = 1.0 / p.dr;
-    A.x0 = p.x0;
-    A.y0 = p.y0;
-    A.z0 = p.z0;
-    A.dx = p.dx;
-    A.dy = p.dy;
-    A.half_span = plan->half_span;
-    A.dem = dem;
-    A.dem_relief = p.dem_relief;
-    for (int i = 0; i < 32; ++i) A.sinc_poly[i] = plan->sinc_poly[i];
-    A.half_span_bins = plan->half_span / p.dr;
-    A.kappa = (float)(2.0 * p.dr / p.wavelength);
-    A.tie_eps = 4e-5f;
-    A.round_half = p.interp == SARBP_NEAREST ? 1 : 0;
-    {
-        // exp(-j pi kappa): the nearest path measures the phase from half a bin below the sample
-        const double k = 2.0 * p.dr / p.wavelength;
-        const double fr = 0.5 * k - floor(0.5 * k);
-        A.half_rot = make_float2((float)cos(-2.0 * 3.14159265358979323846 * fr),
-                                 (float)sin(-2.0 * 3.14159265358979323846 * fr));
+    } else {
+        A.accumulate = accumulate;
     }
     const bool d = dem != nullptr;
     switch (p.interp) {
         case SARBP_NEAREST:
-            d ? launch<SARBP_NEAREST, true>(A, p.accum, plan->ppt, plan->f64, plan->lds_bytes, stream)
-              : launch<SARBP_NEAREST, false>(A, p.accum, plan->ppt, plan->f64, plan->lds_bytes, stream);
+            d ? launch<SARBP_NEAREST, true>(A, p.accum, L.ppt, L.f64, L.lds_bytes, stream)
+              : launch<SARBP_NEAREST, false>(A, p.accum, L.ppt, L.f64, L.lds_bytes, stream);
             break;
         case SARBP_LINEAR:
-            d ? launch<SARBP_LINEAR, true>(A, p.accum, plan->ppt, plan->f64, plan->lds_bytes, stream)
-              : launch<SARBP_LINEAR, false>(A, p.accum, plan->ppt, plan->f64, plan->lds_bytes, stream);
+            d ? launch<SARBP_LINEAR, true>(A, p.accum, L.ppt, L.f64, L.lds_bytes, stream)
+              : launch<SARBP_LINEAR, false>(A, p.accum, L.ppt, L.f64, L.lds_bytes, stream);
             break;
         default:
-            d ? launch<SARBP_SINC8, true>(A, p.accum, plan->ppt, plan->f64, plan->lds_bytes, stream)
-              : launch<SARBP_SINC8, false>(A, p.accum, plan->ppt, plan->f64, plan->lds_bytes, stream);
+            d ? launch<SARBP_SINC8, true>(A, p.accum, L.ppt, L.f64, L.lds_bytes, stream)
+              : launch<SARBP_SINC8, false>(A, p.accum, L.ppt, L.f64, L.lds_bytes, stream);
             break;
     }
     if (hipGetLastError() != hipSuccess) return SARBP_EDEVICE;

@@ -1,0 +1,255 @@
+// Host-side emulation of the backprojection kernels' index and window-position
+// arithmetic (sarbp_check_indices, include/sarbp.h).  It runs, on the CPU, the
+// same per-tile frame, per-pulse set-up, staging index steps and per-pixel window
+// positions as the kernels (shared through sarbp_geom.h, instantiated with the
+// host math policy), and checks every LDS window index and staging index against
+// its range.  For nearest interpolation it also replays the fp32 bin decisions
+// and the tie band, and compares the bins they keep with the definition's
+// floor(u + 1/2) in double precision.
+//
+// The page "基于GPU的SAR后向投影成像优化与CUDA加速实践" (GPU-based SAR
+// backprojection), section 4.4, names index errors that read outside the echo
+// window as the usual source of a noisy image and recommends checking for them
+// with a memory checker; this emulation is that check for the kernels' arithmetic,
+// run on the host over a caller's own geometry.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "sarbp_geom.h"
+#include "sarbp_internal.h"
+
+namespace {
+
+struct Checker {
+    const sarbp_params& p;
+    const BpLayout& L;
+    BpArgs A;
+    const double* pos;
+    int n;
+    const float* dem;
+    sarbp_index_report* r;
+
+    Checker(const sarbp_params& p_, const BpLayout& L_, const double* pos_, int n_, const float* dem_,
+            sarbp_index_report* r_)
+        : p(p_), L(L_), pos(pos_), n(n_), dem(dem_), r(r_) {
+        sarbp_bp_args(p, L, &A);
+        A.n = n;
+        A.split_len = n;
+    }
+
+    // The definition's fractional bin u of pixel (i, j) at height z for pulse q.
+    double def_bin(int q, int i, int j, double z) const {
+        const double* a = pos + 3 * (size_t)q;
+        return definition_bin<HostMath>(a[0], a[1], a[2], A.x0, A.y0, z, A.dx, A.dy, A.r0, A.dr, i, j);
+    }
+
+    void stage_check(const int* klo_s, int np) {
+        const int B = p.interp == SARBP_SINC8 ? 1 : 2;
+        const int wu = A.win / B;
+        for (int u = 0; u < np * wu; ++u) {
+            int pp, k;
+            bool bad;
+            if (B == 1)
+                stage_step<HostMath, 1>(A, klo_s, u, wu, &pp, &k, &bad);
+            else
+                stage_step<HostMath, 2>(A, klo_s, u, wu, &pp, &k, &bad);
+            bool ok = pp == u / wu && pp >= 0 && pp < np;
+            if (ok) {
+                const int ke = B == 1 ? carrier_index<1>(k, A.n_range, bad) : carrier_index<2>(k, A.n_range, bad);
+                ok = ke >= 0 && ke + B - 1 <= A.n_range + 9;
+                if (!bad) ok = ok && k - klo_s[pp] >= 0 && k - klo_s[pp] + B - 1 <= A.win - 1;
+            }
+            if (!ok) ++r->staging_violations;
+        }
+    }
+
+    // One window position of a pixel: bin k (LDS entry) and fraction f.
+    template <int MODE, bool DEM, bool F64>
+    void locate(const float4* cst, int pl, float dxl, float dy, float dd, float dz, const double* pxd, int m,
+                int ppt, uint32_t* k, float* f, double* ub) const {
+        if (F64) {
+            locate_f64<MODE, DEM>(cst, pl, pxd[0], pxd[1 + m], pxd[1 + ppt + m], pxd[1 + 2 * ppt + m], f, k);
+            *ub = (double)*k + (double)*f;
+        } else {
+            const int CS = DEM ? 3 : 2;
+            const float4 c0 = cst[CS * pl], c1 = cst[CS * pl + 1], c2 = DEM ? cst[CS * pl + 2] : c1;
+            const float num = pixel_num(dxl, dy, dd, dz, c0, c2, DEM);
+            const float u = bin_position<MODE, HostMath>(num, c0, c1);
+            *f = HostMath::fract(u);
+            *k = HostMath::to_u32(u);
+            *ub = (double)u;
+        }
+    }
+
+    template <int PPT, bool DEM, bool F64>
+    void run() {
+        const int CS = (DEM || F64) ? 3 : 2;
+        const int P = A.chunk;
+        std::vector<float4> cst((size_t)CS * P);
+        std::vector<int> klo(P);
+        std::vector<float> rho(P);
+        std::vector<int> mode(P);
+        const int nb = A.group_blocks;
+        const bool nearest = p.interp == SARBP_NEAREST;
+        for (int b = 0; b < nb; ++b) {
+            const TileFrame T = tile_frame<PPT>(A, b);
+            // Lane offsets, as in the kernel: lanes past the grid's edge repeat the last column or row.
+            float dxl[BP_TX], dyv[BP_WAVES][PPT], ddv[BP_TX][BP_WAVES][PPT], dzv[BP_TX][BP_WAVES][PPT];
+            double pxd[BP_TX][BP_WAVES][1 + 3 * PPT];
+            float hv[BP_TX][BP_WAVES][PPT];
+            double cz = T.zl;
+            bool bad_tile = false;
+            double hc = 0.0;
+            if (DEM) {
+                float hmin = INFINITY, hmax = -INFINITY;
+                for (int lane = 0; lane < BP_TX; ++lane)
+                    for (int w = 0; w < BP_WAVES; ++w)
+                        for (int m = 0; m < PPT; ++m) {
+                            const int io = std::min(T.i0 + lane, T.i_last);
+                            const int jo = std::min(T.j0 + w + BP_WAVES * m, T.j_last);
+                            hv[lane][w][m] = dem[(size_t)jo * A.nx + io];
+                            hmin = fminf(hmin, hv[lane][w][m]);
+                            hmax = fmaxf(hmax, hv[lane][w][m]);
+                        }
+                bad_tile = !((double)hmax - (double)hmin <= A.dem_relief);
+                hc = 0.5 * ((double)hmin + (double)hmax);
+                cz = A.z0 + hc;
+            }
+            if (bad_tile) {
+                ++r->nan_tiles;
+                continue;
+            }
+            for (int lane = 0; lane < BP_TX; ++lane) {
+                const int io = std::min(T.i0 + lane, T.i_last);
+                const double ddx = ((double)io - T.cxp) * A.dx;
+                dxl[lane] = (float)ddx;
+                for (int w = 0; w < BP_WAVES; ++w)
+                    for (int m = 0; m < PPT; ++m) {
+                        const int jo = std::min(T.j0 + w + BP_WAVES * m, T.j_last);
+                        const double ddy = ((double)jo - T.cyp) * A.dy;
+                        const double ddz = DEM ? (double)hv[lane][w][m] - hc : 0.0;
+                        dyv[w][m] = (float)ddy;
+                        ddv[lane][w][m] = (float)(ddx * ddx + ddy * ddy + (DEM ? ddz * ddz : 0.0));
+                        dzv[lane][w][m] = (float)ddz;
+                        double* x = pxd[lane][w];
+                        x[0] = ddx;
+                        x[1 + m] = ddy;
+                        x[1 + PPT + m] = ddx * ddx + ddy * ddy + (DEM ? ddz * ddz : 0.0);
+                        x[1 + 2 * PPT + m] = ddz;
+                    }
+            }
+            const int stagger = BP_STAGGER ? ((b / A.slots) ^ (b >> 3)) & 1 : 0;
+            for (int n0 = 0, np = 0; n0 < n; n0 += np) {
+                np = std::min((n0 == 0 && stagger) ? std::max(1, P >> 1) : P, n - n0);
+                int cmode = 0;
+                float crho = 0.f;
+                for (int t = 0; t < np; ++t) {
+                    const double* a = pos + 3 * (size_t)(n0 + t);
+                    float rh = 0.f;
+                    mode[t] = F64 ? pulse_setup_f64(A, a[0], a[1], a[2], T.cx, T.cy, cz, &cst[(size_t)CS * t], &klo[t])
+                                  : pulse_setup(A, a[0], a[1], a[2], T.cx, T.cy, cz, &cst[(size_t)CS * t], &klo[t],
+                                                &rh, DEM);
+                    cmode |= mode[t];
+                    if (!F64) crho = std::max(crho, rh);
+                }
+                const int mi = (cmode & 2) ? 2 : (cmode & 1);
+                ++r->mode_chunks[mi];
+                stage_check(klo.data(), np);
+                // the tie band (twice the error bound of the chunk's window positions)
+                const float band = fmaf(A.tie_rho[mi], crho, A.tie_base[mi]);
+                const float tie_lim = 0.5f - band;
+                if (nearest) r->tie_band_max = std::max(r->tie_band_max, band);
+                if (mi == 2)
+                    pixels<2, PPT, DEM, F64>(T, np, n0, cst.data(), klo.data(), dxl, dyv, ddv, dzv, pxd, hv, hc,
+                                             tie_lim, band);
+                else if (mi == 1)
+                    pixels<1, PPT, DEM, F64>(T, np, n0, cst.data(), klo.data(), dxl, dyv, ddv, dzv, pxd, hv, hc,
+                                             tie_lim, band);
+                else
+                    pixels<0, PPT, DEM, F64>(T, np, n0, cst.data(), klo.data(), dxl, dyv, ddv, dzv, pxd, hv, hc,
+                                             tie_lim, band);
+            }
+        }
+    }
+
+    template <int MODE, int PPT, bool DEM, bool F64>
+    void pixels(const TileFrame& T, int np, int n0, const float4* cst, const int* klo, const float* dxl,
+                const float (*dyv)[PPT], const float (*ddv)[BP_WAVES][PPT], const float (*dzv)[BP_WAVES][PPT],
+                const double (*pxd)[BP_WAVES][1 + 3 * PPT], const float (*hv)[BP_WAVES][PPT], double hc,
+                float tie_lim, float band) {
+        const bool nearest = p.interp == SARBP_NEAREST;
+        const double half = nearest ? 0.5 : 0.0;
+        for (int t = 0; t < np; ++t) {
+            const bool bad = klo[t] == INT32_MIN;
+            for (int lane = 0; lane < BP_TX; ++lane) {
+                const int i = T.i0 + lane;
+                for (int w = 0; w < BP_WAVES; ++w)
+                    for (int m = 0; m < PPT; ++m) {
+                        const int j = T.j0 + w + BP_WAVES * m;
+                        uint32_t k;
+                        float f;
+                        double ub;
+                        locate<MODE, DEM, F64>(cst, t, dxl[lane], dyv[w][m], ddv[lane][w][m], dzv[lane][w][m],
+                                               pxd[lane][w], m, PPT, &k, &f, &ub);
+                        ++r->decisions;
+                        if (bad) continue;
+                        if (!(ub >= 0.0) || !(k <= (uint32_t)(A.win - 1))) ++r->window_violations;
+                        r->min_position = std::min(r->min_position, ub);
+                        r->max_position_margin = std::max(r->max_position_margin, ub - (double)A.win);
+                        if (i >= A.nx || j >= A.ny) continue; // lanes past the edge: results not stored
+                        const double z = DEM ? A.z0 + (double)hv[lane][w][m] : T.zl;
+                        const double u = def_bin(n0 + t, i, j, z);
+                        const double want = u - (double)klo[t] + half; // the exact window position
+                        const double err = fabs(ub - want);
+                        r->max_position_error = std::max(r->max_position_error, err);
+                        r->max_error_to_band = std::max(r->max_error_to_band, err / (0.5 * (double)band));
+                        if (!nearest) continue;
+                        const int kdef = (int)floor(u + 0.5);
+                        if (fabsf(f - 0.5f) > tie_lim) {
+                            ++r->nearest_rechecks;
+                            const int kr = kdef - klo[t];
+                            if (kr < 0 || kr > A.win - 1) ++r->nearest_recheck_clamped;
+                        } else if ((int)k + klo[t] != kdef) {
+                            ++r->nearest_escapes;
+                        }
+                    }
+            }
+        }
+        (void)hc;
+    }
+};
+
+} // namespace
+
+extern "C" int sarbp_check_indices(const sarbp_params* params, int32_t n_cu, const double* positions_h, int32_t n,
+                                   const float* dem_h, sarbp_index_report* report) {
+    if (report == nullptr || positions_h == nullptr || n < 1) return SARBP_EINVAL;
+    memset(report, 0, sizeof(*report));
+    int st = sarbp_validate(params);
+    if (st != SARBP_OK) return st;
+    if (n > params->n_pulses) return SARBP_EINVAL;
+    if (dem_h != nullptr && !(params->dem_relief > 0.0)) return SARBP_EINVAL;
+    BpLayout L;
+    st = sarbp_plan_layout(*params, n_cu > 0 ? n_cu : 256, &L);
+    if (st != SARBP_OK) return st;
+    report->window = L.win;
+    report->chunk = L.chunk;
+    report->pixels_per_lane = L.ppt;
+    report->fp64_ranges = L.f64;
+    report->min_position = INFINITY;
+    report->max_position_margin = -INFINITY;
+    Checker c(*params, L, positions_h, n, dem_h, report);
+    const bool dem = dem_h != nullptr;
+    if (L.f64) {
+        dem ? c.run<2, true, true>() : c.run<2, false, true>();
+    } else if (L.ppt == 1) {
+        dem ? c.run<1, true, false>() : c.run<1, false, false>();
+    } else {
+        dem ? c.run<2, true, false>() : c.run<2, false, false>();
+    }
+    return SARBP_OK;
+}

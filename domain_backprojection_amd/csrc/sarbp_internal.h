@@ -45,12 +45,12 @@
 #define BP_LDS_BUDGET 76000 // bytes per workgroup: two 1024-lane workgroups per CU fit in 160 KiB
 #endif
 
-struct sarbp_plan {
-    sarbp_params p;
-    int device;
-    // exp(+j 4 pi (r0 + k dr) / lambda) for k = -4 .. n_range + 3, stored at [k + 4]
-    float2* phase_tab;
-    // backprojection launch geometry
+// Backprojection launch geometry of a plan: a function of its parameters and
+// the device's compute-unit count alone (sarbp_plan_layout), so that the host
+// emulation of the kernels' index arithmetic (sarbp_check_indices) can build it
+// without a device.
+struct BpLayout {
+    int n_cu;         // compute units the layout is for
     int tiles_x, tiles_y;
     int ppt;          // backprojection pixels per lane (1 or 2): tiles of 64 x 16 ppt
     int f64;          // 1: range differences in fp64 (windows of many carrier cycles; ppt = 2)
@@ -58,12 +58,19 @@ struct sarbp_plan {
     int margin_lo;    // bins below the tile's lowest range kept in the window
     int chunk;        // pulses per LDS step
     size_t lds_bytes; // dynamic LDS per workgroup
-    int n_cu;         // compute units of the plan's device
-    int* progress;    // [2 * n_cu] per-workgroup pulse progress (scheduling hints only)
+    double half_span; // half tile diagonal [m]
     // sinc8: monomial coefficients in g = f - 1/2 of the degree-7 interpolant of
     // tap t - 3 (t = 0..3) of the windowed sinc, coefficient j at [4 j + t]
     float sinc_poly[32];
-    double half_span; // half tile diagonal [m]
+};
+
+struct sarbp_plan {
+    sarbp_params p;
+    int device;
+    BpLayout L;
+    // exp(+j 4 pi (r0 + k dr) / lambda) for k = -4 .. n_range + 3, stored at [k + 4]
+    float2* phase_tab;
+    int* progress;    // [2 * n_cu] per-workgroup pulse progress (scheduling hints only)
     // range compression
     int rc_log2;       // log2(n_fast), 0 when disabled
     float2* rc_filter; // conj(FFT(ref)) * W / n_fast
@@ -93,10 +100,29 @@ struct BpArgs {
     const float* dem;      // [ny][nx] pixel heights above z0 (terrain kernels), else null
     double dem_relief;     // bound on one tile's height range (terrain kernels)
     float kappa;           // 2 dr / lambda: phase cycles per bin
-    float tie_eps;         // nearest: fp64 recheck band around a rounding tie [bins]
+    // nearest: fp64 recheck band around a rounding tie [bins], per accuracy mode:
+    // tie_base[m] + tie_rho[m] * (the chunk's largest range-term size, in bins)
+    float tie_base[3], tie_rho[3];
     int round_half;        // nearest: window positions carry u + 1/2
     float2 half_rot;       // nearest: exp(-j pi kappa), folded into the staged samples
 };
+
+// Largest nearest tie band [bins] the fp32 kernels accept on a 64 x 32 tile; a
+// plan beyond it takes the fp64-range kernels, whose band is 1e-6 bins.  (The
+// band's fp64 rechecks cost about 100 instructions each: at 2.5e-4 bins that is
+// about one update in five.)
+#ifndef BP_NEAREST_TIE_MAX
+#define BP_NEAREST_TIE_MAX 2.5e-4
+#endif
+
+// Validate parameters (SARBP_OK, SARBP_EINVAL, SARBP_EUNSUPPORTED); no device use.
+int sarbp_validate(const sarbp_params* p);
+// The backprojection layout of p on a device of n_cu compute units (SARBP_OK or
+// SARBP_EUNSUPPORTED); p must have passed sarbp_validate.
+int sarbp_plan_layout(const sarbp_params& p, int n_cu, BpLayout* L);
+// The launch-independent fields of the backprojection kernels' arguments
+// (pointers, pulse counts and split fields are left for the launch).
+void sarbp_bp_args(const sarbp_params& p, const BpLayout& L, BpArgs* A);
 
 int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* echo, const float* dem,
                     float2* image, int n, int accumulate, hipStream_t stream, float2* workspace = nullptr,

@@ -11,6 +11,7 @@
 #include <new>
 #include <vector>
 
+#include "sarbp_geom.h"
 #include "sarbp_internal.h"
 
 int sarbp_rc_prepare_device();
@@ -47,7 +48,9 @@ void fft_host(std::vector<std::complex<double>>& a) {
     }
 }
 
-int validate(const sarbp_params* p) {
+} // namespace
+
+int sarbp_validate(const sarbp_params* p) {
     if (p == nullptr) return SARBP_EINVAL;
     if (p->n_pulses < 1 || p->nx < 1 || p->ny < 1) return SARBP_EINVAL;
     if (p->interp < SARBP_NEAREST || p->interp > SARBP_SINC8) return SARBP_EINVAL;
@@ -75,6 +78,8 @@ int validate(const sarbp_params* p) {
     }
     return SARBP_OK;
 }
+
+namespace {
 
 template <typename T>
 int upload(const std::vector<T>& host, T** dev) {
@@ -183,23 +188,9 @@ void sinc8_polynomials(float* out) {
 
 } // namespace
 
-extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
-    if (out == nullptr) return SARBP_EINVAL;
-    *out = nullptr;
-    int st = validate(params);
-    if (st != SARBP_OK) return st;
-    sarbp_plan* plan = new (std::nothrow) sarbp_plan();
-    if (plan == nullptr) return SARBP_ENOMEM;
-    memset(plan, 0, sizeof(*plan));
-    plan->p = *params;
-    const sarbp_params& p = plan->p;
-    if (hipGetDevice(&plan->device) != hipSuccess ||
-        hipDeviceGetAttribute(&plan->n_cu, hipDeviceAttributeMultiprocessorCount, plan->device) != hipSuccess) {
-        delete plan;
-        return SARBP_EDEVICE;
-    }
-    if (plan->n_cu < 1) plan->n_cu = 1;
-
+int sarbp_plan_layout(const sarbp_params& p, int n_cu, BpLayout* L) {
+    memset(L, 0, sizeof(*L));
+    L->n_cu = n_cu < 1 ? 1 : n_cu;
     // Backprojection tiling and LDS window size.  Every pixel of a tile lies
     // within half_span of the tile centre, so (triangle inequality) its range
     // lies within R_t +- half_span and its bin within the window below.
@@ -209,8 +200,8 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     // slower, so large grids keep two).  Terrain plans keep 64 x 32 tiles: the
     // relief bound and its NaN blocks are defined on them.
     const int64_t layers = p.nz > 1 ? p.nz : 1;
-    plan->tiles_x = (p.nx + BP_TX - 1) / BP_TX;
-    const int64_t tiles2 = (int64_t)plan->tiles_x * ((p.ny + 2 * BP_WAVES - 1) / (2 * BP_WAVES)) * layers;
+    L->tiles_x = (p.nx + BP_TX - 1) / BP_TX;
+    const int64_t tiles2 = (int64_t)L->tiles_x * ((p.ny + 2 * BP_WAVES - 1) / (2 * BP_WAVES)) * layers;
     // The fp32 kernels carry a pixel's window position (0 .. W bins) to about 2^-24
     // of the window, and its phase to 2^-24 of the kappa W carrier cycles across
     // the window (kappa = 2 dr / lambda; W ~ 4 half_span / lambda for large tiles).
@@ -219,32 +210,36 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     const double hs32 = 0.5 * sqrt((BP_TX * p.dx) * (BP_TX * p.dx) +
                                    (2.0 * BP_WAVES * p.dy) * (2.0 * BP_WAVES * p.dy) + p.dem_relief * p.dem_relief);
     const double win32 = ceil(2.0 * hs32 / p.dr) + 6.0; // the window of 64 x 32 tiles, margins included
-    plan->f64 = (2.0 * p.dr / p.wavelength) * win32 > 4096.0;
-    plan->ppt = (tiles2 < 2 * (int64_t)plan->n_cu && !(p.dem_relief > 0.0) && !plan->f64) ? 1 : 2;
-    const int ty = BP_WAVES * plan->ppt;
-    plan->tiles_y = (p.ny + ty - 1) / ty;
-    if ((int64_t)plan->tiles_x * plan->tiles_y * layers > INT32_MAX) {
-        release(plan);
-        return SARBP_EINVAL;
+    L->f64 = (2.0 * p.dr / p.wavelength) * win32 > 4096.0;
+    // Nearest: the fp32 bin decision is rechecked in fp64 within a tie band that
+    // grows with the window and the tile (tie_band_coefficients); where the band of
+    // a 64 x 32 tile would pass BP_NEAREST_TIE_MAX, the fp64-range kernels serve
+    // the plan.  (rho <= 1.06 half_span / dr while the series applies.)
+    if (p.interp == SARBP_NEAREST && !L->f64) {
+        float base[3], rho_coef[3];
+        tie_band_coefficients((int)win32, false, base, rho_coef);
+        const double band = (double)base[0] + (double)rho_coef[0] * 1.06 * hs32 / p.dr;
+        if (band > BP_NEAREST_TIE_MAX) L->f64 = 1;
     }
+    L->ppt = (tiles2 < 2 * (int64_t)L->n_cu && !(p.dem_relief > 0.0) && !L->f64) ? 1 : 2;
+    const int ty = BP_WAVES * L->ppt;
+    L->tiles_y = (p.ny + ty - 1) / ty;
+    if ((int64_t)L->tiles_x * L->tiles_y * layers > INT32_MAX) return SARBP_EINVAL;
     // (with terrain, the tile centre is at the tile's mid-height: |dz| <= dem_relief / 2)
-    plan->half_span = 0.5 * sqrt((BP_TX * p.dx) * (BP_TX * p.dx) + ((double)ty * p.dy) * ((double)ty * p.dy) +
-                                 p.dem_relief * p.dem_relief);
-    const double span_bins = ceil(2.0 * plan->half_span / p.dr);
+    L->half_span = 0.5 * sqrt((BP_TX * p.dx) * (BP_TX * p.dx) + ((double)ty * p.dy) * ((double)ty * p.dy) +
+                              p.dem_relief * p.dem_relief);
+    const double span_bins = ceil(2.0 * L->half_span / p.dr);
     // The window holds the bins floor(u) can take (the sinc8 taps are folded into
     // each bin's polynomial), with a spare bin each side.
     const int taps_hi = 1;
-    plan->margin_lo = 2;
-    if (span_bins > 1.0e6) {
-        release(plan);
-        return SARBP_EUNSUPPORTED;
-    }
-    plan->win = (int)span_bins + plan->margin_lo + 2 + taps_hi;
+    L->margin_lo = 2;
+    if (span_bins > 1.0e6) return SARBP_EUNSUPPORTED;
+    L->win = (int)span_bins + L->margin_lo + 2 + taps_hi;
     // linear and nearest windows are staged two bins per lane step: make W even
-    if (p.interp != SARBP_SINC8) plan->win += plan->win & 1;
+    if (p.interp != SARBP_SINC8) L->win += L->win & 1;
     const int eb = p.interp == SARBP_NEAREST ? 8 : (p.interp == SARBP_LINEAR ? 16 : 64);
-    if (p.interp == SARBP_SINC8) sinc8_polynomials(plan->sinc_poly);
-    const int per_pulse = plan->win * eb + ((p.dem_relief > 0.0 || plan->f64) ? 3 : 2) * 16 + 4;
+    if (p.interp == SARBP_SINC8) sinc8_polynomials(L->sinc_poly);
+    const int per_pulse = L->win * eb + ((p.dem_relief > 0.0 || L->f64) ? 3 : 2) * 16 + 4;
     // Coarse grids (long windows) that would stage fewer than 8 pulses per step
     // use up to 150 KiB of LDS: one workgroup per CU instead of two.
     int chunk = (BP_LDS_BUDGET - 64) / per_pulse;
@@ -253,16 +248,77 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     // (the staging divides step indices u < chunk * wu by wu <= win with a 32-bit
     // multiply-high, exact while chunk * wu * wu < 2^32; the LDS bound keeps
     // chunk * win below 19200, so this holds whenever a chunk fits)
-    if (chunk < 1 || (uint64_t)chunk * plan->win * plan->win >= (1ull << 32)) {
-        release(plan);
-        return SARBP_EUNSUPPORTED;
+    if (chunk < 1 || (uint64_t)chunk * L->win * L->win >= (1ull << 32)) return SARBP_EUNSUPPORTED;
+    L->chunk = chunk;
+    // + the chunk's issue-priority word and the double-buffered mode and tie-band words
+    L->lds_bytes = (size_t)chunk * per_pulse + 32;
+    return SARBP_OK;
+}
+
+void sarbp_bp_args(const sarbp_params& p, const BpLayout& L, BpArgs* A) {
+    *A = BpArgs();
+    A->n_range = p.n_range;
+    A->nx = p.nx;
+    A->ny = p.ny;
+    A->tiles_x = L.tiles_x;
+    A->ntiles = L.tiles_x * L.tiles_y;
+    A->group_blocks = A->ntiles * (p.nz > 1 ? p.nz : 1);
+    A->nblocks = A->group_blocks;
+    A->dz = p.nz > 1 ? p.dz : 0.0;
+    A->win = L.win;
+    const uint64_t wu = (uint64_t)(p.interp == SARBP_SINC8 ? L.win : L.win / 2);
+    A->win_magic = (uint32_t)(((1ull << 32) + wu - 1) / wu);
+    A->margin_lo = L.margin_lo;
+    A->chunk = L.chunk;
+    A->slots = L.n_cu;
+    A->r0 = p.r0;
+    A->dr = p.dr;
+    A->inv_dr = 1.0 / p.dr;
+    A->x0 = p.x0;
+    A->y0 = p.y0;
+    A->z0 = p.z0;
+    A->dx = p.dx;
+    A->dy = p.dy;
+    A->half_span = L.half_span;
+    A->dem_relief = p.dem_relief;
+    for (int i = 0; i < 32; ++i) A->sinc_poly[i] = L.sinc_poly[i];
+    A->half_span_bins = L.half_span / p.dr;
+    A->kappa = (float)(2.0 * p.dr / p.wavelength);
+    tie_band_coefficients(L.win, L.f64 != 0, A->tie_base, A->tie_rho);
+    A->round_half = p.interp == SARBP_NEAREST ? 1 : 0;
+    // exp(-j pi kappa): the nearest path measures the phase from half a bin below the sample
+    const double k = 2.0 * p.dr / p.wavelength;
+    const double fr = 0.5 * k - floor(0.5 * k);
+    A->half_rot = make_float2((float)cos(-2.0 * kPi * fr), (float)sin(-2.0 * kPi * fr));
+}
+
+extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
+    if (out == nullptr) return SARBP_EINVAL;
+    *out = nullptr;
+    int st = sarbp_validate(params);
+    if (st != SARBP_OK) return st;
+    sarbp_plan* plan = new (std::nothrow) sarbp_plan();
+    if (plan == nullptr) return SARBP_ENOMEM;
+    memset(plan, 0, sizeof(*plan));
+    plan->p = *params;
+    const sarbp_params& p = plan->p;
+    int n_cu = 0;
+    if (hipGetDevice(&plan->device) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, plan->device) != hipSuccess) {
+        delete plan;
+        return SARBP_EDEVICE;
     }
-    plan->chunk = chunk;
-    plan->lds_bytes = (size_t)chunk * per_pulse + 16; // + the chunk's issue-priority word
-    if (plan->lds_bytes > 64 * 1024) {
-        st = sarbp_bp_allow_lds(p.interp, p.accum, false, plan->ppt, plan->f64, plan->lds_bytes);
+    plan->L.n_cu = n_cu;
+
+    st = sarbp_plan_layout(p, n_cu, &plan->L);
+    if (st != SARBP_OK) {
+        release(plan);
+        return st;
+    }
+    if (plan->L.lds_bytes > 64 * 1024) {
+        st = sarbp_bp_allow_lds(p.interp, p.accum, false, plan->L.ppt, plan->L.f64, plan->L.lds_bytes);
         if (st == SARBP_OK && p.dem_relief > 0.0)
-            st = sarbp_bp_allow_lds(p.interp, p.accum, true, plan->ppt, plan->f64, plan->lds_bytes);
+            st = sarbp_bp_allow_lds(p.interp, p.accum, true, plan->L.ppt, plan->L.f64, plan->L.lds_bytes);
         if (st != SARBP_OK) {
             release(plan);
             return st;
@@ -270,7 +326,7 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     }
 
     st = upload(phase_table(p), &plan->phase_tab);
-    if (st == SARBP_OK) st = upload(std::vector<int>((size_t)2 * plan->n_cu, 0), &plan->progress);
+    if (st == SARBP_OK) st = upload(std::vector<int>((size_t)2 * plan->L.n_cu, 0), &plan->progress);
     if (st != SARBP_OK) {
         release(plan);
         return st;

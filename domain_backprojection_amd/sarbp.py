@@ -9,7 +9,7 @@ The functions keep the C names: :func:`sarbp_plan_create`,
 :func:`sarbp_backproject`, :func:`sarbp_backproject_dem`, :func:`sarbp_range_compress`,
 :func:`sarbp_interpolate_track`, :func:`sarbp_stream_create`,
 :func:`sarbp_backproject_host`, :func:`sarbp_stream_destroy`, :func:`sarbp_destroy`,
-:func:`sarbp_status_string`, :func:`sarbp_version`.  :class:`Plan` and
+:func:`sarbp_check_indices`, :func:`sarbp_status_string`, :func:`sarbp_version`.  :class:`Plan` and
 :class:`HostStream` wrap the handles' lifetimes.
 """
 from __future__ import annotations
@@ -74,6 +74,33 @@ class sarbp_params(ctypes.Structure):
     ]
 
 
+class sarbp_index_report(ctypes.Structure):
+    """Mirror of ``sarbp_index_report``."""
+
+    _fields_ = [
+        ("decisions", ctypes.c_int64),
+        ("window_violations", ctypes.c_int64),
+        ("staging_violations", ctypes.c_int64),
+        ("nearest_rechecks", ctypes.c_int64),
+        ("nearest_recheck_clamped", ctypes.c_int64),
+        ("nearest_escapes", ctypes.c_int64),
+        ("nan_tiles", ctypes.c_int64),
+        ("max_position_error", ctypes.c_double),
+        ("max_error_to_band", ctypes.c_double),
+        ("min_position", ctypes.c_double),
+        ("max_position_margin", ctypes.c_double),
+        ("window", ctypes.c_int32),
+        ("chunk", ctypes.c_int32),
+        ("pixels_per_lane", ctypes.c_int32),
+        ("fp64_ranges", ctypes.c_int32),
+        ("mode_chunks", ctypes.c_int32 * 3),
+        ("tie_band_max", ctypes.c_float),
+    ]
+
+    def as_dict(self) -> dict:
+        return {f: (list(getattr(self, f)) if f == "mode_chunks" else getattr(self, f)) for f, _ in self._fields_}
+
+
 _vp = ctypes.c_void_p
 _lib.sarbp_plan_create.argtypes = [ctypes.POINTER(sarbp_params), ctypes.POINTER(_vp)]
 _lib.sarbp_plan_create.restype = ctypes.c_int
@@ -102,11 +129,14 @@ _lib.sarbp_split_workspace_bytes.restype = ctypes.c_size_t
 _lib.sarbp_backproject_split.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_size_t,
                                          _vp]
 _lib.sarbp_backproject_split.restype = ctypes.c_int
+_lib.sarbp_check_indices.argtypes = [ctypes.POINTER(sarbp_params), ctypes.c_int32, _vp, ctypes.c_int32, _vp,
+                                     ctypes.POINTER(sarbp_index_report)]
+_lib.sarbp_check_indices.restype = ctypes.c_int
 
 EXPORTS = ("sarbp_plan_create", "sarbp_backproject", "sarbp_range_compress", "sarbp_destroy",
            "sarbp_status_string", "sarbp_version", "sarbp_stream_create", "sarbp_backproject_host",
            "sarbp_stream_destroy", "sarbp_interpolate_track", "sarbp_backproject_dem",
-           "sarbp_split_workspace_bytes", "sarbp_backproject_split")
+           "sarbp_split_workspace_bytes", "sarbp_backproject_split", "sarbp_check_indices")
 
 
 class SarbpError(RuntimeError):
@@ -227,6 +257,29 @@ def sarbp_backproject_split(handle, positions: torch.Tensor, echo: torch.Tensor,
                                       ws_bytes, _stream(stream))
     if st != SARBP_OK:
         raise SarbpError(st, "sarbp_backproject_split")
+
+
+def sarbp_check_indices(params: sarbp_params, positions, dem=None, n_cu: int = 0) -> dict:
+    """Host emulation of the backprojection kernels' index arithmetic for the plan
+    `params` over host float64 positions (n, 3) (and float32 heights (ny, nx) for the
+    terrain kernels); returns the report's fields as a dict.  No device is used."""
+    import numpy as np
+
+    pos = np.ascontiguousarray(positions, dtype=np.float64)
+    if pos.ndim != 2 or pos.shape[1] != 3:
+        raise ValueError("positions must be (n, 3)")
+    dem_p = None
+    if dem is not None:
+        dem = np.ascontiguousarray(dem, dtype=np.float32)
+        if dem.shape != (params.ny, params.nx):
+            raise ValueError("dem must be (ny, nx)")
+        dem_p = dem.ctypes.data
+    rep = sarbp_index_report()
+    st = _lib.sarbp_check_indices(ctypes.byref(params), int(n_cu), pos.ctypes.data, int(pos.shape[0]), dem_p,
+                                  ctypes.byref(rep))
+    if st != SARBP_OK:
+        raise SarbpError(st, "sarbp_check_indices")
+    return rep.as_dict()
 
 
 def sarbp_range_compress(handle, raw: torch.Tensor, out: torch.Tensor, n: int | None = None, stream=None) -> None:

@@ -247,6 +247,50 @@ int sarbp_backproject_host(sarbp_stream* s, const double* positions_h, const voi
 /* Release the stream object after its work has finished.  NULL is a no-op. */
 void sarbp_stream_destroy(sarbp_stream* s);
 
+/* ---- Host-side check of the kernels' index arithmetic (section 4.4 of the page:
+ * an index outside the staged echo window fills the image with noise, so index
+ * bounds are worth checking with a memory checker).  No device is used. ------ */
+
+typedef struct {
+    int64_t decisions;               /* window positions evaluated: pixels x pulses, lanes past the grid's edge included */
+    int64_t window_violations;       /* positions outside [0, W) of their pulse's LDS window (must be 0)               */
+    int64_t staging_violations;      /* staging steps whose pulse, carrier-table index or window bin is out of range (must be 0) */
+    int64_t nearest_rechecks;        /* nearest: decisions inside the fp64 tie band (rechecked in fp64)                */
+    int64_t nearest_recheck_clamped; /* nearest: rechecked bins outside the window (must be 0)                         */
+    int64_t nearest_escapes;         /* nearest: decisions outside the band whose bin differs from floor(u + 1/2) (must be 0) */
+    int64_t nan_tiles;               /* terrain tiles beyond dem_relief (skipped; their pixels come out NaN)           */
+    double max_position_error;       /* largest |window position - exact one| over in-grid pixels [bins]               */
+    double max_error_to_band;        /* largest ratio of that error to the error bound of its chunk (half the tie band) */
+    double min_position;             /* smallest window position (>= 0 required)                                        */
+    double max_position_margin;      /* largest window position minus W (< 0 required)                                  */
+    int32_t window;                  /* W: LDS window entries per pulse                                                 */
+    int32_t chunk;                   /* pulses per LDS chunk                                                            */
+    int32_t pixels_per_lane;         /* 1 or 2 (tiles of 64 x 16 or 64 x 32 pixels)                                    */
+    int32_t fp64_ranges;             /* 1: the plan runs the fp64-range kernels                                         */
+    int32_t mode_chunks[3];          /* chunks whose window position used the two-term series, three terms, exact form */
+    float tie_band_max;              /* the widest tie band of any chunk [bins] (the fp32 decision is rechecked within it) */
+} sarbp_index_report;
+
+/* Emulate on the host, for the plan `params` would create on a device of n_cu
+ * compute units (0: 256, one MI355X), the backprojection kernels' index and
+ * window-position arithmetic for n pulses (one call, unsplit): each workgroup's
+ * tile frame and lane offsets, each pulse chunk's fp64 set-up, staging steps and
+ * accuracy mode, and every lane's fp32 (or fp64-range) window position, with the
+ * kernels' own source code (the only difference: the exact form's fp32 square
+ * root and reciprocal are correctly rounded on the host, within about one ulp of
+ * the device's).  Counts out-of-range indices and, for nearest interpolation,
+ * bin decisions that would differ from the double-precision definition.
+ *   positions_h : host, float64 [n][3]; 1 <= n <= params->n_pulses
+ *   dem_h       : host, float32 [ny][nx] terrain heights (the sarbp_backproject_dem
+ *                 kernels), or NULL (sarbp_backproject; required NULL when
+ *                 dem_relief = 0)
+ * Cost: about the kernel's work per pixel and pulse on one host thread (a few
+ * tens of nanoseconds each).  Returns SARBP_OK with *report filled, SARBP_EINVAL
+ * or SARBP_EUNSUPPORTED as sarbp_plan_create would, or SARBP_EINVAL for a null
+ * pointer or n out of range. */
+int sarbp_check_indices(const sarbp_params* params, int32_t n_cu, const double* positions_h, int32_t n,
+                        const float* dem_h, sarbp_index_report* report);
+
 /* Static description of a status code (never NULL). */
 const char* sarbp_status_string(int status);
 

@@ -32,6 +32,7 @@ import pytest
 import oracle
 import synth
 from _parity import REL_L2, rel_l2
+from _probe import nearest_index_mismatches
 
 N_CASES = 128
 WAVELENGTHS = (0.0086, 0.03125, 0.0556, 0.236)
@@ -161,3 +162,12 @@ def test_random_geometry_matches_oracle(sb, seed):
         assert err <= REL_L2, err
         assert err_g <= REL_L2, err_g
         assert np.linalg.norm(grouped - got) <= 1e-5 * np.linalg.norm(got)
+    if scene.interp == "nearest":
+        # every pixel of every pulse (at most 64, evenly spaced, first and last included)
+        pulses = sorted(set(np.linspace(0, scene.na - 1, min(scene.na, 64)).astype(int).tolist()))
+        kw = {}
+        if scene.dem is not None:
+            kw["dem_relief"] = max(synth.block_relief(scene.dem), 1e-3)
+        bad = nearest_index_mismatches(sb, scene, pulses, dem=scene.dem, layers=layers, **kw)
+        print(f"[random {seed}] nearest index probe: {len(pulses)} pulses, {bad} mismatches", flush=True)
+        assert bad == 0

@@ -16,8 +16,10 @@ complex multiply-accumulate 8; sqrt/sin/cos count 1) times Na*Nx*Ny per launch,
 divided by the launch's average duration measured with HIP events on the
 launch stream; `peak` is the MI355X vector fp32 figure, 157.3 TFLOP/s.
 
-`cpu_baseline` times the fp64 CPU oracle (test infrastructure, untuned) on a
-bounded row sample of the same scene with all host threads.
+`cpu_baseline` times the fp64 CPU oracle (test infrastructure, untuned) on the
+same scene with all host threads (the whole frame when that takes at most 30 s,
+else a row band), and `parity` compares the timed launch's image with the
+oracle's over those rows.
 """
 from __future__ import annotations
 
@@ -40,7 +42,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bp_linear_std_traffic.json")
 # Everything that shapes the backprojection kernel or its launch: a change to any
 # of these invalidates the committed counter readings.
 BP_SOURCES = [os.path.join(ROOT, "domain_backprojection_amd", "csrc", f)
-              for f in ("sarbp_bp.hip", "sarbp_internal.h", "sarbp_plan.hip")]
+              for f in ("sarbp_bp.hip", "sarbp_geom.h", "sarbp_internal.h", "sarbp_plan.hip")]
 
 
 def log(msg):
@@ -108,23 +110,26 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(scene, target_s=12.0):
-    """The fp64 oracle on host threads: a row band of the benchmark scene sized to
-    about target_s, plus single-thread runs on the tiny scene and on 1/64 of the rows."""
+def cpu_baseline(scene, target_s=12.0, whole_s=30.0):
+    """The fp64 oracle on host threads over the benchmark scene: the whole frame when the
+    probe predicts at most whole_s seconds, else a central row band sized to about target_s;
+    plus single-thread runs on the tiny scene and on 1/64 of the rows.  Returns the record
+    and the oracle rows it computed (for the parity check)."""
     import oracle
     import synth
 
     threads = oracle.threads()
-    # Probe on a band large enough that thread start-up does not dominate, then
-    # size the timed band to about target_s (the whole frame if that is shorter).
+    # Probe on a band large enough that thread start-up does not dominate, then size the
+    # timed band.
     rows = 32
     t = time.perf_counter()
     oracle.scene_backproject(scene, rows=(0, rows), nthreads=threads)
     dt = time.perf_counter() - t
-    rows = int(min(scene.ny, max(rows, rows * target_s / max(dt, 1e-3))))
+    per_row = max(dt, 1e-3) / rows
+    rows = scene.ny if per_row * scene.ny <= whole_s else int(min(scene.ny, max(rows, target_s / per_row)))
     j0 = (scene.ny - rows) // 2
     t = time.perf_counter()
-    oracle.scene_backproject(scene, rows=(j0, j0 + rows), nthreads=threads)
+    band = oracle.scene_backproject(scene, rows=(j0, j0 + rows), nthreads=threads)
     dt = time.perf_counter() - t
     upd = rows * scene.nx * scene.na
 
@@ -137,13 +142,52 @@ def cpu_baseline(scene, target_s=12.0):
     t = time.perf_counter()
     oracle.scene_backproject(scene, rows=(j1, j1 + r64), nthreads=1)
     dt_64 = time.perf_counter() - t
-    return {"value": upd / dt / 1e9, "unit": "G pixel-pulse updates/s", "cores": threads, "kind": "oracle",
-            "sample": f"rows {j0}..{j0 + rows - 1} of the {scene.nx}x{scene.ny} grid ({rows * scene.nx} px x "
-                      f"{scene.na} pulses, {upd:.3e} updates, {dt:.1f} s)",
-            "cpu_model": cpu_model(),
-            "single_thread": {"tiny_full_G_per_s": tiny.updates / dt_tiny / 1e9,
-                              "std_1_64_rows_G_per_s": r64 * scene.nx * scene.na / dt_64 / 1e9,
-                              "std_1_64_rows_s": dt_64}}
+    rec = {"value": upd / dt / 1e9, "unit": "G pixel-pulse updates/s", "cores": threads, "kind": "oracle",
+           "sample": f"rows {j0}..{j0 + rows - 1} of the {scene.nx}x{scene.ny} grid ({rows * scene.nx} px x "
+                     f"{scene.na} pulses, {upd:.3e} updates, {dt:.1f} s)",
+           "cpu_model": cpu_model(),
+           "single_thread": {"tiny_full_G_per_s": tiny.updates / dt_tiny / 1e9,
+                             "std_1_64_rows_G_per_s": r64 * scene.nx * scene.na / dt_64 / 1e9,
+                             "std_1_64_rows_s": dt_64}}
+    return rec, (j0, j0 + rows), band
+
+
+def parity(scene, got, rows, want, peak_db=0.05):
+    """The timed GPU image against the oracle's rows [j0, j1): relative L2 error over those
+    pixels (all, clutter outside the target windows, the windows), and for each target whose
+    window lies in the band, whether its peak is on the oracle's pixel and the magnitude
+    difference there in dB."""
+    import math
+
+    import numpy as np
+
+    import synth
+
+    j0, j1 = rows
+    g = got[j0:j1].astype(np.complex128)
+    rho_az, rho_rg = synth.resolution(scene)
+    hx, hy = max(1, math.ceil(rho_az / scene.dx)), max(1, math.ceil(rho_rg / scene.dy))
+    mask = np.zeros(want.shape, bool)
+    peaks, worst_db = [], 0.0
+    for (i, j) in scene.targets:
+        if j - hy < j0 or j + hy >= j1:
+            continue
+        sl = (slice(j - hy - j0, j + hy + 1 - j0), slice(max(0, i - hx), min(scene.nx, i + hx + 1)))
+        mask[sl] = True
+        gw, ow = np.abs(g[sl]), np.abs(want[sl])
+        kg, ko = np.unravel_index(np.argmax(gw), gw.shape), np.unravel_index(np.argmax(ow), ow.shape)
+        db = 20 * math.log10(gw[ko] / ow[ko])
+        worst_db = max(worst_db, abs(db))
+        peaks.append(bool(kg == ko and abs(db) <= peak_db))
+
+    def rel(a, b):
+        return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+    return {"rel_l2": rel(g, want), "rel_l2_clutter": rel(g[~mask], want[~mask]),
+            "rel_l2_target_windows": rel(g[mask], want[mask]) if mask.any() else None,
+            "peaks_ok": all(peaks), "peaks_on_oracle_pixel": f"{sum(peaks)}/{len(peaks)}",
+            "max_peak_db": worst_db, "pixels": int(g.size), "rows": [int(j0), int(j1)],
+            "against": "fp64 CPU oracle on the same seeded scene", "bar": {"rel_l2": 2e-3, "peak_db": peak_db}}
 
 
 def aux_end_to_end(sb, steps, warmup):
@@ -411,6 +455,7 @@ def main():
         img = plan.new_image()
         torch.cuda.synchronize()
         tm, wall = time_launches(lambda: plan.backproject(pos, echo, image=img), args.steps, args.warmup)
+        got = img.cpu().numpy()  # the last timed launch's image, for the parity check
     ms = tm["mean"]
     log(f"bench: {args.steps} launches, {ms:.3f} ms per launch (HIP events; median {tm['median']:.3f}, "
         f"min {tm['min']:.3f}), wall {wall:.3f} s")
@@ -462,8 +507,10 @@ def main():
         line["aux"]["volume"] = aux_volume(sarbp, max(5, args.steps // 5), max(5, args.warmup // 5))
         log(f"bench: end-to-end {line['aux']}")
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(s)
+        line["cpu_baseline"], rows, want = cpu_baseline(s)
         log(f"bench: cpu baseline {line['cpu_baseline']}")
+        line["parity"] = parity(s, got, rows, want)
+        log(f"bench: parity {line['parity']}")
     print(json.dumps(line), flush=True)
 
 

@@ -4,8 +4,8 @@ compare with the CPU oracle under the acceptance bar.
 Acceptance bar (floating point, from the workload statement):
   * rel-L2 = ||I_gpu - I_oracle|| / ||I_oracle|| <= 2e-3 over the compared pixels
   * every target's strongest pixel in a +-ceil(rho_az/dx) x +-ceil(rho_rg/dy) window
-    around its true pixel is the same pixel in both images, up to the oracle's own
-    plateaus (pixels within PEAK_TIE of the oracle's maximum are the same peak)
+    around its true pixel is the same pixel in both images (nearest: up to the
+    definition's own plateaus, see PEAK_TIE; every such tie is reported)
   * | 20 log10(|I_gpu| / |I_oracle|) | <= 0.05 dB at the oracle's peak pixel
 Integer decisions (nearest bin) must match exactly.
 """
@@ -15,12 +15,17 @@ import numpy as np
 
 REL_L2 = 2e-3
 PEAK_DB = 0.05
-# With nearest interpolation, neighbouring pixels that select the same range bin
-# for every pulse form a plateau: on the tiny scene three pixels of one target
-# differ by 2e-6 in the fp64 definition itself.  A peak is unique only up to such
-# ties, so any pixel within this relative gap of the oracle's maximum counts as it
-# (the GPU's pointwise error is ~1e-4 relative).
+# With nearest interpolation the definition itself has plateaus: neighbouring pixels that
+# select the same range bin for every pulse differ only through the phase term (on the tiny
+# scene three pixels of one target differ by 2e-6).  There, and only there, the GPU's peak
+# may sit on another pixel of the oracle's plateau: the oracle's gap between that pixel and
+# its maximum must be at most PEAK_TIE (relative) and at most the GPU's own measured error in
+# that window (the largest |I_gpu - I_oracle| there, relative to the peak), so the two
+# candidates are indistinguishable at the precision the run shows.  Every such tie is
+# recorded in TIES and printed.  Linear and sinc8 are continuous in the range and must put
+# every peak on the oracle's pixel.
 PEAK_TIE = 1e-4
+TIES = []
 
 
 def rel_l2(got, want):
@@ -42,17 +47,30 @@ def target_windows(scene):
     return wins
 
 
-def check_peaks(got_at, want_at, wins):
-    """got_at / want_at: callables mapping an (P, 2) pixel array to complex values."""
+def check_peaks(got_at, want_at, wins, interp, label=""):
+    """got_at / want_at: callables mapping an (P, 2) pixel array to complex values.  Returns
+    the worst peak magnitude difference in dB over the windows."""
+    worst = 0.0
     for w in wins:
         g = got_at(w)
         o = want_at(w)
         ao = np.abs(o)
         kg, ko = int(np.argmax(np.abs(g))), int(np.argmax(ao))
-        assert ao[kg] >= ao[ko] * (1.0 - PEAK_TIE), (
-            f"peak moved: gpu {w[kg]} oracle {w[ko]} (oracle there {ao[kg]:.6g} vs {ao[ko]:.6g})")
+        if kg != ko:
+            gap = (ao[ko] - ao[kg]) / ao[ko]
+            err = float(np.max(np.abs(g - o)) / ao[ko])
+            tie = interp == "nearest" and gap <= PEAK_TIE and gap <= err
+            rec = {"label": label, "gpu": w[kg].tolist(), "oracle": w[ko].tolist(), "gap": float(gap),
+                   "window_error": err, "accepted": bool(tie)}
+            TIES.append(rec)
+            print(f"[peak tie] {label} gpu {w[kg].tolist()} oracle {w[ko].tolist()}: oracle gap {gap:.3g}, "
+                  f"GPU error in the window {err:.3g} -> {'accepted' if tie else 'rejected'}", flush=True)
+            assert tie, (f"peak moved: gpu {w[kg]} oracle {w[ko]} (oracle there {ao[kg]:.6g} vs {ao[ko]:.6g}, "
+                         f"gap {gap:.3g}, window error {err:.3g}, {interp})")
         db = 20 * math.log10(abs(g[ko]) / ao[ko])
         assert abs(db) <= PEAK_DB, f"peak magnitude differs by {db:.4f} dB at {w[ko]}"
+        worst = max(worst, abs(db))
+    return worst
 
 
 def sample_pixels(scene, count, seed):

@@ -8,6 +8,7 @@ import pytest
 import oracle
 import synth
 from _parity import PEAK_DB, PEAK_TIE, REL_L2, check_peaks, rel_l2, sample_pixels, target_windows
+from _probe import nearest_index_mismatches
 
 pytestmark = pytest.mark.gpu
 
@@ -49,7 +50,8 @@ def test_tiny_config_full_image(sb, interp):
     got = _run_bp(sb, s)
     want = oracle.scene_backproject(s)
     assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
-    check_peaks(lambda w: got[w[:, 1], w[:, 0]], lambda w: want[w[:, 1], w[:, 0]], target_windows(s))
+    check_peaks(lambda w: got[w[:, 1], w[:, 0]], lambda w: want[w[:, 1], w[:, 0]], target_windows(s), s.interp,
+                f"{s.name} {s.interp}")
 
 
 @pytest.mark.parametrize("interp", ["linear", "nearest", "sinc8"])
@@ -211,7 +213,8 @@ def test_accumulation_modes_full_image(sb, interp, accum):
     got = _run_bp(sb, s, accum=accum)
     want = oracle.scene_backproject(s)
     assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
-    check_peaks(lambda w: got[w[:, 1], w[:, 0]], lambda w: want[w[:, 1], w[:, 0]], target_windows(s))
+    check_peaks(lambda w: got[w[:, 1], w[:, 0]], lambda w: want[w[:, 1], w[:, 0]], target_windows(s), s.interp,
+                f"{s.name} {s.interp}")
     r = synth.make_scene("hifi", na=203, nr=1024, nx=70, ny=45, interp=interp, n_targets=1)
     with sb.Plan.for_scene(r, accum=accum) as plan:
         pos = torch.from_numpy(r.positions).cuda()
@@ -428,7 +431,8 @@ def test_terrain_full_image(sb, interp):
     want = oracle.scene_backproject(s)
     assert np.isfinite(got).all()
     assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
-    check_peaks(lambda w: got[w[:, 1], w[:, 0]], lambda w: want[w[:, 1], w[:, 0]], target_windows(s))
+    check_peaks(lambda w: got[w[:, 1], w[:, 0]], lambda w: want[w[:, 1], w[:, 0]], target_windows(s), s.interp,
+                f"{s.name} {s.interp}")
 
 
 @pytest.mark.parametrize("interp", ["linear", "nearest"])
@@ -568,11 +572,10 @@ def test_volume_matches_oracle(sb, interp):
         win = np.array([(a, b, c) for c in range(max(0, l - 2), min(nz, l + 3)) for b in range(j - 2, j + 3)
                         for a in range(i - 2, i + 3)])
         g, o = got[win[:, 2], win[:, 1], win[:, 0]], want[win[:, 2], win[:, 1], win[:, 0]]
-        kg, ko = int(np.argmax(np.abs(g))), int(np.argmax(np.abs(o)))
-        assert abs(o[kg]) >= abs(o[ko]) * (1 - PEAK_TIE), (win[kg], win[ko])
+        check_peaks(lambda w: g, lambda w: o, [win], interp, f"volume {interp} voxel {(i, j, l)}")
+        ko = int(np.argmax(np.abs(o)))
         if interp != "nearest":  # nearest's plateaus may put the definition's own peak a voxel off
             assert tuple(win[ko]) == (i, j, l)
-        assert abs(20 * math.log10(abs(g[ko]) / abs(o[ko]))) <= PEAK_DB
 
 
 def test_volume_through_the_host_pipeline(sb):
@@ -589,28 +592,6 @@ def test_volume_through_the_host_pipeline(sb):
 
 
 # ----------------------------------------------------------------------------- nearest: bit-exact index
-
-def _index_probe(sb, scene, pulses):
-    """One pulse per call with echo s[k] = k + 1: |I| - 1 is the bin the GPU chose."""
-    import torch
-
-    ramp = torch.arange(1, scene.nr + 1, dtype=torch.float32).to(torch.complex64).cuda()[None, :].contiguous()
-    ii, jj = np.meshgrid(np.arange(scene.nx), np.arange(scene.ny), indexing="xy")
-    ij = np.stack([ii.ravel(), jj.ravel()], 1)
-    mismatches = 0
-    with sb.Plan.for_scene(scene, interp="nearest", n_pulses=1) as plan:
-        img = plan.new_image()
-        for n in pulses:
-            pos = torch.from_numpy(scene.positions[n:n + 1].copy()).cuda()
-            plan.backproject(pos, ramp, image=img)
-            mag = img.abs().cpu().numpy().ravel().astype(np.float64)
-            k_gpu = np.rint(mag) - 1
-            assert np.max(np.abs(mag - np.rint(mag))) < 0.02
-            k_orc = oracle.nearest_index(scene.positions[n], scene.r0, scene.dr, scene.x0, scene.y0, scene.z0,
-                                         scene.dx, scene.dy, ij)
-            mismatches += int(np.count_nonzero(k_gpu != k_orc))
-    return mismatches
-
 
 @pytest.mark.parametrize("scene", ["tiny", "std", "large", "hifi"])
 def test_nearest_index_bit_exact(sb, scene):
@@ -630,7 +611,33 @@ def test_nearest_index_bit_exact(sb, scene):
                         targets=np.zeros((0, 2), np.int64))
     pulses = sorted(set(np.linspace(0, s.na - 1, 64).astype(int).tolist()) | {0, s.na - 1})
     _say(f"[index probe {scene}] {len(pulses)} pulses x {s.nx * s.ny} pixels")
-    assert _index_probe(sb, s, pulses) == 0
+    assert nearest_index_mismatches(sb, s, pulses) == 0
+
+
+def _probe_track(na, ground, height, step=0.3, squint=0.3, seed=1):
+    """A squinted straight track at the given ground range and height with a small wobble."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    s = (np.arange(na) - (na - 1) / 2) * step
+    pos = np.stack([s * math.cos(squint), -ground + s * math.sin(squint), np.full(na, height)], 1)
+    return pos + rng.uniform(0, 0.3, 3) * np.sin(np.arange(na)[:, None] * 0.01 + rng.uniform(0, 6, 3))
+
+
+@pytest.mark.parametrize("lam, dr, px, ground, height", [
+    (0.236, 0.05, 1.5, 10000.0, 5000.0),   # 2152-bin windows: the fp64-range kernels
+    (0.236, 0.1, 0.2, 10000.0, 5000.0),    # fp32, three-term series, band ~1.1e-4
+    (0.0556, 0.1, 0.3, 150.0, 120.0),      # fp32, exact form at 190 m, band ~4e-4
+    (0.03125, 0.05, 0.1, 400.0, 300.0),    # fp32, exact form, 5 cm bins
+], ids=["L-1.5m-f64", "L-10cm-series", "C-190m-exact", "X-5cm-exact"])
+def test_nearest_index_bit_exact_long_windows(sb, lam, dr, px, ground, height):
+    """Long echo windows and wide fp32 tie bands: all 96 pulses x every pixel of a 96 x 96 grid."""
+    na, nx, nr = 96, 96, 16384
+    rc = math.hypot(ground, height)
+    s = synth.Scene(name="probe", seed=0, na=na, nr=nr, nx=nx, ny=nx, x0=-(nx // 2) * px, y0=-(nx // 2) * px,
+                    z0=0.0, dx=px, dy=px, r0=rc - (nr // 2) * dr, dr=dr, wavelength=lam, interp="nearest",
+                    positions=_probe_track(na, ground, height), echo=None, raw=None,
+                    targets=np.zeros((0, 2), np.int64))
+    _say(f"[index probe long window] lambda {lam} dr {dr} pixel {px} at {rc:.0f} m: {na} pulses x {nx * nx} px")
+    assert nearest_index_mismatches(sb, s, range(na)) == 0
 
 
 # ----------------------------------------------------------------------------- range compression
@@ -682,55 +689,102 @@ def test_range_compression_taylor_parameters(sb, nbar, sll):
     assert rel_l2(got, want) < 1e-5
 
 
-# ----------------------------------------------------------------------------- full-size configs, sampled
+# ----------------------------------------------------------------------------- full-size configs
 
-@pytest.mark.parametrize("scene, sample_seed", [("std", 79), ("hifi", 81), ("large", 80)])
-def test_full_size_sampled(sb, scene, sample_seed):
+_SCENES = {}
+
+
+def _scene(name):
+    """Full-size scenes, generated once per test session (the hi-fi and large scenes take tens
+    of seconds of host time)."""
     import time
 
-    t = time.time()
-    s = synth.make_scene(scene)
-    _say(f"[full {scene}] generated {s.na}x{s.nr} echo, {s.nx}x{s.ny} grid in {time.time() - t:.1f}s")
+    if name not in _SCENES:
+        t = time.time()
+        _SCENES[name] = synth.make_scene(name)
+        s = _SCENES[name]
+        _say(f"[{name}] generated {s.na}x{s.nr} echo, {s.nx}x{s.ny} grid in {time.time() - t:.1f}s")
+    return _SCENES[name]
+
+
+def _check_image(s, got, want, label):
+    """Whole-image parity: rel-L2 over every pixel, over the clutter alone (outside the target
+    windows) and over the target windows; each target's peak pixel and magnitude."""
+    wins = target_windows(s)
+    mask = np.zeros(want.shape, bool)
+    for w in wins:
+        mask[w[:, 1], w[:, 0]] = True
+    e_all, e_clut, e_tgt = rel_l2(got, want), rel_l2(got[~mask], want[~mask]), rel_l2(got[mask], want[mask])
+    db = check_peaks(lambda w: got[w[:, 1], w[:, 0]], lambda w: want[w[:, 1], w[:, 0]], wins, s.interp, label)
+    _say(f"[{label}] whole image {got.shape[1]}x{got.shape[0]}: rel-L2 {e_all:.2e} (clutter {e_clut:.2e}, "
+         f"target windows {e_tgt:.2e}); {len(wins)} peaks on the oracle's pixels, worst {db:.4f} dB")
+    assert e_all <= REL_L2 and e_clut <= REL_L2 and e_tgt <= REL_L2, (e_all, e_clut, e_tgt)
+
+
+@pytest.mark.parametrize("scene", ["std", "hifi"])
+def test_full_size_whole_image(sb, scene):
+    """The standard scene (linear) and the hi-fi scene (sinc8, perturbed track) against the
+    oracle's whole image: 1024 x 1024 pixels x 4096 pulses."""
+    import time
+
     import torch
 
+    s = _scene(scene)
+    with sb.Plan.for_scene(s) as plan:
+        img = plan.backproject(torch.from_numpy(s.positions).cuda(), torch.from_numpy(s.echo).cuda())
+        torch.cuda.synchronize()
+        got = img.cpu().numpy().astype(np.complex128)
+    t = time.time()
+    want = oracle.scene_backproject(s)
+    _say(f"[{scene}] oracle image in {time.time() - t:.1f}s on {oracle.threads()} threads")
+    _check_image(s, got, want, f"{scene} {s.interp}")
+
+
+def test_large_scene_sampled(sb):
+    """The large scene (16384 pulses x 8192 bins -> 2048 x 2048): its oracle image would take
+    minutes, so 4000 random pixels (clutter) and every target window are compared, each set
+    against the bar on its own."""
+    import torch
+
+    s = _scene("large")
     with sb.Plan.for_scene(s) as plan:
         img = plan.backproject(torch.from_numpy(s.positions).cuda(), torch.from_numpy(s.echo).cuda())
         torch.cuda.synchronize()
         got = img.cpu().numpy()
     wins = target_windows(s)
-    ij = np.concatenate([sample_pixels(s, 1500, sample_seed)] + wins)
+    rnd = sample_pixels(s, 4000, 80)
+    ij = np.concatenate([rnd] + wins)
     want = oracle.scene_pixels(s, ij)
     g = got[ij[:, 1], ij[:, 0]].astype(np.complex128)
-    assert rel_l2(g, want) <= REL_L2, rel_l2(g, want)
+    nr_ = len(rnd)
+    e_rnd, e_tgt = rel_l2(g[:nr_], want[:nr_]), rel_l2(g[nr_:], want[nr_:])
     lut = {tuple(p): v for p, v in zip(ij.tolist(), want)}
-    check_peaks(lambda w: got[w[:, 1], w[:, 0]], lambda w: np.array([lut[tuple(p)] for p in w.tolist()]), wins)
-    _say(f"[full {scene}] rel-L2 {rel_l2(g, want):.2e} on {len(ij)} pixels")
+    db = check_peaks(lambda w: got[w[:, 1], w[:, 0]], lambda w: np.array([lut[tuple(p)] for p in w.tolist()]), wins,
+                     s.interp, "large linear")
+    _say(f"[large] rel-L2 {e_rnd:.2e} on {nr_} random pixels, {e_tgt:.2e} on {len(ij) - nr_} target-window "
+         f"pixels; worst peak {db:.4f} dB")
+    assert e_rnd <= REL_L2 and e_tgt <= REL_L2, (e_rnd, e_tgt)
 
 
-def test_end_to_end_sampled(sb):
-    """Raw LFM echoes -> GPU range compression -> GPU backprojection, against the fp64
-    oracle chain (numpy matched filter, then the C oracle on sampled pixels)."""
+def test_end_to_end_whole_image(sb):
+    """Raw LFM echoes -> GPU range compression -> GPU backprojection, against the fp64 oracle
+    chain (numpy matched filter, then the C oracle over the whole 1024 x 1024 image)."""
     import torch
 
-    s = synth.make_scene("e2e")
-    _say(f"[e2e] raw {s.na}x{s.nr}")
+    s = _scene("e2e")
     with sb.Plan.for_scene(s, n_fast=s.nr) as plan:
         raw = torch.from_numpy(s.raw).cuda()
         rc = plan.range_compress(raw)
         img = plan.backproject(torch.from_numpy(s.positions).cuda(), rc)
         torch.cuda.synchronize()
-        rc_gpu = rc.cpu().numpy()
-        got = img.cpu().numpy()
-    rc_orc = oracle.rc.range_compress(s.raw, s.fs, s.chirp_T, s.chirp_B, s.window)
-    assert rel_l2(rc_gpu.astype(np.complex128), rc_orc) < 1e-5
-    wins = target_windows(s)
-    ij = np.concatenate([sample_pixels(s, 1000, 55)] + wins)
-    want = oracle.backproject_pixels(s.positions, rc_orc, s.r0, s.dr, s.x0, s.y0, s.z0, s.dx, s.dy,
-                                     s.wavelength, s.interp, ij)
-    g = got[ij[:, 1], ij[:, 0]].astype(np.complex128)
-    assert rel_l2(g, want) <= REL_L2, rel_l2(g, want)
-    lut = {tuple(p): v for p, v in zip(ij.tolist(), want)}
-    check_peaks(lambda w: got[w[:, 1], w[:, 0]], lambda w: np.array([lut[tuple(p)] for p in w.tolist()]), wins)
+        got = img.cpu().numpy().astype(np.complex128)
+        rc_got = rc.cpu().numpy()
+    rc_want = oracle.rc.range_compress(s.raw, s.fs, s.chirp_T, s.chirp_B, s.window)
+    e_rc = rel_l2(rc_got.astype(np.complex128), rc_want)
+    _say(f"[e2e] range compression rel-L2 {e_rc:.2e}")
+    assert e_rc < 1e-5
+    want = oracle.scene_backproject(s, echo=rc_want)
+    _check_image(s, got, want, "e2e linear")
 
 
 # ----------------------------------------------------------------------------- geometry edge cases

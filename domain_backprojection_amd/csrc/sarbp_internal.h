@@ -71,6 +71,7 @@ struct sarbp_plan {
     // exp(+j 4 pi (r0 + k dr) / lambda) for k = -4 .. n_range + 3, stored at [k + 4]
     float2* phase_tab;
     int* progress;    // [2 * n_cu] per-workgroup pulse progress (scheduling hints only)
+    void* scratch;    // device address of the library's static scratch on the plan's device (not owned)
     // range compression
     int rc_log2;       // log2(n_fast), 0 when disabled
     float2* rc_filter; // conj(FFT(ref)) * W / n_fast
@@ -127,6 +128,14 @@ void sarbp_bp_args(const sarbp_params& p, const BpLayout& L, BpArgs* A);
 int sarbp_launch_bp(const sarbp_plan* plan, const double* pos, const float2* echo, const float* dem,
                     float2* image, int n, int accumulate, hipStream_t stream, float2* workspace = nullptr,
                     int nsplit = 1);
+// Argument checks shared by the pulse-group entry points (SARBP_OK or SARBP_EINVAL).
+int sarbp_split_check(const sarbp_plan* plan, const double* positions_d, const void* echo_d, const float* dem_d,
+                      const void* image_d, int32_t n, int32_t accumulate);
+// SARBP_OK when the current device is the plan's.
+int sarbp_check_device(const sarbp_plan* plan);
+// The device address of the static scratch array on `device` (the current device),
+// looked up once per device and cached.
+int sarbp_scratch_address(int device, void** out);
 // Pulse groups of a split backprojection of n pulses (1: no split) and its workspace bytes.
 int sarbp_split_count(const sarbp_plan* plan, int n);
 int sarbp_launch_rc(const sarbp_plan* plan, const float2* raw, float2* out, int n, hipStream_t stream);

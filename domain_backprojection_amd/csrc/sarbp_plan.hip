@@ -325,6 +325,14 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
         }
     }
 
+    // The device address of the library's static pulse-group scratch on this device
+    // (sarbp_backproject_split_noalloc); taken here, once per device.
+    st = sarbp_scratch_address(plan->device, &plan->scratch);
+    if (st != SARBP_OK) {
+        release(plan);
+        return st;
+    }
+
     st = upload(phase_table(p), &plan->phase_tab);
     if (st == SARBP_OK) st = upload(std::vector<int>((size_t)2 * plan->L.n_cu, 0), &plan->progress);
     if (st != SARBP_OK) {
@@ -369,12 +377,14 @@ extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {
     return SARBP_OK;
 }
 
-namespace {
-int check_device(const sarbp_plan* plan) {
+int sarbp_check_device(const sarbp_plan* plan) {
     int cur = -1;
     if (hipGetDevice(&cur) != hipSuccess) return SARBP_EDEVICE;
     return cur == plan->device ? SARBP_OK : SARBP_EINVAL;
 }
+
+namespace {
+int check_device(const sarbp_plan* plan) { return sarbp_check_device(plan); }
 } // namespace
 
 extern "C" int sarbp_backproject(const sarbp_plan* plan, const double* positions_d, const void* echo_d, void* image_d,
@@ -409,13 +419,20 @@ extern "C" size_t sarbp_split_workspace_bytes(const sarbp_plan* plan, int32_t n)
     return (size_t)s * layers * (size_t)plan->p.ny * (size_t)plan->p.nx * sizeof(float2);
 }
 
-extern "C" int sarbp_backproject_split(const sarbp_plan* plan, const double* positions_d, const void* echo_d,
-                                       const float* dem_d, void* image_d, int32_t n, int32_t accumulate,
-                                       void* workspace_d, size_t workspace_bytes, void* stream) {
+int sarbp_split_check(const sarbp_plan* plan, const double* positions_d, const void* echo_d, const float* dem_d,
+                      const void* image_d, int32_t n, int32_t accumulate) {
     if (plan == nullptr || !aligned8(positions_d) || !aligned8(echo_d) || !aligned8(image_d)) return SARBP_EINVAL;
     if (n < 1 || n > plan->p.n_pulses || (accumulate != 0 && accumulate != 1)) return SARBP_EINVAL;
     if (dem_d != nullptr && (!(plan->p.dem_relief > 0.0) || (reinterpret_cast<uintptr_t>(dem_d) & 3u) != 0))
         return SARBP_EINVAL;
+    return SARBP_OK;
+}
+
+extern "C" int sarbp_backproject_split(const sarbp_plan* plan, const double* positions_d, const void* echo_d,
+                                       const float* dem_d, void* image_d, int32_t n, int32_t accumulate,
+                                       void* workspace_d, size_t workspace_bytes, void* stream) {
+    int st = sarbp_split_check(plan, positions_d, echo_d, dem_d, image_d, n, accumulate);
+    if (st != SARBP_OK) return st;
     const size_t need = sarbp_split_workspace_bytes(plan, n);
     if (need > 0) {
         if (!aligned8(workspace_d) || workspace_bytes < need) return SARBP_EINVAL;
@@ -424,7 +441,7 @@ extern "C" int sarbp_backproject_split(const sarbp_plan* plan, const double* pos
         const uintptr_t i = reinterpret_cast<uintptr_t>(image_d), w = reinterpret_cast<uintptr_t>(workspace_d);
         if (i < w + need && w < i + ib) return SARBP_EINVAL; // the workspace overlaps the image
     }
-    const int st = check_device(plan);
+    st = check_device(plan);
     if (st != SARBP_OK) return st;
     return sarbp_launch_bp(plan, positions_d, static_cast<const float2*>(echo_d), dem_d,
                            static_cast<float2*>(image_d), n, accumulate, static_cast<hipStream_t>(stream),
@@ -452,6 +469,7 @@ extern "C" const char* sarbp_status_string(int status) {
         case SARBP_ENOMEM: return "out of memory";
         case SARBP_EDEVICE: return "HIP runtime or kernel launch failure";
         case SARBP_EUNSUPPORTED: return "unsupported configuration";
+        case SARBP_ESCRATCH: return "the call needs more scratch than the library's static buffer holds";
         default: return "unknown status";
     }
 }

@@ -9,6 +9,7 @@ The functions keep the C names: :func:`sarbp_plan_create`,
 :func:`sarbp_backproject`, :func:`sarbp_backproject_dem`, :func:`sarbp_range_compress`,
 :func:`sarbp_interpolate_track`, :func:`sarbp_stream_create`,
 :func:`sarbp_backproject_host`, :func:`sarbp_stream_destroy`, :func:`sarbp_destroy`,
+:func:`sarbp_backproject_split_noalloc`,
 :func:`sarbp_check_indices`, :func:`sarbp_status_string`, :func:`sarbp_version`.  :class:`Plan` and
 :class:`HostStream` wrap the handles' lifetimes.
 """
@@ -34,6 +35,8 @@ SARBP_EINVAL = -1
 SARBP_ENOMEM = -2
 SARBP_EDEVICE = -3
 SARBP_EUNSUPPORTED = -4
+SARBP_ESCRATCH = -5
+SARBP_STATIC_SCRATCH_BYTES = 8 << 20
 
 SARBP_NEAREST = 0
 SARBP_LINEAR = 1
@@ -129,6 +132,8 @@ _lib.sarbp_split_workspace_bytes.restype = ctypes.c_size_t
 _lib.sarbp_backproject_split.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_size_t,
                                          _vp]
 _lib.sarbp_backproject_split.restype = ctypes.c_int
+_lib.sarbp_backproject_split_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp]
+_lib.sarbp_backproject_split_noalloc.restype = ctypes.c_int
 _lib.sarbp_check_indices.argtypes = [ctypes.POINTER(sarbp_params), ctypes.c_int32, _vp, ctypes.c_int32, _vp,
                                      ctypes.POINTER(sarbp_index_report)]
 _lib.sarbp_check_indices.restype = ctypes.c_int
@@ -136,7 +141,8 @@ _lib.sarbp_check_indices.restype = ctypes.c_int
 EXPORTS = ("sarbp_plan_create", "sarbp_backproject", "sarbp_range_compress", "sarbp_destroy",
            "sarbp_status_string", "sarbp_version", "sarbp_stream_create", "sarbp_backproject_host",
            "sarbp_stream_destroy", "sarbp_interpolate_track", "sarbp_backproject_dem",
-           "sarbp_split_workspace_bytes", "sarbp_backproject_split", "sarbp_check_indices")
+           "sarbp_split_workspace_bytes", "sarbp_backproject_split", "sarbp_backproject_split_noalloc",
+           "sarbp_check_indices")
 
 
 class SarbpError(RuntimeError):
@@ -257,6 +263,28 @@ def sarbp_backproject_split(handle, positions: torch.Tensor, echo: torch.Tensor,
                                       ws_bytes, _stream(stream))
     if st != SARBP_OK:
         raise SarbpError(st, "sarbp_backproject_split")
+
+
+def sarbp_backproject_split_noalloc(handle, positions: torch.Tensor, echo: torch.Tensor, image: torch.Tensor,
+                                    n: int | None = None, accumulate: int = 0, stream=None,
+                                    dem: torch.Tensor | None = None) -> None:
+    """As :func:`sarbp_backproject_split` with the partial images in the library's static
+    device array (no workspace, no allocation; calls on one GPU must not overlap)."""
+    if n is None:
+        n = positions.shape[0]
+    if positions.dim() != 2 or positions.shape[1] != 3 or positions.shape[0] < n or echo.shape[0] < n:
+        raise ValueError("positions must be (>= n, 3) and echo (>= n, n_range)")
+    dem_p = None
+    if dem is not None:
+        if tuple(dem.shape) != tuple(image.shape):
+            raise ValueError("dem must have the image's shape (ny, nx)")
+        dem_p = _dev_ptr(dem, torch.float32, "dem")
+    st = _lib.sarbp_backproject_split_noalloc(handle, _dev_ptr(positions, torch.float64, "positions"),
+                                              _dev_ptr(echo, torch.complex64, "echo"), dem_p,
+                                              _dev_ptr(image, torch.complex64, "image"), int(n), int(accumulate),
+                                              _stream(stream))
+    if st != SARBP_OK:
+        raise SarbpError(st, "sarbp_backproject_split_noalloc")
 
 
 def sarbp_check_indices(params: sarbp_params, positions, dem=None, n_cu: int = 0) -> dict:

@@ -30,7 +30,8 @@
  *     a compute unit; it steers scheduling only, so overlapping calls that
  *     share it stay correct (they may run slightly slower).  Calls that write
  *     the same image must be ordered by the caller.  No entry point allocates
- *     device memory except sarbp_plan_create and sarbp_stream_create.
+ *     device memory except sarbp_plan_create and sarbp_stream_create (the library's
+ *     one static device array is described at sarbp_backproject_split_noalloc).
  */
 #ifndef SARBP_H
 #define SARBP_H
@@ -48,6 +49,7 @@ extern "C" {
 #define SARBP_ENOMEM (-2)       /* a device or host allocation failed (plan creation only) */
 #define SARBP_EDEVICE (-3)      /* a HIP runtime call or kernel launch failed */
 #define SARBP_EUNSUPPORTED (-4) /* valid request the library cannot serve (e.g. LDS too small) */
+#define SARBP_ESCRATCH (-5)     /* the call needs more than the library's static scratch (see below) */
 
 /* Interpolation of the range-compressed echo at a fractional bin u (section 2.2):
  *   NEAREST: s[floor(u + 1/2)]
@@ -172,6 +174,32 @@ size_t sarbp_split_workspace_bytes(const sarbp_plan* plan, int32_t n);
 int sarbp_backproject_split(const sarbp_plan* plan, const double* positions_d, const void* echo_d,
                             const float* dem_d, void* image_d, int32_t n, int32_t accumulate, void* workspace_d,
                             size_t workspace_bytes, void* stream);
+
+/* ---- For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the pulse-group
+ * backprojection with its partial images in a static device array of the library
+ * instead of a caller workspace. ------------------------------------------------ */
+
+/* Size of that array, per GPU: 8 MiB.  On a 256-CU MI355X every plan's pulse-group
+ * workspace fits: at most 2 x 256 workgroups' tiles of up to 2048 pixels, 8 bytes
+ * each. */
+#define SARBP_STATIC_SCRATCH_BYTES (8u << 20)
+
+/* As sarbp_backproject_split with no workspace argument: the S partial images go to
+ * the library's static array on the plan's device (its address on each device is
+ * taken once, by the first sarbp_plan_create there).  The call itself allocates
+ * nothing and runs the same kernels, so its image equals sarbp_backproject_split's
+ * bit for bit.  When sarbp_split_workspace_bytes(plan, n) is 0 it runs unsplit,
+ * as sarbp_backproject does.  The array keeps the last call's partials; every
+ * element is written before it is read, so no clearing is needed, but all calls on
+ * one GPU share it: two calls that may run at the same time on one GPU (on
+ * different streams or host threads) race and give wrong images -- order them.
+ * Returns SARBP_ESCRATCH when the workspace would exceed
+ * SARBP_STATIC_SCRATCH_BYTES (possible only on a GPU with more compute units), and
+ * otherwise the codes of sarbp_backproject_split. */
+int sarbp_backproject_split_noalloc(const sarbp_plan* plan, const double* positions_d, const void* echo_d,
+                                    const float* dem_d, void* image_d, int32_t n, int32_t accumulate,
+                                    void* stream);
 
 /* Range-compress n raw pulses (section 3.1 of the page):
  *   out_n = IFFT( FFT(raw_n) * conj(FFT(ref)) * W ) with 1/n_fast on the inverse,

@@ -130,7 +130,7 @@ __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem,
                                               int p0, int n0, int i_pix, int j_pix0, float dxl, const float* dyv,
                                               const float* ddv, float* accr, float* acci, float* cmpr, float* cmpi,
                                               const float* dzv, const float* hv, double zl, uint32_t wstride,
-                                              const double* pxd, float tie_lim) {
+                                              const double* pxd, float tie_lim, int win_c) {
     constexpr int CS = (DEM || F64) ? 3 : 2;
     float g[G][PPT];
     uint32_t kb[G][PPT];
@@ -165,7 +165,7 @@ __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem,
                     const int kabs = nearest_bin_fp64<DevMath>(A.pos[pn], A.pos[pn + 1], A.pos[pn + 2], A.x0, A.y0, zp,
                                                                A.dx, A.dy, A.r0, A.dr, i_pix, j_pix0 + BP_WAVES * m);
                     int kr = kabs - klo_s[p0 + q];
-                    kr = kr < 0 ? 0 : (kr > A.win - 1 ? A.win - 1 : kr);
+                    kr = kr < 0 ? 0 : (kr > win_c - 1 ? win_c - 1 : kr);
                     g[q][m] = g[q][m] + (float)((int)kb[q][m] - kr); // = ub - kr
                     kb[q][m] = (uint32_t)kr;
                 }
@@ -190,9 +190,10 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
                                                  const int* klo_s, int np, int n0, int i_pix, int j_pix0,
                                                  float dxl, const float* dyv, const float* ddv, float* accr,
                                                  float* acci, float* cmpr, float* cmpi, const float* dzv,
-                                                 const float* hv, double zl, const double* pxd, float tie_lim) {
+                                                 const float* hv, double zl, const double* pxd, float tie_lim,
+                                                 int win_c) {
     const int eb = entry_bytes<INTERP>();
-    const uint32_t wstride = (uint32_t)(A.win * eb);
+    const uint32_t wstride = (uint32_t)(win_c * eb);
     const float kappa = A.kappa;
     if constexpr (INTERP == SARBP_NEAREST) {
         int p = 0;
@@ -200,10 +201,10 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
         for (; p + G <= np; p += G)
             nearest_group<G, MODE, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, p, n0, i_pix, j_pix0, dxl,
                                                                    dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl,
-                                                                   wstride, pxd, tie_lim);
+                                                                   wstride, pxd, tie_lim, win_c);
         for (; p < np; ++p)
             nearest_group<1, MODE, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, p, n0, i_pix, j_pix0, dxl, dyv, ddv, accr,
-                                                  acci, cmpr, cmpi, dzv, hv, zl, wstride, pxd, tie_lim);
+                                                  acci, cmpr, cmpi, dzv, hv, zl, wstride, pxd, tie_lim, win_c);
         return;
     }
     constexpr int kUnroll = F64 ? BP_PUNROLL_F64 : (INTERP == SARBP_LINEAR ? BP_PUNROLL_LINEAR : BP_PUNROLL_SINC8);
@@ -297,15 +298,21 @@ __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
     return make_float2(fmaf(a.x, b.x, -(a.y * b.y)), fmaf(a.x, b.y, a.y * b.x));
 }
 
-template <int INTERP>
-__device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int np, int n0, int tid) {
+template <int INTERP, bool EXACTW>
+__device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int np, int n0, int tid, int W) {
     constexpr int B = INTERP == SARBP_SINC8 ? 1 : 2;
-    const int W = A.win, Wu = W / B, nr = A.n_range;
+    const int Wu = W / B, nr = A.n_range;
     const int nu = np * Wu;
+    // the pulse of a step: the plan's multiply-high for its window, an fp32 quotient
+    // with an exact correction for a chunk's own window
+    const float rwu = EXACTW ? 1.0f / (float)Wu : 0.f;
     for (int u = tid; u < nu; u += BP_THREADS) {
         int p, k;
         bool bad;
-        stage_step<DevMath, B>(A, klo_s, u, Wu, &p, &k, &bad);
+        if constexpr (EXACTW)
+            stage_step_f32<B>(klo_s, u, Wu, rwu, &p, &k, &bad);
+        else
+            stage_step<DevMath, B>(klo_s, u, Wu, A.win_magic, &p, &k, &bad);
         const float2* row = A.echo + (size_t)(n0 + p) * (size_t)nr;
         const int ke = carrier_index<B>(k, nr, bad);
         const float2 c0 = A.phase[ke];
@@ -419,6 +426,7 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     // window allows for up to dem_relief.  A tile beyond that bound is NaN.
     float dzv[PPT], hv[PPT];
     bool bad_tile = false;
+    double za = zl, zb = zl; // the tile's height range (one plane, or the terrain's)
 #pragma unroll
     for (int m = 0; m < PPT; ++m) dzv[m] = hv[m] = 0.f;
     if constexpr (DEM) {
@@ -450,6 +458,8 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         bad_tile = !((double)hmax - (double)hmin <= A.dem_relief);
         const double hc = 0.5 * ((double)hmin + (double)hmax);
         cz = A.z0 + hc;
+        za = A.z0 + (double)hmin;
+        zb = A.z0 + (double)hmax;
 #pragma unroll
         for (int m = 0; m < PPT; ++m) {
             const double ddy = ((double)j_off[m] - cyp) * A.dy;
@@ -461,19 +471,44 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         }
     }
 
-    const int P = A.chunk, W = A.win;
+    const int P = A.chunk;
     constexpr int CS = (DEM || F64) ? 3 : 2; // float4 constants per pulse
-    float4* cst = reinterpret_cast<float4*>(smem + (size_t)P * W * entry_bytes<INTERP>());
+    // sinc8 stages each chunk's exact window extent, about half the plan's (tile
+    // diagonal) window: its entries are the costliest to stage (measured 5 % faster on
+    // the hi-fi scene).  Linear and nearest stage the plan's window: there the exact
+    // extent's extra set-up cost about as much as its shorter staging saved.
+    constexpr bool EXACTW = INTERP == SARBP_SINC8;
+    // LDS: room for P windows of the plan's (longest) length, each chunk packing its
+    // own; then per pulse the constants, the window start and the tile centre's
+    // position u_c; then the chunk words and the tile's pixel box.
+    float4* cst = reinterpret_cast<float4*>(smem + (size_t)P * A.win * entry_bytes<INTERP>());
     int* klo_s = reinterpret_cast<int*>(cst + CS * P);
-    int* prio_s = klo_s + P;
-    // The accuracy mode of a chunk is the OR of its pulses' modes, and its nearest
-    // tie band follows from the largest of their range-term sizes rho.  The words
-    // are double-buffered: chunk c writes mode_s[c & 1] and rho_s[c & 1] and clears
-    // the other pair, which the previous chunk finished reading before its last
-    // barrier.  (rho >= 0, so its float bits order as integers.)
+    double* uc_s = reinterpret_cast<double*>(klo_s + ((P + 1) & ~1));
+    int* prio_s = reinterpret_cast<int*>(uc_s + (EXACTW ? P : 0)); // (u_c is kept only for exact windows)
+    // The accuracy mode of a chunk is the OR of its pulses' modes, its window length
+    // the longest of theirs, and its nearest tie band follows from the largest of
+    // their range-term sizes rho.  The words are double-buffered: chunk c writes
+    // mode_s/rho_s/wlen_s[c & 1] and clears the other set, which the previous chunk
+    // finished reading before its last barrier.  (rho >= 0, so its float bits order
+    // as integers.)
     int* mode_s = prio_s + 1;
     int* rho_s = mode_s + 2;
-    if (tid == 0) mode_s[0] = mode_s[1] = rho_s[0] = rho_s[1] = 0;
+    int* wlen_s = rho_s + 2;
+    // the tile's pixel box and reference point, read by the set-up lanes of each chunk
+    double* box_s = reinterpret_cast<double*>(prio_s + 8);
+    if (tid == 0) {
+        mode_s[0] = mode_s[1] = rho_s[0] = rho_s[1] = wlen_s[0] = wlen_s[1] = 0;
+        box_s[6] = cx;
+        box_s[7] = cy;
+        box_s[8] = cz;
+        const TileBox b = tile_box(A, T, za, zb);
+        box_s[0] = b.xa;
+        box_s[1] = b.xb;
+        box_s[2] = b.ya;
+        box_s[3] = b.yb;
+        box_s[4] = b.za;
+        box_s[5] = b.zb;
+    }
     __syncthreads();
 
     // The first chunk is half size on alternate workgroups: both placements of a
@@ -481,22 +516,48 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     const int stagger = BP_STAGGER ? (((int)blockIdx.x / A.slots) ^ ((int)blockIdx.x >> 3)) & 1 : 0;
     for (int n0 = 0, np = 0, c = 0; n0 < (bad_tile ? 0 : pn); n0 += np, ++c) {
         np = min((n0 == 0 && stagger) ? max(1, P >> 1) : P, pn - n0);
+        // Set-up: lanes 0 .. np-1 (waves 0 and 1) take each pulse's constants in fp64;
+        // with exact windows, lanes WL .. WL+np-1 (the next waves) take its window in
+        // parallel, and the tile centre's position within it follows the barrier.
+        constexpr int WL = 128;
         if (tid < np) {
             const size_t pa = 3 * (size_t)(pb + n0 + tid);
             const double ax = A.pos[pa], ay = A.pos[pa + 1], az = A.pos[pa + 2];
+            const double gx = box_s[6], gy = box_s[7], gz = box_s[8];
             float rho = 0.f;
-            const int need = F64 ? pulse_setup_f64(A, ax, ay, az, cx, cy, cz, cst + CS * tid, klo_s + tid)
-                                 : pulse_setup(A, ax, ay, az, cx, cy, cz, cst + CS * tid, klo_s + tid, &rho, DEM);
+            double uc;
+            const int need = F64 ? pulse_setup_f64(A, ax, ay, az, gx, gy, gz, cst + CS * tid, &uc)
+                                 : pulse_setup(A, ax, ay, az, gx, gy, gz, cst + CS * tid, &uc, &rho, DEM);
+            if constexpr (EXACTW) {
+                uc_s[tid] = uc;
+            } else {
+                const int klo = centre_window(A, uc);
+                klo_s[tid] = klo;
+                pulse_finish(A, uc, klo, cst + CS * tid, DEM, F64);
+            }
             if (need) atomicOr(mode_s + (c & 1), need);
             if constexpr (INTERP == SARBP_NEAREST && !F64) atomicMax(rho_s + (c & 1), __float_as_int(rho));
+        } else if (EXACTW && tid >= WL && tid < WL + np) {
+            const int t = tid - WL;
+            const size_t pa = 3 * (size_t)(pb + n0 + t);
+            const TileBox box = {box_s[0], box_s[1], box_s[2], box_s[3], box_s[4], box_s[5]};
+            atomicMax(wlen_s + (c & 1), pulse_window(A, A.pos[pa], A.pos[pa + 1], A.pos[pa + 2], box, klo_s + t));
         }
         if (tid == 0) {
             *prio_s = chunk_priority(A, n0, pn);
             mode_s[(c + 1) & 1] = 0;
             rho_s[(c + 1) & 1] = 0;
+            wlen_s[(c + 1) & 1] = 0;
         }
         __syncthreads();
-        stage_chunk<INTERP>(A, smem, klo_s, np, pb + n0, tid);
+        int win_c = A.win;
+        if constexpr (EXACTW) {
+            // each pulse's tile-centre position within its window (read by the pulse
+            // loop after the next barrier), while all lanes stage the windows
+            if (tid < np) pulse_finish(A, uc_s[tid], klo_s[tid], cst + CS * tid, DEM, F64);
+            win_c = chunk_window(__builtin_amdgcn_readfirstlane(wlen_s[c & 1]), 1, A.win);
+        }
+        stage_chunk<INTERP, EXACTW>(A, smem, klo_s, np, pb + n0, tid, win_c);
         __syncthreads();
         set_priority(*prio_s);
         const int mode = __builtin_amdgcn_readfirstlane(mode_s[c & 1]); // the same word for every lane
@@ -506,17 +567,20 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         float tie_lim = 0.f;
         if constexpr (INTERP == SARBP_NEAREST) {
             const float rho = __int_as_float(__builtin_amdgcn_readfirstlane(rho_s[c & 1]));
-            tie_lim = 0.5f - fmaf(A.tie_rho[mi], rho, A.tie_base[mi]);
+            tie_lim = 0.5f - fmaf(A.tie_rho[mi], rho, fmaf(A.tie_win, (float)win_c, A.tie_base[mi]));
         }
         if (m2)
             accumulate_chunk<INTERP, 2, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, np, pb + n0, i0 + lane, j0 + wave, dxl, dyv,
-                                                        ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, tie_lim);
+                                                        ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, tie_lim,
+                                                        win_c);
         else if (m1)
             accumulate_chunk<INTERP, 1, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, np, pb + n0, i0 + lane, j0 + wave, dxl, dyv,
-                                                        ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, tie_lim);
+                                                        ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, tie_lim,
+                                                        win_c);
         else
             accumulate_chunk<INTERP, 0, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, np, pb + n0, i0 + lane, j0 + wave, dxl, dyv,
-                                                        ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, tie_lim);
+                                                        ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, tie_lim,
+                                                        win_c);
         if constexpr (ACC == SARBP_ACC_CHUNK64) {
 #pragma unroll
             for (int m = 0; m < PPT; ++m) {

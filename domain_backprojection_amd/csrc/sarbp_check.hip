@@ -47,21 +47,26 @@ struct Checker {
         return definition_bin<HostMath>(a[0], a[1], a[2], A.x0, A.y0, z, A.dx, A.dy, A.r0, A.dr, i, j);
     }
 
-    void stage_check(const int* klo_s, int np) {
+    void stage_check(const int* klo_s, int np, int win_c) {
         const int B = p.interp == SARBP_SINC8 ? 1 : 2;
-        const int wu = A.win / B;
+        const int wu = win_c / B;
+        const bool exactw = p.interp == SARBP_SINC8;
+        const float rwu = 1.0f / (float)wu;
+        if (win_c % B != 0 || win_c > A.win) ++r->staging_violations;
         for (int u = 0; u < np * wu; ++u) {
             int pp, k;
             bool bad;
-            if (B == 1)
-                stage_step<HostMath, 1>(A, klo_s, u, wu, &pp, &k, &bad);
+            if (exactw)
+                stage_step_f32<1>(klo_s, u, wu, rwu, &pp, &k, &bad);
+            else if (B == 1)
+                stage_step<HostMath, 1>(klo_s, u, wu, A.win_magic, &pp, &k, &bad);
             else
-                stage_step<HostMath, 2>(A, klo_s, u, wu, &pp, &k, &bad);
+                stage_step<HostMath, 2>(klo_s, u, wu, A.win_magic, &pp, &k, &bad);
             bool ok = pp == u / wu && pp >= 0 && pp < np;
             if (ok) {
                 const int ke = B == 1 ? carrier_index<1>(k, A.n_range, bad) : carrier_index<2>(k, A.n_range, bad);
                 ok = ke >= 0 && ke + B - 1 <= A.n_range + 9;
-                if (!bad) ok = ok && k - klo_s[pp] >= 0 && k - klo_s[pp] + B - 1 <= A.win - 1;
+                if (!bad) ok = ok && k - klo_s[pp] >= 0 && k - klo_s[pp] + B - 1 <= win_c - 1;
             }
             if (!ok) ++r->staging_violations;
         }
@@ -95,13 +100,14 @@ struct Checker {
         std::vector<int> mode(P);
         const int nb = A.group_blocks;
         const bool nearest = p.interp == SARBP_NEAREST;
+        const bool exactw = p.interp == SARBP_SINC8; // (the kernels' EXACTW)
         for (int b = 0; b < nb; ++b) {
             const TileFrame T = tile_frame<PPT>(A, b);
             // Lane offsets, as in the kernel: lanes past the grid's edge repeat the last column or row.
             float dxl[BP_TX], dyv[BP_WAVES][PPT], ddv[BP_TX][BP_WAVES][PPT], dzv[BP_TX][BP_WAVES][PPT];
             double pxd[BP_TX][BP_WAVES][1 + 3 * PPT];
             float hv[BP_TX][BP_WAVES][PPT];
-            double cz = T.zl;
+            double cz = T.zl, za = T.zl, zb = T.zl;
             bool bad_tile = false;
             double hc = 0.0;
             if (DEM) {
@@ -118,7 +124,10 @@ struct Checker {
                 bad_tile = !((double)hmax - (double)hmin <= A.dem_relief);
                 hc = 0.5 * ((double)hmin + (double)hmax);
                 cz = A.z0 + hc;
+                za = A.z0 + (double)hmin;
+                zb = A.z0 + (double)hmax;
             }
+            const TileBox box = tile_box(A, T, za, zb);
             if (bad_tile) {
                 ++r->nan_tiles;
                 continue;
@@ -145,33 +154,42 @@ struct Checker {
             const int stagger = BP_STAGGER ? ((b / A.slots) ^ (b >> 3)) & 1 : 0;
             for (int n0 = 0, np = 0; n0 < n; n0 += np) {
                 np = std::min((n0 == 0 && stagger) ? std::max(1, P >> 1) : P, n - n0);
-                int cmode = 0;
+                int cmode = 0, wmax = 0;
                 float crho = 0.f;
                 for (int t = 0; t < np; ++t) {
                     const double* a = pos + 3 * (size_t)(n0 + t);
                     float rh = 0.f;
-                    mode[t] = F64 ? pulse_setup_f64(A, a[0], a[1], a[2], T.cx, T.cy, cz, &cst[(size_t)CS * t], &klo[t])
-                                  : pulse_setup(A, a[0], a[1], a[2], T.cx, T.cy, cz, &cst[(size_t)CS * t], &klo[t],
-                                                &rh, DEM);
+                    double uc;
+                    mode[t] = F64 ? pulse_setup_f64(A, a[0], a[1], a[2], T.cx, T.cy, cz, &cst[(size_t)CS * t], &uc)
+                                  : pulse_setup(A, a[0], a[1], a[2], T.cx, T.cy, cz, &cst[(size_t)CS * t], &uc, &rh,
+                                                DEM);
+                    if (exactw)
+                        wmax = std::max(wmax, pulse_window(A, a[0], a[1], a[2], box, &klo[t]));
+                    else
+                        klo[t] = centre_window(A, uc);
+                    pulse_finish(A, uc, klo[t], &cst[(size_t)CS * t], DEM, F64);
                     cmode |= mode[t];
                     if (!F64) crho = std::max(crho, rh);
                 }
+                const int win_c = exactw ? chunk_window(wmax, 1, A.win) : A.win;
                 const int mi = (cmode & 2) ? 2 : (cmode & 1);
                 ++r->mode_chunks[mi];
-                stage_check(klo.data(), np);
+                r->window_mean += win_c;
+                ++r->chunks;
+                stage_check(klo.data(), np, win_c);
                 // the tie band (twice the error bound of the chunk's window positions)
-                const float band = fmaf(A.tie_rho[mi], crho, A.tie_base[mi]);
+                const float band = fmaf(A.tie_rho[mi], crho, fmaf(A.tie_win, (float)win_c, A.tie_base[mi]));
                 const float tie_lim = 0.5f - band;
                 if (nearest) r->tie_band_max = std::max(r->tie_band_max, band);
                 if (mi == 2)
                     pixels<2, PPT, DEM, F64>(T, np, n0, cst.data(), klo.data(), dxl, dyv, ddv, dzv, pxd, hv, hc,
-                                             tie_lim, band);
+                                             tie_lim, band, win_c);
                 else if (mi == 1)
                     pixels<1, PPT, DEM, F64>(T, np, n0, cst.data(), klo.data(), dxl, dyv, ddv, dzv, pxd, hv, hc,
-                                             tie_lim, band);
+                                             tie_lim, band, win_c);
                 else
                     pixels<0, PPT, DEM, F64>(T, np, n0, cst.data(), klo.data(), dxl, dyv, ddv, dzv, pxd, hv, hc,
-                                             tie_lim, band);
+                                             tie_lim, band, win_c);
             }
         }
     }
@@ -180,7 +198,7 @@ struct Checker {
     void pixels(const TileFrame& T, int np, int n0, const float4* cst, const int* klo, const float* dxl,
                 const float (*dyv)[PPT], const float (*ddv)[BP_WAVES][PPT], const float (*dzv)[BP_WAVES][PPT],
                 const double (*pxd)[BP_WAVES][1 + 3 * PPT], const float (*hv)[BP_WAVES][PPT], double hc,
-                float tie_lim, float band) {
+                float tie_lim, float band, int win_c) {
         const bool nearest = p.interp == SARBP_NEAREST;
         const double half = nearest ? 0.5 : 0.0;
         for (int t = 0; t < np; ++t) {
@@ -197,9 +215,9 @@ struct Checker {
                                                pxd[lane][w], m, PPT, &k, &f, &ub);
                         ++r->decisions;
                         if (bad) continue;
-                        if (!(ub >= 0.0) || !(k <= (uint32_t)(A.win - 1))) ++r->window_violations;
+                        if (!(ub >= 0.0) || !(k <= (uint32_t)(win_c - 1))) ++r->window_violations;
                         r->min_position = std::min(r->min_position, ub);
-                        r->max_position_margin = std::max(r->max_position_margin, ub - (double)A.win);
+                        r->max_position_margin = std::max(r->max_position_margin, ub - (double)win_c);
                         if (i >= A.nx || j >= A.ny) continue; // lanes past the edge: results not stored
                         const double z = DEM ? A.z0 + (double)hv[lane][w][m] : T.zl;
                         const double u = def_bin(n0 + t, i, j, z);
@@ -212,7 +230,7 @@ struct Checker {
                         if (fabsf(f - 0.5f) > tie_lim) {
                             ++r->nearest_rechecks;
                             const int kr = kdef - klo[t];
-                            if (kr < 0 || kr > A.win - 1) ++r->nearest_recheck_clamped;
+                            if (kr < 0 || kr > win_c - 1) ++r->nearest_recheck_clamped;
                         } else if ((int)k + klo[t] != kdef) {
                             ++r->nearest_escapes;
                         }
@@ -251,5 +269,6 @@ extern "C" int sarbp_check_indices(const sarbp_params* params, int32_t n_cu, con
     } else {
         dem ? c.run<2, true, false>() : c.run<2, false, false>();
     }
+    if (report->chunks > 0) report->window_mean /= (double)report->chunks;
     return SARBP_OK;
 }

@@ -93,6 +93,58 @@ __host__ __device__ __forceinline__ TileFrame tile_frame(const BpArgs& A, int gb
     return t;
 }
 
+// The box spanned by a tile's in-grid pixel centres: x in [xa, xb], y in [ya, yb]
+// and heights z in [za, zb] (one plane: za = zb; terrain: the tile's height range).
+struct TileBox {
+    double xa, xb, ya, yb, za, zb;
+};
+
+__host__ __device__ __forceinline__ TileBox tile_box(const BpArgs& A, const TileFrame& t, double za, double zb) {
+    TileBox b;
+    b.xa = t.cx + ((double)t.i0 - t.cxp) * A.dx;
+    b.xb = t.cx + ((double)t.i_last - t.cxp) * A.dx;
+    b.ya = t.cy + ((double)t.j0 - t.cyp) * A.dy;
+    b.yb = t.cy + ((double)t.j_last - t.cyp) * A.dy;
+    b.za = za;
+    b.zb = zb;
+    return b;
+}
+
+// The echo window of one pulse for one tile: the bins floor(u) the tile's pixels
+// can take, u = (R - r0) / dr, from the nearest and the farthest point of the
+// tile's box to the antenna (the nearest: each coordinate clamped into the box;
+// the farthest: the far corner), with margin_lo spare bins below and three above
+// (room for the fp32 window position's error and for nearest's + 1/2).  Sets the
+// first bin, or INT32_MIN for a pulse without finite geometry, and returns the
+// length W_p = floor(u_max) - floor(u_min) + margin_lo + 3, which the triangle
+// inequality keeps within the plan's window (the tile's diagonal in bins plus the
+// same margins).
+__host__ __device__ inline int pulse_window(const BpArgs& A, double ax, double ay, double az, const TileBox& b,
+                                            int* klo) {
+    const double nx = fmin(fmax(ax, b.xa), b.xb) - ax, ny = fmin(fmax(ay, b.ya), b.yb) - ay,
+                 nz = fmin(fmax(az, b.za), b.zb) - az;
+    const double fx = fmax(fabs(b.xa - ax), fabs(b.xb - ax)), fy = fmax(fabs(b.ya - ay), fabs(b.yb - ay)),
+                 fz = fmax(fabs(b.za - az), fabs(b.zb - az));
+    const double umin = (sqrt(nx * nx + ny * ny + nz * nz) - A.r0) * A.inv_dr;
+    const double umax = (sqrt(fx * fx + fy * fy + fz * fz) - A.r0) * A.inv_dr;
+    const double kmin = floor(umin) - (double)A.margin_lo;
+    const double w = floor(umax) - floor(umin) + (double)(A.margin_lo + 3);
+    if (!(fabs(kmin) < 1.0e9 && w >= 0.0 && w < 2.0e9)) {
+        *klo = INT32_MIN;
+        return A.margin_lo + 3;
+    }
+    *klo = (int)kmin;
+    return w < (double)A.win ? (int)w : A.win;
+}
+
+// The window length of a chunk: the longest of its pulses' windows, even where
+// staging takes two bins per step, and within the plan's window.
+__host__ __device__ __forceinline__ int chunk_window(int wmax, int bins_per_step, int win) {
+    int w = wmax < 6 ? 6 : wmax;
+    if (bins_per_step == 2) w += w & 1;
+    return w < win ? w : win;
+}
+
 // Per-pulse constants of the current tile, two float4 per pulse:
 //   c0 = (2 ux, 2 uy, ft, a)   c1 = (b, c, 1/R_t^2, a2)
 // with u = c - a_n, ft = u_c - k_lo (fractional bin of the tile centre within
@@ -106,43 +158,69 @@ __host__ __device__ __forceinline__ TileFrame tile_frame(const BpArgs& A, int gb
 // *rho_out receives the bound (|d|^2 + 2 |d| R_t) / (2 R_t dr), |d| <= half_span,
 // on the range-difference terms in bins, from which the nearest tie band is sized.
 __host__ __device__ inline int pulse_setup(const BpArgs& A, double ax, double ay, double az, double cx, double cy,
-                                           double cz, float4* cst, int* klo_out, float* rho_out, bool dem) {
+                                           double cz, float4* cst, double* uc_out, float* rho_out, bool dem) {
     const double ux = cx - ax, uy = cy - ay, uz = cz - az;
     const double R2 = ux * ux + uy * uy + uz * uz;
     const double Rt = sqrt(R2);
     const double uc = (Rt - A.r0) * A.inv_dr;
-    const double klo_d = floor(uc - A.half_span_bins) - (double)A.margin_lo;
-    const bool ok = isfinite(Rt) && Rt > 0.0 && isfinite(uc) && fabs(klo_d) < 1.0e9;
+    const bool ok = isfinite(Rt) && Rt > 0.0 && isfinite(uc) && fabs(uc) < 1.0e9;
     if (!ok) {
-        // Non-finite geometry: park every pixel on window entry margin_lo and
-        // let the staging fill the window with NaN, so NaN propagates.
-        cst[0] = make_float4(0.f, 0.f, (float)A.margin_lo + 0.25f, 0.f);
-        cst[1] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (dem) cst[2] = make_float4(0.f, 0.f, 0.f, 0.f);
-        *klo_out = INT32_MIN;
+        *uc_out = NAN; // parked by pulse_finish
         *rho_out = 0.f;
         return 0;
     }
     const double inv_r = 1.0 / Rt;
     const double idr = A.inv_dr;
-    // nearest rounds u: the +1/2 is folded into the window position
-    const double ft = uc - klo_d + (A.round_half ? 0.5 : 0.0);
     // q_m bounds |q| over the tile: |d| <= half_span and |u| = R_t.
     const double hs = A.half_span;
     const double q = (hs * hs + 2.0 * hs * Rt) * inv_r * inv_r;
     const double a = 0.5 * inv_r * idr;
-    cst[0] = make_float4((float)(2.0 * ux), (float)(2.0 * uy), (float)ft, (float)a);
+    cst[0] = make_float4((float)(2.0 * ux), (float)(2.0 * uy), 0.f, (float)a); // .z: ft, set by pulse_finish
     cst[1] = make_float4((float)(-0.125 * inv_r * inv_r * inv_r * idr),
                          (float)(0.0625 * inv_r * inv_r * inv_r * inv_r * inv_r * idr), (float)(inv_r * inv_r),
                          (float)(a * (1.0 + (3.0 / 32.0) * q * q)));
     if (dem) cst[2] = make_float4((float)(2.0 * uz), 0.f, 0.f, 0.f);
-    *klo_out = (int)klo_d;
+    *uc_out = uc;
     *rho_out = (float)(0.5 * q * Rt * idr * 1.0000001);
     // Truncation error of each series for the worst pixel of the tile, in bins,
     // against 1e-6 bins (below the fp32 rounding of the window position).
     const double e2 = Rt * (q * q * q * (1.0 / 64.0) + q * q * q * q * (5.0 / 128.0)) * idr;
     const double e3 = Rt * q * q * q * q * (5.0 / 128.0) * idr;
     return (q > 0.25 || e3 > 1e-6) ? 2 : (e2 > 1e-6 ? 1 : 0);
+}
+
+// The window of a pulse from the tile centre's bin u_c alone: k_lo = floor(u_c -
+// half_span / dr) - margin_lo, with the plan's length (the triangle inequality
+// bounds every pixel's range by R_t +- half_span).  INT32_MIN for a pulse without
+// finite geometry.
+__host__ __device__ __forceinline__ int centre_window(const BpArgs& A, double uc) {
+    const double klo = floor(uc - A.half_span_bins) - (double)A.margin_lo;
+    return fabs(klo) < 1.0e9 ? (int)klo : INT32_MIN;
+}
+
+// The tile centre's position within its pulse window, ft = u_c - k_lo (+ 1/2 for
+// nearest, whose window positions carry u + 1/2), once both the set-up (u_c) and
+// the window (k_lo) are known.  A pulse without finite geometry is parked: every
+// pixel on window entry margin_lo, whose staged samples are NaN, so NaN propagates.
+__host__ __device__ inline void pulse_finish(const BpArgs& A, double uc, int klo, float4* cst, bool dem, bool f64) {
+    if (klo == INT32_MIN || !isfinite(uc)) {
+        if (f64) {
+            double2* cd = reinterpret_cast<double2*>(cst);
+            cd[0] = make_double2(0.0, 0.0);
+            cd[1] = make_double2((double)A.margin_lo + 0.25, 0.0);
+            cd[2] = make_double2(0.0, 0.0);
+        } else {
+            cst[0] = make_float4(0.f, 0.f, (float)A.margin_lo + 0.25f, 0.f);
+            cst[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (dem) cst[2] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        return;
+    }
+    const double ft = uc - (double)klo + (A.round_half ? 0.5 : 0.0);
+    if (f64)
+        reinterpret_cast<double2*>(cst)[1].x = ft;
+    else
+        cst[0].z = (float)ft;
 }
 
 // Per-pulse constants of the fp64-range kernels (tiles whose range extent is too
@@ -153,27 +231,22 @@ __host__ __device__ inline int pulse_setup(const BpArgs& A, double ax, double ay
 // whose first omitted term stays below 1e-7 bins over the tile, else exactly
 // (mode 2).  (1e-7 bins is below the fp32 rounding of the fraction returned.)
 __host__ __device__ inline int pulse_setup_f64(const BpArgs& A, double ax, double ay, double az, double cx, double cy,
-                                               double cz, float4* cst, int* klo_out) {
+                                               double cz, float4* cst, double* uc_out) {
     double2* cd = reinterpret_cast<double2*>(cst);
     const double ux = cx - ax, uy = cy - ay, uz = cz - az;
     const double Rt = sqrt(ux * ux + uy * uy + uz * uz);
     const double uc = (Rt - A.r0) * A.inv_dr;
-    const double klo_d = floor(uc - A.half_span_bins) - (double)A.margin_lo;
-    if (!(isfinite(Rt) && Rt > 0.0 && isfinite(uc) && fabs(klo_d) < 1.0e9)) {
-        cd[0] = make_double2(0.0, 0.0);
-        cd[1] = make_double2((double)A.margin_lo + 0.25, 0.0);
-        cd[2] = make_double2(0.0, 0.0);
-        *klo_out = INT32_MIN;
+    if (!(isfinite(Rt) && Rt > 0.0 && isfinite(uc) && fabs(uc) < 1.0e9)) {
+        *uc_out = NAN; // parked by pulse_finish
         return 0;
     }
     const double inv_r = 1.0 / Rt;
-    const double ft = uc - klo_d + (A.round_half ? 0.5 : 0.0);
     const double hs = A.half_span;
     const double q = (hs * hs + 2.0 * hs * Rt) * inv_r * inv_r;
     cd[0] = make_double2(2.0 * ux, 2.0 * uy);
-    cd[1] = make_double2(ft, inv_r * inv_r);
+    cd[1] = make_double2(0.0, inv_r * inv_r); // .x: ft, set by pulse_finish
     cd[2] = make_double2(Rt * A.inv_dr, 2.0 * uz); // 2 uz: the terrain kernels' vertical term
-    *klo_out = (int)klo_d;
+    *uc_out = uc;
     const double q2 = q * q, q4 = q2 * q2, rb = Rt * A.inv_dr; // R_t in bins
     if (q > 0.25 || rb * (429.0 / 32768.0) * q4 * q4 > 1e-7) return 2;
     return rb * (7.0 / 256.0) * q4 * q > 1e-7 ? 1 : 0;
@@ -242,7 +315,8 @@ __host__ __device__ __forceinline__ float bin_position(float num, const float4& 
 //   * the series' truncation, at most 1e-6 bins by the choice of mode (none in
 //     the exact form).
 // A little more is kept (10 / 30 for the rho terms, and 1e-9 bins for the fp64
-// reference itself).  tie_band = base[MODE] + rho_coef[MODE] * rho.
+// reference itself).  tie_band = base[MODE] + win_coef * W + rho_coef[MODE] * rho,
+// W the chunk's window length.
 #define SARBP_TIE_C_SERIES 10.0
 #define SARBP_TIE_C_EXACT 30.0
 #define SARBP_TIE_TRUNC 1e-6
@@ -250,14 +324,15 @@ __host__ __device__ __forceinline__ float bin_position(float num, const float4& 
 // error is the series' 1e-7 bins plus the 2^-25 of that rounding.
 #define SARBP_TIE_F64 1e-6
 
-__host__ __device__ inline void tie_band_coefficients(int win, bool f64, float base[3], float rho_coef[3]) {
+__host__ __device__ inline void tie_band_coefficients(bool f64, float base[3], float* win_coef, float rho_coef[3]) {
     const double u = 1.0 / 16777216.0;
+    *win_coef = f64 ? 0.f : (float)(4.0 * u);
     for (int m = 0; m < 3; ++m) {
         if (f64) {
             base[m] = (float)SARBP_TIE_F64;
             rho_coef[m] = 0.f;
         } else {
-            base[m] = (float)(2.0 * (2.0 * u * win + (m < 2 ? SARBP_TIE_TRUNC : 0.0)) + 1e-9);
+            base[m] = (float)(2.0 * (m < 2 ? SARBP_TIE_TRUNC : 0.0) + 1e-9);
             rho_coef[m] = (float)(2.0 * u * (m < 2 ? SARBP_TIE_C_SERIES : SARBP_TIE_C_EXACT));
         }
     }
@@ -290,17 +365,41 @@ __host__ __device__ __forceinline__ int nearest_bin_fp64(double ax, double ay, d
 
 // Staging of one chunk: step u covers B consecutive bins of one pulse's window
 // (B = 2 for linear and nearest, whose windows have even length W; 1 for sinc8).
-// The pulse is p = u / (W / B), one multiply-high by the launch's win_magic;
+// The pulse is p = u / (W / B), one multiply-high by magic = ceil(2^32 / (W / B))
+// (window_magic; exact while the chunk's steps times W / B stay below 2^32);
 // the step's first bin is k (absolute).  A pulse without finite geometry
 // (klo = INT32_MIN) takes k = 0 and reads the carrier table's NaN entries.
 template <class M, int B>
-__host__ __device__ __forceinline__ void stage_step(const BpArgs& A, const int* klo_s, int u, int wu, int* p_out,
+__host__ __device__ __forceinline__ void stage_step(const int* klo_s, int u, int wu, uint32_t magic, int* p_out,
                                                     int* k_out, bool* bad_out) {
-    const int p = (int)M::mulhi((uint32_t)u, A.win_magic);
+    const int p = (int)M::mulhi((uint32_t)u, magic);
     const int klo = klo_s[p];
     const bool bad = (klo == INT32_MIN);
     *p_out = p;
     *k_out = (bad ? 0 : klo) + B * (u - (int)M::mul24((uint32_t)p, (uint32_t)wu));
+    *bad_out = bad;
+}
+
+__host__ __device__ __forceinline__ uint32_t window_magic(int wu) { return 0xffffffffu / (uint32_t)wu + 1u; }
+
+// The same step with the pulse from an fp32 quotient: p = trunc(u * (1 / (W / B))),
+// then corrected by one either way so that 0 <= u - p (W / B) < W / B exactly (u < 2^24).
+template <int B>
+__host__ __device__ __forceinline__ void stage_step_f32(const int* klo_s, int u, int wu, float rwu, int* p_out,
+                                                        int* k_out, bool* bad_out) {
+    int p = (int)((float)u * rwu);
+    int r = u - p * wu;
+    if (r < 0) {
+        --p;
+        r += wu;
+    } else if (r >= wu) {
+        ++p;
+        r -= wu;
+    }
+    const int klo = klo_s[p];
+    const bool bad = (klo == INT32_MIN);
+    *p_out = p;
+    *k_out = (bad ? 0 : klo) + B * r;
     *bad_out = bad;
 }
 

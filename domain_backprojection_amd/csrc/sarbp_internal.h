@@ -54,7 +54,7 @@ struct BpLayout {
     int tiles_x, tiles_y;
     int ppt;          // backprojection pixels per lane (1 or 2): tiles of 64 x 16 ppt
     int f64;          // 1: range differences in fp64 (windows of many carrier cycles; ppt = 2)
-    int win;          // LDS window entries per pulse
+    int win;          // LDS window entries per pulse, at most (a chunk stages its pulses' exact extent)
     int margin_lo;    // bins below the tile's lowest range kept in the window
     int chunk;        // pulses per LDS step
     size_t lds_bytes; // dynamic LDS per workgroup
@@ -89,7 +89,7 @@ struct BpArgs {
     int group_blocks;      // ntiles * voxel layers: the workgroups of one pulse group
     int split_len;         // pulses per group (n when the pulses are not split)
     size_t split_stride;   // complex64 elements between the groups' partial images (0 unsplit)
-    int win, margin_lo, chunk, accumulate;
+    int win, margin_lo, chunk, accumulate; // win: the plan's (longest) window
     uint32_t win_magic;    // ceil(2^32 / wu), wu = win / (bins per staging step): u / wu = umulhi(u, win_magic)
     int slots;             // compute units: workgroup b and b + slots usually share a CU
     int* progress;         // [2 * slots] pulse progress per workgroup, read by its CU partner
@@ -102,8 +102,8 @@ struct BpArgs {
     double dem_relief;     // bound on one tile's height range (terrain kernels)
     float kappa;           // 2 dr / lambda: phase cycles per bin
     // nearest: fp64 recheck band around a rounding tie [bins], per accuracy mode:
-    // tie_base[m] + tie_rho[m] * (the chunk's largest range-term size, in bins)
-    float tie_base[3], tie_rho[3];
+    // tie_base[m] + tie_win * (the chunk's window) + tie_rho[m] * (its largest range-term size, in bins)
+    float tie_base[3], tie_win, tie_rho[3];
     int round_half;        // nearest: window positions carry u + 1/2
     float2 half_rot;       // nearest: exp(-j pi kappa), folded into the staged samples
 };

@@ -216,9 +216,9 @@ int sarbp_plan_layout(const sarbp_params& p, int n_cu, BpLayout* L) {
     // a 64 x 32 tile would pass BP_NEAREST_TIE_MAX, the fp64-range kernels serve
     // the plan.  (rho <= 1.06 half_span / dr while the series applies.)
     if (p.interp == SARBP_NEAREST && !L->f64) {
-        float base[3], rho_coef[3];
-        tie_band_coefficients((int)win32, false, base, rho_coef);
-        const double band = (double)base[0] + (double)rho_coef[0] * 1.06 * hs32 / p.dr;
+        float base[3], win_coef, rho_coef[3];
+        tie_band_coefficients(false, base, &win_coef, rho_coef);
+        const double band = (double)base[0] + (double)win_coef * win32 + (double)rho_coef[0] * 1.06 * hs32 / p.dr;
         if (band > BP_NEAREST_TIE_MAX) L->f64 = 1;
     }
     L->ppt = (tiles2 < 2 * (int64_t)L->n_cu && !(p.dem_relief > 0.0) && !L->f64) ? 1 : 2;
@@ -239,7 +239,10 @@ int sarbp_plan_layout(const sarbp_params& p, int n_cu, BpLayout* L) {
     if (p.interp != SARBP_SINC8) L->win += L->win & 1;
     const int eb = p.interp == SARBP_NEAREST ? 8 : (p.interp == SARBP_LINEAR ? 16 : 64);
     if (p.interp == SARBP_SINC8) sinc8_polynomials(L->sinc_poly);
-    const int per_pulse = L->win * eb + ((p.dem_relief > 0.0 || L->f64) ? 3 : 2) * 16 + 4;
+    // per pulse: its window entries, constants, window start, and (sinc8, whose
+    // chunks stage their exact window extent) the tile centre's bin u_c in fp64
+    const int per_pulse =
+        L->win * eb + ((p.dem_relief > 0.0 || L->f64) ? 3 : 2) * 16 + 4 + (p.interp == SARBP_SINC8 ? 8 : 0);
     // Coarse grids (long windows) that would stage fewer than 8 pulses per step
     // use up to 150 KiB of LDS: one workgroup per CU instead of two.
     int chunk = (BP_LDS_BUDGET - 64) / per_pulse;
@@ -250,8 +253,9 @@ int sarbp_plan_layout(const sarbp_params& p, int n_cu, BpLayout* L) {
     // chunk * win below 19200, so this holds whenever a chunk fits)
     if (chunk < 1 || (uint64_t)chunk * L->win * L->win >= (1ull << 32)) return SARBP_EUNSUPPORTED;
     L->chunk = chunk;
-    // + the chunk's issue-priority word and the double-buffered mode and tie-band words
-    L->lds_bytes = (size_t)chunk * per_pulse + 32;
+    // + alignment, the chunk's issue-priority word, the double-buffered mode, tie-band and
+    // window words, and the tile's pixel box (6 doubles)
+    L->lds_bytes = (size_t)chunk * per_pulse + 4 + 32 + 72; // (the box and the reference point: 9 doubles)
     return SARBP_OK;
 }
 
@@ -266,8 +270,7 @@ void sarbp_bp_args(const sarbp_params& p, const BpLayout& L, BpArgs* A) {
     A->nblocks = A->group_blocks;
     A->dz = p.nz > 1 ? p.dz : 0.0;
     A->win = L.win;
-    const uint64_t wu = (uint64_t)(p.interp == SARBP_SINC8 ? L.win : L.win / 2);
-    A->win_magic = (uint32_t)(((1ull << 32) + wu - 1) / wu);
+    A->win_magic = window_magic(p.interp == SARBP_SINC8 ? L.win : L.win / 2);
     A->margin_lo = L.margin_lo;
     A->chunk = L.chunk;
     A->slots = L.n_cu;
@@ -284,7 +287,7 @@ void sarbp_bp_args(const sarbp_params& p, const BpLayout& L, BpArgs* A) {
     for (int i = 0; i < 32; ++i) A->sinc_poly[i] = L.sinc_poly[i];
     A->half_span_bins = L.half_span / p.dr;
     A->kappa = (float)(2.0 * p.dr / p.wavelength);
-    tie_band_coefficients(L.win, L.f64 != 0, A->tie_base, A->tie_rho);
+    tie_band_coefficients(L.f64 != 0, A->tie_base, &A->tie_win, A->tie_rho);
     A->round_half = p.interp == SARBP_NEAREST ? 1 : 0;
     // exp(-j pi kappa): the nearest path measures the phase from half a bin below the sample
     const double k = 2.0 * p.dr / p.wavelength;

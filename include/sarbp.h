@@ -290,8 +290,10 @@ typedef struct {
     double max_position_error;       /* largest |window position - exact one| over in-grid pixels [bins]               */
     double max_error_to_band;        /* largest ratio of that error to the error bound of its chunk (half the tie band) */
     double min_position;             /* smallest window position (>= 0 required)                                        */
-    double max_position_margin;      /* largest window position minus W (< 0 required)                                  */
-    int32_t window;                  /* W: LDS window entries per pulse                                                 */
+    double max_position_margin;      /* largest window position minus its chunk's window length (< 0 required)          */
+    double window_mean;              /* mean window length of the chunks (each stages its pulses' exact extent)         */
+    int64_t chunks;                  /* pulse chunks staged (all workgroups)                                            */
+    int32_t window;                  /* W: the plan's longest LDS window, entries per pulse                             */
     int32_t chunk;                   /* pulses per LDS chunk                                                            */
     int32_t pixels_per_lane;         /* 1 or 2 (tiles of 64 x 16 or 64 x 32 pixels)                                    */
     int32_t fp64_ranges;             /* 1: the plan runs the fp64-range kernels                                         */

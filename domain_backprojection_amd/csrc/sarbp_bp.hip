@@ -298,6 +298,82 @@ __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
     return make_float2(fmaf(a.x, b.x, -(a.y * b.y)), fmaf(a.x, b.y, a.y * b.x));
 }
 
+// One sinc8 window entry from its 8 taps k-3 .. k+4 and the carrier of bin k.
+// Taps pair up as (k+t-3, k+4-t), t = 0..3: tap k+4-t's weight polynomial is tap
+// k+t-3's with g -> -g, so coefficient j takes the pair's sum (j even) or
+// difference (j odd) times sinc_poly[4 j + t].  Stored highest degree first.
+__device__ __forceinline__ void sinc8_entry(const BpArgs& A, char* smem, int u, const float2* tap, float2 c0) {
+    float2 ps[4], pd[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const float2 sa = tap[t], sb = tap[7 - t];
+        ps[t] = make_float2(sa.x + sb.x, sa.y + sb.y);
+        pd[t] = make_float2(sa.x - sb.x, sa.y - sb.y);
+    }
+    float2 cj[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float2* src = (j & 1) ? pd : ps;
+        float r = 0.f, i = 0.f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            r = fmaf(A.sinc_poly[4 * j + t], src[t].x, r);
+            i = fmaf(A.sinc_poly[4 * j + t], src[t].y, i);
+        }
+        cj[j] = cmul(make_float2(r, i), c0);
+    }
+    float4* dst = reinterpret_cast<float4*>(smem) + (size_t)u * 4;
+    dst[0] = make_float4(cj[7].x, cj[7].y, cj[6].x, cj[6].y);
+    dst[1] = make_float4(cj[5].x, cj[5].y, cj[4].x, cj[4].y);
+    dst[2] = make_float4(cj[3].x, cj[3].y, cj[2].x, cj[2].y);
+    dst[3] = make_float4(cj[1].x, cj[1].y, cj[0].x, cj[0].y);
+}
+
+// Staging when every window of the chunk, with its taps, lies inside the record
+// (the set-up checks): no clamped indices or zero selects, and the samples
+// addressed by 32-bit byte offsets from the chunk's first record (taken only while
+// a chunk's records span less than 4 GiB).  Same entries as stage_chunk.
+template <int INTERP, bool EXACTW>
+__device__ void stage_inside(const BpArgs& A, char* smem, const int* klo_s, int np, int n0, int tid, int W) {
+    constexpr int B = INTERP == SARBP_SINC8 ? 1 : 2;
+    const int Wu = W / B, nr = A.n_range;
+    const int nu = np * Wu;
+    const float rwu = EXACTW ? 1.0f / (float)Wu : 0.f;
+    const char* base = reinterpret_cast<const char*>(A.echo + (size_t)n0 * (size_t)nr);
+    const char* ph = reinterpret_cast<const char*>(A.phase + 4); // carrier of bin 0
+    for (int u = tid; u < nu; u += BP_THREADS) {
+        int p, k;
+        bool bad;
+        if constexpr (EXACTW)
+            stage_step_f32<B>(klo_s, u, Wu, rwu, &p, &k, &bad);
+        else
+            stage_step<DevMath, B>(klo_s, u, Wu, A.win_magic, &p, &k, &bad);
+        const uint32_t off = ((uint32_t)p * (uint32_t)nr + (uint32_t)k) * 8u;
+        const float2* e = reinterpret_cast<const float2*>(ph + (uint32_t)k * 8u);
+        if constexpr (INTERP == SARBP_LINEAR) {
+            const float2* q = reinterpret_cast<const float2*>(base + off);
+            const float2 s0 = q[0], s1 = q[1], s2 = q[2], c0 = e[0], c1 = e[1];
+            const float2 a0 = cmul(s0, c0), d0 = cmul(make_float2(s1.x - s0.x, s1.y - s0.y), c0);
+            const float2 a1 = cmul(s1, c1), d1 = cmul(make_float2(s2.x - s1.x, s2.y - s1.y), c1);
+            float4* dst = reinterpret_cast<float4*>(smem) + 2 * u;
+            dst[0] = make_float4(a0.x, a0.y, d0.x, d0.y);
+            dst[1] = make_float4(a1.x, a1.y, d1.x, d1.y);
+        } else if constexpr (INTERP == SARBP_NEAREST) {
+            const float2* q = reinterpret_cast<const float2*>(base + off);
+            const float2 s0 = q[0], s1 = q[1], c0 = e[0], c1 = e[1];
+            const float2 v0 = cmul(s0, cmul(c0, A.half_rot));
+            const float2 v1 = cmul(s1, cmul(c1, A.half_rot));
+            reinterpret_cast<float4*>(smem)[u] = make_float4(v0.x, v0.y, v1.x, v1.y);
+        } else {
+            const float2* q = reinterpret_cast<const float2*>(base + off - 24u); // taps k-3 .. k+4
+            float2 tap[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) tap[t] = q[t];
+            sinc8_entry(A, smem, u, tap, e[0]);
+        }
+    }
+}
+
 template <int INTERP, bool EXACTW>
 __device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int np, int n0, int tid, int W) {
     constexpr int B = INTERP == SARBP_SINC8 ? 1 : 2;
@@ -317,47 +393,36 @@ __device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int n
         const int ke = carrier_index<B>(k, nr, bad);
         const float2 c0 = A.phase[ke];
         if constexpr (INTERP == SARBP_LINEAR) {
+            // every load of the step before any of its selects, so that their latencies overlap
+            const bool in0 = (uint32_t)k < (uint32_t)nr, in1 = (uint32_t)(k + 1) < (uint32_t)nr,
+                       in2 = (uint32_t)(k + 2) < (uint32_t)nr;
+            const float2 r0 = row[in0 ? (uint32_t)k : 0u], r1 = row[in1 ? (uint32_t)(k + 1) : 0u],
+                         r2 = row[in2 ? (uint32_t)(k + 2) : 0u];
             const float2 c1 = A.phase[ke + 1];
-            const float2 s0 = sample_or_zero(row, k, nr), s1 = sample_or_zero(row, k + 1, nr),
-                         s2 = sample_or_zero(row, k + 2, nr);
+            __builtin_amdgcn_sched_barrier(0);
+            const float2 s0 = make_float2(in0 ? r0.x : 0.f, in0 ? r0.y : 0.f),
+                         s1 = make_float2(in1 ? r1.x : 0.f, in1 ? r1.y : 0.f),
+                         s2 = make_float2(in2 ? r2.x : 0.f, in2 ? r2.y : 0.f);
             const float2 a0 = cmul(s0, c0), d0 = cmul(make_float2(s1.x - s0.x, s1.y - s0.y), c0);
             const float2 a1 = cmul(s1, c1), d1 = cmul(make_float2(s2.x - s1.x, s2.y - s1.y), c1);
             float4* dst = reinterpret_cast<float4*>(smem) + 2 * u;
             dst[0] = make_float4(a0.x, a0.y, d0.x, d0.y);
             dst[1] = make_float4(a1.x, a1.y, d1.x, d1.y);
         } else if constexpr (INTERP == SARBP_NEAREST) {
+            const bool in0 = (uint32_t)k < (uint32_t)nr, in1 = (uint32_t)(k + 1) < (uint32_t)nr;
+            const float2 r0 = row[in0 ? (uint32_t)k : 0u], r1 = row[in1 ? (uint32_t)(k + 1) : 0u];
             const float2 c1 = A.phase[ke + 1];
-            const float2 v0 = cmul(sample_or_zero(row, k, nr), cmul(c0, A.half_rot));
-            const float2 v1 = cmul(sample_or_zero(row, k + 1, nr), cmul(c1, A.half_rot));
+            __builtin_amdgcn_sched_barrier(0);
+            const float2 s0 = make_float2(in0 ? r0.x : 0.f, in0 ? r0.y : 0.f),
+                         s1 = make_float2(in1 ? r1.x : 0.f, in1 ? r1.y : 0.f);
+            const float2 v0 = cmul(s0, cmul(c0, A.half_rot));
+            const float2 v1 = cmul(s1, cmul(c1, A.half_rot));
             reinterpret_cast<float4*>(smem)[u] = make_float4(v0.x, v0.y, v1.x, v1.y);
         } else {
-            // Taps k-3 .. k+4 pair up as (k+t-3, k+4-t), t = 0..3: tap k+4-t's weight
-            // polynomial is tap k+t-3's with g -> -g, so coefficient j takes the
-            // pair's sum (j even) or difference (j odd) times sinc_poly[4 j + t].
-            float2 ps[4], pd[4];
+            float2 tap[8];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const float2 sa = sample_or_zero(row, k + t - 3, nr), sb = sample_or_zero(row, k + 4 - t, nr);
-                ps[t] = make_float2(sa.x + sb.x, sa.y + sb.y);
-                pd[t] = make_float2(sa.x - sb.x, sa.y - sb.y);
-            }
-            float2 cj[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float2* src = (j & 1) ? pd : ps;
-                float r = 0.f, i = 0.f;
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    r = fmaf(A.sinc_poly[4 * j + t], src[t].x, r);
-                    i = fmaf(A.sinc_poly[4 * j + t], src[t].y, i);
-                }
-                cj[j] = cmul(make_float2(r, i), c0);
-            }
-            float4* dst = reinterpret_cast<float4*>(smem) + (size_t)u * 4;
-            dst[0] = make_float4(cj[7].x, cj[7].y, cj[6].x, cj[6].y);
-            dst[1] = make_float4(cj[5].x, cj[5].y, cj[4].x, cj[4].y);
-            dst[2] = make_float4(cj[3].x, cj[3].y, cj[2].x, cj[2].y);
-            dst[3] = make_float4(cj[1].x, cj[1].y, cj[0].x, cj[0].y);
+            for (int t = 0; t < 8; ++t) tap[t] = sample_or_zero(row, k + t - 3, nr);
+            sinc8_entry(A, smem, u, tap, c0);
         }
     }
 }
@@ -494,10 +559,11 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     int* mode_s = prio_s + 1;
     int* rho_s = mode_s + 2;
     int* wlen_s = rho_s + 2;
+    int* edge_s = wlen_s + 2; // nonzero: a window of the chunk reaches past the record (or has no geometry)
     // the tile's pixel box and reference point, read by the set-up lanes of each chunk
-    double* box_s = reinterpret_cast<double*>(prio_s + 8);
+    double* box_s = reinterpret_cast<double*>(prio_s + 10);
     if (tid == 0) {
-        mode_s[0] = mode_s[1] = rho_s[0] = rho_s[1] = wlen_s[0] = wlen_s[1] = 0;
+        mode_s[0] = mode_s[1] = rho_s[0] = rho_s[1] = wlen_s[0] = wlen_s[1] = edge_s[0] = edge_s[1] = 0;
         box_s[6] = cx;
         box_s[7] = cy;
         box_s[8] = cz;
@@ -534,6 +600,8 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
                 const int klo = centre_window(A, uc);
                 klo_s[tid] = klo;
                 pulse_finish(A, uc, klo, cst + CS * tid, DEM, F64);
+                // the window's samples klo .. klo + W (linear's last step reads one past the window)
+                if (!(klo != INT32_MIN && klo >= 0 && klo <= A.n_range - 1 - A.win)) atomicOr(edge_s + (c & 1), 1);
             }
             if (need) atomicOr(mode_s + (c & 1), need);
             if constexpr (INTERP == SARBP_NEAREST && !F64) atomicMax(rho_s + (c & 1), __float_as_int(rho));
@@ -542,12 +610,16 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
             const size_t pa = 3 * (size_t)(pb + n0 + t);
             const TileBox box = {box_s[0], box_s[1], box_s[2], box_s[3], box_s[4], box_s[5]};
             atomicMax(wlen_s + (c & 1), pulse_window(A, A.pos[pa], A.pos[pa + 1], A.pos[pa + 2], box, klo_s + t));
+            // the taps klo - 3 .. klo + W + 4 (within the plan's window) inside the record?
+            const int klo = klo_s[t];
+            if (!(klo != INT32_MIN && klo >= 3 && klo <= A.n_range - 5 - A.win)) atomicOr(edge_s + (c & 1), 1);
         }
         if (tid == 0) {
             *prio_s = chunk_priority(A, n0, pn);
             mode_s[(c + 1) & 1] = 0;
             rho_s[(c + 1) & 1] = 0;
             wlen_s[(c + 1) & 1] = 0;
+            edge_s[(c + 1) & 1] = 0;
         }
         __syncthreads();
         int win_c = A.win;
@@ -557,7 +629,10 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
             if (tid < np) pulse_finish(A, uc_s[tid], klo_s[tid], cst + CS * tid, DEM, F64);
             win_c = chunk_window(__builtin_amdgcn_readfirstlane(wlen_s[c & 1]), 1, A.win);
         }
-        stage_chunk<INTERP, EXACTW>(A, smem, klo_s, np, pb + n0, tid, win_c);
+        if (A.fast_stage && __builtin_amdgcn_readfirstlane(edge_s[c & 1]) == 0)
+            stage_inside<INTERP, EXACTW>(A, smem, klo_s, np, pb + n0, tid, win_c);
+        else
+            stage_chunk<INTERP, EXACTW>(A, smem, klo_s, np, pb + n0, tid, win_c);
         __syncthreads();
         set_priority(*prio_s);
         const int mode = __builtin_amdgcn_readfirstlane(mode_s[c & 1]); // the same word for every lane

@@ -177,6 +177,23 @@ struct Checker {
                 r->window_mean += win_c;
                 ++r->chunks;
                 stage_check(klo.data(), np, win_c);
+                // the in-record staging path: taken when every window, with its taps, lies
+                // in the record; then every sample it reads must be in the record
+                bool inside = A.fast_stage != 0;
+                for (int t = 0; t < np; ++t) {
+                    const int kl = klo[t];
+                    inside = inside && kl != INT32_MIN &&
+                             (exactw ? (kl >= 3 && kl <= A.n_range - 5 - A.win) : (kl >= 0 && kl <= A.n_range - 1 - A.win));
+                }
+                if (inside) {
+                    ++r->chunks_in_record;
+                    for (int t = 0; t < np; ++t) {
+                        const int lo = klo[t] - (exactw ? 3 : 0);
+                        const int hi = klo[t] + win_c - 1 + (exactw ? 4 : (p.interp == SARBP_LINEAR ? 1 : 0));
+                        const uint64_t last = ((uint64_t)t * (uint64_t)A.n_range + (uint64_t)hi) * 8u + 8u;
+                        if (lo < 0 || hi > A.n_range - 1 || last >= (1ull << 32)) ++r->staging_violations;
+                    }
+                }
                 // the tie band (twice the error bound of the chunk's window positions)
                 const float band = fmaf(A.tie_rho[mi], crho, fmaf(A.tie_win, (float)win_c, A.tie_base[mi]));
                 const float tie_lim = 0.5f - band;

@@ -91,6 +91,7 @@ struct BpArgs {
     size_t split_stride;   // complex64 elements between the groups' partial images (0 unsplit)
     int win, margin_lo, chunk, accumulate; // win: the plan's (longest) window
     uint32_t win_magic;    // ceil(2^32 / wu), wu = win / (bins per staging step): u / wu = umulhi(u, win_magic)
+    int fast_stage;        // 1: a chunk's records span less than 4 GiB, so staging may use 32-bit byte offsets
     int slots;             // compute units: workgroup b and b + slots usually share a CU
     int* progress;         // [2 * slots] pulse progress per workgroup, read by its CU partner
     double r0, dr, inv_dr, x0, y0, z0, dx, dy;

@@ -255,7 +255,7 @@ int sarbp_plan_layout(const sarbp_params& p, int n_cu, BpLayout* L) {
     L->chunk = chunk;
     // + alignment, the chunk's issue-priority word, the double-buffered mode, tie-band and
     // window words, and the tile's pixel box (6 doubles)
-    L->lds_bytes = (size_t)chunk * per_pulse + 4 + 32 + 72; // (the box and the reference point: 9 doubles)
+    L->lds_bytes = (size_t)chunk * per_pulse + 4 + 40 + 72; // (the box and the reference point: 9 doubles)
     return SARBP_OK;
 }
 
@@ -271,6 +271,7 @@ void sarbp_bp_args(const sarbp_params& p, const BpLayout& L, BpArgs* A) {
     A->dz = p.nz > 1 ? p.dz : 0.0;
     A->win = L.win;
     A->win_magic = window_magic(p.interp == SARBP_SINC8 ? L.win : L.win / 2);
+    A->fast_stage = (uint64_t)L.chunk * (uint64_t)p.n_range * 8u + 64u < (1ull << 32) ? 1 : 0;
     A->margin_lo = L.margin_lo;
     A->chunk = L.chunk;
     A->slots = L.n_cu;

@@ -94,6 +94,7 @@ class sarbp_index_report(ctypes.Structure):
         ("max_position_margin", ctypes.c_double),
         ("window_mean", ctypes.c_double),
         ("chunks", ctypes.c_int64),
+        ("chunks_in_record", ctypes.c_int64),
         ("window", ctypes.c_int32),
         ("chunk", ctypes.c_int32),
         ("pixels_per_lane", ctypes.c_int32),

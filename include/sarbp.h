@@ -293,6 +293,7 @@ typedef struct {
     double max_position_margin;      /* largest window position minus its chunk's window length (< 0 required)          */
     double window_mean;              /* mean window length of the chunks (each stages its pulses' exact extent)         */
     int64_t chunks;                  /* pulse chunks staged (all workgroups)                                            */
+    int64_t chunks_in_record;        /* of which staged by the in-record path (every window and its taps in the record) */
     int32_t window;                  /* W: the plan's longest LDS window, entries per pulse                             */
     int32_t chunk;                   /* pulses per LDS chunk                                                            */
     int32_t pixels_per_lane;         /* 1 or 2 (tiles of 64 x 16 or 64 x 32 pixels)                                    */

@@ -37,13 +37,14 @@
 //   v_sin_f32 / v_cos_f32 pair (inputs in revolutions) on a bounded argument
 //   replaces a large-argument reduction.
 // * Staged per bin k: linear (A, D) = (s[k] E[k], (s[k+1] - s[k]) E[k]), a
-//   sample is one ds_read_b128 and two FMAs; nearest s[k] E[k] exp(-j pi kappa);
+//   sample is one ds_read_b128 and two FMAs; nearest s[k] E[k], its phase taken
+//   from the bin's middle, exp(j 2 pi kappa (g - 1/2)) with g = fract(u + 1/2);
 //   sinc8 the 8 coefficients of the degree-7 polynomial in f that is the
 //   windowed-sinc interpolant at k + f, times E[k], so a sample is one complex
 //   Horner evaluation.  The window position is positive by construction, so
 //   v_cvt_u32_f32 (truncation) is its floor and v_fract_f32 its fraction.
-// * Nearest interpolation rechecks lanes within tie_eps of a rounding tie in
-//   fp64, in the definition's operation order, so the chosen bin matches the
+// * Nearest interpolation rechecks lanes within the tie band of a rounding tie
+//   in fp64, in the definition's operation order, so the chosen bin matches the
 //   double-precision definition exactly.
 // * Template parameters select the accumulator (fp32, Kahan-compensated, or
 //   fp32 per chunk summed in fp64) and terrain (per-pixel heights: the tile is
@@ -122,17 +123,19 @@ __device__ __forceinline__ void mac(float& ar, float& ai, float& cr, float& ci, 
 
 // Nearest interpolation over G consecutive pulses p0 .. p0+G-1: every bin
 // decision of the group first, then one (rare) branch that retakes the decisions
-// within tie_eps of a rounding tie in fp64, then the fetches and accumulations.
-// ub carries u + 1/2: its floor is the nearest bin and g - 1/2 = u - bin; the
-// staged sample carries exp(-j pi kappa), so exp(j 2 pi kappa g) completes the phase.
+// within the tie band of a rounding tie in fp64 (antenna positions from LDS), then
+// the fetches and accumulations.  ub carries u + 1/2: its floor is the nearest bin
+// and g - 1/2 = u - bin; the staged sample carries the bin's carrier, and
+// exp(j 2 pi a), a = kappa (g - 1/2), completes the phase.  The tie test is made on a
+// (nearest_phase / nearest_tie_limit), which the phase needs anyway.
 template <int G, int MODE, int ACC, bool DEM, int PPT, bool F64>
 __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem, const float4* cst, const int* klo_s,
-                                              int p0, int n0, int i_pix, int j_pix0, float dxl, const float* dyv,
-                                              const float* ddv, float* accr, float* acci, float* cmpr, float* cmpi,
-                                              const float* dzv, const float* hv, double zl, uint32_t wstride,
-                                              const double* pxd, float tie_lim, int win_c) {
+                                              const double* pos_s, int p0, int i_pix, int j_pix0, float dxl,
+                                              const float* dyv, const float* ddv, float* accr, float* acci,
+                                              float* cmpr, float* cmpi, const float* dzv, const float* hv, double zl,
+                                              uint32_t wstride, const double* pxd, float a_lim, int win_c) {
     constexpr int CS = (DEM || F64) ? 3 : 2;
-    float g[G][PPT];
+    float a[G][PPT];
     uint32_t kb[G][PPT];
     bool tie = false;
 #pragma unroll
@@ -142,31 +145,34 @@ __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem,
         const float4 c2 = DEM ? cst[CS * (p0 + q) + 2] : c1;
 #pragma unroll
         for (int m = 0; m < PPT; ++m) {
+            float g;
             if constexpr (F64) {
-                locate_f64<MODE, DEM>(cst, p0 + q, pxd[0], pxd[1 + m], pxd[1 + PPT + m], pxd[1 + 2 * PPT + m], &g[q][m],
+                locate_f64<MODE, DEM>(cst, p0 + q, pxd[0], pxd[1 + m], pxd[1 + PPT + m], pxd[1 + 2 * PPT + m], &g,
                                       &kb[q][m]);
             } else {
                 const float num = pixel_num(dxl, dyv[m], ddv[m], dzv[m], c0, c2, DEM);
                 const float ub = bin_position<MODE, DevMath>(num, c0, c1);
-                g[q][m] = DevMath::fract(ub);
+                g = DevMath::fract(ub);
                 kb[q][m] = DevMath::to_u32(ub);
             }
-            tie |= fabsf(g[q][m] - 0.5f) > tie_lim;
+            a[q][m] = nearest_phase(A.kappa, g);
+            tie |= fabsf(a[q][m]) > a_lim;
         }
     }
     if (tie) {
 #pragma unroll
         for (int q = 0; q < G; ++q) {
-            const size_t pn = 3 * (size_t)(n0 + p0 + q);
+            const double* ps = pos_s + 3 * (p0 + q);
 #pragma unroll
             for (int m = 0; m < PPT; ++m) {
-                if (fabsf(g[q][m] - 0.5f) > tie_lim) {
+                if (fabsf(a[q][m]) > a_lim) {
                     const double zp = DEM ? A.z0 + (double)hv[m] : zl; // the pixel's height
-                    const int kabs = nearest_bin_fp64<DevMath>(A.pos[pn], A.pos[pn + 1], A.pos[pn + 2], A.x0, A.y0, zp,
-                                                               A.dx, A.dy, A.r0, A.dr, i_pix, j_pix0 + BP_WAVES * m);
+                    const int kabs = nearest_bin_fp64<DevMath>(ps[0], ps[1], ps[2], A.x0, A.y0, zp, A.dx, A.dy, A.r0,
+                                                               A.dr, i_pix, j_pix0 + BP_WAVES * m);
                     int kr = kabs - klo_s[p0 + q];
                     kr = kr < 0 ? 0 : (kr > win_c - 1 ? win_c - 1 : kr);
-                    g[q][m] = g[q][m] + (float)((int)kb[q][m] - kr); // = ub - kr
+                    // g moves by the bins the decision moved: a = kappa (g + kb - kr - 1/2)
+                    a[q][m] = fmaf(A.kappa, (float)((int)kb[q][m] - kr), a[q][m]);
                     kb[q][m] = (uint32_t)kr;
                 }
             }
@@ -179,7 +185,7 @@ __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem,
         for (int m = 0; m < PPT; ++m) {
             const float2 sv = *reinterpret_cast<const float2*>(smem + ((kb[q][m] << 3) + wbase));
             float sn, cs;
-            sincos_rev(A.kappa * g[q][m], &sn, &cs);
+            sincos_rev(a[q][m], &sn, &cs);
             mac<ACC>(accr[m], acci[m], cmpr[m], cmpi[m], sv.x, sv.y, cs, sn);
         }
     }
@@ -187,11 +193,11 @@ __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem,
 
 template <int INTERP, int MODE, int ACC, bool DEM, int PPT, bool F64>
 __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* smem, const float4* cst,
-                                                 const int* klo_s, int np, int n0, int i_pix, int j_pix0,
-                                                 float dxl, const float* dyv, const float* ddv, float* accr,
-                                                 float* acci, float* cmpr, float* cmpi, const float* dzv,
-                                                 const float* hv, double zl, const double* pxd, float tie_lim,
-                                                 int win_c) {
+                                                 const int* klo_s, const double* pos_s, int np, int i_pix,
+                                                 int j_pix0, float dxl, const float* dyv, const float* ddv,
+                                                 float* accr, float* acci, float* cmpr, float* cmpi,
+                                                 const float* dzv, const float* hv, double zl, const double* pxd,
+                                                 float a_lim, int win_c) {
     const int eb = entry_bytes<INTERP>();
     const uint32_t wstride = (uint32_t)(win_c * eb);
     const float kappa = A.kappa;
@@ -199,12 +205,11 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
         int p = 0;
         constexpr int G = F64 ? 1 : BP_NEAREST_GROUP;
         for (; p + G <= np; p += G)
-            nearest_group<G, MODE, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, p, n0, i_pix, j_pix0, dxl,
-                                                                   dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl,
-                                                                   wstride, pxd, tie_lim, win_c);
+            nearest_group<G, MODE, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, pos_s, p, i_pix, j_pix0, dxl, dyv, ddv,
+                                                       accr, acci, cmpr, cmpi, dzv, hv, zl, wstride, pxd, a_lim, win_c);
         for (; p < np; ++p)
-            nearest_group<1, MODE, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, p, n0, i_pix, j_pix0, dxl, dyv, ddv, accr,
-                                                  acci, cmpr, cmpi, dzv, hv, zl, wstride, pxd, tie_lim, win_c);
+            nearest_group<1, MODE, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, pos_s, p, i_pix, j_pix0, dxl, dyv, ddv,
+                                                       accr, acci, cmpr, cmpi, dzv, hv, zl, wstride, pxd, a_lim, win_c);
         return;
     }
     constexpr int kUnroll = F64 ? BP_PUNROLL_F64 : (INTERP == SARBP_LINEAR ? BP_PUNROLL_LINEAR : BP_PUNROLL_SINC8);
@@ -361,8 +366,7 @@ __device__ void stage_inside(const BpArgs& A, char* smem, const int* klo_s, int 
         } else if constexpr (INTERP == SARBP_NEAREST) {
             const float2* q = reinterpret_cast<const float2*>(base + off);
             const float2 s0 = q[0], s1 = q[1], c0 = e[0], c1 = e[1];
-            const float2 v0 = cmul(s0, cmul(c0, A.half_rot));
-            const float2 v1 = cmul(s1, cmul(c1, A.half_rot));
+            const float2 v0 = cmul(s0, c0), v1 = cmul(s1, c1);
             reinterpret_cast<float4*>(smem)[u] = make_float4(v0.x, v0.y, v1.x, v1.y);
         } else {
             const float2* q = reinterpret_cast<const float2*>(base + off - 24u); // taps k-3 .. k+4
@@ -415,8 +419,7 @@ __device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int n
             __builtin_amdgcn_sched_barrier(0);
             const float2 s0 = make_float2(in0 ? r0.x : 0.f, in0 ? r0.y : 0.f),
                          s1 = make_float2(in1 ? r1.x : 0.f, in1 ? r1.y : 0.f);
-            const float2 v0 = cmul(s0, cmul(c0, A.half_rot));
-            const float2 v1 = cmul(s1, cmul(c1, A.half_rot));
+            const float2 v0 = cmul(s0, c0), v1 = cmul(s1, c1);
             reinterpret_cast<float4*>(smem)[u] = make_float4(v0.x, v0.y, v1.x, v1.y);
         } else {
             float2 tap[8];
@@ -548,8 +551,11 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     // position u_c; then the chunk words and the tile's pixel box.
     float4* cst = reinterpret_cast<float4*>(smem + (size_t)P * A.win * entry_bytes<INTERP>());
     int* klo_s = reinterpret_cast<int*>(cst + CS * P);
+    // exact windows keep u_c per pulse; nearest keeps the antenna positions (3 per
+    // pulse) for its tie rechecks
     double* uc_s = reinterpret_cast<double*>(klo_s + ((P + 1) & ~1));
-    int* prio_s = reinterpret_cast<int*>(uc_s + (EXACTW ? P : 0)); // (u_c is kept only for exact windows)
+    double* pos_s = uc_s;
+    int* prio_s = reinterpret_cast<int*>(uc_s + (EXACTW ? P : (INTERP == SARBP_NEAREST ? 3 * P : 0)));
     // The accuracy mode of a chunk is the OR of its pulses' modes, its window length
     // the longest of theirs, and its nearest tie band follows from the largest of
     // their range-term sizes rho.  The words are double-buffered: chunk c writes
@@ -589,6 +595,11 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         if (tid < np) {
             const size_t pa = 3 * (size_t)(pb + n0 + tid);
             const double ax = A.pos[pa], ay = A.pos[pa + 1], az = A.pos[pa + 2];
+            if constexpr (INTERP == SARBP_NEAREST) {
+                pos_s[3 * tid] = ax;
+                pos_s[3 * tid + 1] = ay;
+                pos_s[3 * tid + 2] = az;
+            }
             const double gx = box_s[6], gy = box_s[7], gz = box_s[8];
             float rho = 0.f;
             double uc;
@@ -638,24 +649,26 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         const int mode = __builtin_amdgcn_readfirstlane(mode_s[c & 1]); // the same word for every lane
         const int m1 = mode & 1, m2 = mode & 2;
         const int mi = m2 ? 2 : (m1 ? 1 : 0);
-        // nearest: |fract(ub) - 1/2| beyond tie_lim means ub is within the tie band of an integer
-        float tie_lim = 0.f;
+        // nearest: |fract(ub) - 1/2| beyond tie_lim means ub is within the tie band of an
+        // integer; the test is made on the phase a = kappa (fract(ub) - 1/2) against a_lim
+        float a_lim = 0.f;
         if constexpr (INTERP == SARBP_NEAREST) {
             const float rho = __int_as_float(__builtin_amdgcn_readfirstlane(rho_s[c & 1]));
-            tie_lim = 0.5f - fmaf(A.tie_rho[mi], rho, fmaf(A.tie_win, (float)win_c, A.tie_base[mi]));
+            const float tie_lim = 0.5f - fmaf(A.tie_rho[mi], rho, fmaf(A.tie_win, (float)win_c, A.tie_base[mi]));
+            a_lim = nearest_tie_limit(A.kappa, tie_lim);
         }
         if (m2)
-            accumulate_chunk<INTERP, 2, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, np, pb + n0, i0 + lane, j0 + wave, dxl, dyv,
-                                                        ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, tie_lim,
-                                                        win_c);
+            accumulate_chunk<INTERP, 2, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, pos_s, np, i0 + lane, j0 + wave, dxl,
+                                                            dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, a_lim,
+                                                            win_c);
         else if (m1)
-            accumulate_chunk<INTERP, 1, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, np, pb + n0, i0 + lane, j0 + wave, dxl, dyv,
-                                                        ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, tie_lim,
-                                                        win_c);
+            accumulate_chunk<INTERP, 1, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, pos_s, np, i0 + lane, j0 + wave, dxl,
+                                                            dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, a_lim,
+                                                            win_c);
         else
-            accumulate_chunk<INTERP, 0, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, np, pb + n0, i0 + lane, j0 + wave, dxl, dyv,
-                                                        ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, tie_lim,
-                                                        win_c);
+            accumulate_chunk<INTERP, 0, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, pos_s, np, i0 + lane, j0 + wave, dxl,
+                                                            dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, a_lim,
+                                                            win_c);
         if constexpr (ACC == SARBP_ACC_CHUNK64) {
 #pragma unroll
             for (int m = 0; m < PPT; ++m) {

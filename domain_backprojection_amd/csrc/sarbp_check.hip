@@ -218,6 +218,7 @@ struct Checker {
                 float tie_lim, float band, int win_c) {
         const bool nearest = p.interp == SARBP_NEAREST;
         const double half = nearest ? 0.5 : 0.0;
+        const float a_lim = nearest_tie_limit(A.kappa, tie_lim);
         for (int t = 0; t < np; ++t) {
             const bool bad = klo[t] == INT32_MIN;
             for (int lane = 0; lane < BP_TX; ++lane) {
@@ -244,7 +245,7 @@ struct Checker {
                         r->max_error_to_band = std::max(r->max_error_to_band, err / (0.5 * (double)band));
                         if (!nearest) continue;
                         const int kdef = (int)floor(u + 0.5);
-                        if (fabsf(f - 0.5f) > tie_lim) {
+                        if (fabsf(nearest_phase(A.kappa, f)) > a_lim) { // the kernel's tie test
                             ++r->nearest_rechecks;
                             const int kr = kdef - klo[t];
                             if (kr < 0 || kr > win_c - 1) ++r->nearest_recheck_clamped;

@@ -338,6 +338,17 @@ __host__ __device__ inline void tie_band_coefficients(bool f64, float base[3], f
     }
 }
 
+// Nearest interpolation measures the carrier phase from the middle of the chosen
+// bin: a = kappa (g - 1/2) revolutions, g = fract(u + 1/2), taken with one rounding.
+// The tie test is made on a as well: |a| > a_lim with a_lim = kappa tie_lim
+// (1 - 2^-22) flags every decision with |g - 1/2| > tie_lim, because the two
+// roundings of a_lim keep it below kappa tie_lim (1 - 2^-24) and the one of a
+// keeps |a| at or above kappa |g - 1/2| (1 - 2^-24).  (A negative tie_lim flags all.)
+__host__ __device__ inline float nearest_phase(float kappa, float g) { return fmaf(kappa, g, -0.5f * kappa); }
+__host__ __device__ inline float nearest_tie_limit(float kappa, float tie_lim) {
+    return kappa * tie_lim * (1.0f - 0x1p-22f);
+}
+
 // The definition's fractional bin of pixel (i, j) at height z for an antenna at
 // (ax, ay, az), in its double-precision operation order (no contraction):
 // u = (sqrt(dx^2 + dy^2 + dz^2) - r0) / dr.

@@ -106,7 +106,6 @@ struct BpArgs {
     // tie_base[m] + tie_win * (the chunk's window) + tie_rho[m] * (its largest range-term size, in bins)
     float tie_base[3], tie_win, tie_rho[3];
     int round_half;        // nearest: window positions carry u + 1/2
-    float2 half_rot;       // nearest: exp(-j pi kappa), folded into the staged samples
 };
 
 // Largest nearest tie band [bins] the fp32 kernels accept on a 64 x 32 tile; a

@@ -239,10 +239,11 @@ int sarbp_plan_layout(const sarbp_params& p, int n_cu, BpLayout* L) {
     if (p.interp != SARBP_SINC8) L->win += L->win & 1;
     const int eb = p.interp == SARBP_NEAREST ? 8 : (p.interp == SARBP_LINEAR ? 16 : 64);
     if (p.interp == SARBP_SINC8) sinc8_polynomials(L->sinc_poly);
-    // per pulse: its window entries, constants, window start, and (sinc8, whose
-    // chunks stage their exact window extent) the tile centre's bin u_c in fp64
-    const int per_pulse =
-        L->win * eb + ((p.dem_relief > 0.0 || L->f64) ? 3 : 2) * 16 + 4 + (p.interp == SARBP_SINC8 ? 8 : 0);
+    // per pulse: its window entries, constants, window start, and in fp64 (sinc8, whose
+    // chunks stage their exact window extent) the tile centre's bin u_c or (nearest,
+    // for its tie rechecks) the antenna position
+    const int per_pulse = L->win * eb + ((p.dem_relief > 0.0 || L->f64) ? 3 : 2) * 16 + 4 +
+                          (p.interp == SARBP_SINC8 ? 8 : (p.interp == SARBP_NEAREST ? 24 : 0));
     // Coarse grids (long windows) that would stage fewer than 8 pulses per step
     // use up to 150 KiB of LDS: one workgroup per CU instead of two.
     int chunk = (BP_LDS_BUDGET - 64) / per_pulse;
@@ -290,10 +291,6 @@ void sarbp_bp_args(const sarbp_params& p, const BpLayout& L, BpArgs* A) {
     A->kappa = (float)(2.0 * p.dr / p.wavelength);
     tie_band_coefficients(L.f64 != 0, A->tie_base, &A->tie_win, A->tie_rho);
     A->round_half = p.interp == SARBP_NEAREST ? 1 : 0;
-    // exp(-j pi kappa): the nearest path measures the phase from half a bin below the sample
-    const double k = 2.0 * p.dr / p.wavelength;
-    const double fr = 0.5 * k - floor(0.5 * k);
-    A->half_rot = make_float2((float)cos(-2.0 * kPi * fr), (float)sin(-2.0 * kPi * fr));
 }
 
 extern "C" int sarbp_plan_create(const sarbp_params* params, sarbp_plan** out) {

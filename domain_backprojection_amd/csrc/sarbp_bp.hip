@@ -137,7 +137,7 @@ __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem,
     constexpr int CS = (DEM || F64) ? 3 : 2;
     float a[G][PPT];
     uint32_t kb[G][PPT];
-    bool tie = false;
+    float amax = 0.f; // the group's largest |a| (NaN positions, of pulses with no geometry, drop out)
 #pragma unroll
     for (int q = 0; q < G; ++q) {
         const float4 c0 = cst[CS * (p0 + q)];
@@ -156,10 +156,10 @@ __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem,
                 kb[q][m] = DevMath::to_u32(ub);
             }
             a[q][m] = nearest_phase(A.kappa, g);
-            tie |= fabsf(a[q][m]) > a_lim;
+            amax = fmaxf(amax, fabsf(a[q][m]));
         }
     }
-    if (tie) {
+    if (amax > a_lim) {
 #pragma unroll
         for (int q = 0; q < G; ++q) {
             const double* ps = pos_s + 3 * (p0 + q);

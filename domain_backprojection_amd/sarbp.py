@@ -314,10 +314,15 @@ def sarbp_check_indices(params: sarbp_params, positions, dem=None, n_cu: int = 0
 
 
 def sarbp_range_compress(handle, raw: torch.Tensor, out: torch.Tensor, n: int | None = None, stream=None) -> None:
-    """raw and out complex64 (n, n_fast) on the device."""
+    """raw and out complex64 (n, n_fast) on the device, rows of the plan's n_fast samples
+    (the caller's Plan checks n_fast itself; here the two must agree row for row)."""
+    if raw.dim() != 2 or out.dim() != 2:
+        raise ValueError("raw and out must be 2-D (pulses, samples)")
+    if raw.shape[1] != out.shape[1]:
+        raise ValueError(f"raw rows hold {raw.shape[1]} samples but out rows {out.shape[1]}")
     if n is None:
         n = raw.shape[0]
-    if raw.shape[0] < n or out.shape[0] < n:
+    if n < 0 or raw.shape[0] < n or out.shape[0] < n:
         raise ValueError("raw and out must hold n pulses")
     st = _lib.sarbp_range_compress(handle, _dev_ptr(raw, torch.complex64, "raw"),
                                    _dev_ptr(out, torch.complex64, "out"), int(n), _stream(stream))
@@ -451,10 +456,12 @@ class Plan:
         return image
 
     def range_compress(self, raw, out=None, n=None, stream=None) -> torch.Tensor:
-        if out is None:
-            out = torch.empty_like(raw)
         if raw.dim() != 2 or raw.shape[1] != self.params.n_fast:
             raise ValueError("raw must be (n, n_fast)")
+        if out is None:
+            out = torch.empty_like(raw)
+        if out.dim() != 2 or out.shape[1] != self.params.n_fast:
+            raise ValueError("out must be (n, n_fast)")
         sarbp_range_compress(self.handle, raw, out, n=n, stream=stream)
         return out
 

@@ -140,3 +140,31 @@ def test_null_arguments(sb):
     assert sb._lib.sarbp_backproject_split(None, 8, 8, None, 8, 1, 0, None, 0, None) == sb.SARBP_EINVAL
     # output overlapping the sample positions
     assert sb._lib.sarbp_interpolate_track(4096, 8192, 10, 65536, 8192, 4, None) == sb.SARBP_EINVAL
+
+
+def test_range_compress_shapes_checked_before_launch(sb):
+    """A compressed row is n_fast samples: raw and out rows that disagree with each other
+    (or, through a Plan, with the plan's n_fast) are refused on the host, before any
+    device call, so the kernel never reads or writes past a narrower buffer."""
+    import torch
+
+    raw = torch.zeros(4, 64, dtype=torch.complex64)
+    narrow = torch.zeros(4, 32, dtype=torch.complex64)
+    with pytest.raises(ValueError):
+        sb.sarbp_range_compress(None, raw, narrow)
+    with pytest.raises(ValueError):
+        sb.sarbp_range_compress(None, narrow, raw)
+    with pytest.raises(ValueError):
+        sb.sarbp_range_compress(None, raw, torch.zeros(256, dtype=torch.complex64))
+    with pytest.raises(ValueError):
+        sb.sarbp_range_compress(None, raw, torch.zeros(2, 64, dtype=torch.complex64))  # fewer pulses than raw
+    # a Plan with n_fast = 64, its handle never created (no device here)
+    plan = sb.Plan.__new__(sb.Plan)
+    plan.params = _good(sb, n_fast=64, fs=1e6, chirp_T=1e-5, chirp_B=1e5)
+    plan.handle = None
+    with pytest.raises(ValueError):
+        plan.range_compress(raw, out=narrow)
+    with pytest.raises(ValueError):
+        plan.range_compress(narrow)
+    with pytest.raises(ValueError):
+        plan.range_compress(raw, out=torch.zeros(4, 64, 1, dtype=torch.complex64))

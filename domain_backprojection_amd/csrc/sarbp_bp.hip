@@ -98,6 +98,11 @@ __device__ __forceinline__ void set_priority(int p) {
     else __builtin_amdgcn_s_setprio(0);
 }
 
+// Complex product, as the staging forms its entries.
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+    return make_float2(fmaf(a.x, b.x, -(a.y * b.y)), fmaf(a.x, b.y, a.y * b.x));
+}
+
 // acc += v * (cs + j sn).  ACC_FP32 and ACC_CHUNK64 use four FMAs on the fp32
 // accumulator; ACC_KAHAN forms the product first and adds it with a compensation
 // term (Kahan summation: the low part lost by each add is carried to the next).
@@ -128,8 +133,8 @@ __device__ __forceinline__ void mac(float& ar, float& ai, float& cr, float& ci, 
 // and g - 1/2 = u - bin; the staged sample carries the bin's carrier, and
 // exp(j 2 pi a), a = kappa (g - 1/2), completes the phase.  The tie test is made on a
 // (nearest_phase / nearest_tie_limit), which the phase needs anyway.
-template <int G, int MODE, int ACC, bool DEM, int PPT, bool F64>
-__device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem, const float4* cst, const int* klo_s,
+template <int G, int MODE, int ACC, bool DEM, int PPT, bool F64, bool DEFER = false>
+__device__ __forceinline__ bool nearest_group(const BpArgs& A, const char* smem, const float4* cst, const int* klo_s,
                                               const double* pos_s, int p0, int i_pix, int j_pix0, float dxl,
                                               const float* dyv, const float* ddv, float* accr, float* acci,
                                               float* cmpr, float* cmpi, const float* dzv, const float* hv, double zl,
@@ -159,7 +164,8 @@ __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem,
             amax = fmaxf(amax, fabsf(a[q][m]));
         }
     }
-    if (amax > a_lim) {
+    const bool tie = amax > a_lim;
+    if (!DEFER && tie) {
 #pragma unroll
         for (int q = 0; q < G; ++q) {
             const double* ps = pos_s + 3 * (p0 + q);
@@ -189,6 +195,134 @@ __device__ __forceinline__ void nearest_group(const BpArgs& A, const char* smem,
             mac<ACC>(accr[m], acci[m], cmpr[m], cmpi[m], sv.x, sv.y, cs, sn);
         }
     }
+    return tie;
+}
+
+// acc += d, through the compensated sum for ACC_KAHAN.
+template <int ACC>
+__device__ __forceinline__ void add_delta(float& ar, float& ai, float& cr, float& ci, float dr, float di) {
+    if constexpr (ACC == SARBP_ACC_KAHAN) {
+        const float yr = dr - cr, yi = di - ci;
+        const float sr = ar + yr, si = ai + yi;
+        cr = (sr - ar) - yr;
+        ci = (si - ai) - yi;
+        ar = sr;
+        ai = si;
+    } else {
+        ar += dr;
+        ai += di;
+    }
+}
+
+// Deferred tie rechecks (fp32 ranges).  The chunk's loop takes every nearest
+// decision in fp32 and only marks, per lane, the groups of pulses with a decision
+// inside the tie band, so the loop needs no branch.  After the loop each lane with
+// marks appends one word to its wave's queue in LDS: (the chunk's first pulse; the
+// lane, the chunk's accuracy mode and its number of full groups; the marks; the
+// chunk's tie limit).  At the end of the tile, or when the queue fills, the wave
+// resolves the queue at once, one entry per lane (drain_ties): it repeats the
+// marked pulses' set-up and the owner lane's decisions with the same code (so the
+// same constants, a and k_f), finds the definition's bin k_d in fp64 for the
+// decisions inside the band and, where k_d differs from k_f, adds
+// S(k_d) exp(j 2 pi a_d) - S(k_f) exp(j 2 pi a) to the owner, a_d = a + kappa (k_f - k_d)
+// and S(k) = s[k] E[k] formed as the staging forms it.
+struct TieQueue {
+    int4* q;    // this wave's BP_TIE_QUEUE entries in LDS
+    int n;      // entries held (the same on every lane)
+    int pulse0; // global index of the chunk's first pulse
+};
+
+__device__ __forceinline__ int lane_id() { return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
+
+// The staged nearest entry of absolute bin k: s[k] E[k], zero outside the record.
+__device__ __forceinline__ float2 nearest_entry(const float2* row, const float2* phase, int k, int nr) {
+    if ((uint32_t)k >= (uint32_t)nr) return make_float2(0.f, 0.f);
+    return cmul(row[k], phase[k + 4]); // carrier of bin k
+}
+
+// Resolve the wave's queue into the owners' accumulators (every lane of the wave
+// calls it).  box_s: the tile's reference point at [6 .. 8]; dxl .. hv: this
+// lane's pixel offsets and heights (each entry takes its owner's); i_pix, j_pix0:
+// this lane's pixel column and the wave's first row.
+template <int G, int ACC, bool DEM, int PPT>
+__device__ __forceinline__ void drain_ties(const BpArgs& A, TieQueue& tq, const double* box_s, int i_pix, int j_pix0,
+                                           double zl, float dxl, const float* dyv, const float* ddv, const float* dzv,
+                                           const float* hv, float* accr, float* acci, float* cmpr, float* cmpi) {
+    const int lane = lane_id();
+    // the entries were written by other lanes of this wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int nb = tq.n;
+    const int4 t = lane < nb ? tq.q[lane] : make_int4(0, 0, 0, 0);
+    const int ow = t.y & 63;
+    // the owner's offsets, from its registers
+    const float o_dx = __shfl(dxl, ow);
+    float o_dy[PPT], o_dd[PPT], o_dz[PPT], o_h[PPT], dr[PPT], di[PPT];
+#pragma unroll
+    for (int m = 0; m < PPT; ++m) {
+        o_dy[m] = __shfl(dyv[m], ow);
+        o_dd[m] = __shfl(ddv[m], ow);
+        o_dz[m] = DEM ? __shfl(dzv[m], ow) : 0.f;
+        o_h[m] = DEM ? __shfl(hv[m], ow) : 0.f;
+        dr[m] = di[m] = 0.f;
+    }
+    if (lane < nb) {
+        const int pulse0 = t.x, mode = (t.y >> 6) & 3, nfull = t.y >> 8;
+        uint32_t marks = (uint32_t)t.z;
+        const float a_lim = __int_as_float(t.w);
+        const double gx = box_s[6], gy = box_s[7], gz = box_s[8];
+        while (marks != 0) {
+            const int g = __builtin_ctz(marks);
+            marks &= marks - 1;
+            const int p0 = g < nfull ? g * G : nfull * G + (g - nfull), gsz = g < nfull ? G : 1;
+            for (int q = 0; q < gsz; ++q) {
+                const int n = pulse0 + p0 + q;
+                const double ax = A.pos[3 * (size_t)n], ay = A.pos[3 * (size_t)n + 1], az = A.pos[3 * (size_t)n + 2];
+                float4 cl[3];
+                double uc;
+                float rho;
+                pulse_setup(A, ax, ay, az, gx, gy, gz, cl, &uc, &rho, DEM);
+                const int klo = centre_window(A, uc);
+                pulse_finish(A, uc, klo, cl, DEM, false);
+                const float4 c0 = cl[0], c1 = cl[1], c2 = DEM ? cl[2] : cl[1];
+#pragma unroll
+                for (int m = 0; m < PPT; ++m) {
+                    const float num = pixel_num(o_dx, o_dy[m], o_dd[m], o_dz[m], c0, c2, DEM);
+                    const float ub = mode == 2 ? bin_position<2, DevMath>(num, c0, c1)
+                                               : (mode == 1 ? bin_position<1, DevMath>(num, c0, c1)
+                                                            : bin_position<0, DevMath>(num, c0, c1));
+                    const float a = nearest_phase(A.kappa, DevMath::fract(ub));
+                    if (!(fabsf(a) > a_lim)) continue;
+                    const int kf = (int)DevMath::to_u32(ub) + klo;
+                    const double zp = DEM ? A.z0 + (double)o_h[m] : zl; // the pixel's height
+                    const int kd = nearest_bin_fp64<DevMath>(ax, ay, az, A.x0, A.y0, zp, A.dx, A.dy, A.r0, A.dr,
+                                                             i_pix - lane + ow, j_pix0 + BP_WAVES * m);
+                    if (kd == kf) continue;
+                    const float2* row = A.echo + (size_t)n * (size_t)A.n_range;
+                    const float2 vf = nearest_entry(row, A.phase, kf, A.n_range);
+                    const float2 vd = nearest_entry(row, A.phase, kd, A.n_range);
+                    float sf, cf, sd, cd;
+                    sincos_rev(a, &sf, &cf);
+                    sincos_rev(fmaf(A.kappa, (float)(kf - kd), a), &sd, &cd);
+                    const float2 tf = cmul(vf, make_float2(cf, sf)), td = cmul(vd, make_float2(cd, sd));
+                    dr[m] += td.x - tf.x;
+                    di[m] += td.y - tf.y;
+                }
+            }
+        }
+    }
+    // each owner adds its corrections, in queue order
+    for (int e = 0; e < nb; ++e) {
+        const int owe = __builtin_amdgcn_readlane(ow, e);
+#pragma unroll
+        for (int m = 0; m < PPT; ++m) {
+            const float er = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dr[m]), e));
+            const float ei = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(di[m]), e));
+            if (lane == owe && (er != 0.f || ei != 0.f)) add_delta<ACC>(accr[m], acci[m], cmpr[m], cmpi[m], er, ei);
+        }
+    }
+    tq.n = 0;
 }
 
 template <int INTERP, int MODE, int ACC, bool DEM, int PPT, bool F64>
@@ -197,13 +331,47 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
                                                  int j_pix0, float dxl, const float* dyv, const float* ddv,
                                                  float* accr, float* acci, float* cmpr, float* cmpi,
                                                  const float* dzv, const float* hv, double zl, const double* pxd,
-                                                 float a_lim, int win_c) {
+                                                 float a_lim, int win_c, TieQueue& tq, const double* box_s) {
     const int eb = entry_bytes<INTERP>();
     const uint32_t wstride = (uint32_t)(win_c * eb);
     const float kappa = A.kappa;
     if constexpr (INTERP == SARBP_NEAREST) {
         int p = 0;
         constexpr int G = F64 ? 1 : BP_NEAREST_GROUP;
+        if constexpr (!F64 && BP_NEAREST_DEFER) {
+            static_assert(BP_MAX_CHUNK / BP_NEAREST_GROUP + BP_NEAREST_GROUP - 1 <= 32, "one mark bit per group");
+            uint32_t marks = 0; // bit g: group g had a decision inside the tie band on this lane
+            int gi = 0;
+            for (; p + G <= np; p += G, ++gi) {
+                const bool tie = nearest_group<G, MODE, ACC, DEM, PPT, F64, true>(
+                    A, smem, cst, klo_s, pos_s, p, i_pix, j_pix0, dxl, dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl,
+                    wstride, pxd, a_lim, win_c);
+                marks |= (uint32_t)tie << gi;
+            }
+            const int nfull = gi;
+            for (; p < np; ++p, ++gi) {
+                const bool tie = nearest_group<1, MODE, ACC, DEM, PPT, F64, true>(
+                    A, smem, cst, klo_s, pos_s, p, i_pix, j_pix0, dxl, dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl,
+                    wstride, pxd, a_lim, win_c);
+                marks |= (uint32_t)tie << gi;
+            }
+            // queue this lane's marks (one word per lane with any)
+            const uint64_t mm = __builtin_amdgcn_ballot_w64(marks != 0);
+            if (mm != 0) {
+                const int cnt = __popcll(mm);
+                if (__builtin_expect(tq.n + cnt > BP_TIE_QUEUE, 0))
+                    drain_ties<G, ACC, DEM, PPT>(A, tq, box_s, i_pix, j_pix0, zl, dxl, dyv, ddv, dzv, hv, accr, acci,
+                                                 cmpr, cmpi);
+                if (marks != 0) {
+                    const int slot = tq.n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mm >> 32),
+                                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0u));
+                    tq.q[slot] = make_int4(tq.pulse0, lane_id() | (MODE << 6) | (nfull << 8), (int)marks,
+                                           __float_as_int(a_lim));
+                }
+                tq.n += cnt;
+            }
+            return;
+        }
         for (; p + G <= np; p += G)
             nearest_group<G, MODE, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, pos_s, p, i_pix, j_pix0, dxl, dyv, ddv,
                                                        accr, acci, cmpr, cmpi, dzv, hv, zl, wstride, pxd, a_lim, win_c);
@@ -297,10 +465,6 @@ __device__ __forceinline__ float2 sample_or_zero(const float2* row, int k, int n
     const bool in = (uint32_t)k < (uint32_t)nr;
     const float2 v = row[in ? (uint32_t)k : 0u];
     return make_float2(in ? v.x : 0.f, in ? v.y : 0.f);
-}
-
-__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
-    return make_float2(fmaf(a.x, b.x, -(a.y * b.y)), fmaf(a.x, b.y, a.y * b.x));
 }
 
 // One sinc8 window entry from its 8 taps k-3 .. k+4 and the carrier of bin k.
@@ -568,6 +732,12 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     int* edge_s = wlen_s + 2; // nonzero: a window of the chunk reaches past the record (or has no geometry)
     // the tile's pixel box and reference point, read by the set-up lanes of each chunk
     double* box_s = reinterpret_cast<double*>(prio_s + 10);
+    // nearest (fp32 ranges): each wave's queue of tie decisions, after the box
+    TieQueue tq;
+    tq.q = reinterpret_cast<int4*>(smem + ((reinterpret_cast<char*>(box_s + 9) - smem + 15) & ~(ptrdiff_t)15)) +
+           wave * BP_TIE_QUEUE;
+    tq.n = 0;
+    tq.pulse0 = 0;
     if (tid == 0) {
         mode_s[0] = mode_s[1] = rho_s[0] = rho_s[1] = wlen_s[0] = wlen_s[1] = edge_s[0] = edge_s[1] = 0;
         box_s[6] = cx;
@@ -652,6 +822,7 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         // nearest: |fract(ub) - 1/2| beyond tie_lim means ub is within the tie band of an
         // integer; the test is made on the phase a = kappa (fract(ub) - 1/2) against a_lim
         float a_lim = 0.f;
+        tq.pulse0 = pb + n0;
         if constexpr (INTERP == SARBP_NEAREST) {
             const float rho = __int_as_float(__builtin_amdgcn_readfirstlane(rho_s[c & 1]));
             const float tie_lim = 0.5f - fmaf(A.tie_rho[mi], rho, fmaf(A.tie_win, (float)win_c, A.tie_base[mi]));
@@ -660,15 +831,15 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         if (m2)
             accumulate_chunk<INTERP, 2, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, pos_s, np, i0 + lane, j0 + wave, dxl,
                                                             dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, a_lim,
-                                                            win_c);
+                                                            win_c, tq, box_s);
         else if (m1)
             accumulate_chunk<INTERP, 1, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, pos_s, np, i0 + lane, j0 + wave, dxl,
                                                             dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, a_lim,
-                                                            win_c);
+                                                            win_c, tq, box_s);
         else
             accumulate_chunk<INTERP, 0, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, pos_s, np, i0 + lane, j0 + wave, dxl,
                                                             dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, a_lim,
-                                                            win_c);
+                                                            win_c, tq, box_s);
         if constexpr (ACC == SARBP_ACC_CHUNK64) {
 #pragma unroll
             for (int m = 0; m < PPT; ++m) {
@@ -681,6 +852,19 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         __syncthreads();
     }
 
+    if constexpr (INTERP == SARBP_NEAREST && !F64 && BP_NEAREST_DEFER) {
+        if (tq.n > 0) {
+            drain_ties<BP_NEAREST_GROUP, ACC, DEM, PPT>(A, tq, box_s, i0 + lane, j0 + wave, zl, dxl, dyv, ddv, dzv, hv,
+                                                        accr, acci, cmpr, cmpi);
+            if constexpr (ACC == SARBP_ACC_CHUNK64) {
+#pragma unroll
+                for (int m = 0; m < PPT; ++m) {
+                    sumr[m] += (double)accr[m];
+                    sumi[m] += (double)acci[m];
+                }
+            }
+        }
+    }
     if (bad_tile) {
 #pragma unroll
         for (int m = 0; m < PPT; ++m) accr[m] = acci[m] = sumr[m] = sumi[m] = NAN;

@@ -32,6 +32,7 @@ struct Checker {
     int n;
     const float* dem;
     sarbp_index_report* r;
+    unsigned char flagged[BP_WAVES][BP_TX]; // lanes of the current chunk with a decision in the tie band
 
     Checker(const sarbp_params& p_, const BpLayout& L_, const double* pos_, int n_, const float* dem_,
             sarbp_index_report* r_)
@@ -152,6 +153,7 @@ struct Checker {
                     }
             }
             const int stagger = BP_STAGGER ? ((b / A.slots) ^ (b >> 3)) & 1 : 0;
+            int queued[BP_WAVES] = {}, wave_words[BP_WAVES] = {}; // the deferred nearest rechecks' queues
             for (int n0 = 0, np = 0; n0 < n; n0 += np) {
                 np = std::min((n0 == 0 && stagger) ? std::max(1, P >> 1) : P, n - n0);
                 int cmode = 0, wmax = 0;
@@ -207,7 +209,22 @@ struct Checker {
                 else
                     pixels<0, PPT, DEM, F64>(T, np, n0, cst.data(), klo.data(), dxl, dyv, ddv, dzv, pxd, hv, hc,
                                              tie_lim, band, win_c);
+                if (nearest && !F64 && BP_NEAREST_DEFER) {
+                    // each lane with a decision in the band queues one word; a full queue drains first
+                    for (int w = 0; w < BP_WAVES; ++w) {
+                        int cnt = 0;
+                        for (int lane = 0; lane < BP_TX; ++lane) cnt += flagged[w][lane];
+                        if (queued[w] + cnt > BP_TIE_QUEUE) {
+                            ++r->tie_queue_drains;
+                            queued[w] = 0;
+                        }
+                        queued[w] += cnt;
+                        wave_words[w] += cnt;
+                        r->tie_queue_words += cnt;
+                    }
+                }
             }
+            for (int w = 0; w < BP_WAVES; ++w) r->tie_queue_wave_max = std::max(r->tie_queue_wave_max, wave_words[w]);
         }
     }
 
@@ -219,6 +236,8 @@ struct Checker {
         const bool nearest = p.interp == SARBP_NEAREST;
         const double half = nearest ? 0.5 : 0.0;
         const float a_lim = nearest_tie_limit(A.kappa, tie_lim);
+        for (int w = 0; w < BP_WAVES; ++w)
+            for (int lane = 0; lane < BP_TX; ++lane) flagged[w][lane] = 0;
         for (int t = 0; t < np; ++t) {
             const bool bad = klo[t] == INT32_MIN;
             for (int lane = 0; lane < BP_TX; ++lane) {
@@ -247,6 +266,7 @@ struct Checker {
                         const int kdef = (int)floor(u + 0.5);
                         if (fabsf(nearest_phase(A.kappa, f)) > a_lim) { // the kernel's tie test
                             ++r->nearest_rechecks;
+                            flagged[w][lane] = 1;
                             const int kr = kdef - klo[t];
                             if (kr < 0 || kr > win_c - 1) ++r->nearest_recheck_clamped;
                         } else if ((int)k + klo[t] != kdef) {
@@ -276,6 +296,7 @@ extern "C" int sarbp_check_indices(const sarbp_params* params, int32_t n_cu, con
     report->chunk = L.chunk;
     report->pixels_per_lane = L.ppt;
     report->fp64_ranges = L.f64;
+    report->tie_queue_capacity = (params->interp == SARBP_NEAREST && !L.f64 && BP_NEAREST_DEFER) ? BP_TIE_QUEUE : 0;
     report->min_position = INFINITY;
     report->max_position_margin = -INFINITY;
     Checker c(*params, L, positions_h, n, dem_h, report);

@@ -27,6 +27,15 @@
 #ifndef BP_PUNROLL_LINEAR
 #define BP_PUNROLL_LINEAR 4
 #endif
+#ifndef BP_NEAREST_DEFER
+#define BP_NEAREST_DEFER 1
+#endif
+#ifndef BP_TIE_QUEUE
+#define BP_TIE_QUEUE 128 // nearest (fp32 ranges): queued tie-decision words per wave, 16 B each, in LDS
+#endif
+#if BP_TIE_QUEUE < 64
+#error "a chunk adds up to 64 entries (one per lane) to the tie queue"
+#endif
 #ifndef BP_NEAREST_GROUP
 #define BP_NEAREST_GROUP 4
 #endif

@@ -246,8 +246,11 @@ int sarbp_plan_layout(const sarbp_params& p, int n_cu, BpLayout* L) {
                           (p.interp == SARBP_SINC8 ? 8 : (p.interp == SARBP_NEAREST ? 24 : 0));
     // Coarse grids (long windows) that would stage fewer than 8 pulses per step
     // use up to 150 KiB of LDS: one workgroup per CU instead of two.
-    int chunk = (BP_LDS_BUDGET - 64) / per_pulse;
-    if (chunk < 8) chunk = (150 * 1024 - 64) / per_pulse;
+    // nearest with fp32 ranges: each wave's queue of tie decisions (and 16 B of alignment)
+    const int queue =
+        (p.interp == SARBP_NEAREST && !L->f64 && BP_NEAREST_DEFER) ? 16 + BP_WAVES * BP_TIE_QUEUE * 16 : 0;
+    int chunk = (BP_LDS_BUDGET - 64 - queue) / per_pulse;
+    if (chunk < 8) chunk = (150 * 1024 - 64 - queue) / per_pulse;
     if (chunk > BP_MAX_CHUNK) chunk = BP_MAX_CHUNK;
     // (the staging divides step indices u < chunk * wu by wu <= win with a 32-bit
     // multiply-high, exact while chunk * wu * wu < 2^32; the LDS bound keeps
@@ -256,7 +259,7 @@ int sarbp_plan_layout(const sarbp_params& p, int n_cu, BpLayout* L) {
     L->chunk = chunk;
     // + alignment, the chunk's issue-priority word, the double-buffered mode, tie-band and
     // window words, and the tile's pixel box (6 doubles)
-    L->lds_bytes = (size_t)chunk * per_pulse + 4 + 40 + 72; // (the box and the reference point: 9 doubles)
+    L->lds_bytes = (size_t)chunk * per_pulse + 4 + 40 + 72 + queue; // (the box and the reference point: 9 doubles)
     return SARBP_OK;
 }
 

@@ -101,6 +101,10 @@ class sarbp_index_report(ctypes.Structure):
         ("fp64_ranges", ctypes.c_int32),
         ("mode_chunks", ctypes.c_int32 * 3),
         ("tie_band_max", ctypes.c_float),
+        ("tie_queue_words", ctypes.c_int64),
+        ("tie_queue_drains", ctypes.c_int64),
+        ("tie_queue_wave_max", ctypes.c_int32),
+        ("tie_queue_capacity", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:

@@ -300,6 +300,11 @@ typedef struct {
     int32_t fp64_ranges;             /* 1: the plan runs the fp64-range kernels                                         */
     int32_t mode_chunks[3];          /* chunks whose window position used the two-term series, three terms, exact form */
     float tie_band_max;              /* the widest tie band of any chunk [bins] (the fp32 decision is rechecked within it) */
+    int64_t tie_queue_words;         /* nearest, fp32 ranges: words queued for the deferred recheck, one per lane and chunk
+                                        with a decision inside the band                                                 */
+    int64_t tie_queue_drains;        /* of those queues, drains before the end of a tile (the wave's queue was full)     */
+    int32_t tie_queue_wave_max;      /* the most words one wave queued over the call                                    */
+    int32_t tie_queue_capacity;      /* words per wave the kernels' queue holds                                         */
 } sarbp_index_report;
 
 /* Emulate on the host, for the plan `params` would create on a device of n_cu

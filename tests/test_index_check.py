@@ -38,6 +38,15 @@ def _assert_clean(rep, what):
     assert rep["nearest_recheck_clamped"] == 0, (what, rep)
     assert rep["max_error_to_band"] < 1.0, (what, rep)
     assert rep["min_position"] >= 0.0 and rep["max_position_margin"] < 0.0, (what, rep)
+    # deferred nearest rechecks: one queued word per lane and chunk with a decision in the band, so
+    # never more words than rechecked decisions, and words exactly when there are rechecks
+    if rep["tie_queue_capacity"] > 0:
+        assert rep["fp64_ranges"] == 0, (what, rep)
+        assert 0 < rep["tie_queue_words"] <= rep["nearest_rechecks"] or rep["nearest_rechecks"] == 0 == rep[
+            "tie_queue_words"], (what, rep)
+        assert rep["tie_queue_wave_max"] <= rep["tie_queue_words"], (what, rep)
+    else:
+        assert rep["tie_queue_words"] == 0 and rep["tie_queue_drains"] == 0, (what, rep)
 
 
 def _scene_geometry(name):
@@ -64,6 +73,9 @@ def test_scene_geometries(sb, scene, pulses, interp):
     assert rep["max_position_error"] < 1e-5  # ~2^-24 of the window
     if interp == "nearest":
         assert 0 < rep["tie_band_max"] < 4e-5
+        assert rep["tie_queue_capacity"] == 128
+    else:
+        assert rep["tie_queue_capacity"] == 0
 
 
 def test_random_geometries(sb):

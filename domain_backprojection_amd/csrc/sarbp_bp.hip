@@ -594,6 +594,53 @@ __device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int n
     }
 }
 
+// Set-up of a chunk of np pulses from pulse n into one set of records and chunk
+// words (the words must be zero): lanes 0 .. np-1 take each pulse's constants in
+// fp64; with exact windows lanes 128 .. 128+np-1 take its window in parallel, and
+// the tile centre's position within it (pulse_finish) follows in the staging phase.
+static_assert(BP_MAX_CHUNK <= 128, "set-up lanes 0 .. chunk - 1 and window lanes 128 .. 128 + chunk - 1");
+template <int INTERP, bool DEM, bool F64>
+__device__ __forceinline__ void chunk_setup(const BpArgs& A, int tid, int n, int np, float4* cst, int* klo_s,
+                                            double* ext, int* mode_w, int* rho_w, int* wlen_w, int* edge_w,
+                                            const double* box_s) {
+    constexpr int CS = (DEM || F64) ? 3 : 2;
+    constexpr bool EXACTW = INTERP == SARBP_SINC8;
+    constexpr int WL = 128;
+    if (tid < np) {
+        const size_t pa = 3 * (size_t)(n + tid);
+        const double ax = A.pos[pa], ay = A.pos[pa + 1], az = A.pos[pa + 2];
+        if constexpr (bp_ext_doubles(INTERP, F64) == 3) {
+            ext[3 * tid] = ax;
+            ext[3 * tid + 1] = ay;
+            ext[3 * tid + 2] = az;
+        }
+        const double gx = box_s[6], gy = box_s[7], gz = box_s[8];
+        float rho = 0.f;
+        double uc;
+        const int need = F64 ? pulse_setup_f64(A, ax, ay, az, gx, gy, gz, cst + CS * tid, &uc)
+                             : pulse_setup(A, ax, ay, az, gx, gy, gz, cst + CS * tid, &uc, &rho, DEM);
+        if constexpr (EXACTW) {
+            ext[tid] = uc;
+        } else {
+            const int klo = centre_window(A, uc);
+            klo_s[tid] = klo;
+            pulse_finish(A, uc, klo, cst + CS * tid, DEM, F64);
+            // the window's samples klo .. klo + W (linear's last step reads one past the window)
+            if (!(klo != INT32_MIN && klo >= 0 && klo <= A.n_range - 1 - A.win)) atomicOr(edge_w, 1);
+        }
+        if (need) atomicOr(mode_w, need);
+        if constexpr (INTERP == SARBP_NEAREST && !F64) atomicMax(rho_w, __float_as_int(rho));
+    } else if (EXACTW && tid >= WL && tid < WL + np) {
+        const int t = tid - WL;
+        const size_t pa = 3 * (size_t)(n + t);
+        const TileBox box = {box_s[0], box_s[1], box_s[2], box_s[3], box_s[4], box_s[5]};
+        atomicMax(wlen_w, pulse_window(A, A.pos[pa], A.pos[pa + 1], A.pos[pa + 2], box, klo_s + t));
+        // the taps klo - 3 .. klo + W + 4 (within the plan's window) inside the record?
+        const int klo = klo_s[t];
+        if (!(klo != INT32_MIN && klo >= 3 && klo <= A.n_range - 5 - A.win)) atomicOr(edge_w, 1);
+    }
+}
+
 // At most 64 VGPRs, so two 1024-lane workgroups (8 waves per SIMD) fit on a CU:
 // the loop needs that many waves to hide LDS and transcendental latency.
 // F64: the fp64-range variant (pulse_setup_f64 / locate_f64) for plans whose echo
@@ -710,22 +757,23 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     // the hi-fi scene).  Linear and nearest stage the plan's window: there the exact
     // extent's extra set-up cost about as much as its shorter staging saved.
     constexpr bool EXACTW = INTERP == SARBP_SINC8;
+    constexpr int EXT = bp_ext_doubles(INTERP, F64);
     // LDS: room for P windows of the plan's (longest) length, each chunk packing its
-    // own; then per pulse the constants, the window start and the tile centre's
-    // position u_c; then the chunk words and the tile's pixel box.
-    float4* cst = reinterpret_cast<float4*>(smem + (size_t)P * A.win * entry_bytes<INTERP>());
-    int* klo_s = reinterpret_cast<int*>(cst + CS * P);
-    // exact windows keep u_c per pulse; nearest keeps the antenna positions (3 per
-    // pulse) for its tie rechecks
-    double* uc_s = reinterpret_cast<double*>(klo_s + ((P + 1) & ~1));
-    double* pos_s = uc_s;
-    int* prio_s = reinterpret_cast<int*>(uc_s + (EXACTW ? P : (INTERP == SARBP_NEAREST ? 3 * P : 0)));
+    // own; then two sets of per-pulse records (constants, window start, and EXT
+    // doubles: with exact windows the tile centre's position u_c, for nearest with
+    // fp64 ranges the antenna position its in-loop tie rechecks read), so that the
+    // next chunk's set-up can write one set while the loop reads the other; then the
+    // chunk words and the tile's pixel box.
+    float4* cst0 = reinterpret_cast<float4*>(smem + (size_t)P * A.win * entry_bytes<INTERP>());
+    int* klo0 = reinterpret_cast<int*>(cst0 + 2 * CS * P);
+    double* ext0 = reinterpret_cast<double*>(klo0 + 2 * P);
+    int* prio_s = reinterpret_cast<int*>(ext0 + 2 * EXT * P);
     // The accuracy mode of a chunk is the OR of its pulses' modes, its window length
     // the longest of theirs, and its nearest tie band follows from the largest of
-    // their range-term sizes rho.  The words are double-buffered: chunk c writes
-    // mode_s/rho_s/wlen_s[c & 1] and clears the other set, which the previous chunk
-    // finished reading before its last barrier.  (rho >= 0, so its float bits order
-    // as integers.)
+    // their range-term sizes rho.  The words are double-buffered with the records:
+    // chunk c's set-up writes word set c & 1, which the staging phase of chunk c - 1
+    // cleared after chunk c - 2 had finished reading it.  (rho >= 0, so its float
+    // bits order as integers.)
     int* mode_s = prio_s + 1;
     int* rho_s = mode_s + 2;
     int* wlen_s = rho_s + 2;
@@ -756,67 +804,41 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     // The first chunk is half size on alternate workgroups: both placements of a
     // CU's two workgroups (b, b + slots) and (b, b + 8) get opposite parities.
     const int stagger = BP_STAGGER ? (((int)blockIdx.x / A.slots) ^ ((int)blockIdx.x >> 3)) & 1 : 0;
-    for (int n0 = 0, np = 0, c = 0; n0 < (bad_tile ? 0 : pn); n0 += np, ++c) {
-        np = min((n0 == 0 && stagger) ? max(1, P >> 1) : P, pn - n0);
-        // Set-up: lanes 0 .. np-1 (waves 0 and 1) take each pulse's constants in fp64;
-        // with exact windows, lanes WL .. WL+np-1 (the next waves) take its window in
-        // parallel, and the tile centre's position within it follows the barrier.
-        constexpr int WL = 128;
-        if (tid < np) {
-            const size_t pa = 3 * (size_t)(pb + n0 + tid);
-            const double ax = A.pos[pa], ay = A.pos[pa + 1], az = A.pos[pa + 2];
-            if constexpr (INTERP == SARBP_NEAREST) {
-                pos_s[3 * tid] = ax;
-                pos_s[3 * tid + 1] = ay;
-                pos_s[3 * tid + 2] = az;
-            }
-            const double gx = box_s[6], gy = box_s[7], gz = box_s[8];
-            float rho = 0.f;
-            double uc;
-            const int need = F64 ? pulse_setup_f64(A, ax, ay, az, gx, gy, gz, cst + CS * tid, &uc)
-                                 : pulse_setup(A, ax, ay, az, gx, gy, gz, cst + CS * tid, &uc, &rho, DEM);
-            if constexpr (EXACTW) {
-                uc_s[tid] = uc;
-            } else {
-                const int klo = centre_window(A, uc);
-                klo_s[tid] = klo;
-                pulse_finish(A, uc, klo, cst + CS * tid, DEM, F64);
-                // the window's samples klo .. klo + W (linear's last step reads one past the window)
-                if (!(klo != INT32_MIN && klo >= 0 && klo <= A.n_range - 1 - A.win)) atomicOr(edge_s + (c & 1), 1);
-            }
-            if (need) atomicOr(mode_s + (c & 1), need);
-            if constexpr (INTERP == SARBP_NEAREST && !F64) atomicMax(rho_s + (c & 1), __float_as_int(rho));
-        } else if (EXACTW && tid >= WL && tid < WL + np) {
-            const int t = tid - WL;
-            const size_t pa = 3 * (size_t)(pb + n0 + t);
-            const TileBox box = {box_s[0], box_s[1], box_s[2], box_s[3], box_s[4], box_s[5]};
-            atomicMax(wlen_s + (c & 1), pulse_window(A, A.pos[pa], A.pos[pa + 1], A.pos[pa + 2], box, klo_s + t));
-            // the taps klo - 3 .. klo + W + 4 (within the plan's window) inside the record?
-            const int klo = klo_s[t];
-            if (!(klo != INT32_MIN && klo >= 3 && klo <= A.n_range - 5 - A.win)) atomicOr(edge_s + (c & 1), 1);
-        }
+    const int pend = bad_tile ? 0 : pn; // the pulses this workgroup runs
+    int np = min(stagger ? max(1, P >> 1) : P, pend);
+    if (np > 0)
+        chunk_setup<INTERP, DEM, F64>(A, tid, pb, np, cst0, klo0, ext0, mode_s, rho_s, wlen_s, edge_s, box_s);
+    __syncthreads();
+    // Each chunk: staging, barrier, the pulse loop, then the next chunk's set-up on
+    // lanes 0 .. 2 * 64 - 1 (and 128 .. 255 with exact windows), barrier.  The
+    // oldest waves of a workgroup issue first and end the loop long before the
+    // youngest, so the set-up runs while those finish instead of in a phase of its own.
+    for (int n0 = 0, c = 0; n0 < pend; ++c) {
+        const int s = c & 1;
+        const float4* cst = cst0 + s * CS * P;
+        const int* klo_s = klo0 + s * P;
+        const double* ext = ext0 + s * EXT * P;
         if (tid == 0) {
             *prio_s = chunk_priority(A, n0, pn);
-            mode_s[(c + 1) & 1] = 0;
-            rho_s[(c + 1) & 1] = 0;
-            wlen_s[(c + 1) & 1] = 0;
-            edge_s[(c + 1) & 1] = 0;
+            mode_s[s ^ 1] = 0;
+            rho_s[s ^ 1] = 0;
+            wlen_s[s ^ 1] = 0;
+            edge_s[s ^ 1] = 0;
         }
-        __syncthreads();
         int win_c = A.win;
         if constexpr (EXACTW) {
             // each pulse's tile-centre position within its window (read by the pulse
             // loop after the next barrier), while all lanes stage the windows
-            if (tid < np) pulse_finish(A, uc_s[tid], klo_s[tid], cst + CS * tid, DEM, F64);
-            win_c = chunk_window(__builtin_amdgcn_readfirstlane(wlen_s[c & 1]), 1, A.win);
+            if (tid < np) pulse_finish(A, ext[tid], klo_s[tid], cst0 + s * CS * P + CS * tid, DEM, F64);
+            win_c = chunk_window(__builtin_amdgcn_readfirstlane(wlen_s[s]), 1, A.win);
         }
-        if (A.fast_stage && __builtin_amdgcn_readfirstlane(edge_s[c & 1]) == 0)
+        if (A.fast_stage && __builtin_amdgcn_readfirstlane(edge_s[s]) == 0)
             stage_inside<INTERP, EXACTW>(A, smem, klo_s, np, pb + n0, tid, win_c);
         else
             stage_chunk<INTERP, EXACTW>(A, smem, klo_s, np, pb + n0, tid, win_c);
         __syncthreads();
         set_priority(*prio_s);
-        const int mode = __builtin_amdgcn_readfirstlane(mode_s[c & 1]); // the same word for every lane
+        const int mode = __builtin_amdgcn_readfirstlane(mode_s[s]); // the same word for every lane
         const int m1 = mode & 1, m2 = mode & 2;
         const int mi = m2 ? 2 : (m1 ? 1 : 0);
         // nearest: |fract(ub) - 1/2| beyond tie_lim means ub is within the tie band of an
@@ -824,20 +846,20 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         float a_lim = 0.f;
         tq.pulse0 = pb + n0;
         if constexpr (INTERP == SARBP_NEAREST) {
-            const float rho = __int_as_float(__builtin_amdgcn_readfirstlane(rho_s[c & 1]));
+            const float rho = __int_as_float(__builtin_amdgcn_readfirstlane(rho_s[s]));
             const float tie_lim = 0.5f - fmaf(A.tie_rho[mi], rho, fmaf(A.tie_win, (float)win_c, A.tie_base[mi]));
             a_lim = nearest_tie_limit(A.kappa, tie_lim);
         }
         if (m2)
-            accumulate_chunk<INTERP, 2, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, pos_s, np, i0 + lane, j0 + wave, dxl,
+            accumulate_chunk<INTERP, 2, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, ext, np, i0 + lane, j0 + wave, dxl,
                                                             dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, a_lim,
                                                             win_c, tq, box_s);
         else if (m1)
-            accumulate_chunk<INTERP, 1, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, pos_s, np, i0 + lane, j0 + wave, dxl,
+            accumulate_chunk<INTERP, 1, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, ext, np, i0 + lane, j0 + wave, dxl,
                                                             dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, a_lim,
                                                             win_c, tq, box_s);
         else
-            accumulate_chunk<INTERP, 0, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, pos_s, np, i0 + lane, j0 + wave, dxl,
+            accumulate_chunk<INTERP, 0, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, ext, np, i0 + lane, j0 + wave, dxl,
                                                             dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, a_lim,
                                                             win_c, tq, box_s);
         if constexpr (ACC == SARBP_ACC_CHUNK64) {
@@ -849,7 +871,15 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
                 acci[m] = 0.f;
             }
         }
+        const int n1 = n0 + np;
+        const int np1 = min(P, pend - n1);
+        if (np1 > 0)
+            chunk_setup<INTERP, DEM, F64>(A, tid, pb + n1, np1, cst0 + (s ^ 1) * CS * P, klo0 + (s ^ 1) * P,
+                                          ext0 + (s ^ 1) * EXT * P, mode_s + (s ^ 1), rho_s + (s ^ 1),
+                                          wlen_s + (s ^ 1), edge_s + (s ^ 1), box_s);
         __syncthreads();
+        n0 = n1;
+        np = np1;
     }
 
     if constexpr (INTERP == SARBP_NEAREST && !F64 && BP_NEAREST_DEFER) {

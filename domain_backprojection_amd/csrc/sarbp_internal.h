@@ -51,8 +51,16 @@
 #define BP_STAGGER 1
 #endif
 #ifndef BP_LDS_BUDGET
-#define BP_LDS_BUDGET 76000 // bytes per workgroup: two 1024-lane workgroups per CU fit in 160 KiB
+#define BP_LDS_BUDGET 80000 // bytes per workgroup: two 1024-lane workgroups per CU fit in 160 KiB
 #endif
+
+// Doubles kept per pulse beside its constants in a backprojection chunk's records:
+// the tile centre's position u_c for sinc8 (which stages each chunk's exact window),
+// the antenna position for nearest with fp64 ranges (whose tie rechecks run inside
+// the pulse loop), none otherwise.
+__host__ __device__ constexpr int bp_ext_doubles(int interp, bool f64) {
+    return interp == SARBP_SINC8 ? 1 : ((interp == SARBP_NEAREST && f64) ? 3 : 0);
+}
 
 // Backprojection launch geometry of a plan: a function of its parameters and
 // the device's compute-unit count alone (sarbp_plan_layout), so that the host

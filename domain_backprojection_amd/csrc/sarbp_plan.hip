@@ -239,11 +239,13 @@ int sarbp_plan_layout(const sarbp_params& p, int n_cu, BpLayout* L) {
     if (p.interp != SARBP_SINC8) L->win += L->win & 1;
     const int eb = p.interp == SARBP_NEAREST ? 8 : (p.interp == SARBP_LINEAR ? 16 : 64);
     if (p.interp == SARBP_SINC8) sinc8_polynomials(L->sinc_poly);
-    // per pulse: its window entries, constants, window start, and in fp64 (sinc8, whose
-    // chunks stage their exact window extent) the tile centre's bin u_c or (nearest,
-    // for its tie rechecks) the antenna position
-    const int per_pulse = L->win * eb + ((p.dem_relief > 0.0 || L->f64) ? 3 : 2) * 16 + 4 +
-                          (p.interp == SARBP_SINC8 ? 8 : (p.interp == SARBP_NEAREST ? 24 : 0));
+    // per pulse: its window entries, then two sets of records (one read by the pulse
+    // loop while the next chunk's set-up writes the other): constants, window start,
+    // and bp_ext_doubles fp64 words (sinc8, whose chunks stage their exact window
+    // extent: the tile centre's bin u_c; nearest with fp64 ranges, for its tie
+    // rechecks: the antenna position)
+    const int per_pulse = L->win * eb + 2 * (((p.dem_relief > 0.0 || L->f64) ? 3 : 2) * 16 + 4 +
+                                             8 * bp_ext_doubles(p.interp, L->f64 != 0));
     // Coarse grids (long windows) that would stage fewer than 8 pulses per step
     // use up to 150 KiB of LDS: one workgroup per CU instead of two.
     // nearest with fp32 ranges: each wave's queue of tie decisions (and 16 B of alignment)
@@ -257,9 +259,9 @@ int sarbp_plan_layout(const sarbp_params& p, int n_cu, BpLayout* L) {
     // chunk * win below 19200, so this holds whenever a chunk fits)
     if (chunk < 1 || (uint64_t)chunk * L->win * L->win >= (1ull << 32)) return SARBP_EUNSUPPORTED;
     L->chunk = chunk;
-    // + alignment, the chunk's issue-priority word, the double-buffered mode, tie-band and
-    // window words, and the tile's pixel box (6 doubles)
-    L->lds_bytes = (size_t)chunk * per_pulse + 4 + 40 + 72 + queue; // (the box and the reference point: 9 doubles)
+    // + the chunk's issue-priority word, the double-buffered mode, tie-band, window and
+    // edge words (40 bytes), and the tile's pixel box and reference point (9 doubles)
+    L->lds_bytes = (size_t)chunk * per_pulse + 40 + 72 + queue;
     return SARBP_OK;
 }
 

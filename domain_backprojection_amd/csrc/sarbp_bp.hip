@@ -241,7 +241,8 @@ __device__ __forceinline__ float2 nearest_entry(const float2* row, const float2*
 }
 
 // Resolve the wave's queue into the owners' accumulators (every lane of the wave
-// calls it).  box_s: the tile's reference point at [6 .. 8]; dxl .. hv: this
+// calls it): its at most 64 entries, one per lane, in queue order.  box_s: the
+// tile's pixel box at [0 .. 5] and reference point at [6 .. 8]; dxl .. hv: this
 // lane's pixel offsets and heights (each entry takes its owner's); i_pix, j_pix0:
 // this lane's pixel column and the wave's first row.
 template <int G, int ACC, bool DEM, int PPT>
@@ -253,73 +254,80 @@ __device__ __forceinline__ void drain_ties(const BpArgs& A, TieQueue& tq, const 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const int nb = tq.n;
-    const int4 t = lane < nb ? tq.q[lane] : make_int4(0, 0, 0, 0);
-    const int ow = t.y & 63;
-    // the owner's offsets, from its registers
-    const float o_dx = __shfl(dxl, ow);
-    float o_dy[PPT], o_dd[PPT], o_dz[PPT], o_h[PPT], dr[PPT], di[PPT];
+    static_assert(BP_TIE_QUEUE <= 64, "one queue entry per lane");
+    {
+        const int nb = tq.n;
+        const int4 t = lane < nb ? tq.q[lane] : make_int4(0, 0, 0, 0);
+        const int ow = t.y & 63;
+        // the owner's offsets, from its registers
+        const float o_dx = __shfl(dxl, ow);
+        float o_dy[PPT], o_dd[PPT], o_dz[PPT], o_h[PPT], dr[PPT], di[PPT];
 #pragma unroll
-    for (int m = 0; m < PPT; ++m) {
-        o_dy[m] = __shfl(dyv[m], ow);
-        o_dd[m] = __shfl(ddv[m], ow);
-        o_dz[m] = DEM ? __shfl(dzv[m], ow) : 0.f;
-        o_h[m] = DEM ? __shfl(hv[m], ow) : 0.f;
-        dr[m] = di[m] = 0.f;
-    }
-    if (lane < nb) {
-        const int pulse0 = t.x, mode = (t.y >> 6) & 3, nfull = t.y >> 8;
-        uint32_t marks = (uint32_t)t.z;
-        const float a_lim = __int_as_float(t.w);
-        const double gx = box_s[6], gy = box_s[7], gz = box_s[8];
-        while (marks != 0) {
-            const int g = __builtin_ctz(marks);
-            marks &= marks - 1;
-            const int p0 = g < nfull ? g * G : nfull * G + (g - nfull), gsz = g < nfull ? G : 1;
-            for (int q = 0; q < gsz; ++q) {
-                const int n = pulse0 + p0 + q;
-                const double ax = A.pos[3 * (size_t)n], ay = A.pos[3 * (size_t)n + 1], az = A.pos[3 * (size_t)n + 2];
-                float4 cl[3];
-                double uc;
-                float rho;
-                pulse_setup(A, ax, ay, az, gx, gy, gz, cl, &uc, &rho, DEM);
-                const int klo = centre_window(A, uc);
-                pulse_finish(A, uc, klo, cl, DEM, false);
-                const float4 c0 = cl[0], c1 = cl[1], c2 = DEM ? cl[2] : cl[1];
+        for (int m = 0; m < PPT; ++m) {
+            o_dy[m] = __shfl(dyv[m], ow);
+            o_dd[m] = __shfl(ddv[m], ow);
+            o_dz[m] = DEM ? __shfl(dzv[m], ow) : 0.f;
+            o_h[m] = DEM ? __shfl(hv[m], ow) : 0.f;
+            dr[m] = di[m] = 0.f;
+        }
+        if (lane < nb) {
+            const int pulse0 = t.x, mode = (t.y >> 6) & 3, nfull = t.y >> 8;
+            uint32_t marks = (uint32_t)t.z;
+            const float a_lim = __int_as_float(t.w);
+            const double gx = box_s[6], gy = box_s[7], gz = box_s[8];
+            const TileBox box = {box_s[0], box_s[1], box_s[2], box_s[3], box_s[4], box_s[5]};
+            while (marks != 0) {
+                const int g = __builtin_ctz(marks);
+                marks &= marks - 1;
+                const int p0 = g < nfull ? g * G : nfull * G + (g - nfull), gsz = g < nfull ? G : 1;
+                for (int q = 0; q < gsz; ++q) {
+                    const int n = pulse0 + p0 + q;
+                    const double ax = A.pos[3 * (size_t)n], ay = A.pos[3 * (size_t)n + 1],
+                                 az = A.pos[3 * (size_t)n + 2];
+                    float4 cl[3];
+                    double uc;
+                    float rho;
+                    pulse_setup(A, ax, ay, az, gx, gy, gz, cl, &uc, &rho, DEM);
+                    int klo;
+                    pulse_window(A, ax, ay, az, box, &klo);
+                    pulse_finish(A, uc, klo, cl, DEM, false);
+                    const float4 c0 = cl[0], c1 = cl[1], c2 = DEM ? cl[2] : cl[1];
 #pragma unroll
-                for (int m = 0; m < PPT; ++m) {
-                    const float num = pixel_num(o_dx, o_dy[m], o_dd[m], o_dz[m], c0, c2, DEM);
-                    const float ub = mode == 2 ? bin_position<2, DevMath>(num, c0, c1)
-                                               : (mode == 1 ? bin_position<1, DevMath>(num, c0, c1)
-                                                            : bin_position<0, DevMath>(num, c0, c1));
-                    const float a = nearest_phase(A.kappa, DevMath::fract(ub));
-                    if (!(fabsf(a) > a_lim)) continue;
-                    const int kf = (int)DevMath::to_u32(ub) + klo;
-                    const double zp = DEM ? A.z0 + (double)o_h[m] : zl; // the pixel's height
-                    const int kd = nearest_bin_fp64<DevMath>(ax, ay, az, A.x0, A.y0, zp, A.dx, A.dy, A.r0, A.dr,
-                                                             i_pix - lane + ow, j_pix0 + BP_WAVES * m);
-                    if (kd == kf) continue;
-                    const float2* row = A.echo + (size_t)n * (size_t)A.n_range;
-                    const float2 vf = nearest_entry(row, A.phase, kf, A.n_range);
-                    const float2 vd = nearest_entry(row, A.phase, kd, A.n_range);
-                    float sf, cf, sd, cd;
-                    sincos_rev(a, &sf, &cf);
-                    sincos_rev(fmaf(A.kappa, (float)(kf - kd), a), &sd, &cd);
-                    const float2 tf = cmul(vf, make_float2(cf, sf)), td = cmul(vd, make_float2(cd, sd));
-                    dr[m] += td.x - tf.x;
-                    di[m] += td.y - tf.y;
+                    for (int m = 0; m < PPT; ++m) {
+                        const float num = pixel_num(o_dx, o_dy[m], o_dd[m], o_dz[m], c0, c2, DEM);
+                        const float ub = mode == 2 ? bin_position<2, DevMath>(num, c0, c1)
+                                                   : (mode == 1 ? bin_position<1, DevMath>(num, c0, c1)
+                                                                : bin_position<0, DevMath>(num, c0, c1));
+                        const float a = nearest_phase(A.kappa, DevMath::fract(ub));
+                        if (!(fabsf(a) > a_lim)) continue;
+                        const int kf = (int)DevMath::to_u32(ub) + klo;
+                        const double zp = DEM ? A.z0 + (double)o_h[m] : zl; // the pixel's height
+                        const int kd = nearest_bin_fp64<DevMath>(ax, ay, az, A.x0, A.y0, zp, A.dx, A.dy, A.r0, A.dr,
+                                                                 i_pix - lane + ow, j_pix0 + BP_WAVES * m);
+                        if (kd == kf) continue;
+                        const float2* row = A.echo + (size_t)n * (size_t)A.n_range;
+                        const float2 vf = nearest_entry(row, A.phase, kf, A.n_range);
+                        const float2 vd = nearest_entry(row, A.phase, kd, A.n_range);
+                        float sf, cf, sd, cd;
+                        sincos_rev(a, &sf, &cf);
+                        sincos_rev(fmaf(A.kappa, (float)(kf - kd), a), &sd, &cd);
+                        const float2 tf = cmul(vf, make_float2(cf, sf)), td = cmul(vd, make_float2(cd, sd));
+                        dr[m] += td.x - tf.x;
+                        di[m] += td.y - tf.y;
+                    }
                 }
             }
         }
-    }
-    // each owner adds its corrections, in queue order
-    for (int e = 0; e < nb; ++e) {
-        const int owe = __builtin_amdgcn_readlane(ow, e);
+        // each owner adds its corrections, in queue order
+        for (int e = 0; e < nb; ++e) {
+            const int owe = __builtin_amdgcn_readlane(ow, e);
 #pragma unroll
-        for (int m = 0; m < PPT; ++m) {
-            const float er = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dr[m]), e));
-            const float ei = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(di[m]), e));
-            if (lane == owe && (er != 0.f || ei != 0.f)) add_delta<ACC>(accr[m], acci[m], cmpr[m], cmpi[m], er, ei);
+            for (int m = 0; m < PPT; ++m) {
+                const float er = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dr[m]), e));
+                const float ei = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(di[m]), e));
+                if (lane == owe && (er != 0.f || ei != 0.f))
+                    add_delta<ACC>(accr[m], acci[m], cmpr[m], cmpi[m], er, ei);
+            }
         }
     }
     tq.n = 0;
@@ -339,7 +347,7 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
         int p = 0;
         constexpr int G = F64 ? 1 : BP_NEAREST_GROUP;
         if constexpr (!F64 && BP_NEAREST_DEFER) {
-            static_assert(BP_MAX_CHUNK / BP_NEAREST_GROUP + BP_NEAREST_GROUP - 1 <= 32, "one mark bit per group");
+            static_assert(BP_MAX_CHUNK_NEAREST / BP_NEAREST_GROUP + BP_NEAREST_GROUP - 1 <= 32, "one mark bit per group");
             uint32_t marks = 0; // bit g: group g had a decision inside the tie band on this lane
             int gi = 0;
             for (; p + G <= np; p += G, ++gi) {
@@ -502,21 +510,18 @@ __device__ __forceinline__ void sinc8_entry(const BpArgs& A, char* smem, int u, 
 // (the set-up checks): no clamped indices or zero selects, and the samples
 // addressed by 32-bit byte offsets from the chunk's first record (taken only while
 // a chunk's records span less than 4 GiB).  Same entries as stage_chunk.
-template <int INTERP, bool EXACTW>
+template <int INTERP>
 __device__ void stage_inside(const BpArgs& A, char* smem, const int* klo_s, int np, int n0, int tid, int W) {
     constexpr int B = INTERP == SARBP_SINC8 ? 1 : 2;
     const int Wu = W / B, nr = A.n_range;
     const int nu = np * Wu;
-    const float rwu = EXACTW ? 1.0f / (float)Wu : 0.f;
+    const float rwu = 1.0f / (float)Wu;
     const char* base = reinterpret_cast<const char*>(A.echo + (size_t)n0 * (size_t)nr);
     const char* ph = reinterpret_cast<const char*>(A.phase + 4); // carrier of bin 0
     for (int u = tid; u < nu; u += BP_THREADS) {
         int p, k;
         bool bad;
-        if constexpr (EXACTW)
-            stage_step_f32<B>(klo_s, u, Wu, rwu, &p, &k, &bad);
-        else
-            stage_step<DevMath, B>(klo_s, u, Wu, A.win_magic, &p, &k, &bad);
+        stage_step_f32<B>(klo_s, u, Wu, rwu, &p, &k, &bad);
         const uint32_t off = ((uint32_t)p * (uint32_t)nr + (uint32_t)k) * 8u;
         const float2* e = reinterpret_cast<const float2*>(ph + (uint32_t)k * 8u);
         if constexpr (INTERP == SARBP_LINEAR) {
@@ -542,21 +547,17 @@ __device__ void stage_inside(const BpArgs& A, char* smem, const int* klo_s, int 
     }
 }
 
-template <int INTERP, bool EXACTW>
+template <int INTERP>
 __device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int np, int n0, int tid, int W) {
     constexpr int B = INTERP == SARBP_SINC8 ? 1 : 2;
     const int Wu = W / B, nr = A.n_range;
     const int nu = np * Wu;
-    // the pulse of a step: the plan's multiply-high for its window, an fp32 quotient
-    // with an exact correction for a chunk's own window
-    const float rwu = EXACTW ? 1.0f / (float)Wu : 0.f;
+    // the pulse of a step: an fp32 quotient by the chunk's window, exactly corrected
+    const float rwu = 1.0f / (float)Wu;
     for (int u = tid; u < nu; u += BP_THREADS) {
         int p, k;
         bool bad;
-        if constexpr (EXACTW)
-            stage_step_f32<B>(klo_s, u, Wu, rwu, &p, &k, &bad);
-        else
-            stage_step<DevMath, B>(klo_s, u, Wu, A.win_magic, &p, &k, &bad);
+        stage_step_f32<B>(klo_s, u, Wu, rwu, &p, &k, &bad);
         const float2* row = A.echo + (size_t)(n0 + p) * (size_t)nr;
         const int ke = carrier_index<B>(k, nr, bad);
         const float2 c0 = A.phase[ke];
@@ -594,50 +595,43 @@ __device__ void stage_chunk(const BpArgs& A, char* smem, const int* klo_s, int n
     }
 }
 
-// Set-up of a chunk of np pulses from pulse n into one set of records and chunk
-// words (the words must be zero): lanes 0 .. np-1 take each pulse's constants in
-// fp64; with exact windows lanes 128 .. 128+np-1 take its window in parallel, and
-// the tile centre's position within it (pulse_finish) follows in the staging phase.
-static_assert(BP_MAX_CHUNK <= 128, "set-up lanes 0 .. chunk - 1 and window lanes 128 .. 128 + chunk - 1");
+// Set-up of the next chunk's candidate pulses n .. n + cand - 1 into one set of
+// records and chunk words (the words must be zero).  Lanes 0 .. cand-1 take each
+// pulse's constants in fp64 and its tile-centre bin u_c; lanes wl .. wl+cand-1 (wl
+// a wave boundary past cand) take its exact window in parallel.  The chunk's length
+// follows from the longest of these windows (chunk_length), so some candidates may
+// be left for the chunk after; the chunk's accuracy mode, tie-band size and
+// in-record flag are taken over all candidates, which only makes them cautious.
+static_assert(BP_MAX_CHUNK <= 448 && BP_MAX_CHUNK_NEAREST <= BP_MAX_CHUNK,
+              "set-up lanes 0 .. chunk - 1 and window lanes wl .. wl + chunk - 1 lie in one workgroup");
 template <int INTERP, bool DEM, bool F64>
-__device__ __forceinline__ void chunk_setup(const BpArgs& A, int tid, int n, int np, float4* cst, int* klo_s,
-                                            double* ext, int* mode_w, int* rho_w, int* wlen_w, int* edge_w,
-                                            const double* box_s) {
+__device__ __forceinline__ void chunk_setup(const BpArgs& A, int tid, int n, int cand, int wl, float4* cst,
+                                            int* klo_s, double* ext, int* mode_w, int* rho_w, int* wlen_w,
+                                            int* edge_w, const double* box_s) {
     constexpr int CS = (DEM || F64) ? 3 : 2;
-    constexpr bool EXACTW = INTERP == SARBP_SINC8;
-    constexpr int WL = 128;
-    if (tid < np) {
+    if (tid < cand) {
         const size_t pa = 3 * (size_t)(n + tid);
         const double ax = A.pos[pa], ay = A.pos[pa + 1], az = A.pos[pa + 2];
-        if constexpr (bp_ext_doubles(INTERP, F64) == 3) {
-            ext[3 * tid] = ax;
-            ext[3 * tid + 1] = ay;
-            ext[3 * tid + 2] = az;
+        if constexpr (bp_ext_doubles(INTERP, F64) == 4) {
+            double* ps = ext + A.chunk + 3 * tid; // the antenna positions follow the u_c words
+            ps[0] = ax;
+            ps[1] = ay;
+            ps[2] = az;
         }
         const double gx = box_s[6], gy = box_s[7], gz = box_s[8];
         float rho = 0.f;
         double uc;
         const int need = F64 ? pulse_setup_f64(A, ax, ay, az, gx, gy, gz, cst + CS * tid, &uc)
                              : pulse_setup(A, ax, ay, az, gx, gy, gz, cst + CS * tid, &uc, &rho, DEM);
-        if constexpr (EXACTW) {
-            ext[tid] = uc;
-        } else {
-            const int klo = centre_window(A, uc);
-            klo_s[tid] = klo;
-            pulse_finish(A, uc, klo, cst + CS * tid, DEM, F64);
-            // the window's samples klo .. klo + W (linear's last step reads one past the window)
-            if (!(klo != INT32_MIN && klo >= 0 && klo <= A.n_range - 1 - A.win)) atomicOr(edge_w, 1);
-        }
+        ext[tid] = uc;
         if (need) atomicOr(mode_w, need);
         if constexpr (INTERP == SARBP_NEAREST && !F64) atomicMax(rho_w, __float_as_int(rho));
-    } else if (EXACTW && tid >= WL && tid < WL + np) {
-        const int t = tid - WL;
+    } else if (tid >= wl && tid < wl + cand) {
+        const int t = tid - wl;
         const size_t pa = 3 * (size_t)(n + t);
         const TileBox box = {box_s[0], box_s[1], box_s[2], box_s[3], box_s[4], box_s[5]};
         atomicMax(wlen_w, pulse_window(A, A.pos[pa], A.pos[pa + 1], A.pos[pa + 2], box, klo_s + t));
-        // the taps klo - 3 .. klo + W + 4 (within the plan's window) inside the record?
-        const int klo = klo_s[t];
-        if (!(klo != INT32_MIN && klo >= 3 && klo <= A.n_range - 5 - A.win)) atomicOr(edge_w, 1);
+        if (!window_in_record<INTERP>(A, klo_s[t])) atomicOr(edge_w, 1);
     }
 }
 
@@ -750,21 +744,18 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         }
     }
 
-    const int P = A.chunk;
+    const int P = A.chunk; // pulses per chunk, at most (the record capacity)
     constexpr int CS = (DEM || F64) ? 3 : 2; // float4 constants per pulse
-    // sinc8 stages each chunk's exact window extent, about half the plan's (tile
-    // diagonal) window: its entries are the costliest to stage (measured 5 % faster on
-    // the hi-fi scene).  Linear and nearest stage the plan's window: there the exact
-    // extent's extra set-up cost about as much as its shorter staging saved.
-    constexpr bool EXACTW = INTERP == SARBP_SINC8;
     constexpr int EXT = bp_ext_doubles(INTERP, F64);
-    // LDS: room for P windows of the plan's (longest) length, each chunk packing its
-    // own; then two sets of per-pulse records (constants, window start, and EXT
-    // doubles: with exact windows the tile centre's position u_c, for nearest with
-    // fp64 ranges the antenna position its in-loop tie rechecks read), so that the
-    // next chunk's set-up can write one set while the loop reads the other; then the
-    // chunk words and the tile's pixel box.
-    float4* cst0 = reinterpret_cast<float4*>(smem + (size_t)P * A.win * entry_bytes<INTERP>());
+    constexpr int B = INTERP == SARBP_SINC8 ? 1 : 2; // bins per staging step
+    // LDS: A.entries window entries, which each chunk fills with its pulses' exact
+    // windows (as many pulses as fit at its longest window: the tile's range extent
+    // for this pulse, typically about half the tile diagonal the plan bounds it by);
+    // then two sets of per-pulse records (constants, window start, the tile centre's
+    // bin u_c and, for nearest with fp64 ranges, the antenna position its in-loop tie
+    // rechecks read), so that the next chunk's set-up can write one set while the
+    // loop reads the other; then the chunk words and the tile's pixel box.
+    float4* cst0 = reinterpret_cast<float4*>(smem + (size_t)A.entries * entry_bytes<INTERP>());
     int* klo0 = reinterpret_cast<int*>(cst0 + 2 * CS * P);
     double* ext0 = reinterpret_cast<double*>(klo0 + 2 * P);
     int* prio_s = reinterpret_cast<int*>(ext0 + 2 * EXT * P);
@@ -805,19 +796,22 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     // CU's two workgroups (b, b + slots) and (b, b + 8) get opposite parities.
     const int stagger = BP_STAGGER ? (((int)blockIdx.x / A.slots) ^ ((int)blockIdx.x >> 3)) & 1 : 0;
     const int pend = bad_tile ? 0 : pn; // the pulses this workgroup runs
-    int np = min(stagger ? max(1, P >> 1) : P, pend);
-    if (np > 0)
-        chunk_setup<INTERP, DEM, F64>(A, tid, pb, np, cst0, klo0, ext0, mode_s, rho_s, wlen_s, edge_s, box_s);
+    const int wl = (P + 63) & ~63;     // the first window lane of the set-up
+    int cand = min(P, pend);
+    if (cand > 0)
+        chunk_setup<INTERP, DEM, F64>(A, tid, pb, cand, wl, cst0, klo0, ext0, mode_s, rho_s, wlen_s, edge_s, box_s);
     __syncthreads();
     // Each chunk: staging, barrier, the pulse loop, then the next chunk's set-up on
-    // lanes 0 .. 2 * 64 - 1 (and 128 .. 255 with exact windows), barrier.  The
-    // oldest waves of a workgroup issue first and end the loop long before the
-    // youngest, so the set-up runs while those finish instead of in a phase of its own.
+    // lanes 0 .. cand-1 and wl .. wl+cand-1, barrier.  The oldest waves of a
+    // workgroup issue first and end the loop long before the youngest, so the set-up
+    // runs while those finish instead of in a phase of its own.
     for (int n0 = 0, c = 0; n0 < pend; ++c) {
         const int s = c & 1;
         const float4* cst = cst0 + s * CS * P;
         const int* klo_s = klo0 + s * P;
         const double* ext = ext0 + s * EXT * P;
+        const int win_c = chunk_window(__builtin_amdgcn_readfirstlane(wlen_s[s]), B, A.win);
+        const int np = chunk_length(cand, A.entries, win_c, c == 0 && stagger);
         if (tid == 0) {
             *prio_s = chunk_priority(A, n0, pn);
             mode_s[s ^ 1] = 0;
@@ -825,17 +819,13 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
             wlen_s[s ^ 1] = 0;
             edge_s[s ^ 1] = 0;
         }
-        int win_c = A.win;
-        if constexpr (EXACTW) {
-            // each pulse's tile-centre position within its window (read by the pulse
-            // loop after the next barrier), while all lanes stage the windows
-            if (tid < np) pulse_finish(A, ext[tid], klo_s[tid], cst0 + s * CS * P + CS * tid, DEM, F64);
-            win_c = chunk_window(__builtin_amdgcn_readfirstlane(wlen_s[s]), 1, A.win);
-        }
+        // each pulse's tile-centre position within its window (read by the pulse loop
+        // after the next barrier), while all lanes stage the windows
+        if (tid < np) pulse_finish(A, ext[tid], klo_s[tid], cst0 + s * CS * P + CS * tid, DEM, F64);
         if (A.fast_stage && __builtin_amdgcn_readfirstlane(edge_s[s]) == 0)
-            stage_inside<INTERP, EXACTW>(A, smem, klo_s, np, pb + n0, tid, win_c);
+            stage_inside<INTERP>(A, smem, klo_s, np, pb + n0, tid, win_c);
         else
-            stage_chunk<INTERP, EXACTW>(A, smem, klo_s, np, pb + n0, tid, win_c);
+            stage_chunk<INTERP>(A, smem, klo_s, np, pb + n0, tid, win_c);
         __syncthreads();
         set_priority(*prio_s);
         const int mode = __builtin_amdgcn_readfirstlane(mode_s[s]); // the same word for every lane
@@ -851,15 +841,15 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
             a_lim = nearest_tie_limit(A.kappa, tie_lim);
         }
         if (m2)
-            accumulate_chunk<INTERP, 2, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, ext, np, i0 + lane, j0 + wave, dxl,
+            accumulate_chunk<INTERP, 2, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, ext + P, np, i0 + lane, j0 + wave, dxl,
                                                             dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, a_lim,
                                                             win_c, tq, box_s);
         else if (m1)
-            accumulate_chunk<INTERP, 1, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, ext, np, i0 + lane, j0 + wave, dxl,
+            accumulate_chunk<INTERP, 1, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, ext + P, np, i0 + lane, j0 + wave, dxl,
                                                             dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, a_lim,
                                                             win_c, tq, box_s);
         else
-            accumulate_chunk<INTERP, 0, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, ext, np, i0 + lane, j0 + wave, dxl,
+            accumulate_chunk<INTERP, 0, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, ext + P, np, i0 + lane, j0 + wave, dxl,
                                                             dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, a_lim,
                                                             win_c, tq, box_s);
         if constexpr (ACC == SARBP_ACC_CHUNK64) {
@@ -872,14 +862,13 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
             }
         }
         const int n1 = n0 + np;
-        const int np1 = min(P, pend - n1);
-        if (np1 > 0)
-            chunk_setup<INTERP, DEM, F64>(A, tid, pb + n1, np1, cst0 + (s ^ 1) * CS * P, klo0 + (s ^ 1) * P,
+        cand = min(P, pend - n1);
+        if (cand > 0)
+            chunk_setup<INTERP, DEM, F64>(A, tid, pb + n1, cand, wl, cst0 + (s ^ 1) * CS * P, klo0 + (s ^ 1) * P,
                                           ext0 + (s ^ 1) * EXT * P, mode_s + (s ^ 1), rho_s + (s ^ 1),
                                           wlen_s + (s ^ 1), edge_s + (s ^ 1), box_s);
         __syncthreads();
         n0 = n1;
-        np = np1;
     }
 
     if constexpr (INTERP == SARBP_NEAREST && !F64 && BP_NEAREST_DEFER) {

@@ -51,18 +51,15 @@ struct Checker {
     void stage_check(const int* klo_s, int np, int win_c) {
         const int B = p.interp == SARBP_SINC8 ? 1 : 2;
         const int wu = win_c / B;
-        const bool exactw = p.interp == SARBP_SINC8;
         const float rwu = 1.0f / (float)wu;
-        if (win_c % B != 0 || win_c > A.win) ++r->staging_violations;
+        if (win_c % B != 0 || win_c > A.win || np * win_c > A.entries) ++r->staging_violations;
         for (int u = 0; u < np * wu; ++u) {
             int pp, k;
             bool bad;
-            if (exactw)
+            if (B == 1)
                 stage_step_f32<1>(klo_s, u, wu, rwu, &pp, &k, &bad);
-            else if (B == 1)
-                stage_step<HostMath, 1>(klo_s, u, wu, A.win_magic, &pp, &k, &bad);
             else
-                stage_step<HostMath, 2>(klo_s, u, wu, A.win_magic, &pp, &k, &bad);
+                stage_step_f32<2>(klo_s, u, wu, rwu, &pp, &k, &bad);
             bool ok = pp == u / wu && pp >= 0 && pp < np;
             if (ok) {
                 const int ke = B == 1 ? carrier_index<1>(k, A.n_range, bad) : carrier_index<2>(k, A.n_range, bad);
@@ -97,11 +94,10 @@ struct Checker {
         const int P = A.chunk;
         std::vector<float4> cst((size_t)CS * P);
         std::vector<int> klo(P);
-        std::vector<float> rho(P);
-        std::vector<int> mode(P);
+        std::vector<double> uc(P);
         const int nb = A.group_blocks;
         const bool nearest = p.interp == SARBP_NEAREST;
-        const bool exactw = p.interp == SARBP_SINC8; // (the kernels' EXACTW)
+        const bool sinc8 = p.interp == SARBP_SINC8;
         for (int b = 0; b < nb; ++b) {
             const TileFrame T = tile_frame<PPT>(A, b);
             // Lane offsets, as in the kernel: lanes past the grid's edge repeat the last column or row.
@@ -154,44 +150,40 @@ struct Checker {
             }
             const int stagger = BP_STAGGER ? ((b / A.slots) ^ (b >> 3)) & 1 : 0;
             int queued[BP_WAVES] = {}, wave_words[BP_WAVES] = {}; // the deferred nearest rechecks' queues
-            for (int n0 = 0, np = 0; n0 < n; n0 += np) {
-                np = std::min((n0 == 0 && stagger) ? std::max(1, P >> 1) : P, n - n0);
+            for (int n0 = 0, np = 0, c = 0; n0 < n; n0 += np, ++c) {
+                // the set-up's candidates: constants, u_c and exact window of each; the
+                // chunk's mode, tie-band size and in-record flag over all of them
+                const int cand = std::min(P, n - n0);
                 int cmode = 0, wmax = 0;
                 float crho = 0.f;
-                for (int t = 0; t < np; ++t) {
+                bool inside = A.fast_stage != 0;
+                for (int t = 0; t < cand; ++t) {
                     const double* a = pos + 3 * (size_t)(n0 + t);
                     float rh = 0.f;
-                    double uc;
-                    mode[t] = F64 ? pulse_setup_f64(A, a[0], a[1], a[2], T.cx, T.cy, cz, &cst[(size_t)CS * t], &uc)
-                                  : pulse_setup(A, a[0], a[1], a[2], T.cx, T.cy, cz, &cst[(size_t)CS * t], &uc, &rh,
-                                                DEM);
-                    if (exactw)
-                        wmax = std::max(wmax, pulse_window(A, a[0], a[1], a[2], box, &klo[t]));
-                    else
-                        klo[t] = centre_window(A, uc);
-                    pulse_finish(A, uc, klo[t], &cst[(size_t)CS * t], DEM, F64);
-                    cmode |= mode[t];
+                    cmode |= F64 ? pulse_setup_f64(A, a[0], a[1], a[2], T.cx, T.cy, cz, &cst[(size_t)CS * t], &uc[t])
+                                 : pulse_setup(A, a[0], a[1], a[2], T.cx, T.cy, cz, &cst[(size_t)CS * t], &uc[t],
+                                               &rh, DEM);
+                    wmax = std::max(wmax, pulse_window(A, a[0], a[1], a[2], box, &klo[t]));
                     if (!F64) crho = std::max(crho, rh);
+                    inside = inside && (sinc8 ? window_in_record<SARBP_SINC8>(A, klo[t])
+                                              : window_in_record<SARBP_LINEAR>(A, klo[t]));
                 }
-                const int win_c = exactw ? chunk_window(wmax, 1, A.win) : A.win;
+                const int win_c = chunk_window(wmax, sinc8 ? 1 : 2, A.win);
+                np = chunk_length(cand, A.entries, win_c, c == 0 && stagger);
+                for (int t = 0; t < np; ++t) pulse_finish(A, uc[t], klo[t], &cst[(size_t)CS * t], DEM, F64);
                 const int mi = (cmode & 2) ? 2 : (cmode & 1);
                 ++r->mode_chunks[mi];
                 r->window_mean += win_c;
                 ++r->chunks;
                 stage_check(klo.data(), np, win_c);
-                // the in-record staging path: taken when every window, with its taps, lies
-                // in the record; then every sample it reads must be in the record
-                bool inside = A.fast_stage != 0;
-                for (int t = 0; t < np; ++t) {
-                    const int kl = klo[t];
-                    inside = inside && kl != INT32_MIN &&
-                             (exactw ? (kl >= 3 && kl <= A.n_range - 5 - A.win) : (kl >= 0 && kl <= A.n_range - 1 - A.win));
-                }
+                // the in-record staging path: taken when every candidate's window, with
+                // what its staging reads, lies in the record; then every sample it reads
+                // must be in the record
                 if (inside) {
                     ++r->chunks_in_record;
                     for (int t = 0; t < np; ++t) {
-                        const int lo = klo[t] - (exactw ? 3 : 0);
-                        const int hi = klo[t] + win_c - 1 + (exactw ? 4 : (p.interp == SARBP_LINEAR ? 1 : 0));
+                        const int lo = klo[t] - (sinc8 ? 3 : 0);
+                        const int hi = klo[t] + win_c - 1 + (sinc8 ? 4 : (p.interp == SARBP_LINEAR ? 1 : 0));
                         const uint64_t last = ((uint64_t)t * (uint64_t)A.n_range + (uint64_t)hi) * 8u + 8u;
                         if (lo < 0 || hi > A.n_range - 1 || last >= (1ull << 32)) ++r->staging_violations;
                     }

@@ -29,8 +29,6 @@ struct DevMath {
     __device__ static float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
     __device__ static float fract(float x) { return __builtin_amdgcn_fractf(x); }
     __device__ static uint32_t to_u32(float x) { return (uint32_t)x; } // v_cvt_u32_f32: truncates, saturates
-    __device__ static uint32_t mulhi(uint32_t a, uint32_t b) { return __umulhi(a, b); }
-    __device__ static uint32_t mul24(uint32_t a, uint32_t b) { return __umul24(a, b); }
     __device__ static double dadd(double a, double b) { return __dadd_rn(a, b); }
     __device__ static double dsub(double a, double b) { return __dsub_rn(a, b); }
     __device__ static double dmul(double a, double b) { return __dmul_rn(a, b); }
@@ -48,8 +46,6 @@ struct HostMath {
         if (x >= 4294967296.0f) return 0xffffffffu;
         return (uint32_t)x;
     }
-    static uint32_t mulhi(uint32_t a, uint32_t b) { return (uint32_t)(((uint64_t)a * b) >> 32); }
-    static uint32_t mul24(uint32_t a, uint32_t b) { return (a & 0xffffffu) * (b & 0xffffffu); }
     static double dadd(double a, double b) { return a + b; }
     static double dsub(double a, double b) { return a - b; }
     static double dmul(double a, double b) { return a * b; }
@@ -137,6 +133,26 @@ __host__ __device__ inline int pulse_window(const BpArgs& A, double ax, double a
     return w < (double)A.win ? (int)w : A.win;
 }
 
+// Whether a pulse's staged window, with what its staging reads beyond it, lies in
+// the echo record (the fast staging path then needs no clamps): sinc8 reads the taps
+// klo - 3 .. klo + W + 3, linear klo .. klo + W (its last step reads one past the
+// window), nearest klo .. klo + W - 1; W is taken at the plan's longest window.
+template <int INTERP>
+__host__ __device__ __forceinline__ bool window_in_record(const BpArgs& A, int klo) {
+    if (INTERP == SARBP_SINC8) return klo != INT32_MIN && klo >= 3 && klo <= A.n_range - 5 - A.win;
+    return klo != INT32_MIN && klo >= 0 && klo <= A.n_range - 1 - A.win;
+}
+
+// The pulses of a chunk: as many of its cand set-up candidates as the LDS window
+// entries hold at the chunk's window length; half as many (at least one) for the
+// first chunk of staggered workgroups.
+__host__ __device__ __forceinline__ int chunk_length(int cand, int entries, int win_c, bool half) {
+    int np = entries / win_c;
+    if (np > cand) np = cand;
+    if (half) np = np > 1 ? np >> 1 : 1;
+    return np;
+}
+
 // The window length of a chunk: the longest of its pulses' windows, even where
 // staging takes two bins per step, and within the plan's window.
 __host__ __device__ __forceinline__ int chunk_window(int wmax, int bins_per_step, int win) {
@@ -187,15 +203,6 @@ __host__ __device__ inline int pulse_setup(const BpArgs& A, double ax, double ay
     const double e2 = Rt * (q * q * q * (1.0 / 64.0) + q * q * q * q * (5.0 / 128.0)) * idr;
     const double e3 = Rt * q * q * q * q * (5.0 / 128.0) * idr;
     return (q > 0.25 || e3 > 1e-6) ? 2 : (e2 > 1e-6 ? 1 : 0);
-}
-
-// The window of a pulse from the tile centre's bin u_c alone: k_lo = floor(u_c -
-// half_span / dr) - margin_lo, with the plan's length (the triangle inequality
-// bounds every pixel's range by R_t +- half_span).  INT32_MIN for a pulse without
-// finite geometry.
-__host__ __device__ __forceinline__ int centre_window(const BpArgs& A, double uc) {
-    const double klo = floor(uc - A.half_span_bins) - (double)A.margin_lo;
-    return fabs(klo) < 1.0e9 ? (int)klo : INT32_MIN;
 }
 
 // The tile centre's position within its pulse window, ft = u_c - k_lo (+ 1/2 for
@@ -376,25 +383,10 @@ __host__ __device__ __forceinline__ int nearest_bin_fp64(double ax, double ay, d
 
 // Staging of one chunk: step u covers B consecutive bins of one pulse's window
 // (B = 2 for linear and nearest, whose windows have even length W; 1 for sinc8).
-// The pulse is p = u / (W / B), one multiply-high by magic = ceil(2^32 / (W / B))
-// (window_magic; exact while the chunk's steps times W / B stay below 2^32);
+// The pulse is p = u / (W / B), from an fp32 quotient trunc(u * (1 / (W / B)))
+// corrected by one either way so that 0 <= u - p (W / B) < W / B exactly (u < 2^24);
 // the step's first bin is k (absolute).  A pulse without finite geometry
 // (klo = INT32_MIN) takes k = 0 and reads the carrier table's NaN entries.
-template <class M, int B>
-__host__ __device__ __forceinline__ void stage_step(const int* klo_s, int u, int wu, uint32_t magic, int* p_out,
-                                                    int* k_out, bool* bad_out) {
-    const int p = (int)M::mulhi((uint32_t)u, magic);
-    const int klo = klo_s[p];
-    const bool bad = (klo == INT32_MIN);
-    *p_out = p;
-    *k_out = (bad ? 0 : klo) + B * (u - (int)M::mul24((uint32_t)p, (uint32_t)wu));
-    *bad_out = bad;
-}
-
-__host__ __device__ __forceinline__ uint32_t window_magic(int wu) { return 0xffffffffu / (uint32_t)wu + 1u; }
-
-// The same step with the pulse from an fp32 quotient: p = trunc(u * (1 / (W / B))),
-// then corrected by one either way so that 0 <= u - p (W / B) < W / B exactly (u < 2^24).
 template <int B>
 __host__ __device__ __forceinline__ void stage_step_f32(const int* klo_s, int u, int wu, float rwu, int* p_out,
                                                         int* k_out, bool* bad_out) {

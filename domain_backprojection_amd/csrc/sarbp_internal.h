@@ -20,7 +20,10 @@
 #endif
 #define BP_THREADS (64 * BP_WAVES)
 #ifndef BP_MAX_CHUNK
-#define BP_MAX_CHUNK 112 // pulses staged in LDS per step (measured: 64 -> 112 is 2-4 % faster)
+#define BP_MAX_CHUNK 224 // pulses staged in LDS per step, at most (the set-up takes one lane per pulse)
+#endif
+#ifndef BP_MAX_CHUNK_NEAREST
+#define BP_MAX_CHUNK_NEAREST 112 // nearest: one tie-mark bit per group of pulses in a 32-bit word
 #endif
 // Pulses per unrolled hot-loop iteration (measured best: linear four, sinc8
 // eight).  Nearest works on groups of pulses, with one tie branch per group.
@@ -31,10 +34,10 @@
 #define BP_NEAREST_DEFER 1
 #endif
 #ifndef BP_TIE_QUEUE
-#define BP_TIE_QUEUE 128 // nearest (fp32 ranges): queued tie-decision words per wave, 16 B each, in LDS
+#define BP_TIE_QUEUE 64 // nearest (fp32 ranges): queued tie-decision words per wave, 16 B each, in LDS
 #endif
-#if BP_TIE_QUEUE < 64
-#error "a chunk adds up to 64 entries (one per lane) to the tie queue"
+#if BP_TIE_QUEUE != 64
+#error "a chunk adds up to 64 entries (one per lane) to the tie queue, and its drain takes one per lane"
 #endif
 #ifndef BP_NEAREST_GROUP
 #define BP_NEAREST_GROUP 4
@@ -55,11 +58,10 @@
 #endif
 
 // Doubles kept per pulse beside its constants in a backprojection chunk's records:
-// the tile centre's position u_c for sinc8 (which stages each chunk's exact window),
-// the antenna position for nearest with fp64 ranges (whose tie rechecks run inside
-// the pulse loop), none otherwise.
+// the tile centre's bin u_c, and for nearest with fp64 ranges (whose tie rechecks
+// run inside the pulse loop) the antenna position.
 __host__ __device__ constexpr int bp_ext_doubles(int interp, bool f64) {
-    return interp == SARBP_SINC8 ? 1 : ((interp == SARBP_NEAREST && f64) ? 3 : 0);
+    return (interp == SARBP_NEAREST && f64) ? 4 : 1;
 }
 
 // Backprojection launch geometry of a plan: a function of its parameters and
@@ -73,7 +75,8 @@ struct BpLayout {
     int f64;          // 1: range differences in fp64 (windows of many carrier cycles; ppt = 2)
     int win;          // LDS window entries per pulse, at most (a chunk stages its pulses' exact extent)
     int margin_lo;    // bins below the tile's lowest range kept in the window
-    int chunk;        // pulses per LDS step
+    int chunk;        // pulses per LDS step, at most (the per-pulse record capacity)
+    int entries;      // LDS window entries per step, shared by the step's pulses
     size_t lds_bytes; // dynamic LDS per workgroup
     double half_span; // half tile diagonal [m]
     // sinc8: monomial coefficients in g = f - 1/2 of the degree-7 interpolant of
@@ -106,8 +109,8 @@ struct BpArgs {
     int group_blocks;      // ntiles * voxel layers: the workgroups of one pulse group
     int split_len;         // pulses per group (n when the pulses are not split)
     size_t split_stride;   // complex64 elements between the groups' partial images (0 unsplit)
-    int win, margin_lo, chunk, accumulate; // win: the plan's (longest) window
-    uint32_t win_magic;    // ceil(2^32 / wu), wu = win / (bins per staging step): u / wu = umulhi(u, win_magic)
+    int win, margin_lo, chunk, accumulate; // win: the plan's (longest) window; chunk: pulses per step, at most
+    int entries;           // LDS window entries per step (a step holds entries / its window pulses)
     int fast_stage;        // 1: a chunk's records span less than 4 GiB, so staging may use 32-bit byte offsets
     int slots;             // compute units: workgroup b and b + slots usually share a CU
     int* progress;         // [2 * slots] pulse progress per workgroup, read by its CU partner

@@ -7,6 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <complex>
 #include <new>
 #include <vector>
@@ -239,29 +240,40 @@ int sarbp_plan_layout(const sarbp_params& p, int n_cu, BpLayout* L) {
     if (p.interp != SARBP_SINC8) L->win += L->win & 1;
     const int eb = p.interp == SARBP_NEAREST ? 8 : (p.interp == SARBP_LINEAR ? 16 : 64);
     if (p.interp == SARBP_SINC8) sinc8_polynomials(L->sinc_poly);
-    // per pulse: its window entries, then two sets of records (one read by the pulse
-    // loop while the next chunk's set-up writes the other): constants, window start,
-    // and bp_ext_doubles fp64 words (sinc8, whose chunks stage their exact window
-    // extent: the tile centre's bin u_c; nearest with fp64 ranges, for its tie
-    // rechecks: the antenna position)
-    const int per_pulse = L->win * eb + 2 * (((p.dem_relief > 0.0 || L->f64) ? 3 : 2) * 16 + 4 +
-                                             8 * bp_ext_doubles(p.interp, L->f64 != 0));
-    // Coarse grids (long windows) that would stage fewer than 8 pulses per step
-    // use up to 150 KiB of LDS: one workgroup per CU instead of two.
-    // nearest with fp32 ranges: each wave's queue of tie decisions (and 16 B of alignment)
+    // LDS of a workgroup: `entries` window entries, which each chunk fills with its
+    // pulses' exact windows; two sets of per-pulse records of `rec` bytes for up to
+    // `chunk` pulses (the pulse loop reads one while the next chunk's set-up writes
+    // the other: constants, window start, bp_ext_doubles fp64 words); the chunk's
+    // issue-priority word, its double-buffered mode, tie-band, window and edge words
+    // (40 bytes) and the tile's pixel box and reference point (9 doubles); and for
+    // nearest with fp32 ranges each wave's queue of tie decisions (with 16 bytes of
+    // alignment).
+    const int rec = ((p.dem_relief > 0.0 || L->f64) ? 3 : 2) * 16 + 4 + 8 * bp_ext_doubles(p.interp, L->f64 != 0);
     const int queue =
         (p.interp == SARBP_NEAREST && !L->f64 && BP_NEAREST_DEFER) ? 16 + BP_WAVES * BP_TIE_QUEUE * 16 : 0;
-    int chunk = (BP_LDS_BUDGET - 64 - queue) / per_pulse;
-    if (chunk < 8) chunk = (150 * 1024 - 64 - queue) / per_pulse;
-    if (chunk > BP_MAX_CHUNK) chunk = BP_MAX_CHUNK;
-    // (the staging divides step indices u < chunk * wu by wu <= win with a 32-bit
-    // multiply-high, exact while chunk * wu * wu < 2^32; the LDS bound keeps
-    // chunk * win below 19200, so this holds whenever a chunk fits)
-    if (chunk < 1 || (uint64_t)chunk * L->win * L->win >= (1ull << 32)) return SARBP_EUNSUPPORTED;
+    const int fixed = 40 + 72 + queue;
+    const int cap = p.interp == SARBP_NEAREST ? BP_MAX_CHUNK_NEAREST : BP_MAX_CHUNK;
+    // Pulses per chunk when every window is the plan's longest.  Coarse grids (long
+    // windows) that would stage fewer than 8 use up to 150 KiB of LDS: one
+    // workgroup per CU instead of two.
+    int avail = BP_LDS_BUDGET - fixed;
+    if (avail / (L->win * eb + 2 * rec) < 8) avail = 150 * 1024 - fixed;
+    const int pmin = avail / (L->win * eb + 2 * rec);
+    if (pmin < 1) return SARBP_EUNSUPPORTED;
+    // Records for chunks of windows half that long (one pulse sees a tile's range
+    // extent, typically about half the diagonal that bounds it), between pmin and
+    // the cap; the window entries take the rest, at least one longest window.
+    int chunk = avail / (L->win * eb / 2 + 2 * rec);
+    chunk = std::min(cap, std::max(pmin, chunk));
+    int entries = ((avail - 2 * chunk * rec) / eb) & ~1; // (even: 16-byte records follow)
+    if (entries < L->win) {
+        chunk = std::max(1, std::min(chunk, (avail - L->win * eb) / (2 * rec)));
+        entries = ((avail - 2 * chunk * rec) / eb) & ~1;
+    }
+    if (entries < L->win) return SARBP_EUNSUPPORTED;
     L->chunk = chunk;
-    // + the chunk's issue-priority word, the double-buffered mode, tie-band, window and
-    // edge words (40 bytes), and the tile's pixel box and reference point (9 doubles)
-    L->lds_bytes = (size_t)chunk * per_pulse + 40 + 72 + queue;
+    L->entries = entries;
+    L->lds_bytes = (size_t)entries * eb + 2 * (size_t)chunk * rec + fixed;
     return SARBP_OK;
 }
 
@@ -276,10 +288,10 @@ void sarbp_bp_args(const sarbp_params& p, const BpLayout& L, BpArgs* A) {
     A->nblocks = A->group_blocks;
     A->dz = p.nz > 1 ? p.dz : 0.0;
     A->win = L.win;
-    A->win_magic = window_magic(p.interp == SARBP_SINC8 ? L.win : L.win / 2);
     A->fast_stage = (uint64_t)L.chunk * (uint64_t)p.n_range * 8u + 64u < (1ull << 32) ? 1 : 0;
     A->margin_lo = L.margin_lo;
     A->chunk = L.chunk;
+    A->entries = L.entries;
     A->slots = L.n_cu;
     A->r0 = p.r0;
     A->dr = p.dr;

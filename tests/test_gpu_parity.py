@@ -640,6 +640,26 @@ def test_nearest_index_bit_exact_long_windows(sb, lam, dr, px, ground, height):
     assert nearest_index_mismatches(sb, s, range(na)) == 0
 
 
+@pytest.mark.parametrize("n, na", [(128, 4096), (192, 2048)], ids=["128px-4096p", "192px-2048p"])
+def test_nearest_tie_queue_whole_image(sb, n, na):
+    """Nearest on the standard geometry with many pulses per tile, so that a wave queues
+    more than 64 tie decisions (the drain replays them 64 at a time; the 192-pixel case
+    also drains mid-tile): every pixel against the oracle.  Besides the rel-L2 bar, each
+    pixel must be within 2e-3 of the image's peak magnitude: the fp32 tie band keeps
+    every term's phase error below 2 pi kappa band / 2 (8e-4 rad here), so even a
+    coherent sum of such errors stays below 1.1e-3 of a target's peak."""
+    s = synth.make_scene("std", nx=n, ny=n, na=na, interp="nearest")
+    rep = sb.sarbp_check_indices(sb.make_params(**s.params()), s.positions)
+    assert rep["tie_queue_wave_max"] > 64, rep
+    _say(f"[nearest tie queue] {n}x{n} px x {na} pulses: {rep['tie_queue_words']} queued words, "
+         f"{rep['tie_queue_wave_max']} in one wave, {rep['tie_queue_drains']} mid-tile drains")
+    got = _run_bp(sb, s)
+    want = oracle.scene_backproject(s)
+    assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
+    err = np.abs(got - want)
+    assert err.max() <= 2e-3 * np.abs(want).max(), (err.max(), np.unravel_index(err.argmax(), err.shape))
+
+
 # ----------------------------------------------------------------------------- range compression
 
 def test_range_compression_matches_oracle(sb):
@@ -721,15 +741,22 @@ def _check_image(s, got, want, label):
     assert e_all <= REL_L2 and e_clut <= REL_L2 and e_tgt <= REL_L2, (e_all, e_clut, e_tgt)
 
 
-@pytest.mark.parametrize("scene", ["std", "hifi"])
-def test_full_size_whole_image(sb, scene):
-    """The standard scene (linear) and the hi-fi scene (sinc8, perturbed track) against the
-    oracle's whole image: 1024 x 1024 pixels x 4096 pulses."""
+@pytest.mark.parametrize("scene, interp", [("std", None), ("std", "nearest"), ("hifi", None)],
+                         ids=["std", "std-nearest", "hifi"])
+def test_full_size_whole_image(sb, scene, interp):
+    """The standard scene (linear, and nearest on the same echo) and the hi-fi scene (sinc8,
+    perturbed track) against the oracle's whole image: 1024 x 1024 pixels x 4096 pulses.
+    Nearest also bounds every pixel's error by 2e-3 of the image's peak magnitude (the
+    coherent worst case of its fp32 phase bound): its tie rechecks run on a few rows of
+    this geometry hundreds of times per tile, and a wrong recheck shows there."""
+    import dataclasses
     import time
 
     import torch
 
     s = _scene(scene)
+    if interp is not None:
+        s = dataclasses.replace(s, interp=interp)
     with sb.Plan.for_scene(s) as plan:
         img = plan.backproject(torch.from_numpy(s.positions).cuda(), torch.from_numpy(s.echo).cuda())
         torch.cuda.synchronize()
@@ -738,6 +765,9 @@ def test_full_size_whole_image(sb, scene):
     want = oracle.scene_backproject(s)
     _say(f"[{scene}] oracle image in {time.time() - t:.1f}s on {oracle.threads()} threads")
     _check_image(s, got, want, f"{scene} {s.interp}")
+    if s.interp == "nearest":
+        err = np.abs(got - want)
+        assert err.max() <= 2e-3 * np.abs(want).max(), (err.max(), np.unravel_index(err.argmax(), err.shape))
 
 
 def test_large_scene_sampled(sb):

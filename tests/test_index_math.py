@@ -2,9 +2,10 @@
 from their stated rules (no GPU; the kernels' own arithmetic is covered by the GPU
 parity tests):
 
-* backprojection staging divides a step index u by the window's step count wu with a
-  32-bit multiply-high by ceil(2^32 / wu); the plan keeps chunk * wu * wu < 2^32 and
-  u < chunk * wu <= 19200, where the division must be exact;
+* backprojection staging divides a step index u by the chunk window's step count wu
+  as trunc(u * fl32(1 / wu)) in fp32, corrected by one either way; u stays below the
+  LDS entries of a chunk (at most 150 KiB / 8 B = 19200), where the quotient must be
+  exact;
 * the range-compression FFT stores pass outputs in a padded LDS layout: a pass with
   Ns < 32 (other than a transform's last) stores entry i at i + Ns floor(i / (Ns R)).
   Every pass must write distinct slots inside 9N/8 entries, the next pass must read
@@ -16,11 +17,14 @@ import pytest
 
 
 def test_window_step_division_is_exact():
-    u = np.arange(19200, dtype=np.uint64)
+    u = np.arange(19200, dtype=np.int64)
+    uf = u.astype(np.float32)
     for wu in range(3, 19201):
-        magic = np.uint64(((1 << 32) + wu - 1) // wu)
-        p = (u * magic) >> np.uint64(32)
-        assert np.array_equal(p, u // np.uint64(wu)), wu
+        rwu = np.float32(1.0) / np.float32(wu)  # correctly rounded fp32 reciprocal
+        p = (uf * rwu).astype(np.int64)  # fp32 product, truncated
+        r = u - p * wu
+        p = np.where(r < 0, p - 1, np.where(r >= wu, p + 1, p))
+        assert np.array_equal(p, u // wu), wu
 
 
 def _radix(L, p):

@@ -64,7 +64,7 @@ typedef enum { SARBP_NEAREST = 0, SARBP_LINEAR = 1, SARBP_SINC8 = 2 } sarbp_inte
  * kernel, or partial sums folded into double precision).  The image stays complex64.
  *   SARBP_ACC_FP32    fp32 registers (default, fastest)
  *   SARBP_ACC_KAHAN   fp32 with a Kahan compensation term per pixel, per pulse
- *   SARBP_ACC_CHUNK64 fp32 within each LDS pulse chunk (<= 112 pulses), chunk partial
+ *   SARBP_ACC_CHUNK64 fp32 within each LDS pulse chunk (<= 224 pulses), chunk partial
  *                     sums added in fp64 (nearly free) */
 typedef enum { SARBP_ACC_FP32 = 0, SARBP_ACC_KAHAN = 1, SARBP_ACC_CHUNK64 = 2 } sarbp_accum;
 
@@ -295,7 +295,7 @@ typedef struct {
     int64_t chunks;                  /* pulse chunks staged (all workgroups)                                            */
     int64_t chunks_in_record;        /* of which staged by the in-record path (every window and its taps in the record) */
     int32_t window;                  /* W: the plan's longest LDS window, entries per pulse                             */
-    int32_t chunk;                   /* pulses per LDS chunk                                                            */
+    int32_t chunk;                   /* pulses per LDS chunk, at most (each holds what its exact windows let fit)       */
     int32_t pixels_per_lane;         /* 1 or 2 (tiles of 64 x 16 or 64 x 32 pixels)                                    */
     int32_t fp64_ranges;             /* 1: the plan runs the fp64-range kernels                                         */
     int32_t mode_chunks[3];          /* chunks whose window position used the two-term series, three terms, exact form */

@@ -73,12 +73,14 @@ def counter_record():
 
 
 def time_launches(fn, steps, warmup):
-    """Mean, median and minimum per-launch time [ms] of `steps` back-to-back calls,
-    from HIP events recorded between the launches on the launch stream."""
+    """Per-launch time [ms]: the mean over `steps` back-to-back calls between two HIP events
+    on the launch stream (the timed region, synchronized on both sides), then the median and
+    minimum of a second pass of `steps` calls with an event after each (those events put
+    a few microseconds between the launches, so they stay out of the timed region)."""
     import torch
 
-    # At least `warmup` launches and 0.1 s of them: after an idle gap the clock
-    # takes a few tens of milliseconds of load to settle.
+    # At least `warmup` launches and 0.1 s of them: after an idle gap the clock takes a
+    # few tens of milliseconds of load to settle.
     t0, n = time.perf_counter(), 0
     while n < warmup or time.perf_counter() - t0 < 0.1:
         fn()
@@ -87,17 +89,24 @@ def time_launches(fn, steps, warmup):
             torch.cuda.synchronize()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    mean = start.elapsed_time(stop) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record(stream)
     for k in range(steps):
         fn()
         ev[k + 1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     per = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(steps))
     med = per[steps // 2] if steps % 2 else 0.5 * (per[steps // 2 - 1] + per[steps // 2])
-    return {"mean": ev[0].elapsed_time(ev[steps]) / steps, "median": med, "min": per[0]}, wall
+    return {"mean": mean, "median": med, "min": per[0]}, wall
 
 
 def cpu_model():

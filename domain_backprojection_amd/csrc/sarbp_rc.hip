@@ -13,10 +13,12 @@
 // (or two radix-8 ones) in registers.  Twiddles exp(-2 pi i k r / (Ns R)) come
 // from v_sin_f32 / v_cos_f32, whose inputs are in revolutions: the dyadic angle
 // k r / (Ns R) is exact in fp32, so no table is read.  The first pass reads the
-// raw record straight from global memory, the matched-filter multiply is fused
-// into the first pass of the inverse transform (computed as
-// conj(FFT(conj(X H)))), and the last pass writes the conjugated result straight
-// to global memory, so the record crosses HBM once each way.
+// raw record straight from global memory, and the last pass writes the
+// conjugated result straight to global memory, so the record crosses HBM once
+// each way.  The inverse (computed as conj(FFT(conj(X H)))) runs the forward's
+// radices in reverse order, so its first butterfly takes the points the forward's
+// last butterfly produced: those two passes and the matched-filter multiply run
+// as one, in registers (fused_pass).
 //
 // LDS layout: a pass with Ns < 32 writes each lane's outputs Ns apart, so the
 // lanes of a wave would land on a few banks.  Its output buffer is padded by Ns
@@ -111,7 +113,7 @@ __device__ __forceinline__ void dft<16>(float2* v) {
     }
 }
 
-enum Src { SRC_LDS = 0, SRC_RAW = 1, SRC_LDS_FILTER = 2 };
+enum Src { SRC_LDS = 0, SRC_RAW = 1 };
 enum Dst { DST_LDS = 0, DST_OUT_CONJ = 1 };
 
 constexpr int rc_threads(int log2n) {
@@ -119,13 +121,24 @@ constexpr int rc_threads(int log2n) {
 }
 
 // Radix of pass `p` for a transform of 2^L points: passes of 16 and up to three
-// of 8 so that every pass is radix 8 or 16.
+// of 8 so that every pass is radix 8 or 16.  The forward transform runs them in
+// this order and the inverse in the reverse order (INV), so that the inverse's
+// first butterfly j takes the very points j + r N/R the forward's last butterfly j
+// produced (see fused_pass).
 constexpr int rc_radix(int L, int p) {
     const int n8 = (L % 4 == 1) ? 3 : (L % 4 == 2 ? 2 : (L % 4 == 3 ? 1 : 0));
     return p < n8 ? 8 : 16;
 }
 constexpr int rc_passes(int L) {
     return (L % 4 == 1) ? 3 + (L - 9) / 4 : (L % 4 == 2 ? 2 + (L - 6) / 4 : (L % 4 == 3 ? 1 + (L - 3) / 4 : L / 4));
+}
+constexpr int rc_radix_dir(int L, bool inv, int p) { return inv ? rc_radix(L, rc_passes(L) - 1 - p) : rc_radix(L, p); }
+// Ns of pass p: the product of the radices before it.
+constexpr int rc_ns(int L, bool inv, int p) { return p == 0 ? 1 : rc_ns(L, inv, p - 1) * rc_radix_dir(L, inv, p - 1); }
+// The pad unit of pass p's writes (passes with Ns < 32 pad their output, except a
+// transform's last).
+constexpr int rc_pad(int L, bool inv, int p) {
+    return (p < rc_passes(L) - 1 && rc_ns(L, inv, p) < 32) ? rc_ns(L, inv, p) : 0;
 }
 
 // One Stockham pass: butterfly j reads x[j + r N/R], twiddles input r by
@@ -149,8 +162,6 @@ __device__ __forceinline__ void pass(const RcArgs& A, float2* buf, const float2*
                 const int phys = idx + rpad + PADR * (r * NB / NS);
                 if constexpr (SRC == SRC_RAW) {
                     v[b][r] = rin[idx];
-                } else if constexpr (SRC == SRC_LDS_FILTER) {
-                    v[b][r] = cconj(cmul(buf[phys], A.filt[idx]));
                 } else {
                     v[b][r] = buf[phys];
                 }
@@ -188,18 +199,64 @@ __device__ __forceinline__ void pass(const RcArgs& A, float2* buf, const float2*
     if constexpr (DST == DST_LDS) __syncthreads();
 }
 
-// Passes P .. of one transform; PPREV is the pad unit of pass P - 1's writes.
-// Passes with Ns < 32 pad their output, except a transform's last pass.
-template <int L, int P, int NS, int SRC0, int DST_LAST, int PPREV>
-__device__ __forceinline__ void fft_from(const RcArgs& A, float2* buf, const float2* rin, float2* rout) {
-    if constexpr (P < rc_passes(L)) {
-        constexpr int R = rc_radix(L, P);
-        constexpr bool first = (P == 0), last = (P == rc_passes(L) - 1);
-        constexpr int PADW = (!last && NS < 32) ? NS : 0;
-        pass<L, R, NS, first ? SRC0 : SRC_LDS, last ? DST_LAST : DST_LDS, first ? 0 : PPREV, PADW>(A, buf, rin,
-                                                                                                   rout);
-        fft_from<L, P + 1, NS * R, SRC0, DST_LAST, PADW>(A, buf, rin, rout);
+// Passes P .. PEND - 1 of one transform (forward, or inverse with INV); the first
+// of them reads from SRC0 (or LDS), the transform's last writes to DST_LAST.
+template <int L, bool INV, int P, int PEND, int SRC0, int DST_LAST>
+__device__ __forceinline__ void fft_range(const RcArgs& A, float2* buf, const float2* rin, float2* rout) {
+    if constexpr (P < PEND) {
+        constexpr int R = rc_radix_dir(L, INV, P), NS = rc_ns(L, INV, P);
+        constexpr bool last = (P == rc_passes(L) - 1);
+        pass<L, R, NS, P == 0 ? SRC0 : SRC_LDS, last ? DST_LAST : DST_LDS, P == 0 ? 0 : rc_pad(L, INV, P - 1),
+             rc_pad(L, INV, P)>(A, buf, rin, rout);
+        fft_range<L, INV, P + 1, PEND, SRC0, DST_LAST>(A, buf, rin, rout);
     }
+}
+
+// The forward transform's last pass, the matched-filter multiply and the inverse
+// transform's first pass in one: forward butterfly j (radix R, Ns = N/R) reads
+// LDS, twiddles and transforms its R points, whose outputs are X[j + r N/R]; each
+// is multiplied by H and conjugated (the inverse is computed as conj(FFT(conj(.))));
+// the inverse's first pass (radix R, Ns = 1, no twiddles) transforms the same R
+// values and writes them, padded, for its next pass.  One LDS round trip and its
+// barriers fewer than running the two passes apart.
+template <int L>
+__device__ __forceinline__ void fused_pass(const RcArgs& A, float2* buf) {
+    constexpr int PF = rc_passes(L) - 1; // the forward's last pass
+    constexpr int N = 1 << L, R = rc_radix_dir(L, false, PF), NS = rc_ns(L, false, PF);
+    constexpr int T = rc_threads(L), NB = N / R, BPT = (NB + T - 1) / T, PADR = PF == 0 ? 0 : rc_pad(L, false, PF - 1);
+    constexpr int PADW = rc_pad(L, true, 0);
+    static_assert(R == rc_radix_dir(L, true, 0) && NS == NB, "the two passes meet on the same points");
+    float2 v[BPT][R];
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) {
+        const int j = threadIdx.x + b * T;
+        if (NB % T == 0 || j < NB) {
+            const int rpad = PADR ? PADR * (j / NS) : 0;
+#pragma unroll
+            for (int r = 0; r < R; ++r) v[b][r] = buf[j + r * NB + rpad + PADR * (r * NB / NS)];
+        }
+    }
+    __syncthreads(); // every lane has read its inputs before any output overwrites them
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) {
+        const int j = threadIdx.x + b * T;
+        if (NB % T == 0 || j < NB) {
+            const float step = (float)j * (1.0f / (float)(NS * R)); // k = j (j < Ns)
+#pragma unroll
+            for (int r = 1; r < R; ++r) {
+                const float ang = step * (float)r;
+                v[b][r] = cmul(v[b][r], make_float2(__builtin_amdgcn_cosf(ang), -__builtin_amdgcn_sinf(ang)));
+            }
+            dft<R>(v[b]);
+#pragma unroll
+            for (int r = 0; r < R; ++r) v[b][r] = cconj(cmul(v[b][r], A.filt[j + r * NS]));
+            dft<R>(v[b]);
+            const int base = j * R + (PADW ? PADW * j : 0);
+#pragma unroll
+            for (int r = 0; r < R; ++r) buf[base + r] = v[b][r];
+        }
+    }
+    __syncthreads();
 }
 
 constexpr size_t rc_lds_bytes(int L) { return ((size_t)1 << L) / 8 * 9 * sizeof(float2); }
@@ -210,8 +267,11 @@ __global__ __launch_bounds__(rc_threads(L)) void rc_kernel(RcArgs A) {
     constexpr size_t N = (size_t)1 << L;
     const float2* rin = A.raw + (size_t)blockIdx.x * N;
     float2* rout = A.out + (size_t)blockIdx.x * N;
-    fft_from<L, 0, 1, SRC_RAW, DST_LDS, 0>(A, rc_buf, rin, rout);             // X = FFT(x) -> LDS
-    fft_from<L, 0, 1, SRC_LDS_FILTER, DST_OUT_CONJ, 0>(A, rc_buf, rin, rout); // y = conj(FFT(conj(X H)))
+    constexpr int P = rc_passes(L);
+    static_assert(P >= 2, "the fused pass joins two transforms of at least two passes");
+    fft_range<L, false, 0, P - 1, SRC_RAW, DST_LDS>(A, rc_buf, rin, rout); // X = FFT(x), all but its last pass
+    fused_pass<L>(A, rc_buf);                                               // ... its last, * H, conj, inverse first
+    fft_range<L, true, 1, P, SRC_LDS, DST_OUT_CONJ>(A, rc_buf, rin, rout);  // y = conj(FFT(conj(X H)))
 }
 
 template <int L>

@@ -10,7 +10,9 @@ parity tests):
   Ns < 32 (other than a transform's last) stores entry i at i + Ns floor(i / (Ns R)).
   Every pass must write distinct slots inside 9N/8 entries, the next pass must read
   back exactly what was written, and each 32-lane half of a wave must store to 32
-  distinct 8-byte slots modulo 32 (one bank row).
+  distinct 8-byte slots modulo 32 (one bank row).  The inverse transform runs the
+  forward's radices in reverse order, and its first pass is fused with the forward's
+  last: butterfly j of both must cover the same points j + r N/R.
 """
 import numpy as np
 import pytest
@@ -27,9 +29,11 @@ def test_window_step_division_is_exact():
         assert np.array_equal(p, u // wu), wu
 
 
-def _radix(L, p):
+def _radix(L, p, inv=False):
     n8 = {1: 3, 2: 2, 3: 1, 0: 0}[L % 4]
-    return 8 if p < n8 else 16
+    P = _passes(L)
+    q = P - 1 - p if inv else p
+    return 8 if q < n8 else 16
 
 
 def _passes(L):
@@ -47,7 +51,7 @@ def test_rc_padded_layout(L):
     for transform in range(2):
         ns, pad_prev = 1, 0
         for p in range(P):
-            R = _radix(L, p)
+            R = _radix(L, p, inv=transform == 1)
             nb = N // R
             last = p == P - 1
             pad_w = ns if (not last and ns < 32) else 0
@@ -74,5 +78,12 @@ def test_rc_padded_layout(L):
             pad_prev = pad_w
             ns *= R
         if transform == 0:
-            # the filter pass reads the forward transform's output in natural order
+            # the fused pass reads the forward transform's output in natural order
             assert np.array_equal(written[:N], np.arange(N))
+            # ... where the forward's last butterfly j and the inverse's first cover the same points
+            Rf, Ri = _radix(L, P - 1), _radix(L, 0, inv=True)
+            assert Rf == Ri
+            nb = N // Rf
+            fwd_out = [sorted((np.arange(nb)[:, None] + np.arange(Rf)[None, :] * nb)[j]) for j in range(nb)]
+            inv_in = [sorted(j + np.arange(Ri) * (N // Ri)) for j in range(N // Ri)]
+            assert all(np.array_equal(a, b) for a, b in zip(fwd_out, inv_in))

@@ -217,19 +217,26 @@ __device__ __forceinline__ void add_delta(float& ar, float& ai, float& cr, float
 // Deferred tie rechecks (fp32 ranges).  The chunk's loop takes every nearest
 // decision in fp32 and only marks, per lane, the groups of pulses with a decision
 // inside the tie band, so the loop needs no branch.  After the loop each lane with
-// marks appends one word to its wave's queue in LDS: (the chunk's first pulse; the
-// lane, the chunk's accuracy mode and its number of full groups; the marks; the
-// chunk's tie limit).  At the end of the tile, or when the queue fills, the wave
-// resolves the queue at once, one entry per lane (drain_ties): it repeats the
-// marked pulses' set-up and the owner lane's decisions with the same code (so the
-// same constants, a and k_f), finds the definition's bin k_d in fp64 for the
-// decisions inside the band and, where k_d differs from k_f, adds
-// S(k_d) exp(j 2 pi a_d) - S(k_f) exp(j 2 pi a) to the owner, a_d = a + kappa (k_f - k_d)
-// and S(k) = s[k] E[k] formed as the staging forms it.
+// marks appends one word to the workgroup's queue in LDS: (the chunk's first
+// pulse; the lane, the chunk's accuracy mode, its number of full groups and the
+// wave; the marks; the chunk's tie limit).  A chunk adds at most one word per
+// lane, so the queue holds BP_TIE_QUEUE >= 2 BP_THREADS words and is resolved
+// between chunks once it holds more than BP_TIE_QUEUE - BP_THREADS, and at the end
+// of the tile (drain_ties).  There every lane of the workgroup takes words of any
+// wave: it repeats the marked pulses' set-up and the owner lane's decisions with
+// the same code and the owner's offsets from the same function (so the same
+// constants, a and k_f), finds the definition's bin k_d in fp64 for the decisions
+// inside the band and, where k_d differs from k_f, forms the correction
+// S(k_d) exp(j 2 pi a_d) - S(k_f) exp(j 2 pi a), a_d = a + kappa (k_f - k_d) and
+// S(k) = s[k] E[k] formed as the staging forms it, which it leaves in the word's
+// slot.  Then each owner adds its corrections in queue order (for one lane, the
+// order of its chunks).
+static_assert(BP_WAVES <= 16 && BP_MAX_CHUNK_NEAREST / BP_NEAREST_GROUP < 32, "a tie-queue word's wave and group-count fields");
 struct TieQueue {
-    int4* q;    // this wave's BP_TIE_QUEUE entries in LDS
-    int n;      // entries held (the same on every lane)
-    int pulse0; // global index of the chunk's first pulse
+    int4* q;             // the workgroup's BP_TIE_QUEUE words in LDS (a word's correction replaces it)
+    unsigned short* own; // each word's owner: wave << 6 | lane
+    int* count;          // words held (an LDS word)
+    int pulse0;          // global index of the chunk's first pulse
 };
 
 __device__ __forceinline__ int lane_id() { return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
@@ -240,97 +247,122 @@ __device__ __forceinline__ float2 nearest_entry(const float2* row, const float2*
     return cmul(row[k], phase[k + 4]); // carrier of bin k
 }
 
-// Resolve the wave's queue into the owners' accumulators (every lane of the wave
-// calls it): its at most 64 entries, one per lane, in queue order.  box_s: the
-// tile's pixel box at [0 .. 5] and reference point at [6 .. 8]; dxl .. hv: this
-// lane's pixel offsets and heights (each entry takes its owner's); i_pix, j_pix0:
-// this lane's pixel column and the wave's first row.
-template <int G, int ACC, bool DEM, int PPT>
-__device__ __forceinline__ void drain_ties(const BpArgs& A, TieQueue& tq, const double* box_s, int i_pix, int j_pix0,
-                                           double zl, float dxl, const float* dyv, const float* ddv, const float* dzv,
-                                           const float* hv, float* accr, float* acci, float* cmpr, float* cmpi) {
-    const int lane = lane_id();
-    // the entries were written by other lanes of this wave
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    static_assert(BP_TIE_QUEUE <= 64, "one queue entry per lane");
-    {
-        const int nb = tq.n;
-        const int4 t = lane < nb ? tq.q[lane] : make_int4(0, 0, 0, 0);
-        const int ow = t.y & 63;
-        // the owner's offsets, from its registers
-        const float o_dx = __shfl(dxl, ow);
-        float o_dy[PPT], o_dd[PPT], o_dz[PPT], o_h[PPT], dr[PPT], di[PPT];
+// The fp32 offsets from the tile's reference point of the pixels that lane ln of
+// wave wv works with: x (dxl), y (dyv), |d|^2 (ddv) and, on terrain, the height h
+// (hv) and its difference to the tile's mid-height hc (dzv).  Lanes past the
+// grid's edge take the last column or row, so every lane's range stays within the
+// staged window.  The pulse loop and the tie rechecks of its decisions (made by
+// any lane of the workgroup) both take them from here.
+template <int PPT, bool DEM>
+__device__ __forceinline__ void lane_offsets(const BpArgs& A, const TileFrame& T, double hc, int ln, int wv,
+                                             float* dxl, float* dyv, float* ddv, float* dzv, float* hv) {
+    const int i_off = min(T.i0 + ln, T.i_last);
+    const double ddx = ((double)i_off - T.cxp) * A.dx;
+    *dxl = (float)ddx;
 #pragma unroll
-        for (int m = 0; m < PPT; ++m) {
-            o_dy[m] = __shfl(dyv[m], ow);
-            o_dd[m] = __shfl(ddv[m], ow);
-            o_dz[m] = DEM ? __shfl(dzv[m], ow) : 0.f;
-            o_h[m] = DEM ? __shfl(hv[m], ow) : 0.f;
-            dr[m] = di[m] = 0.f;
+    for (int m = 0; m < PPT; ++m) {
+        const int j_off = min(T.j0 + wv + BP_WAVES * m, T.j_last);
+        const double ddy = ((double)j_off - T.cyp) * A.dy;
+        dyv[m] = (float)ddy;
+        if constexpr (DEM) {
+            hv[m] = A.dem[(size_t)j_off * A.nx + i_off];
+            const double ddz = (double)hv[m] - hc;
+            dzv[m] = (float)ddz;
+            ddv[m] = (float)(ddx * ddx + ddy * ddy + ddz * ddz);
+        } else {
+            hv[m] = dzv[m] = 0.f;
+            ddv[m] = (float)(ddx * ddx + ddy * ddy);
         }
-        if (lane < nb) {
-            const int pulse0 = t.x, mode = (t.y >> 6) & 3, nfull = t.y >> 8;
-            uint32_t marks = (uint32_t)t.z;
-            const float a_lim = __int_as_float(t.w);
-            const double gx = box_s[6], gy = box_s[7], gz = box_s[8];
-            const TileBox box = {box_s[0], box_s[1], box_s[2], box_s[3], box_s[4], box_s[5]};
-            while (marks != 0) {
-                const int g = __builtin_ctz(marks);
-                marks &= marks - 1;
-                const int p0 = g < nfull ? g * G : nfull * G + (g - nfull), gsz = g < nfull ? G : 1;
-                for (int q = 0; q < gsz; ++q) {
-                    const int n = pulse0 + p0 + q;
-                    const double ax = A.pos[3 * (size_t)n], ay = A.pos[3 * (size_t)n + 1],
-                                 az = A.pos[3 * (size_t)n + 2];
-                    float4 cl[3];
-                    double uc;
-                    float rho;
-                    pulse_setup(A, ax, ay, az, gx, gy, gz, cl, &uc, &rho, DEM);
-                    int klo;
-                    pulse_window(A, ax, ay, az, box, &klo);
-                    pulse_finish(A, uc, klo, cl, DEM, false);
-                    const float4 c0 = cl[0], c1 = cl[1], c2 = DEM ? cl[2] : cl[1];
+    }
+}
+
+// Resolve the workgroup's queue of qn words into the owners' accumulators (every
+// lane of the workgroup calls it, after a barrier that follows the last append).
+// box_s: the tile's pixel box at [0 .. 5] and reference point at [6 .. 8]; T, hc:
+// the tile frame and mid-height; zl: the layer's height.
+template <int G, int ACC, bool DEM, int PPT>
+__device__ __forceinline__ void drain_ties(const BpArgs& A, const TieQueue& tq, int qn, const double* box_s,
+                                           const TileFrame& T, double hc, double zl, float* accr, float* acci,
+                                           float* cmpr, float* cmpi) {
+    const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    float4* dq = reinterpret_cast<float4*>(tq.q);
+    for (int e = tid; e < qn; e += BP_THREADS) {
+        const int4 t = tq.q[e];
+        const int ow = t.y & 63, mode = (t.y >> 6) & 3, nfull = (t.y >> 8) & 31, wo = (t.y >> 13) & 15;
+        const int pulse0 = t.x;
+        uint32_t marks = (uint32_t)t.z;
+        const float a_lim = __int_as_float(t.w);
+        float o_dx, o_dy[PPT], o_dd[PPT], o_dz[PPT], o_h[PPT], dr[PPT], di[PPT];
+        lane_offsets<PPT, DEM>(A, T, hc, ow, wo, &o_dx, o_dy, o_dd, o_dz, o_h);
 #pragma unroll
-                    for (int m = 0; m < PPT; ++m) {
-                        const float num = pixel_num(o_dx, o_dy[m], o_dd[m], o_dz[m], c0, c2, DEM);
-                        const float ub = mode == 2 ? bin_position<2, DevMath>(num, c0, c1)
-                                                   : (mode == 1 ? bin_position<1, DevMath>(num, c0, c1)
-                                                                : bin_position<0, DevMath>(num, c0, c1));
-                        const float a = nearest_phase(A.kappa, DevMath::fract(ub));
-                        if (!(fabsf(a) > a_lim)) continue;
-                        const int kf = (int)DevMath::to_u32(ub) + klo;
-                        const double zp = DEM ? A.z0 + (double)o_h[m] : zl; // the pixel's height
-                        const int kd = nearest_bin_fp64<DevMath>(ax, ay, az, A.x0, A.y0, zp, A.dx, A.dy, A.r0, A.dr,
-                                                                 i_pix - lane + ow, j_pix0 + BP_WAVES * m);
-                        if (kd == kf) continue;
-                        const float2* row = A.echo + (size_t)n * (size_t)A.n_range;
-                        const float2 vf = nearest_entry(row, A.phase, kf, A.n_range);
-                        const float2 vd = nearest_entry(row, A.phase, kd, A.n_range);
-                        float sf, cf, sd, cd;
-                        sincos_rev(a, &sf, &cf);
-                        sincos_rev(fmaf(A.kappa, (float)(kf - kd), a), &sd, &cd);
-                        const float2 tf = cmul(vf, make_float2(cf, sf)), td = cmul(vd, make_float2(cd, sd));
-                        dr[m] += td.x - tf.x;
-                        di[m] += td.y - tf.y;
-                    }
+        for (int m = 0; m < PPT; ++m) dr[m] = di[m] = 0.f;
+        const double gx = box_s[6], gy = box_s[7], gz = box_s[8];
+        const TileBox box = {box_s[0], box_s[1], box_s[2], box_s[3], box_s[4], box_s[5]};
+        while (marks != 0) {
+            const int g = __builtin_ctz(marks);
+            marks &= marks - 1;
+            const int p0 = g < nfull ? g * G : nfull * G + (g - nfull), gsz = g < nfull ? G : 1;
+            for (int q = 0; q < gsz; ++q) {
+                const int n = pulse0 + p0 + q;
+                const double ax = A.pos[3 * (size_t)n], ay = A.pos[3 * (size_t)n + 1], az = A.pos[3 * (size_t)n + 2];
+                float4 cl[3];
+                double uc;
+                float rho;
+                pulse_setup(A, ax, ay, az, gx, gy, gz, cl, &uc, &rho, DEM);
+                int klo;
+                pulse_window(A, ax, ay, az, box, &klo);
+                pulse_finish(A, uc, klo, cl, DEM, false);
+                const float4 c0 = cl[0], c1 = cl[1], c2 = DEM ? cl[2] : cl[1];
+#pragma unroll
+                for (int m = 0; m < PPT; ++m) {
+                    const float num = pixel_num(o_dx, o_dy[m], o_dd[m], o_dz[m], c0, c2, DEM);
+                    const float ub = mode == 2 ? bin_position<2, DevMath>(num, c0, c1)
+                                               : (mode == 1 ? bin_position<1, DevMath>(num, c0, c1)
+                                                            : bin_position<0, DevMath>(num, c0, c1));
+                    const float a = nearest_phase(A.kappa, DevMath::fract(ub));
+                    if (!(fabsf(a) > a_lim)) continue;
+                    const int kf = (int)DevMath::to_u32(ub) + klo;
+                    const double zp = DEM ? A.z0 + (double)o_h[m] : zl; // the pixel's height
+                    const int kd = nearest_bin_fp64<DevMath>(ax, ay, az, A.x0, A.y0, zp, A.dx, A.dy, A.r0, A.dr,
+                                                             T.i0 + ow, T.j0 + wo + BP_WAVES * m);
+                    if (kd == kf) continue;
+                    const float2* row = A.echo + (size_t)n * (size_t)A.n_range;
+                    const float2 vf = nearest_entry(row, A.phase, kf, A.n_range);
+                    const float2 vd = nearest_entry(row, A.phase, kd, A.n_range);
+                    float sf, cf, sd, cd;
+                    sincos_rev(a, &sf, &cf);
+                    sincos_rev(fmaf(A.kappa, (float)(kf - kd), a), &sd, &cd);
+                    const float2 tf = cmul(vf, make_float2(cf, sf)), td = cmul(vd, make_float2(cd, sd));
+                    dr[m] += td.x - tf.x;
+                    di[m] += td.y - tf.y;
                 }
             }
         }
-        // each owner adds its corrections, in queue order
-        for (int e = 0; e < nb; ++e) {
-            const int owe = __builtin_amdgcn_readlane(ow, e);
-#pragma unroll
-            for (int m = 0; m < PPT; ++m) {
-                const float er = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dr[m]), e));
-                const float ei = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(di[m]), e));
-                if (lane == owe && (er != 0.f || ei != 0.f))
-                    add_delta<ACC>(accr[m], acci[m], cmpr[m], cmpi[m], er, ei);
+        dq[e] = make_float4(dr[0], di[0], PPT > 1 ? dr[PPT - 1] : 0.f, PPT > 1 ? di[PPT - 1] : 0.f);
+    }
+    __syncthreads();
+    // each owner adds its corrections, in queue order: 64 words at a time, the
+    // wave's own words with a correction found by a ballot
+    static_assert(PPT <= 2, "a correction word holds two pixels");
+    for (int b = 0; b < qn; b += 64) {
+        const int e = b + lane;
+        bool hit = false;
+        if (e < qn) {
+            const float4 d = dq[e];
+            hit = (tq.own[e] >> 6) == wave && (d.x != 0.f || d.y != 0.f || d.z != 0.f || d.w != 0.f);
+        }
+        uint64_t hits = __builtin_amdgcn_ballot_w64(hit);
+        while (hits != 0) {
+            const int k = (int)__builtin_ctzll(hits);
+            hits &= hits - 1;
+            if (lane == (tq.own[b + k] & 63)) {
+                const float4 d = dq[b + k];
+                if (d.x != 0.f || d.y != 0.f) add_delta<ACC>(accr[0], acci[0], cmpr[0], cmpi[0], d.x, d.y);
+                if (PPT > 1 && (d.z != 0.f || d.w != 0.f))
+                    add_delta<ACC>(accr[PPT - 1], acci[PPT - 1], cmpr[PPT - 1], cmpi[PPT - 1], d.z, d.w);
             }
         }
     }
-    tq.n = 0;
 }
 
 template <int INTERP, int MODE, int ACC, bool DEM, int PPT, bool F64>
@@ -339,7 +371,7 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
                                                  int j_pix0, float dxl, const float* dyv, const float* ddv,
                                                  float* accr, float* acci, float* cmpr, float* cmpi,
                                                  const float* dzv, const float* hv, double zl, const double* pxd,
-                                                 float a_lim, int win_c, TieQueue& tq, const double* box_s) {
+                                                 float a_lim, int win_c, const TieQueue& tq) {
     const int eb = entry_bytes<INTERP>();
     const uint32_t wstride = (uint32_t)(win_c * eb);
     const float kappa = A.kappa;
@@ -363,20 +395,21 @@ __device__ __forceinline__ void accumulate_chunk(const BpArgs& A, const char* sm
                     wstride, pxd, a_lim, win_c);
                 marks |= (uint32_t)tie << gi;
             }
-            // queue this lane's marks (one word per lane with any)
+            // queue this lane's marks (one word per lane with any; the queue has room
+            // for a word from every lane of the workgroup)
             const uint64_t mm = __builtin_amdgcn_ballot_w64(marks != 0);
             if (mm != 0) {
-                const int cnt = __popcll(mm);
-                if (__builtin_expect(tq.n + cnt > BP_TIE_QUEUE, 0))
-                    drain_ties<G, ACC, DEM, PPT>(A, tq, box_s, i_pix, j_pix0, zl, dxl, dyv, ddv, dzv, hv, accr, acci,
-                                                 cmpr, cmpi);
+                const int lane = lane_id(), wave = (int)(threadIdx.x >> 6);
+                int base = 0;
+                if (lane == 0) base = atomicAdd(tq.count, __popcll(mm));
+                base = __builtin_amdgcn_readfirstlane(base);
                 if (marks != 0) {
-                    const int slot = tq.n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mm >> 32),
+                    const int slot = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mm >> 32),
                                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mm, 0u));
-                    tq.q[slot] = make_int4(tq.pulse0, lane_id() | (MODE << 6) | (nfull << 8), (int)marks,
+                    tq.q[slot] = make_int4(tq.pulse0, lane | (MODE << 6) | (nfull << 8) | (wave << 13), (int)marks,
                                            __float_as_int(a_lim));
+                    tq.own[slot] = (unsigned short)((wave << 6) | lane);
                 }
-                tq.n += cnt;
             }
             return;
         }
@@ -672,7 +705,7 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
 #pragma unroll
     for (int m = 0; m < PPT; ++m) j_off[m] = min(j0 + wave + BP_WAVES * m, j_last);
     const double ddx = ((double)i_off - cxp) * A.dx;
-    const float dxl = (float)ddx;
+    float dxl;
     double pxd[1 + 3 * PPT]; // F64: ddx, then ddy, |d|^2 and (terrain) dz of each of the lane's pixels
     pxd[0] = ddx;
     float dyv[PPT], ddv[PPT], accr[PPT], acci[PPT];
@@ -681,8 +714,6 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
 #pragma unroll
     for (int m = 0; m < PPT; ++m) {
         const double ddy = ((double)j_off[m] - cyp) * A.dy;
-        dyv[m] = (float)ddy;
-        ddv[m] = (float)(ddx * ddx + ddy * ddy);
         pxd[1 + m] = ddy;
         pxd[1 + PPT + m] = ddx * ddx + ddy * ddy;
         pxd[1 + 2 * PPT + m] = 0.0;
@@ -700,8 +731,7 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     float dzv[PPT], hv[PPT];
     bool bad_tile = false;
     double za = zl, zb = zl; // the tile's height range (one plane, or the terrain's)
-#pragma unroll
-    for (int m = 0; m < PPT; ++m) dzv[m] = hv[m] = 0.f;
+    double hc = 0.0;         // terrain: the tile's mid-height
     if constexpr (DEM) {
         float hmin = INFINITY, hmax = -INFINITY;
 #pragma unroll
@@ -729,7 +759,7 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         }
         __syncthreads();
         bad_tile = !((double)hmax - (double)hmin <= A.dem_relief);
-        const double hc = 0.5 * ((double)hmin + (double)hmax);
+        hc = 0.5 * ((double)hmin + (double)hmax);
         cz = A.z0 + hc;
         za = A.z0 + (double)hmin;
         zb = A.z0 + (double)hmax;
@@ -737,12 +767,13 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         for (int m = 0; m < PPT; ++m) {
             const double ddy = ((double)j_off[m] - cyp) * A.dy;
             const double ddz = (double)hv[m] - hc;
-            dzv[m] = (float)ddz;
-            ddv[m] = (float)(ddx * ddx + ddy * ddy + ddz * ddz);
             pxd[1 + PPT + m] = ddx * ddx + ddy * ddy + ddz * ddz;
             pxd[1 + 2 * PPT + m] = ddz;
         }
     }
+    // the fp32 offsets of the pulse loop (the tie rechecks of its decisions take
+    // them from the same function)
+    lane_offsets<PPT, DEM>(A, T, hc, lane, wave, &dxl, dyv, ddv, dzv, hv);
 
     const int P = A.chunk; // pulses per chunk, at most (the record capacity)
     constexpr int CS = (DEM || F64) ? 3 : 2; // float4 constants per pulse
@@ -771,13 +802,16 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     int* edge_s = wlen_s + 2; // nonzero: a window of the chunk reaches past the record (or has no geometry)
     // the tile's pixel box and reference point, read by the set-up lanes of each chunk
     double* box_s = reinterpret_cast<double*>(prio_s + 10);
-    // nearest (fp32 ranges): each wave's queue of tie decisions, after the box
+    // nearest (fp32 ranges): the workgroup's queue of tie-recheck words, after the
+    // box: the words, their owners and the count
+    constexpr bool QUEUE = INTERP == SARBP_NEAREST && !F64 && BP_NEAREST_DEFER;
     TieQueue tq;
-    tq.q = reinterpret_cast<int4*>(smem + ((reinterpret_cast<char*>(box_s + 9) - smem + 15) & ~(ptrdiff_t)15)) +
-           wave * BP_TIE_QUEUE;
-    tq.n = 0;
+    tq.q = reinterpret_cast<int4*>(smem + ((reinterpret_cast<char*>(box_s + 9) - smem + 15) & ~(ptrdiff_t)15));
+    tq.own = reinterpret_cast<unsigned short*>(tq.q + BP_TIE_QUEUE);
+    tq.count = reinterpret_cast<int*>(tq.own + BP_TIE_QUEUE);
     tq.pulse0 = 0;
     if (tid == 0) {
+        if constexpr (QUEUE) *tq.count = 0;
         mode_s[0] = mode_s[1] = rho_s[0] = rho_s[1] = wlen_s[0] = wlen_s[1] = edge_s[0] = edge_s[1] = 0;
         box_s[6] = cx;
         box_s[7] = cy;
@@ -843,15 +877,15 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         if (m2)
             accumulate_chunk<INTERP, 2, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, ext + P, np, i0 + lane, j0 + wave, dxl,
                                                             dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, a_lim,
-                                                            win_c, tq, box_s);
+                                                            win_c, tq);
         else if (m1)
             accumulate_chunk<INTERP, 1, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, ext + P, np, i0 + lane, j0 + wave, dxl,
                                                             dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, a_lim,
-                                                            win_c, tq, box_s);
+                                                            win_c, tq);
         else
             accumulate_chunk<INTERP, 0, ACC, DEM, PPT, F64>(A, smem, cst, klo_s, ext + P, np, i0 + lane, j0 + wave, dxl,
                                                             dyv, ddv, accr, acci, cmpr, cmpi, dzv, hv, zl, pxd, a_lim,
-                                                            win_c, tq, box_s);
+                                                            win_c, tq);
         if constexpr (ACC == SARBP_ACC_CHUNK64) {
 #pragma unroll
             for (int m = 0; m < PPT; ++m) {
@@ -869,12 +903,20 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
                                           wlen_s + (s ^ 1), edge_s + (s ^ 1), box_s);
         __syncthreads();
         n0 = n1;
+        if constexpr (QUEUE) {
+            // resolve the tie queue when it could not take another chunk's words
+            const int qn = __builtin_amdgcn_readfirstlane(*tq.count);
+            if (n0 < pend && qn > BP_TIE_QUEUE - BP_THREADS) {
+                drain_ties<BP_NEAREST_GROUP, ACC, DEM, PPT>(A, tq, qn, box_s, T, hc, zl, accr, acci, cmpr, cmpi);
+                if (tid == 0) *tq.count = 0; // read again after the next chunk's first barrier
+            }
+        }
     }
 
-    if constexpr (INTERP == SARBP_NEAREST && !F64 && BP_NEAREST_DEFER) {
-        if (tq.n > 0) {
-            drain_ties<BP_NEAREST_GROUP, ACC, DEM, PPT>(A, tq, box_s, i0 + lane, j0 + wave, zl, dxl, dyv, ddv, dzv, hv,
-                                                        accr, acci, cmpr, cmpi);
+    if constexpr (QUEUE) {
+        const int qn = __builtin_amdgcn_readfirstlane(*tq.count);
+        if (qn > 0) {
+            drain_ties<BP_NEAREST_GROUP, ACC, DEM, PPT>(A, tq, qn, box_s, T, hc, zl, accr, acci, cmpr, cmpi);
             if constexpr (ACC == SARBP_ACC_CHUNK64) {
 #pragma unroll
                 for (int m = 0; m < PPT; ++m) {

@@ -149,7 +149,7 @@ struct Checker {
                     }
             }
             const int stagger = BP_STAGGER ? ((b / A.slots) ^ (b >> 3)) & 1 : 0;
-            int queued[BP_WAVES] = {}, wave_words[BP_WAVES] = {}; // the deferred nearest rechecks' queues
+            int queued = 0, tile_words = 0; // the deferred nearest rechecks' queue (one per workgroup)
             for (int n0 = 0, np = 0, c = 0; n0 < n; n0 += np, ++c) {
                 // the set-up's candidates: constants, u_c and exact window of each; the
                 // chunk's mode, tie-band size and in-record flag over all of them
@@ -202,21 +202,21 @@ struct Checker {
                     pixels<0, PPT, DEM, F64>(T, np, n0, cst.data(), klo.data(), dxl, dyv, ddv, dzv, pxd, hv, hc,
                                              tie_lim, band, win_c);
                 if (nearest && !F64 && BP_NEAREST_DEFER) {
-                    // each lane with a decision in the band queues one word; a full queue drains first
-                    for (int w = 0; w < BP_WAVES; ++w) {
-                        int cnt = 0;
+                    // each lane with a decision in the band queues one word; between chunks
+                    // the queue is resolved when it has no room for another chunk's words
+                    int cnt = 0;
+                    for (int w = 0; w < BP_WAVES; ++w)
                         for (int lane = 0; lane < BP_TX; ++lane) cnt += flagged[w][lane];
-                        if (queued[w] + cnt > BP_TIE_QUEUE) {
-                            ++r->tie_queue_drains;
-                            queued[w] = 0;
-                        }
-                        queued[w] += cnt;
-                        wave_words[w] += cnt;
-                        r->tie_queue_words += cnt;
+                    queued += cnt;
+                    tile_words += cnt;
+                    r->tie_queue_words += cnt;
+                    if (n0 + np < n && queued > BP_TIE_QUEUE - BP_THREADS) {
+                        ++r->tie_queue_drains;
+                        queued = 0;
                     }
                 }
             }
-            for (int w = 0; w < BP_WAVES; ++w) r->tie_queue_wave_max = std::max(r->tie_queue_wave_max, wave_words[w]);
+            r->tie_queue_tile_max = std::max(r->tie_queue_tile_max, tile_words);
         }
     }
 

@@ -34,10 +34,10 @@
 #define BP_NEAREST_DEFER 1
 #endif
 #ifndef BP_TIE_QUEUE
-#define BP_TIE_QUEUE 64 // nearest (fp32 ranges): queued tie-decision words per wave, 16 B each, in LDS
+#define BP_TIE_QUEUE 2048 // nearest (fp32 ranges): queued tie-recheck words per workgroup, 18 B each, in LDS
 #endif
-#if BP_TIE_QUEUE != 64
-#error "a chunk adds up to 64 entries (one per lane) to the tie queue, and its drain takes one per lane"
+#if BP_TIE_QUEUE < 2 * BP_THREADS || BP_TIE_QUEUE > 65536
+#error "a chunk adds up to one tie-queue word per lane, and the queue is resolved when it holds more than BP_TIE_QUEUE - BP_THREADS"
 #endif
 #ifndef BP_NEAREST_GROUP
 #define BP_NEAREST_GROUP 4

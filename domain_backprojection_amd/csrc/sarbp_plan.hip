@@ -246,11 +246,11 @@ int sarbp_plan_layout(const sarbp_params& p, int n_cu, BpLayout* L) {
     // the other: constants, window start, bp_ext_doubles fp64 words); the chunk's
     // issue-priority word, its double-buffered mode, tie-band, window and edge words
     // (40 bytes) and the tile's pixel box and reference point (9 doubles); and for
-    // nearest with fp32 ranges each wave's queue of tie decisions (with 16 bytes of
-    // alignment).
+    // nearest with fp32 ranges the workgroup's queue of tie-recheck words (16 bytes
+    // each, a 2-byte owner each, the count, and 16 bytes of alignment).
     const int rec = ((p.dem_relief > 0.0 || L->f64) ? 3 : 2) * 16 + 4 + 8 * bp_ext_doubles(p.interp, L->f64 != 0);
     const int queue =
-        (p.interp == SARBP_NEAREST && !L->f64 && BP_NEAREST_DEFER) ? 16 + BP_WAVES * BP_TIE_QUEUE * 16 : 0;
+        (p.interp == SARBP_NEAREST && !L->f64 && BP_NEAREST_DEFER) ? 16 + BP_TIE_QUEUE * 18 + 4 : 0;
     const int fixed = 40 + 72 + queue;
     const int cap = p.interp == SARBP_NEAREST ? BP_MAX_CHUNK_NEAREST : BP_MAX_CHUNK;
     // Pulses per chunk when every window is the plan's longest.  Coarse grids (long

@@ -103,7 +103,7 @@ class sarbp_index_report(ctypes.Structure):
         ("tie_band_max", ctypes.c_float),
         ("tie_queue_words", ctypes.c_int64),
         ("tie_queue_drains", ctypes.c_int64),
-        ("tie_queue_wave_max", ctypes.c_int32),
+        ("tie_queue_tile_max", ctypes.c_int32),
         ("tie_queue_capacity", ctypes.c_int32),
     ]
 

@@ -302,9 +302,9 @@ typedef struct {
     float tie_band_max;              /* the widest tie band of any chunk [bins] (the fp32 decision is rechecked within it) */
     int64_t tie_queue_words;         /* nearest, fp32 ranges: words queued for the deferred recheck, one per lane and chunk
                                         with a decision inside the band                                                 */
-    int64_t tie_queue_drains;        /* of those queues, drains before the end of a tile (the wave's queue was full)     */
-    int32_t tie_queue_wave_max;      /* the most words one wave queued over the call                                    */
-    int32_t tie_queue_capacity;      /* words per wave the kernels' queue holds                                         */
+    int64_t tie_queue_drains;        /* the workgroups' queues resolved between chunks (more words than a chunk's room)  */
+    int32_t tie_queue_tile_max;      /* the most words one workgroup (one tile) queued over the call                    */
+    int32_t tie_queue_capacity;      /* words per workgroup the kernels' queue holds                                    */
 } sarbp_index_report;
 
 /* Emulate on the host, for the plan `params` would create on a device of n_cu

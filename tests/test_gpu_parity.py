@@ -642,22 +642,65 @@ def test_nearest_index_bit_exact_long_windows(sb, lam, dr, px, ground, height):
 
 @pytest.mark.parametrize("n, na", [(128, 4096), (192, 2048)], ids=["128px-4096p", "192px-2048p"])
 def test_nearest_tie_queue_whole_image(sb, n, na):
-    """Nearest on the standard geometry with many pulses per tile, so that a wave queues
-    more than 64 tie decisions (the drain replays them 64 at a time; the 192-pixel case
-    also drains mid-tile): every pixel against the oracle.  Besides the rel-L2 bar, each
-    pixel must be within 2e-3 of the image's peak magnitude: the fp32 tie band keeps
-    every term's phase error below 2 pi kappa band / 2 (8e-4 rad here), so even a
-    coherent sum of such errors stays below 1.1e-3 of a target's peak."""
+    """Nearest on the standard geometry with many pulses per tile, so that a workgroup queues
+    hundreds of tie rechecks from many waves, resolved by every lane of the workgroup at the
+    tile's end: every pixel against the oracle.  Besides the rel-L2 bar, each pixel must be
+    within 2e-3 of the image's peak magnitude: the fp32 tie band keeps every term's phase
+    error below 2 pi kappa band / 2 (8e-4 rad here), so even a coherent sum of such errors
+    stays below 1.1e-3 of a target's peak."""
     s = synth.make_scene("std", nx=n, ny=n, na=na, interp="nearest")
     rep = sb.sarbp_check_indices(sb.make_params(**s.params()), s.positions)
-    assert rep["tie_queue_wave_max"] > 64, rep
+    assert rep["tie_queue_tile_max"] > 64, rep
     _say(f"[nearest tie queue] {n}x{n} px x {na} pulses: {rep['tie_queue_words']} queued words, "
-         f"{rep['tie_queue_wave_max']} in one wave, {rep['tie_queue_drains']} mid-tile drains")
+         f"{rep['tie_queue_tile_max']} in one tile, {rep['tie_queue_drains']} mid-tile drains")
     got = _run_bp(sb, s)
     want = oracle.scene_backproject(s)
     assert rel_l2(got, want) <= REL_L2, rel_l2(got, want)
     err = np.abs(got - want)
     assert err.max() <= 2e-3 * np.abs(want).max(), (err.max(), np.unravel_index(err.argmax(), err.shape))
+
+
+@pytest.mark.parametrize("lam, dr, px, ground, height", [
+    (0.0556, 0.1, 0.3, 150.0, 120.0),      # C band at 190 m, band ~4e-4: 16 mid-tile drains
+    (0.03125, 0.05, 0.1, 400.0, 300.0),    # X band, 5 cm bins, band ~2.6e-4: 9
+], ids=["C-190m-exact", "X-5cm-exact"])
+def test_nearest_tie_queue_mid_tile_drains(sb, lam, dr, px, ground, height):
+    """Wide fp32 tie bands on 128 x 128 pixels and 2048 pulses of a seeded random echo: some
+    workgroups queue more tie rechecks than a chunk leaves room for, so the queue is resolved
+    between chunks as well as at the tile's end (the host check counts those drains).  The image
+    must equal the sum of the 2048 single-pulse images -- each of which resolves its own queue
+    at its tile's end, and whose every bin the index probes pin to the oracle's -- up to the
+    order of the fp32 additions.  A correction dropped, applied twice or given to another
+    lane moves a pixel by about one echo sample (~1 here, against a bound of 1e-4 of the
+    image's largest magnitude, ~0.02)."""
+    import torch
+
+    na, n, nr = 2048, 128, 8192
+    rc = math.hypot(ground, height)
+    rng = np.random.Generator(np.random.PCG64(11))
+    echo = synth.complex_normal(rng, (na, nr), 1.0).astype(np.complex64)
+    s = synth.Scene(name="ties", seed=11, na=na, nr=nr, nx=n, ny=n, x0=-(n // 2) * px, y0=-(n // 2) * px, z0=0.0,
+                    dx=px, dy=px, r0=rc - (nr // 2) * dr, dr=dr, wavelength=lam, interp="nearest",
+                    positions=_probe_track(na, ground, height), echo=echo, raw=None,
+                    targets=np.zeros((0, 2), np.int64))
+    rep = sb.sarbp_check_indices(sb.make_params(**s.params()), s.positions)
+    assert rep["tie_queue_drains"] > 0 and rep["nearest_escapes"] == 0 and rep["fp64_ranges"] == 0, rep
+    _say(f"[nearest tie queue, mid-tile] lambda {lam} dr {dr} pixel {px}: {rep['tie_queue_words']} queued words, "
+         f"{rep['tie_queue_tile_max']} in one tile, {rep['tie_queue_drains']} mid-tile drains")
+    with sb.Plan.for_scene(s) as plan:
+        pos = torch.from_numpy(s.positions).cuda()
+        ech = torch.from_numpy(echo).cuda()
+        whole = plan.backproject(pos, ech)
+        acc = plan.new_image()
+        for p in range(na):
+            plan.backproject(pos[p:p + 1], ech[p:p + 1], image=acc, accumulate=1)
+        torch.cuda.synchronize()
+        got = whole.cpu().numpy().astype(np.complex128)
+        want = acc.cpu().numpy().astype(np.complex128)
+    err = np.abs(got - want)
+    assert err.max() <= 1e-4 * np.abs(want).max(), (err.max(), np.abs(want).max(),
+                                                     np.unravel_index(err.argmax(), err.shape))
+    assert rel_l2(got, want) <= 1e-5, rel_l2(got, want)
 
 
 # ----------------------------------------------------------------------------- range compression

@@ -44,7 +44,7 @@ def _assert_clean(rep, what):
         assert rep["fp64_ranges"] == 0, (what, rep)
         assert 0 < rep["tie_queue_words"] <= rep["nearest_rechecks"] or rep["nearest_rechecks"] == 0 == rep[
             "tie_queue_words"], (what, rep)
-        assert rep["tie_queue_wave_max"] <= rep["tie_queue_words"], (what, rep)
+        assert rep["tie_queue_tile_max"] <= rep["tie_queue_words"], (what, rep)
     else:
         assert rep["tie_queue_words"] == 0 and rep["tie_queue_drains"] == 0, (what, rep)
 
@@ -73,7 +73,7 @@ def test_scene_geometries(sb, scene, pulses, interp):
     assert rep["max_position_error"] < 1e-5  # ~2^-24 of the window
     if interp == "nearest":
         assert 0 < rep["tie_band_max"] < 4e-5
-        assert rep["tie_queue_capacity"] == 64
+        assert rep["tie_queue_capacity"] == 2048
     else:
         assert rep["tie_queue_capacity"] == 0
 

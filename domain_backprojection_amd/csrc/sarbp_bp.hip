@@ -220,8 +220,8 @@ __device__ __forceinline__ void add_delta(float& ar, float& ai, float& cr, float
 // marks appends one word to the workgroup's queue in LDS: (the chunk's first
 // pulse; the lane, the chunk's accuracy mode, its number of full groups and the
 // wave; the marks; the chunk's tie limit).  A chunk adds at most one word per
-// lane, so the queue holds BP_TIE_QUEUE >= 2 BP_THREADS words and is resolved
-// between chunks once it holds more than BP_TIE_QUEUE - BP_THREADS, and at the end
+// lane, so the queue holds A.tie_queue >= 2 BP_THREADS words and is resolved
+// between chunks once it holds more than A.tie_queue - BP_THREADS, and at the end
 // of the tile (drain_ties).  There every lane of the workgroup takes words of any
 // wave: it repeats the marked pulses' set-up and the owner lane's decisions with
 // the same code and the owner's offsets from the same function (so the same
@@ -233,7 +233,7 @@ __device__ __forceinline__ void add_delta(float& ar, float& ai, float& cr, float
 // order of its chunks).
 static_assert(BP_WAVES <= 16 && BP_MAX_CHUNK_NEAREST / BP_NEAREST_GROUP < 32, "a tie-queue word's wave and group-count fields");
 struct TieQueue {
-    int4* q;             // the workgroup's BP_TIE_QUEUE words in LDS (a word's correction replaces it)
+    int4* q;             // the workgroup's A.tie_queue words in LDS (a word's correction replaces it)
     unsigned short* own; // each word's owner: wave << 6 | lane
     int* count;          // words held (an LDS word)
     int pulse0;          // global index of the chunk's first pulse
@@ -807,8 +807,8 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     constexpr bool QUEUE = INTERP == SARBP_NEAREST && !F64 && BP_NEAREST_DEFER;
     TieQueue tq;
     tq.q = reinterpret_cast<int4*>(smem + ((reinterpret_cast<char*>(box_s + 9) - smem + 15) & ~(ptrdiff_t)15));
-    tq.own = reinterpret_cast<unsigned short*>(tq.q + BP_TIE_QUEUE);
-    tq.count = reinterpret_cast<int*>(tq.own + BP_TIE_QUEUE);
+    tq.own = reinterpret_cast<unsigned short*>(tq.q + A.tie_queue);
+    tq.count = reinterpret_cast<int*>(tq.own + A.tie_queue);
     tq.pulse0 = 0;
     if (tid == 0) {
         if constexpr (QUEUE) *tq.count = 0;
@@ -906,7 +906,7 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
         if constexpr (QUEUE) {
             // resolve the tie queue when it could not take another chunk's words
             const int qn = __builtin_amdgcn_readfirstlane(*tq.count);
-            if (n0 < pend && qn > BP_TIE_QUEUE - BP_THREADS) {
+            if (n0 < pend && qn > A.tie_queue - BP_THREADS) {
                 drain_ties<BP_NEAREST_GROUP, ACC, DEM, PPT>(A, tq, qn, box_s, T, hc, zl, accr, acci, cmpr, cmpi);
                 if (tid == 0) *tq.count = 0; // read again after the next chunk's first barrier
             }

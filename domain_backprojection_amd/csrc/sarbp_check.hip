@@ -210,7 +210,7 @@ struct Checker {
                     queued += cnt;
                     tile_words += cnt;
                     r->tie_queue_words += cnt;
-                    if (n0 + np < n && queued > BP_TIE_QUEUE - BP_THREADS) {
+                    if (n0 + np < n && queued > L.tie_queue - BP_THREADS) {
                         ++r->tie_queue_drains;
                         queued = 0;
                     }
@@ -288,7 +288,7 @@ extern "C" int sarbp_check_indices(const sarbp_params* params, int32_t n_cu, con
     report->chunk = L.chunk;
     report->pixels_per_lane = L.ppt;
     report->fp64_ranges = L.f64;
-    report->tie_queue_capacity = (params->interp == SARBP_NEAREST && !L.f64 && BP_NEAREST_DEFER) ? BP_TIE_QUEUE : 0;
+    report->tie_queue_capacity = L.tie_queue;
     report->min_position = INFINITY;
     report->max_position_margin = -INFINITY;
     Checker c(*params, L, positions_h, n, dem_h, report);

@@ -34,7 +34,7 @@
 #define BP_NEAREST_DEFER 1
 #endif
 #ifndef BP_TIE_QUEUE
-#define BP_TIE_QUEUE 2048 // nearest (fp32 ranges): queued tie-recheck words per workgroup, 18 B each, in LDS
+#define BP_TIE_QUEUE 2048 // nearest (fp32 ranges): queued tie-recheck words per workgroup, at least (18 B each, in LDS)
 #endif
 #if BP_TIE_QUEUE < 2 * BP_THREADS || BP_TIE_QUEUE > 65536
 #error "a chunk adds up to one tie-queue word per lane, and the queue is resolved when it holds more than BP_TIE_QUEUE - BP_THREADS"
@@ -77,6 +77,7 @@ struct BpLayout {
     int margin_lo;    // bins below the tile's lowest range kept in the window
     int chunk;        // pulses per LDS step, at most (the per-pulse record capacity)
     int entries;      // LDS window entries per step, shared by the step's pulses
+    int tie_queue;    // nearest (fp32 ranges): words of the workgroup's tie-recheck queue, else 0
     size_t lds_bytes; // dynamic LDS per workgroup
     double half_span; // half tile diagonal [m]
     // sinc8: monomial coefficients in g = f - 1/2 of the degree-7 interpolant of
@@ -111,6 +112,7 @@ struct BpArgs {
     size_t split_stride;   // complex64 elements between the groups' partial images (0 unsplit)
     int win, margin_lo, chunk, accumulate; // win: the plan's (longest) window; chunk: pulses per step, at most
     int entries;           // LDS window entries per step (a step holds entries / its window pulses)
+    int tie_queue;         // nearest (fp32 ranges): words of the workgroup's tie-recheck queue
     int fast_stage;        // 1: a chunk's records span less than 4 GiB, so staging may use 32-bit byte offsets
     int slots;             // compute units: workgroup b and b + slots usually share a CU
     int* progress;         // [2 * slots] pulse progress per workgroup, read by its CU partner

@@ -247,11 +247,12 @@ int sarbp_plan_layout(const sarbp_params& p, int n_cu, BpLayout* L) {
     // issue-priority word, its double-buffered mode, tie-band, window and edge words
     // (40 bytes) and the tile's pixel box and reference point (9 doubles); and for
     // nearest with fp32 ranges the workgroup's queue of tie-recheck words (16 bytes
-    // each, a 2-byte owner each, the count, and 16 bytes of alignment).
+    // each, a 2-byte owner each, the count, and 16 bytes of alignment): at least
+    // BP_TIE_QUEUE words, and whatever LDS a full chunk's windows leave over.
     const int rec = ((p.dem_relief > 0.0 || L->f64) ? 3 : 2) * 16 + 4 + 8 * bp_ext_doubles(p.interp, L->f64 != 0);
-    const int queue =
-        (p.interp == SARBP_NEAREST && !L->f64 && BP_NEAREST_DEFER) ? 16 + BP_TIE_QUEUE * 18 + 4 : 0;
-    const int fixed = 40 + 72 + queue;
+    int tq = (p.interp == SARBP_NEAREST && !L->f64 && BP_NEAREST_DEFER) ? BP_TIE_QUEUE : 0;
+    const auto fixed_bytes = [](int q) { return 40 + 72 + (q > 0 ? 16 + q * 18 + 4 : 0); };
+    const int fixed = fixed_bytes(tq);
     const int cap = p.interp == SARBP_NEAREST ? BP_MAX_CHUNK_NEAREST : BP_MAX_CHUNK;
     // Pulses per chunk when every window is the plan's longest.  Coarse grids (long
     // windows) that would stage fewer than 8 use up to 150 KiB of LDS: one
@@ -271,9 +272,20 @@ int sarbp_plan_layout(const sarbp_params& p, int n_cu, BpLayout* L) {
         entries = ((avail - 2 * chunk * rec) / eb) & ~1;
     }
     if (entries < L->win) return SARBP_EUNSUPPORTED;
+    // Nearest's chunk is capped by its mark bits, so LDS beyond a full chunk of the
+    // longest windows goes to the tie queue: fewer queue drains between chunks.
+    if (tq > 0 && chunk == cap && avail == BP_LDS_BUDGET - fixed) {
+        const int need = (cap * L->win + 1) & ~1;
+        const int more = std::min((entries - need) * eb / (18 * 64) * 64, 16384 - tq);
+        if (more > 0) {
+            tq += more;
+            entries = ((BP_LDS_BUDGET - fixed_bytes(tq) - 2 * chunk * rec) / eb) & ~1;
+        }
+    }
     L->chunk = chunk;
     L->entries = entries;
-    L->lds_bytes = (size_t)entries * eb + 2 * (size_t)chunk * rec + fixed;
+    L->tie_queue = tq;
+    L->lds_bytes = (size_t)entries * eb + 2 * (size_t)chunk * rec + fixed_bytes(tq);
     return SARBP_OK;
 }
 
@@ -292,6 +304,7 @@ void sarbp_bp_args(const sarbp_params& p, const BpLayout& L, BpArgs* A) {
     A->margin_lo = L.margin_lo;
     A->chunk = L.chunk;
     A->entries = L.entries;
+    A->tie_queue = L.tie_queue;
     A->slots = L.n_cu;
     A->r0 = p.r0;
     A->dr = p.dr;

@@ -73,7 +73,7 @@ def test_scene_geometries(sb, scene, pulses, interp):
     assert rep["max_position_error"] < 1e-5  # ~2^-24 of the window
     if interp == "nearest":
         assert 0 < rep["tie_band_max"] < 4e-5
-        assert rep["tie_queue_capacity"] == 2048
+        assert rep["tie_queue_capacity"] >= 2048 and rep["tie_queue_capacity"] % 64 == 0
     else:
         assert rep["tie_queue_capacity"] == 0
 

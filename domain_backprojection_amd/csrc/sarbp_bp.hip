@@ -276,16 +276,111 @@ __device__ __forceinline__ void lane_offsets(const BpArgs& A, const TileFrame& T
     }
 }
 
+// One pulse's constants and window start for the current tile, as the chunk's
+// set-up forms them (the same code, so the same fp32 values).
+template <bool DEM>
+__device__ __forceinline__ void replay_setup(const BpArgs& A, int n, const double* box_s, float4* cl, int* klo) {
+    const double ax = A.pos[3 * (size_t)n], ay = A.pos[3 * (size_t)n + 1], az = A.pos[3 * (size_t)n + 2];
+    const TileBox box = {box_s[0], box_s[1], box_s[2], box_s[3], box_s[4], box_s[5]};
+    double uc;
+    float rho;
+    pulse_setup(A, ax, ay, az, box_s[6], box_s[7], box_s[8], cl, &uc, &rho, DEM);
+    pulse_window(A, ax, ay, az, box, klo);
+    pulse_finish(A, uc, *klo, cl, DEM, false);
+}
+
 // Resolve the workgroup's queue of qn words into the owners' accumulators (every
 // lane of the workgroup calls it, after a barrier that follows the last append).
 // box_s: the tile's pixel box at [0 .. 5] and reference point at [6 .. 8]; T, hc:
-// the tile frame and mid-height; zl: the layer's height.
+// the tile frame and mid-height; zl: the layer's height; pb, pn: the first pulse
+// and the pulse count of the workgroup's pulse group.
+//
+// Lanes of one row tend to mark the same pulses, so each marked pulse's set-up is
+// made once: a bitmap of the marked pulses (relative to pb) and its prefix counts
+// go to the echo-window LDS (free between chunks), then a table of the marked
+// pulses' constants and window starts, in that LDS after them and in the queue's
+// unused words.  When the table does not fit, each word repeats its pulses' set-up.
 template <int G, int ACC, bool DEM, int PPT>
 __device__ __forceinline__ void drain_ties(const BpArgs& A, const TieQueue& tq, int qn, const double* box_s,
-                                           const TileFrame& T, double hc, double zl, float* accr, float* acci,
-                                           float* cmpr, float* cmpi) {
+                                           const TileFrame& T, double hc, double zl, char* smem, int pb, int pn,
+                                           float* accr, float* acci, float* cmpr, float* cmpi) {
     const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int CS = DEM ? 3 : 2;      // float4 constants per pulse
+    constexpr int TE = CS * 16 + 4;      // table bytes per pulse
     float4* dq = reinterpret_cast<float4*>(tq.q);
+    const int nbw = (pn + 31) >> 5;      // bitmap words
+    uint32_t* bm = reinterpret_cast<uint32_t*>(smem);
+    int* pref = reinterpret_cast<int*>(bm + nbw); // [nbw + 1]: marked pulses before each bitmap word
+    const int head = ((2 * nbw + 1) * 4 + 15) & ~15;
+    const int region = A.entries * entry_bytes<SARBP_NEAREST>();
+    bool table = head <= region;
+    int cap1 = 0, cap2 = 0;
+    if (table) {
+        for (int w = tid; w < nbw; w += BP_THREADS) bm[w] = 0;
+        __syncthreads();
+        for (int e = tid; e < qn; e += BP_THREADS) {
+            const int4 t = tq.q[e];
+            const int nfull = (t.y >> 8) & 31, r0 = t.x - pb;
+            uint32_t marks = (uint32_t)t.z;
+            while (marks != 0) {
+                const int g = __builtin_ctz(marks);
+                marks &= marks - 1;
+                const int r = r0 + (g < nfull ? g * G : nfull * G + (g - nfull)), gsz = g < nfull ? G : 1;
+                const uint64_t bits = ((1ull << gsz) - 1) << (r & 31);
+                atomicOr(&bm[r >> 5], (uint32_t)bits);
+                if (bits >> 32) atomicOr(&bm[(r >> 5) + 1], (uint32_t)(bits >> 32));
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            int run = 0;
+            for (int b = 0; b < nbw; b += 64) {
+                const int w = b + lane;
+                const int c = w < nbw ? __popc(bm[w]) : 0;
+                int x = c; // inclusive prefix over the wave
+#pragma unroll
+                for (int off = 1; off < 64; off <<= 1) {
+                    const int y = __shfl_up(x, off);
+                    if (lane >= off) x += y;
+                }
+                if (w < nbw) pref[w] = run + x - c;
+                run += __shfl(x, 63);
+            }
+            if (lane == 0) pref[nbw] = run;
+        }
+        __syncthreads();
+        const int K = pref[nbw]; // the marked pulses (the same for every lane)
+        cap1 = (region - head) / TE;
+        cap2 = (A.tie_queue - qn) * 16 / TE;
+        table = K <= cap1 + cap2;
+        if (table) {
+            // the k-th marked pulse: the last bitmap word with at most k marks before it, then its bit
+            for (int k = tid; k < K; k += BP_THREADS) {
+                int lo = 0, hi = nbw - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (pref[mid] <= k)
+                        lo = mid;
+                    else
+                        hi = mid - 1;
+                }
+                uint32_t bits = bm[lo];
+                for (int j = k - pref[lo]; j > 0; --j) bits &= bits - 1;
+                float4 cl[3];
+                int klo;
+                replay_setup<DEM>(A, pb + 32 * lo + __builtin_ctz(bits), box_s, cl, &klo);
+                const bool first = k < cap1;
+                float4* tc = first ? reinterpret_cast<float4*>(smem + head) + k * CS
+                                   : reinterpret_cast<float4*>(tq.q + qn) + (k - cap1) * CS;
+                int* tk = first ? reinterpret_cast<int*>(reinterpret_cast<float4*>(smem + head) + cap1 * CS) + k
+                                : reinterpret_cast<int*>(reinterpret_cast<float4*>(tq.q + qn) + cap2 * CS) + (k - cap1);
+#pragma unroll
+                for (int c = 0; c < CS; ++c) tc[c] = cl[c];
+                *tk = klo;
+            }
+        }
+        __syncthreads();
+    }
     for (int e = tid; e < qn; e += BP_THREADS) {
         const int4 t = tq.q[e];
         const int ow = t.y & 63, mode = (t.y >> 6) & 3, nfull = (t.y >> 8) & 31, wo = (t.y >> 13) & 15;
@@ -296,22 +391,30 @@ __device__ __forceinline__ void drain_ties(const BpArgs& A, const TieQueue& tq, 
         lane_offsets<PPT, DEM>(A, T, hc, ow, wo, &o_dx, o_dy, o_dd, o_dz, o_h);
 #pragma unroll
         for (int m = 0; m < PPT; ++m) dr[m] = di[m] = 0.f;
-        const double gx = box_s[6], gy = box_s[7], gz = box_s[8];
-        const TileBox box = {box_s[0], box_s[1], box_s[2], box_s[3], box_s[4], box_s[5]};
         while (marks != 0) {
             const int g = __builtin_ctz(marks);
             marks &= marks - 1;
             const int p0 = g < nfull ? g * G : nfull * G + (g - nfull), gsz = g < nfull ? G : 1;
             for (int q = 0; q < gsz; ++q) {
                 const int n = pulse0 + p0 + q;
-                const double ax = A.pos[3 * (size_t)n], ay = A.pos[3 * (size_t)n + 1], az = A.pos[3 * (size_t)n + 2];
                 float4 cl[3];
-                double uc;
-                float rho;
-                pulse_setup(A, ax, ay, az, gx, gy, gz, cl, &uc, &rho, DEM);
                 int klo;
-                pulse_window(A, ax, ay, az, box, &klo);
-                pulse_finish(A, uc, klo, cl, DEM, false);
+                if (table) {
+                    const int r = n - pb;
+                    const int k = pref[r >> 5] + __popc(bm[r >> 5] & ((1u << (r & 31)) - 1u));
+                    const bool first = k < cap1;
+                    const float4* tc = first ? reinterpret_cast<const float4*>(smem + head) + k * CS
+                                             : reinterpret_cast<const float4*>(tq.q + qn) + (k - cap1) * CS;
+                    const int* tk =
+                        first ? reinterpret_cast<const int*>(reinterpret_cast<const float4*>(smem + head) + cap1 * CS) + k
+                              : reinterpret_cast<const int*>(reinterpret_cast<const float4*>(tq.q + qn) + cap2 * CS) +
+                                    (k - cap1);
+#pragma unroll
+                    for (int c = 0; c < CS; ++c) cl[c] = tc[c];
+                    klo = *tk;
+                } else {
+                    replay_setup<DEM>(A, n, box_s, cl, &klo);
+                }
                 const float4 c0 = cl[0], c1 = cl[1], c2 = DEM ? cl[2] : cl[1];
 #pragma unroll
                 for (int m = 0; m < PPT; ++m) {
@@ -322,6 +425,8 @@ __device__ __forceinline__ void drain_ties(const BpArgs& A, const TieQueue& tq, 
                     const float a = nearest_phase(A.kappa, DevMath::fract(ub));
                     if (!(fabsf(a) > a_lim)) continue;
                     const int kf = (int)DevMath::to_u32(ub) + klo;
+                    const double ax = A.pos[3 * (size_t)n], ay = A.pos[3 * (size_t)n + 1],
+                                 az = A.pos[3 * (size_t)n + 2];
                     const double zp = DEM ? A.z0 + (double)o_h[m] : zl; // the pixel's height
                     const int kd = nearest_bin_fp64<DevMath>(ax, ay, az, A.x0, A.y0, zp, A.dx, A.dy, A.r0, A.dr,
                                                              T.i0 + ow, T.j0 + wo + BP_WAVES * m);
@@ -907,7 +1012,8 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
             // resolve the tie queue when it could not take another chunk's words
             const int qn = __builtin_amdgcn_readfirstlane(*tq.count);
             if (n0 < pend && qn > A.tie_queue - BP_THREADS) {
-                drain_ties<BP_NEAREST_GROUP, ACC, DEM, PPT>(A, tq, qn, box_s, T, hc, zl, accr, acci, cmpr, cmpi);
+                drain_ties<BP_NEAREST_GROUP, ACC, DEM, PPT>(A, tq, qn, box_s, T, hc, zl, smem, pb, pn, accr, acci,
+                                                            cmpr, cmpi);
                 if (tid == 0) *tq.count = 0; // read again after the next chunk's first barrier
             }
         }
@@ -916,7 +1022,8 @@ __global__ __launch_bounds__(BP_THREADS) __attribute__((amdgpu_waves_per_eu(8)))
     if constexpr (QUEUE) {
         const int qn = __builtin_amdgcn_readfirstlane(*tq.count);
         if (qn > 0) {
-            drain_ties<BP_NEAREST_GROUP, ACC, DEM, PPT>(A, tq, qn, box_s, T, hc, zl, accr, acci, cmpr, cmpi);
+            drain_ties<BP_NEAREST_GROUP, ACC, DEM, PPT>(A, tq, qn, box_s, T, hc, zl, smem, pb, pn, accr, acci, cmpr,
+                                                        cmpi);
             if constexpr (ACC == SARBP_ACC_CHUNK64) {
 #pragma unroll
                 for (int m = 0; m < PPT; ++m) {

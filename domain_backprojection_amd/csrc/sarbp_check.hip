@@ -32,7 +32,23 @@ struct Checker {
     int n;
     const float* dem;
     sarbp_index_report* r;
-    unsigned char flagged[BP_WAVES][BP_TX]; // lanes of the current chunk with a decision in the tie band
+    uint32_t flagged[BP_WAVES][BP_TX]; // per lane of the current chunk: its groups of pulses with a decision in the band
+    std::vector<uint32_t> marked;      // the pulses the queued words mark (a bitmap over the call's pulses)
+
+    // A queue resolution of qn words: whether the set-ups of the pulses its words mark
+    // fit the kernels' table (the window LDS after the bitmap and its prefix counts,
+    // and the queue's unused words), as the kernel decides it.
+    void resolve_queue(int qn, bool dem) {
+        int K = 0;
+        for (uint32_t w : marked) K += __builtin_popcount(w);
+        const int nbw = (int)marked.size();
+        const int region = L.entries * entry_bytes<SARBP_NEAREST>();
+        const int head = ((2 * nbw + 1) * 4 + 15) & ~15;
+        const int te = (dem ? 3 : 2) * 16 + 4;
+        const bool table = head <= region && K <= (region - head) / te + (L.tie_queue - qn) * 16 / te;
+        ++(table ? r->tie_queue_tables : r->tie_queue_table_misses);
+        std::fill(marked.begin(), marked.end(), 0u);
+    }
 
     Checker(const sarbp_params& p_, const BpLayout& L_, const double* pos_, int n_, const float* dem_,
             sarbp_index_report* r_)
@@ -150,6 +166,7 @@ struct Checker {
             }
             const int stagger = BP_STAGGER ? ((b / A.slots) ^ (b >> 3)) & 1 : 0;
             int queued = 0, tile_words = 0; // the deferred nearest rechecks' queue (one per workgroup)
+            marked.assign((size_t)(n + 31) / 32, 0u);
             for (int n0 = 0, np = 0, c = 0; n0 < n; n0 += np, ++c) {
                 // the set-up's candidates: constants, u_c and exact window of each; the
                 // chunk's mode, tie-band size and in-record flag over all of them
@@ -205,18 +222,29 @@ struct Checker {
                     // each lane with a decision in the band queues one word; between chunks
                     // the queue is resolved when it has no room for another chunk's words
                     int cnt = 0;
+                    const int nf = np / BP_NEAREST_GROUP;
                     for (int w = 0; w < BP_WAVES; ++w)
-                        for (int lane = 0; lane < BP_TX; ++lane) cnt += flagged[w][lane];
+                        for (int lane = 0; lane < BP_TX; ++lane) {
+                            cnt += flagged[w][lane] != 0;
+                            for (uint32_t g = flagged[w][lane]; g != 0; g &= g - 1) {
+                                const int gi = __builtin_ctz(g);
+                                const int p0 = gi < nf ? gi * BP_NEAREST_GROUP : nf * BP_NEAREST_GROUP + (gi - nf);
+                                for (int q = 0; q < (gi < nf ? BP_NEAREST_GROUP : 1); ++q)
+                                    marked[(n0 + p0 + q) >> 5] |= 1u << ((n0 + p0 + q) & 31);
+                            }
+                        }
                     queued += cnt;
                     tile_words += cnt;
                     r->tie_queue_words += cnt;
                     if (n0 + np < n && queued > L.tie_queue - BP_THREADS) {
                         ++r->tie_queue_drains;
+                        resolve_queue(queued, DEM);
                         queued = 0;
                     }
                 }
             }
             r->tie_queue_tile_max = std::max(r->tie_queue_tile_max, tile_words);
+            if (nearest && !F64 && BP_NEAREST_DEFER && queued > 0) resolve_queue(queued, DEM);
         }
     }
 
@@ -258,7 +286,11 @@ struct Checker {
                         const int kdef = (int)floor(u + 0.5);
                         if (fabsf(nearest_phase(A.kappa, f)) > a_lim) { // the kernel's tie test
                             ++r->nearest_rechecks;
-                            flagged[w][lane] = 1;
+                            {
+                                const int nf = np / BP_NEAREST_GROUP; // the kernel's mark: one bit per group
+                                flagged[w][lane] |= 1u << (t < nf * BP_NEAREST_GROUP ? t / BP_NEAREST_GROUP
+                                                                                     : nf + (t - nf * BP_NEAREST_GROUP));
+                            }
                             const int kr = kdef - klo[t];
                             if (kr < 0 || kr > win_c - 1) ++r->nearest_recheck_clamped;
                         } else if ((int)k + klo[t] != kdef) {

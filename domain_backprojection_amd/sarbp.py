@@ -105,6 +105,8 @@ class sarbp_index_report(ctypes.Structure):
         ("tie_queue_drains", ctypes.c_int64),
         ("tie_queue_tile_max", ctypes.c_int32),
         ("tie_queue_capacity", ctypes.c_int32),
+        ("tie_queue_tables", ctypes.c_int64),
+        ("tie_queue_table_misses", ctypes.c_int64),
     ]
 
     def as_dict(self) -> dict:

@@ -305,6 +305,8 @@ typedef struct {
     int64_t tie_queue_drains;        /* the workgroups' queues resolved between chunks (more words than a chunk's room)  */
     int32_t tie_queue_tile_max;      /* the most words one workgroup (one tile) queued over the call                    */
     int32_t tie_queue_capacity;      /* words per workgroup the kernels' queue holds                                    */
+    int64_t tie_queue_tables;        /* queue resolutions whose marked pulses' set-ups fit a table in LDS               */
+    int64_t tie_queue_table_misses;  /* queue resolutions that repeat each word's set-ups instead (no table fits)        */
 } sarbp_index_report;
 
 /* Emulate on the host, for the plan `params` would create on a device of n_cu

@@ -45,8 +45,12 @@ def _assert_clean(rep, what):
         assert 0 < rep["tie_queue_words"] <= rep["nearest_rechecks"] or rep["nearest_rechecks"] == 0 == rep[
             "tie_queue_words"], (what, rep)
         assert rep["tie_queue_tile_max"] <= rep["tie_queue_words"], (what, rep)
+        # every resolution (between chunks or at a tile's end) either fits the set-up table or replays
+        resolutions = rep["tie_queue_tables"] + rep["tie_queue_table_misses"]
+        assert resolutions >= rep["tie_queue_drains"] and (resolutions > 0) == (rep["tie_queue_words"] > 0), (what, rep)
     else:
         assert rep["tie_queue_words"] == 0 and rep["tie_queue_drains"] == 0, (what, rep)
+        assert rep["tie_queue_tables"] == 0 and rep["tie_queue_table_misses"] == 0, (what, rep)
 
 
 def _scene_geometry(name):

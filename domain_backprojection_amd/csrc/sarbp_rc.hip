@@ -36,6 +36,7 @@ struct RcArgs {
     const float2* raw;
     float2* out;
     const float2* filt; // H[m], 1/N included
+    int n;              // records
 };
 
 __device__ __forceinline__ float2 cmul(float2 a, float2 b) {
@@ -113,7 +114,7 @@ __device__ __forceinline__ void dft<16>(float2* v) {
     }
 }
 
-enum Src { SRC_LDS = 0, SRC_RAW = 1 };
+enum Src { SRC_LDS = 0, SRC_RAW = 1, SRC_REG = 2 };
 enum Dst { DST_LDS = 0, DST_OUT_CONJ = 1 };
 
 constexpr int rc_threads(int log2n) {
@@ -146,13 +147,14 @@ constexpr int rc_pad(int L, bool inv, int p) {
 // (j / Ns) Ns R + k + r Ns.  PADR is the pad unit of the previous pass's writes
 // (0: unpadded), PADW this pass's (see the LDS layout above).
 template <int L, int R, int NS, int SRC, int DST, int PADR, int PADW>
-__device__ __forceinline__ void pass(const RcArgs& A, float2* buf, const float2* rin, float2* rout) {
+__device__ __forceinline__ void pass(const RcArgs& A, float2* buf, const float2* rin, float2* rout, int tx,
+                                     const float2* vreg = nullptr) {
     constexpr int N = 1 << L, T = rc_threads(L), NB = N / R, BPT = (NB + T - 1) / T;
     static_assert(NB % NS == 0, "group size divides the butterfly stride");
     float2 v[BPT][R];
 #pragma unroll
     for (int b = 0; b < BPT; ++b) {
-        const int j = threadIdx.x + b * T;
+        const int j = tx + b * T;
         if (NB % T == 0 || j < NB) {
             // (j + r NB) / Ns = j / Ns + r NB / Ns: the previous writer's pad
             const int rpad = PADR ? PADR * (j / NS) : 0;
@@ -162,6 +164,8 @@ __device__ __forceinline__ void pass(const RcArgs& A, float2* buf, const float2*
                 const int phys = idx + rpad + PADR * (r * NB / NS);
                 if constexpr (SRC == SRC_RAW) {
                     v[b][r] = rin[idx];
+                } else if constexpr (SRC == SRC_REG) {
+                    v[b][r] = vreg[b * R + r]; // the inputs, already loaded (load_record)
                 } else {
                     v[b][r] = buf[phys];
                 }
@@ -169,10 +173,10 @@ __device__ __forceinline__ void pass(const RcArgs& A, float2* buf, const float2*
         }
     }
     // every lane must have read its inputs before any output overwrites them
-    if constexpr (SRC != SRC_RAW && DST == DST_LDS) __syncthreads();
+    if constexpr (SRC == SRC_LDS && DST == DST_LDS) __syncthreads();
 #pragma unroll
     for (int b = 0; b < BPT; ++b) {
-        const int j = threadIdx.x + b * T;
+        const int j = tx + b * T;
         if (NB % T == 0 || j < NB) {
             const int k = j & (NS - 1);
             if constexpr (NS > 1) {
@@ -202,13 +206,13 @@ __device__ __forceinline__ void pass(const RcArgs& A, float2* buf, const float2*
 // Passes P .. PEND - 1 of one transform (forward, or inverse with INV); the first
 // of them reads from SRC0 (or LDS), the transform's last writes to DST_LAST.
 template <int L, bool INV, int P, int PEND, int SRC0, int DST_LAST>
-__device__ __forceinline__ void fft_range(const RcArgs& A, float2* buf, const float2* rin, float2* rout) {
+__device__ __forceinline__ void fft_range(const RcArgs& A, float2* buf, const float2* rin, float2* rout, int tx) {
     if constexpr (P < PEND) {
         constexpr int R = rc_radix_dir(L, INV, P), NS = rc_ns(L, INV, P);
         constexpr bool last = (P == rc_passes(L) - 1);
         pass<L, R, NS, P == 0 ? SRC0 : SRC_LDS, last ? DST_LAST : DST_LDS, P == 0 ? 0 : rc_pad(L, INV, P - 1),
-             rc_pad(L, INV, P)>(A, buf, rin, rout);
-        fft_range<L, INV, P + 1, PEND, SRC0, DST_LAST>(A, buf, rin, rout);
+             rc_pad(L, INV, P)>(A, buf, rin, rout, tx);
+        fft_range<L, INV, P + 1, PEND, SRC0, DST_LAST>(A, buf, rin, rout, tx);
     }
 }
 
@@ -220,7 +224,7 @@ __device__ __forceinline__ void fft_range(const RcArgs& A, float2* buf, const fl
 // values and writes them, padded, for its next pass.  One LDS round trip and its
 // barriers fewer than running the two passes apart.
 template <int L>
-__device__ __forceinline__ void fused_pass(const RcArgs& A, float2* buf) {
+__device__ __forceinline__ void fused_pass(const RcArgs& A, float2* buf, int tx) {
     constexpr int PF = rc_passes(L) - 1; // the forward's last pass
     constexpr int N = 1 << L, R = rc_radix_dir(L, false, PF), NS = rc_ns(L, false, PF);
     constexpr int T = rc_threads(L), NB = N / R, BPT = (NB + T - 1) / T, PADR = PF == 0 ? 0 : rc_pad(L, false, PF - 1);
@@ -229,7 +233,7 @@ __device__ __forceinline__ void fused_pass(const RcArgs& A, float2* buf) {
     float2 v[BPT][R];
 #pragma unroll
     for (int b = 0; b < BPT; ++b) {
-        const int j = threadIdx.x + b * T;
+        const int j = tx + b * T;
         if (NB % T == 0 || j < NB) {
             const int rpad = PADR ? PADR * (j / NS) : 0;
 #pragma unroll
@@ -239,7 +243,7 @@ __device__ __forceinline__ void fused_pass(const RcArgs& A, float2* buf) {
     __syncthreads(); // every lane has read its inputs before any output overwrites them
 #pragma unroll
     for (int b = 0; b < BPT; ++b) {
-        const int j = threadIdx.x + b * T;
+        const int j = tx + b * T;
         if (NB % T == 0 || j < NB) {
             const float step = (float)j * (1.0f / (float)(NS * R)); // k = j (j < Ns)
 #pragma unroll
@@ -261,30 +265,97 @@ __device__ __forceinline__ void fused_pass(const RcArgs& A, float2* buf) {
 
 constexpr size_t rc_lds_bytes(int L) { return ((size_t)1 << L) / 8 * 9 * sizeof(float2); }
 
+// The first pass's inputs of one record: butterfly j's points j + r N/R.
 template <int L>
+__device__ __forceinline__ void load_record(const float2* rin, float2* v, int tx) {
+    constexpr int N = 1 << L, R = rc_radix_dir(L, false, 0), T = rc_threads(L), NB = N / R, BPT = (NB + T - 1) / T;
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) {
+        const int j = tx + b * T;
+        if (NB % T == 0 || j < NB) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) v[b * R + r] = rin[j + r * NB];
+        }
+    }
+}
+
+// One record per workgroup (LOOP false), or (LOOP true) records blockIdx.x,
+// blockIdx.x + gridDim.x, ..., each workgroup loading the next record's
+// first-pass inputs into registers before it transforms the current one, so that
+// record's HBM latency overlaps the LDS passes.  The launch takes the loop when a
+// single record fills a CU's LDS: then nothing else on the CU hides its loads.
+template <int L, bool LOOP>
 __global__ __launch_bounds__(rc_threads(L)) void rc_kernel(RcArgs A) {
     extern __shared__ __align__(16) float2 rc_buf[];
     constexpr size_t N = (size_t)1 << L;
-    const float2* rin = A.raw + (size_t)blockIdx.x * N;
-    float2* rout = A.out + (size_t)blockIdx.x * N;
     constexpr int P = rc_passes(L);
     static_assert(P >= 2, "the fused pass joins two transforms of at least two passes");
-    fft_range<L, false, 0, P - 1, SRC_RAW, DST_LDS>(A, rc_buf, rin, rout); // X = FFT(x), all but its last pass
-    fused_pass<L>(A, rc_buf);                                               // ... its last, * H, conj, inverse first
-    fft_range<L, true, 1, P, SRC_LDS, DST_OUT_CONJ>(A, rc_buf, rin, rout);  // y = conj(FFT(conj(X H)))
+    if constexpr (!LOOP) {
+        const int tx = (int)threadIdx.x;
+        const float2* rin = A.raw + (size_t)blockIdx.x * N;
+        float2* rout = A.out + (size_t)blockIdx.x * N;
+        fft_range<L, false, 0, P - 1, SRC_RAW, DST_LDS>(A, rc_buf, rin, rout, tx); // X = FFT(x), all but its last pass
+        fused_pass<L>(A, rc_buf, tx);                                           // ... its last, * H, conj, inverse first
+        fft_range<L, true, 1, P, SRC_LDS, DST_OUT_CONJ>(A, rc_buf, rin, rout, tx); // y = conj(FFT(conj(X H)))
+    } else {
+        constexpr int R0 = rc_radix_dir(L, false, 0), T = rc_threads(L), NB0 = (int)(N / R0),
+                      BPT0 = (NB0 + T - 1) / T;
+        float2 pre[BPT0 * R0];
+        int rec = blockIdx.x;
+        load_record<L>(A.raw + (size_t)rec * N, pre, (int)threadIdx.x);
+        for (;;) {
+            // the lane index, opaque to the compiler on each record, so that it does
+            // not keep every pass's twiddles in registers across records
+            int tx = (int)threadIdx.x;
+            asm volatile("" : "+v"(tx));
+            float2 v[BPT0 * R0];
+#pragma unroll
+            for (int i = 0; i < BPT0 * R0; ++i) v[i] = pre[i];
+            const int next = rec + (int)gridDim.x;
+            if (next < A.n) load_record<L>(A.raw + (size_t)next * N, pre, tx);
+            float2* rout = A.out + (size_t)rec * N;
+            pass<L, R0, 1, SRC_REG, DST_LDS, 0, rc_pad(L, false, 0)>(A, rc_buf, nullptr, rout, tx, v);
+            fft_range<L, false, 1, P - 1, SRC_LDS, DST_LDS>(A, rc_buf, nullptr, rout, tx);
+            fused_pass<L>(A, rc_buf, tx);
+            fft_range<L, true, 1, P, SRC_LDS, DST_OUT_CONJ>(A, rc_buf, nullptr, rout, tx);
+            if (next >= A.n) break;
+            rec = next;
+            __syncthreads(); // the last pass has read the LDS before the next record's first pass writes it
+        }
+    }
+}
+
+// Workgroups of the one-record kernel resident per CU (bound by LDS for the long
+// records), looked up once.
+template <int L>
+int rc_per_cu() {
+    static const int per_cu = [] {
+        int b = 0;
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, rc_kernel<L, false>, rc_threads(L), rc_lds_bytes(L)) ==
+                           hipSuccess &&
+                       b > 0
+                   ? b
+                   : 1;
+    }();
+    return per_cu;
 }
 
 template <int L>
-int launch(const RcArgs& A, int n, hipStream_t stream) {
-    hipLaunchKernelGGL(rc_kernel<L>, dim3(n), dim3(rc_threads(L)), rc_lds_bytes(L), stream, A);
+int launch(const RcArgs& A, int n, int n_cu, hipStream_t stream) {
+    if (rc_per_cu<L>() == 1 && n_cu > 0 && n > n_cu)
+        hipLaunchKernelGGL((rc_kernel<L, true>), dim3(n_cu), dim3(rc_threads(L)), rc_lds_bytes(L), stream, A);
+    else
+        hipLaunchKernelGGL((rc_kernel<L, false>), dim3(n), dim3(rc_threads(L)), rc_lds_bytes(L), stream, A);
     return hipGetLastError() == hipSuccess ? SARBP_OK : SARBP_EDEVICE;
 }
 
 template <int L>
 int allow_lds() {
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(rc_kernel<L>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)rc_lds_bytes(L)) == hipSuccess
+    const int bytes = (int)rc_lds_bytes(L);
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(rc_kernel<L, false>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess &&
+                   hipFuncSetAttribute(reinterpret_cast<const void*>(rc_kernel<L, true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, bytes) == hipSuccess
                ? SARBP_OK
                : SARBP_EDEVICE;
 }
@@ -302,16 +373,18 @@ int sarbp_launch_rc(const sarbp_plan* plan, const float2* raw, float2* out, int 
     A.raw = raw;
     A.out = out;
     A.filt = plan->rc_filter;
+    A.n = n;
+    const int cu = plan->L.n_cu;
     switch (plan->rc_log2) {
-        case 6: return launch<6>(A, n, stream);
-        case 7: return launch<7>(A, n, stream);
-        case 8: return launch<8>(A, n, stream);
-        case 9: return launch<9>(A, n, stream);
-        case 10: return launch<10>(A, n, stream);
-        case 11: return launch<11>(A, n, stream);
-        case 12: return launch<12>(A, n, stream);
-        case 13: return launch<13>(A, n, stream);
-        case 14: return launch<14>(A, n, stream);
+        case 6: return launch<6>(A, n, cu, stream);
+        case 7: return launch<7>(A, n, cu, stream);
+        case 8: return launch<8>(A, n, cu, stream);
+        case 9: return launch<9>(A, n, cu, stream);
+        case 10: return launch<10>(A, n, cu, stream);
+        case 11: return launch<11>(A, n, cu, stream);
+        case 12: return launch<12>(A, n, cu, stream);
+        case 13: return launch<13>(A, n, cu, stream);
+        case 14: return launch<14>(A, n, cu, stream);
         default: return SARBP_EINVAL;
     }
 }

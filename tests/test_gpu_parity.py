@@ -739,6 +739,28 @@ def test_range_compression_sizes(sb, n_fast, window):
     assert rel_l2(got, want) < 1e-5
 
 
+def test_range_compression_several_records_per_workgroup(sb):
+    """16384-point records fill a CU's LDS, so the launch runs one workgroup per CU and each
+    takes several records in turn, loading the next while it transforms the current one:
+    600 records (2 or 3 per workgroup on 256 CUs, a ragged last round) against the oracle."""
+    import torch
+
+    n_fast, na = 16384, 600
+    rng = np.random.Generator(np.random.PCG64(16384))
+    x = (rng.standard_normal((na, n_fast)) + 1j * rng.standard_normal((na, n_fast))).astype(np.complex64)
+    with sb.Plan(n_pulses=na, n_range=n_fast, r0=0.0, dr=1.0, nx=1, ny=1, x0=0, y0=0, z0=0, dx=1, dy=1,
+                 wavelength=0.03, interp="linear", n_fast=n_fast, fs=synth.FS, chirp_T=synth.CHIRP_T,
+                 chirp_B=synth.BANDWIDTH, window=1) as plan:
+        out = plan.range_compress(torch.from_numpy(x).cuda())
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().astype(np.complex128)
+    want = oracle.rc.range_compress(x, synth.FS, synth.CHIRP_T, synth.BANDWIDTH, 1)
+    assert rel_l2(got, want) < 1e-5
+    # every record on its own, so that a record skipped or written twice cannot hide in the total
+    per = np.linalg.norm(got - want, axis=1) / np.linalg.norm(want, axis=1)
+    assert per.max() < 1e-5, (per.max(), int(per.argmax()))
+
+
 @pytest.mark.parametrize("nbar, sll", [(4, 35.0), (6, 45.0), (3, 25.0)])
 def test_range_compression_taylor_parameters(sb, nbar, sll):
     """The Taylor taper's parameters reach the filter (end-to-end scene's chirp, 8192 samples)."""

@@ -106,6 +106,19 @@ __host__ __device__ __forceinline__ TileBox tile_box(const BpArgs& A, const Tile
     return b;
 }
 
+// A uniform input of the per-pulse set-up, made opaque to the optimiser at each
+// call: quantities derived from it (2 h, h^2, the margins as doubles) are then
+// formed by the set-up lanes where they are used, instead of being computed once
+// before the chunk loop and held in registers across the pulse loop, which has
+// none to spare (they went to scratch).  No effect on the host build.
+template <class T>
+__host__ __device__ __forceinline__ T per_call(T x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+s"(x));
+#endif
+    return x;
+}
+
 // The echo window of one pulse for one tile: the bins floor(u) the tile's pixels
 // can take, u = (R - r0) / dr, from the nearest and the farthest point of the
 // tile's box to the antenna (the nearest: each coordinate clamped into the box;
@@ -123,14 +136,15 @@ __host__ __device__ inline int pulse_window(const BpArgs& A, double ax, double a
                  fz = fmax(fabs(b.za - az), fabs(b.zb - az));
     const double umin = (sqrt(nx * nx + ny * ny + nz * nz) - A.r0) * A.inv_dr;
     const double umax = (sqrt(fx * fx + fy * fy + fz * fz) - A.r0) * A.inv_dr;
-    const double kmin = floor(umin) - (double)A.margin_lo;
-    const double w = floor(umax) - floor(umin) + (double)(A.margin_lo + 3);
+    const int mlo = per_call(A.margin_lo), win = per_call(A.win);
+    const double kmin = floor(umin) - (double)mlo;
+    const double w = floor(umax) - floor(umin) + (double)(mlo + 3);
     if (!(fabs(kmin) < 1.0e9 && w >= 0.0 && w < 2.0e9)) {
         *klo = INT32_MIN;
-        return A.margin_lo + 3;
+        return mlo + 3;
     }
     *klo = (int)kmin;
-    return w < (double)A.win ? (int)w : A.win;
+    return w < (double)win ? (int)w : win;
 }
 
 // Whether a pulse's staged window, with what its staging reads beyond it, lies in
@@ -188,7 +202,7 @@ __host__ __device__ inline int pulse_setup(const BpArgs& A, double ax, double ay
     const double inv_r = 1.0 / Rt;
     const double idr = A.inv_dr;
     // q_m bounds |q| over the tile: |d| <= half_span and |u| = R_t.
-    const double hs = A.half_span;
+    const double hs = per_call(A.half_span);
     const double q = (hs * hs + 2.0 * hs * Rt) * inv_r * inv_r;
     const double a = 0.5 * inv_r * idr;
     cst[0] = make_float4((float)(2.0 * ux), (float)(2.0 * uy), 0.f, (float)a); // .z: ft, set by pulse_finish
@@ -223,7 +237,7 @@ __host__ __device__ inline void pulse_finish(const BpArgs& A, double uc, int klo
         }
         return;
     }
-    const double ft = uc - (double)klo + (A.round_half ? 0.5 : 0.0);
+    const double ft = uc - (double)klo + (per_call(A.round_half) ? 0.5 : 0.0);
     if (f64)
         reinterpret_cast<double2*>(cst)[1].x = ft;
     else
@@ -248,7 +262,7 @@ __host__ __device__ inline int pulse_setup_f64(const BpArgs& A, double ax, doubl
         return 0;
     }
     const double inv_r = 1.0 / Rt;
-    const double hs = A.half_span;
+    const double hs = per_call(A.half_span);
     const double q = (hs * hs + 2.0 * hs * Rt) * inv_r * inv_r;
     cd[0] = make_double2(2.0 * ux, 2.0 * uy);
     cd[1] = make_double2(0.0, inv_r * inv_r); // .x: ft, set by pulse_finish

@@ -147,8 +147,7 @@ constexpr int rc_pad(int L, bool inv, int p) {
 // (j / Ns) Ns R + k + r Ns.  PADR is the pad unit of the previous pass's writes
 // (0: unpadded), PADW this pass's (see the LDS layout above).
 template <int L, int R, int NS, int SRC, int DST, int PADR, int PADW>
-__device__ __forceinline__ void pass(const RcArgs& A, float2* buf, const float2* rin, float2* rout, int tx,
-                                     const float2* vreg = nullptr) {
+__device__ __forceinline__ void pass(float2* buf, const float2* rin, float2* rout, int tx, const float2* vreg = nullptr) {
     constexpr int N = 1 << L, T = rc_threads(L), NB = N / R, BPT = (NB + T - 1) / T;
     static_assert(NB % NS == 0, "group size divides the butterfly stride");
     float2 v[BPT][R];
@@ -211,7 +210,7 @@ __device__ __forceinline__ void fft_range(const RcArgs& A, float2* buf, const fl
         constexpr int R = rc_radix_dir(L, INV, P), NS = rc_ns(L, INV, P);
         constexpr bool last = (P == rc_passes(L) - 1);
         pass<L, R, NS, P == 0 ? SRC0 : SRC_LDS, last ? DST_LAST : DST_LDS, P == 0 ? 0 : rc_pad(L, INV, P - 1),
-             rc_pad(L, INV, P)>(A, buf, rin, rout, tx);
+             rc_pad(L, INV, P)>(buf, rin, rout, tx);
         fft_range<L, INV, P + 1, PEND, SRC0, DST_LAST>(A, buf, rin, rout, tx);
     }
 }
@@ -314,7 +313,7 @@ __global__ __launch_bounds__(rc_threads(L)) void rc_kernel(RcArgs A) {
             const int next = rec + (int)gridDim.x;
             if (next < A.n) load_record<L>(A.raw + (size_t)next * N, pre, tx);
             float2* rout = A.out + (size_t)rec * N;
-            pass<L, R0, 1, SRC_REG, DST_LDS, 0, rc_pad(L, false, 0)>(A, rc_buf, nullptr, rout, tx, v);
+            pass<L, R0, 1, SRC_REG, DST_LDS, 0, rc_pad(L, false, 0)>(rc_buf, nullptr, rout, tx, v);
             fft_range<L, false, 1, P - 1, SRC_LDS, DST_LDS>(A, rc_buf, nullptr, rout, tx);
             fused_pass<L>(A, rc_buf, tx);
             fft_range<L, true, 1, P, SRC_LDS, DST_OUT_CONJ>(A, rc_buf, nullptr, rout, tx);

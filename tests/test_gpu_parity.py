@@ -660,16 +660,19 @@ def test_nearest_tie_queue_whole_image(sb, n, na):
     assert err.max() <= 2e-3 * np.abs(want).max(), (err.max(), np.unravel_index(err.argmax(), err.shape))
 
 
-@pytest.mark.parametrize("lam, dr, px, ground, height, table", [
-    (0.0556, 0.1, 0.3, 150.0, 120.0, "all"),       # C band at 190 m, band ~4e-4: 16 mid-tile drains
-    (0.03125, 0.05, 0.1, 400.0, 300.0, "some"),    # X band, 5 cm bins, band ~2.6e-4: 9
-], ids=["C-190m-exact", "X-5cm-exact"])
-def test_nearest_tie_queue_mid_tile_drains(sb, lam, dr, px, ground, height, table):
+@pytest.mark.parametrize("lam, dr, px, ground, height, table, accum", [
+    (0.0556, 0.1, 0.3, 150.0, 120.0, "all", "fp32"),       # C band at 190 m, band ~4e-4: 16 mid-tile drains
+    (0.03125, 0.05, 0.1, 400.0, 300.0, "some", "fp32"),    # X band, 5 cm bins, band ~2.6e-4: 9
+    (0.0556, 0.1, 0.3, 150.0, 120.0, "all", "kahan"),
+    (0.0556, 0.1, 0.3, 150.0, 120.0, "all", "chunk64"),
+], ids=["C-190m-exact", "X-5cm-exact", "C-190m-exact-kahan", "C-190m-exact-chunk64"])
+def test_nearest_tie_queue_mid_tile_drains(sb, lam, dr, px, ground, height, table, accum):
     """Wide fp32 tie bands on 128 x 128 pixels and 2048 pulses of a seeded random echo: some
     workgroups queue more tie rechecks than a chunk leaves room for, so the queue is resolved
     between chunks as well as at the tile's end (the host check counts those drains).  On the X-band
     geometry some resolutions mark more pulses than the LDS set-up table holds and repeat each
-    word's set-ups instead, so both ways of resolving the queue are exercised.  The image
+    word's set-ups instead, so both ways of resolving the queue are exercised; the compensated
+    and chunk-fp64 accumulators take the corrections between chunks as well.  The image
     must equal the sum of the 2048 single-pulse images -- each of which resolves its own queue
     at its tile's end, and whose every bin the index probes pin to the oracle's -- up to the
     order of the fp32 additions.  A correction dropped, applied twice or given to another
@@ -691,7 +694,7 @@ def test_nearest_tie_queue_mid_tile_drains(sb, lam, dr, px, ground, height, tabl
     _say(f"[nearest tie queue, mid-tile] lambda {lam} dr {dr} pixel {px}: {rep['tie_queue_words']} queued words, "
          f"{rep['tie_queue_tile_max']} in one tile, {rep['tie_queue_drains']} mid-tile drains, "
          f"{rep['tie_queue_tables']} resolutions by set-up table, {rep['tie_queue_table_misses']} by replay")
-    with sb.Plan.for_scene(s) as plan:
+    with sb.Plan.for_scene(s, accum=accum) as plan:
         pos = torch.from_numpy(s.positions).cuda()
         ech = torch.from_numpy(echo).cuda()
         whole = plan.backproject(pos, ech)
